@@ -1,0 +1,109 @@
+"""Brute force for tiny inputs: every op evaluated at 50 significant digits with mpmath and
+rounded to the output format with exact rational arithmetic (``fractions.Fraction``).
+
+This is deliberately a different computation from the oracle: no numpy, no float64
+intermediates, and its own round-to-nearest-even written on exact rationals (find the
+binade, scale to an integer grid, compare the remainder with one half).
+"""
+
+from fractions import Fraction
+
+import mpmath
+
+mpmath.mp.dps = 50
+
+# (significant bits, exponent of the smallest quantum, overflow threshold exponent)
+FORMATS = {
+    "bf16": (8, -133, 128),
+    "f32": (24, -149, 128),
+}
+
+
+def _binade(a: Fraction) -> int:
+    """e with 2**e <= a < 2**(e+1), for a > 0."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def round_fraction(q: Fraction, fmt: str):
+    """Nearest value of ``fmt`` to the exact rational q, ties to even; ±inf on overflow."""
+    p, qmin, ovf = FORMATS[fmt]
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    qe = max(_binade(a) - (p - 1), qmin)
+    scaled = a / Fraction(2) ** qe
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = Fraction(n) * Fraction(2) ** qe
+    if r >= Fraction(2) ** ovf:
+        return sign * float("inf")
+    return sign * float(r)
+
+
+def mpf_to_fraction(v) -> Fraction:
+    """Exact value of an mpf: (-1)^sign * man * 2^exp from its raw tuple."""
+    sign, man, exp, _ = mpmath.mpf(v)._mpf_
+    q = Fraction(man) * Fraction(2) ** exp if exp >= 0 else Fraction(man, 2 ** (-exp))
+    return -q if sign else q
+
+
+def round_mp(v, fmt):
+    return round_fraction(mpf_to_fraction(v), fmt)
+
+
+def f32(v):
+    import struct
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def rms_row(x, w, eps):
+    d = len(x)
+    xs = [mpmath.mpf(v) for v in x]
+    ms = mpmath.fsum(v * v for v in xs) / d
+    den = mpmath.sqrt(ms + mpmath.mpf(f32(eps)))
+    return [xs[j] / den * (mpmath.mpf(w[j]) if w is not None else 1) for j in range(d)]
+
+
+def layer_row(x, w, b, eps):
+    d = len(x)
+    xs = [mpmath.mpf(v) for v in x]
+    mu = mpmath.fsum(xs) / d
+    var = mpmath.fsum((v - mu) ** 2 for v in xs) / d
+    den = mpmath.sqrt(var + mpmath.mpf(f32(eps)))
+    out = []
+    for j in range(d):
+        y = (xs[j] - mu) / den
+        if w is not None:
+            y *= mpmath.mpf(w[j])
+        if b is not None:
+            y += mpmath.mpf(b[j])
+        out.append(y)
+    return out
+
+
+def rope_row(x, w, *, normalize, eps, dims, traditional, base, scale, pos, forward):
+    """One [D] row rotated at integer position ``pos``."""
+    d = len(x)
+    xs = rms_row(x, w, eps) if normalize else [mpmath.mpf(v) for v in x]
+    out = list(xs)
+    half = dims // 2
+    for i in range(half):
+        theta = mpmath.power(mpmath.mpf(f32(base)), mpmath.mpf(-2 * i) / dims)
+        a = mpmath.mpf(f32(scale)) * pos * theta
+        c, s = mpmath.cos(a), mpmath.sin(a)
+        if not forward:
+            s = -s
+        iu, iv = (2 * i, 2 * i + 1) if traditional else (i, i + half)
+        u, v = xs[iu], xs[iv]
+        out[iu] = u * c - v * s
+        out[iv] = u * s + v * c
+    assert len(out) == d
+    return out

@@ -1,0 +1,474 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Every pin is a function of the oracle module, so the same pins run against the real oracle
+(``test_oracle_pins.py``) and against copies of it with a planted mistake
+(``test_oracle_mutants.py``, which demands that every planted mistake fails some pin).
+
+What pins what:
+  * rounding      -- torch's float32 -> bfloat16 cast (a library routine) on float32 inputs;
+                     exact rational rounding (``brute.round_fraction``) on float64 inputs,
+                     including the double-rounding hazards;
+  * RmsNorm       -- hand-worked fixtures, the constant-row closed form, mean(out^2) =
+                     ms/(ms+eps), power-of-two scale invariance (bit-exact), torch's
+                     ``rms_norm`` in float64, 50-digit brute force;
+  * AddRmsNorm    -- hand-worked fixtures, h against torch's float32 add + cast, out against
+                     RmsNorm of the returned h, 50-digit brute force;
+  * LayerNorm     -- hand-worked fixtures, constant row gives b, no-affine moments,
+                     torch's ``layer_norm`` in float64, 50-digit brute force;
+  * NormRope      -- hand-worked fixtures (cos 1, sin 1 ...), identity at position 0,
+                     per-pair norm preservation, inverse undoes forward, half/interleaved
+                     permutation, relative-position property, cache placement, RMS over
+                     all D, 50-digit brute force.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _vals(strs):
+    return None if strs is None else np.array([float(Fraction(s)) for s in strs])
+
+
+def _rng(seed=1234):
+    return np.random.default_rng(seed)
+
+
+def _bf16_values(a):
+    """Round arbitrary draws onto the bf16 grid with torch (input preparation only)."""
+    t = torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def _f32_values(a):
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    ok = np.abs(a - b) <= atol + rtol * np.abs(b)
+    assert ok.all(), f"{what}: max abs diff {np.max(np.abs(a - b))}"
+
+
+def _same_values(a, b, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    ok = (a == b) | (np.isnan(a) & np.isnan(b))
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} values differ"
+
+
+# ------------------------------------------------------------------------------ rounding
+
+def pin_round_bf16_matches_torch_on_f32(o):
+    """Every float32 input (random bit patterns across all exponents, plus ties, subnormals
+    and the overflow edge) rounds as torch's float32 -> bfloat16 cast does."""
+    rng = _rng(1)
+    bits = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2**16, size=20_000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    special = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF, 0xFF7F8000, 0x00008000, 0x00018000,
+                        0x80008000, 0x00000001, 0x3F808000, 0x3F818000, 0x00000000, 0x80000000,
+                        0x7F800000, 0xFF800000], dtype=np.uint32)
+    allbits = np.concatenate([bits, ties, special])
+    v = allbits.view(np.float32)
+    v = v[~np.isnan(v)]
+    want = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = o.bf16_bits(o.round_bf16(v.astype(np.float64)))
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} mismatches"
+
+
+def pin_round_exact_on_f64(o):
+    """float64 inputs (not float32 values) round to the nearest bf16 / fp32 value of the
+    exact input, ties to even, as exact rational arithmetic decides. Includes values a hair
+    past a bf16 midpoint whose float32 rounding would land on the midpoint (the double
+    rounding trap) and exact midpoints."""
+    rng = _rng(2)
+    cases = list(rng.standard_normal(3000) * np.exp2(rng.integers(-140, 130, 3000)))
+    for m in range(1, 64):
+        mid = 1.0 + (2 * m + 1) * 2.0 ** -8
+        cases += [mid, mid + 2.0 ** -40, mid - 2.0 ** -40, -mid, -(mid + 2.0 ** -40)]
+        cases += [mid * 2.0 ** -130, (mid + 2.0 ** -30) * 2.0 ** -131]
+    f32mid = 1.0 + 2.0 ** -24
+    cases += [f32mid, f32mid + 2.0 ** -50, 1.0 + 3 * 2.0 ** -24, 3.4e38, 3.403e38, 1e-45, 7e-46]
+    for y in cases:
+        for fmt, fn in (("bf16", o.round_bf16), ("f32", o.round_f32)):
+            want = brute.round_fraction(Fraction(y), fmt)
+            got = float(fn(np.array([y]))[0])
+            assert got == want, (fmt, y, got, want)
+
+
+def pin_round_specials(o):
+    """NaN stays NaN, infinities stay, the sign of zero and of tiny values is kept."""
+    y = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, -1e-300, 1e-300])
+    for fn in (o.round_bf16, o.round_f32):
+        r = fn(y)
+        assert np.isnan(r[0]) and r[1] == np.inf and r[2] == -np.inf
+        assert np.signbit(r[4]) and not np.signbit(r[3])
+        assert r[5] == 0 and np.signbit(r[5]) and r[6] == 0 and not np.signbit(r[6])
+
+
+# ------------------------------------------------------------------------------- RmsNorm
+
+def pin_rms_golden(o):
+    g = _golden("rms_norm_hand.json")
+    for c in g["cases"]:
+        x = _vals(c["x"])[None, :]
+        w = _vals(c["w"])
+        want = _vals(c["expect"])
+        got = o.rms_norm(x, w, c["eps"], "f64")[0]
+        _close(got, want, 1e-15, 1e-300, c["why"])
+        for dt in ("bf16", "f32"):
+            gr = o.rms_norm(x, w, c["eps"], dt)[0]
+            exp = [brute.round_fraction(Fraction(s), dt) for s in c["expect"]]
+            _same_values(gr, exp, c["why"])
+
+
+def pin_rms_constant_row(o):
+    """x = c everywhere: out_j = w_j c / sqrt(c^2 + eps), eps taken as its float32 value."""
+    rng = _rng(3)
+    for c in (1.0, -3.25, 1e-3, 7e4, 2.0 ** -20):
+        for eps in (1e-6, 1e-5, 0.1):
+            w = rng.uniform(0.5, 1.5, 16)
+            x = np.full((1, 16), c)
+            got = o.rms_norm(x, w, eps, "f64")[0]
+            e = float(np.float32(eps))
+            want = w * c / math.sqrt(c * c + e)
+            _close(got, want, 1e-14, 0, f"c={c} eps={eps}")
+
+
+def pin_rms_mean_square(o):
+    """With w = 1: mean(out^2) = ms / (ms + eps)."""
+    rng = _rng(4)
+    x = rng.standard_normal((32, 300)) * np.exp(rng.uniform(-6, 6, (32, 1)))
+    for eps in (1e-6, 1e-2, 0.5):
+        out = o.rms_norm(x, None, eps, "f64")
+        ms = np.mean(x * x, axis=-1)
+        e = float(np.float32(eps))
+        _close(np.mean(out * out, axis=-1), ms / (ms + e), 1e-12, 0, f"eps={eps}")
+
+
+def pin_rms_scale_invariance(o):
+    """eps = 0: RMSNorm(alpha x) == RMSNorm(x) bit for bit for alpha = 2^k (every step scales
+    exactly), and to 1e-13 for other alpha."""
+    rng = _rng(5)
+    x = _bf16_values(rng.standard_normal((16, 256)))
+    w = _bf16_values(rng.normal(1, 0.1, 256))
+    for dt in ("bf16", "f32", "f64"):
+        base = o.rms_norm(x, w, 0.0, dt)
+        for k in (-7, -1, 1, 5, 20):
+            _same_values(o.rms_norm(x * 2.0 ** k, w, 0.0, dt), base, f"2^{k} {dt}")
+    base = o.rms_norm(x, w, 0.0, "f64")
+    for alpha in (3.0, -0.7, 1e5):
+        _close(o.rms_norm(x * alpha, w, 0.0, "f64"), np.sign(alpha) * base, 1e-13, 1e-300)
+
+
+def pin_rms_torch(o):
+    """torch.nn.functional.rms_norm in float64 on the CPU (an independent library routine)."""
+    rng = _rng(6)
+    for d in (1, 7, 64, 1000):
+        x = rng.standard_normal((9, d)) * 3
+        w = rng.normal(1, 0.2, d)
+        for eps in (1e-6, 1e-5, 0.25):
+            e = float(np.float32(eps))
+            want = torch.nn.functional.rms_norm(torch.from_numpy(x), (d,), torch.from_numpy(w),
+                                                eps=e).numpy()
+            _close(o.rms_norm(x, w, eps, "f64"), want, 1e-13, 1e-300, f"d={d}")
+            want1 = torch.nn.functional.rms_norm(torch.from_numpy(x), (d,), None, eps=e).numpy()
+            _close(o.rms_norm(x, None, eps, "f64"), want1, 1e-13, 1e-300, f"d={d} no w")
+
+
+def pin_rms_brute(o):
+    """2 x 8 inputs against the 50-digit evaluation, rounded exactly."""
+    rng = _rng(7)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        for eps in (1e-6, 0.3):
+            x = cast(rng.standard_normal((2, 8)) * 2)
+            w = cast(rng.uniform(0.5, 1.5, 8))
+            got = o.rms_norm(x, w, eps, dt)
+            for i in range(2):
+                want = [brute.round_mp(v, dt) for v in brute.rms_row(x[i], w, eps)]
+                _same_values(got[i], want, f"{dt} row {i}")
+
+
+# ---------------------------------------------------------------------------- AddRmsNorm
+
+def pin_add_golden(o):
+    g = _golden("add_rms_norm_hand.json")
+    for c in g["cases"]:
+        x = _vals(c["x"])[None, :]
+        r = _vals(c["r"])[None, :]
+        out, h = o.add_rms_norm(x, r, _vals(c["w"]), c["eps"], c["dtype"])
+        _same_values(h[0], _vals(c["expect_h"]), c["why"])
+        if c["expect"] is not None:
+            exp = [brute.round_fraction(Fraction(s), c["dtype"]) for s in c["expect"]]
+            _same_values(out[0], exp, c["why"])
+
+
+def pin_add_residual_torch(o):
+    """h equals torch's (x.float() + r.float()).to(dtype) bit for bit: one float32 add then
+    one rounding is the correctly rounded sum for these formats."""
+    rng = _rng(8)
+    for dt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        for scale in (1.0, 1e3, 1e-30):
+            xt = torch.from_numpy(rng.standard_t(3, (64, 96)) * scale).to(tdt)
+            rt = torch.from_numpy(rng.standard_t(3, (64, 96)) * scale).to(tdt)
+            want = (xt.float() + rt.float()).to(tdt).to(torch.float64).numpy()
+            _, h = o.add_rms_norm(xt.to(torch.float64).numpy(), rt.to(torch.float64).numpy(),
+                                  None, 1e-6, dt)
+            _same_values(h, want, f"{dt} scale {scale}")
+
+
+def pin_add_normalises_returned_h(o):
+    """out is RmsNorm of the returned (rounded) h, bit for bit."""
+    rng = _rng(9)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        x = cast(rng.standard_normal((64, 40)))
+        r = cast(rng.standard_normal((64, 40)))
+        w = cast(rng.uniform(0.5, 1.5, 40))
+        out, h = o.add_rms_norm(x, r, w, 1e-6, dt)
+        _same_values(out, o.rms_norm(h, w, 1e-6, dt), dt)
+
+
+def pin_add_brute(o):
+    rng = _rng(10)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        x = cast(rng.standard_normal((2, 8)))
+        r = cast(rng.standard_normal((2, 8)))
+        w = cast(rng.normal(1, 0.1, 8))
+        out, h = o.add_rms_norm(x, r, w, 1e-6, dt)
+        for i in range(2):
+            hs = [brute.round_fraction(Fraction(float(a)) + Fraction(float(b)), dt)
+                  for a, b in zip(x[i], r[i])]
+            _same_values(h[i], hs, "h")
+            want = [brute.round_mp(v, dt) for v in brute.rms_row(hs, w, 1e-6)]
+            _same_values(out[i], want, f"{dt} row {i}")
+
+
+# ----------------------------------------------------------------------------- LayerNorm
+
+def pin_ln_golden(o):
+    g = _golden("layer_norm_hand.json")
+    for c in g["cases"]:
+        x = _vals(c["x"])[None, :]
+        got = o.layer_norm(x, _vals(c["w"]), _vals(c["b"]), c["eps"], "f64")[0]
+        if "expect" in c:
+            _close(got, _vals(c["expect"]), 1e-15, 1e-300, c["why"])
+        else:
+            _close(got, np.array([float(s) for s in c["expect_decimal"]]), 1e-15, 0, c["why"])
+
+
+def pin_ln_constant_row(o):
+    """A constant row of bf16 values gives exactly b (and 0 without b)."""
+    rng = _rng(11)
+    for d in (1, 5, 4096, 8192):
+        c = float(_bf16_values([rng.normal(0.5, 2)])[0])
+        x = np.full((2, d), c)
+        w = _bf16_values(rng.normal(1, 0.1, d))
+        b = _bf16_values(rng.normal(0, 0.1, d))
+        for dt in ("bf16", "f32"):
+            _same_values(o.layer_norm(x, w, b, 1e-5, dt)[0], b, f"d={d}")
+            assert np.all(o.layer_norm(x, w, None, 1e-5, dt) == 0)
+
+
+def pin_ln_moments(o):
+    """Without affine: mean(out) = 0 and mean(out^2) = v / (v + eps), v the biased variance."""
+    rng = _rng(12)
+    x = rng.normal(0.5, 2, (16, 513)) + rng.normal(0, 50, (16, 1))
+    for eps in (1e-5, 0.5):
+        out = o.layer_norm(x, None, None, eps, "f64")
+        v = np.var(x, axis=-1)
+        e = float(np.float32(eps))
+        _close(np.mean(out, axis=-1), np.zeros(16), 0, 1e-13, "mean")
+        _close(np.mean(out * out, axis=-1), v / (v + e), 1e-12, 0, "variance")
+
+
+def pin_ln_torch(o):
+    """torch.nn.functional.layer_norm in float64 on the CPU, affine, scale-only and none."""
+    rng = _rng(13)
+    for d in (2, 33, 1024):
+        x = rng.normal(0.5, 2, (7, d))
+        w = rng.normal(1, 0.1, d)
+        b = rng.normal(0, 0.1, d)
+        for eps in (1e-5, 0.1):
+            e = float(np.float32(eps))
+            for ww, bb in ((w, b), (w, None), (None, None)):
+                want = torch.nn.functional.layer_norm(
+                    torch.from_numpy(x), (d,),
+                    None if ww is None else torch.from_numpy(ww),
+                    None if bb is None else torch.from_numpy(bb), eps=e).numpy()
+                _close(o.layer_norm(x, ww, bb, eps, "f64"), want, 1e-12, 1e-14, f"d={d}")
+
+
+def pin_ln_brute(o):
+    rng = _rng(14)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        x = cast(rng.normal(0.5, 2, (2, 8)))
+        w = cast(rng.normal(1, 0.1, 8))
+        b = cast(rng.normal(0, 0.1, 8))
+        for ww, bb in ((w, b), (None, None)):
+            got = o.layer_norm(x, ww, bb, 1e-5, dt)
+            for i in range(2):
+                want = [brute.round_mp(v, dt) for v in brute.layer_row(x[i], ww, bb, 1e-5)]
+                _same_values(got[i], want, f"{dt} row {i}")
+
+
+# ------------------------------------------------------------------------------ NormRope
+
+def _rope(o, x, w=None, **kw):
+    args = dict(normalize=True, eps=1e-6, dims=x.shape[-1], traditional=False, base=10000.0,
+                scale=1.0, offset=0, forward=True, dtype="f64")
+    args.update(kw)
+    return o.norm_rope(x, w, **args)
+
+
+def pin_rope_golden(o):
+    g = _golden("rope_hand.json")
+    for c in g["cases"]:
+        x = _vals(c["x"]).reshape(1, 1, 1, -1)
+        got = _rope(o, x, None, normalize=c["normalize"], eps=c.get("eps", 0.0), dims=c["dims"],
+                    traditional=c["traditional"], base=c["base"], scale=c["scale"],
+                    offset=c["offset"], forward=c["forward"])[0, 0, 0]
+        if "expect" in c:
+            _close(got, _vals(c["expect"]), 1e-15, 1e-300, c["why"])
+        else:
+            _close(got, np.array([float(s) for s in c["expect_decimal"]]), 1e-14, 1e-15, c["why"])
+
+
+def pin_rope_frequencies(o):
+    """theta_i against 50-digit powers, and angle = scale * position * theta_i."""
+    for dims, base in ((128, 10000.0), (64, 500000.0), (6, 3.0)):
+        th = o.rope_frequencies(dims, base)
+        assert th.shape == (dims // 2,)
+        want = [float(brute.mpmath.power(brute.f32(base), brute.mpmath.mpf(-2 * i) / dims))
+                for i in range(dims // 2)]
+        _close(th, want, 4.5e-16, 0, f"dims={dims}")
+    a = o.rope_angles([0, 5, 1535], 128, 10000.0, 0.75)
+    _close(a[2], 0.75 * 1535 * o.rope_frequencies(128, 10000.0), 4.5e-16, 0, "angles")
+    _close(a[:, 0], [0.0, 3.75, 0.75 * 1535], 0, 0, "pair 0 angle is scale * position")
+
+
+def pin_rope_identity_at_zero(o):
+    """Position 0 (offset 0, l = 0) is RmsNorm of the row; other positions are not."""
+    rng = _rng(15)
+    x = _bf16_values(rng.standard_normal((2, 3, 4, 64)))
+    w = _bf16_values(rng.uniform(0.5, 1.5, 64))
+    for trad in (False, True):
+        for dt in ("bf16", "f32", "f64"):
+            y = _rope(o, x, w, traditional=trad, dtype=dt)
+            _same_values(y[:, :, 0], o.rms_norm(x[:, :, 0], w, 1e-6, dt), "p=0")
+            assert not np.array_equal(y[:, :, 1], o.rms_norm(x[:, :, 1], w, 1e-6, dt))
+
+
+def pin_rope_norm_preserving(o):
+    """Each pair keeps its length: u'^2 + v'^2 = u^2 + v^2."""
+    rng = _rng(16)
+    x = rng.standard_normal((2, 2, 8, 32))
+    for trad in (False, True):
+        xn = _rope(o, x, None, normalize=False, offset=900, scale=1.5, traditional=trad)
+        idx = np.arange(16)
+        iu, iv = (2 * idx, 2 * idx + 1) if trad else (idx, idx + 16)
+        _close(xn[..., iu] ** 2 + xn[..., iv] ** 2, x[..., iu] ** 2 + x[..., iv] ** 2, 1e-12, 1e-14)
+        assert not np.allclose(xn, x)
+
+
+def pin_rope_inverse(o):
+    """forward=false undoes forward=true (the normalised row comes back)."""
+    rng = _rng(17)
+    x = rng.standard_normal((2, 2, 16, 48))
+    w = rng.uniform(0.5, 1.5, 48)
+    for trad in (False, True):
+        for dims in (48, 32, 0):
+            kw = dict(dims=dims, traditional=trad, offset=1024, base=5000.0, scale=0.9)
+            y = _rope(o, x, w, **kw)
+            back = _rope(o, y, None, normalize=False, forward=False, **kw)
+            _close(back, _rope(o, x, w, **dict(kw, offset=0, scale=0.0)), 1e-12, 1e-13)
+
+
+def pin_rope_half_vs_interleaved(o):
+    """Interleaved mode equals half mode on the first dims features de-interleaved."""
+    rng = _rng(18)
+    D, dims = 40, 24
+    x = rng.standard_normal((1, 2, 5, D))
+    w = rng.uniform(0.5, 1.5, D)
+    perm = np.concatenate([np.arange(0, dims, 2), np.arange(1, dims, 2), np.arange(dims, D)])
+    inv = np.argsort(perm)
+    a = _rope(o, x, w, dims=dims, traditional=True, offset=3)
+    b = _rope(o, x[..., perm], w[perm], dims=dims, traditional=False, offset=3)[..., inv]
+    _close(a, b, 1e-13, 1e-15)  # the sum of squares runs in another order
+
+
+def pin_rope_relative_position(o):
+    """<R_m q, R_n k> depends only on m - n (the property RoPE is built for)."""
+    rng = _rng(19)
+    q = rng.standard_normal((1, 1, 1, 64))
+    k = rng.standard_normal((1, 1, 1, 64))
+    for trad in (False, True):
+        def rot(v, p):
+            return _rope(o, v, None, normalize=False, offset=p, traditional=trad)[0, 0, 0]
+        for m, n, s in ((5, 2, 100), (0, 40, 777), (1500, 1499, -1499)):
+            a = np.dot(rot(q, m), rot(k, n))
+            b = np.dot(rot(q, m + s), rot(k, n + s))
+            assert abs(a - b) <= 1e-12 * (1 + abs(a)), (m, n, s, a, b)
+
+
+def pin_rope_passthrough_and_span(o):
+    """Features >= dims equal RmsNorm of the whole row (RMS over all D, not rotated)."""
+    rng = _rng(20)
+    x = rng.standard_normal((2, 2, 6, 24))
+    w = rng.uniform(0.5, 1.5, 24)
+    y = _rope(o, x, w, dims=8, offset=11)
+    _same_values(y[..., 8:], o.rms_norm(x, w, 1e-6, "f64")[..., 8:], "passthrough")
+    y0 = _rope(o, x, None, dims=8, offset=11, normalize=False)
+    _same_values(y0[..., 8:], x[..., 8:], "no normalisation")
+
+
+def pin_rope_cache(o):
+    """Cache rows offset .. offset + L - 1 hold the plain result; the rest keep their values."""
+    rng = _rng(21)
+    x = _bf16_values(rng.standard_normal((2, 3, 5, 16)))
+    w = _bf16_values(rng.uniform(0.5, 1.5, 16))
+    cache = _bf16_values(rng.standard_normal((2, 3, 12, 16)))
+    for trad in (False, True):
+        kw = dict(traditional=trad, offset=6, dtype="bf16")
+        y = _rope(o, x, w, **kw)
+        c = _rope(o, x, w, cache=cache, **kw)
+        _same_values(c[:, :, 6:11], y, "written rows")
+        _same_values(c[:, :, :6], cache[:, :, :6], "rows before")
+        _same_values(c[:, :, 11:], cache[:, :, 11:], "rows after")
+
+
+def pin_rope_brute(o):
+    """B = H = 1, L = 2, D = 8, dims 4 and 8, both modes, both directions, with and without
+    normalisation, against 50-digit evaluation rounded exactly."""
+    rng = _rng(22)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        x = cast(rng.standard_normal((1, 1, 2, 8)))
+        w = cast(rng.uniform(0.5, 1.5, 8))
+        for dims in (4, 8):
+            for trad in (False, True):
+                for fwd in (True, False):
+                    for norm in (True, False):
+                        kw = dict(normalize=norm, eps=1e-6, dims=dims, traditional=trad,
+                                  base=10000.0, scale=1.0, forward=fwd)
+                        got = o.norm_rope(x, w, offset=700, dtype=dt, **kw)
+                        for l in range(2):
+                            want = [brute.round_mp(v, dt) for v in
+                                    brute.rope_row(x[0, 0, l], w, pos=700 + l, **kw)]
+                            _same_values(got[0, 0, l], want, f"{dt} {kw} l={l}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,100 @@
+"""Planted mistakes in copies of the oracle (CPU only): each must fail at least one pin.
+
+A copy of ``oracle/`` is written to a temporary directory under a fresh package name with
+one source edit, imported, and run through every pin; the test passes when some pin
+raises. This shows the pins can tell a plausible mistake (a dropped term, a wrong sign or
+index, a wrong divisor, a wrong rounding) from the real definition.
+"""
+
+import importlib
+import os
+import shutil
+import sys
+
+import pytest
+
+import pins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+# (file, text to replace, replacement, what the mistake is)
+MUTANTS = [
+    ("norms.py", "y = x / np.sqrt(mean_sq + f32_param(eps))", "y = x / np.sqrt(mean_sq)",
+     "RmsNorm drops eps"),
+    ("norms.py", "mean_sq = np.sum(x * x, axis=-1, keepdims=True) / d",
+     "mean_sq = np.sum(x * x, axis=-1, keepdims=True)", "RmsNorm sums instead of averaging"),
+    ("norms.py", "    if w is not None:\n        y = y * w\n    return round_to(y, dtype)\n\n\ndef add",
+     "    return round_to(y, dtype)\n\n\ndef add", "RmsNorm ignores w"),
+    ("norms.py", "y = x / np.sqrt(mean_sq + f32_param(eps))",
+     "y = x / np.sqrt(mean_sq + eps)", "eps not taken as its float32 value"),
+    ("norms.py", "h = round_to(_f64(x) + _f64(r), dtype)", "h = _f64(x) + _f64(r)",
+     "residual h not rounded to the storage dtype"),
+    ("norms.py", "return rms_norm(h, w, eps, dtype), h",
+     "return rms_norm(_f64(x) + _f64(r), w, eps, dtype), h",
+     "AddRmsNorm normalises the unrounded sum"),
+    ("norms.py", "var = np.sum(centred * centred, axis=-1, keepdims=True) / d",
+     "var = np.sum(centred * centred, axis=-1, keepdims=True) / (d - 1)",
+     "LayerNorm uses the unbiased variance"),
+    ("norms.py", "y = centred / np.sqrt(var + f32_param(eps))",
+     "y = x / np.sqrt(var + f32_param(eps))", "LayerNorm does not centre the output"),
+    ("norms.py", "y = centred / np.sqrt(var + f32_param(eps))",
+     "y = centred / (np.sqrt(var) + f32_param(eps))", "LayerNorm adds eps outside the root"),
+    ("norms.py", "y = y + b", "y = y - b", "LayerNorm subtracts the bias"),
+    ("rounding.py", "np.rint(np.ldexp(y, -q))", "np.trunc(np.ldexp(y, -q))",
+     "bf16 rounding truncates"),
+    ("rounding.py", "np.rint(np.ldexp(y, -q))", "np.floor(np.ldexp(y, -q) + 0.5)",
+     "bf16 rounding sends ties up"),
+    ("rounding.py", "_BF16_MIN_QUANTUM_EXP = -133", "_BF16_MIN_QUANTUM_EXP = -126",
+     "bf16 subnormals flushed"),
+    ("rounding.py", "_BF16_SIG_BITS = 8", "_BF16_SIG_BITS = 7", "bf16 keeps one bit too few"),
+    ("rope.py", "y[..., iu] = u * c - v * s\n    y[..., iv] = u * s + v * c",
+     "y[..., iu] = u * c + v * s\n    y[..., iv] = -u * s + v * c", "rotation turns clockwise"),
+    ("rope.py", "    if traditional:\n        return 2 * i, 2 * i + 1",
+     "    if not traditional:\n        return 2 * i, 2 * i + 1", "pair modes swapped"),
+    ("rope.py", "return i, i + half", "return i, i + half - 1", "half-mode partner off by one"),
+    ("rope.py", "(-2.0 * i) / dims", "(-1.0 * i) / dims", "frequency exponent halved"),
+    ("rope.py", "(-2.0 * i) / dims", "(-2.0 * i) / (dims - 2)", "frequency exponent over dims - 2"),
+    ("rope.py", "rope_angles(offset + np.arange(L)", "rope_angles(np.arange(L)",
+     "offset ignored"),
+    ("rope.py", "rope_angles(offset + np.arange(L)", "rope_angles(offset + np.arange(L) + 1",
+     "positions start one late"),
+    ("rope.py", "return (f32_param(scale) * p)", "return (p + 0 * f32_param(scale))",
+     "scale ignored"),
+    ("rope.py", "        s = -s", "        s = s", "inverse rotation not inverted"),
+    ("rope.py", "mean_sq = np.sum(x * x, axis=-1, keepdims=True) / D",
+     "mean_sq = np.sum(x[..., :dims] ** 2, axis=-1, keepdims=True) / max(dims, 1)",
+     "RMS over the rotated features only"),
+    ("rope.py", "xn = xn * np.asarray(w, dtype=np.float64)", "xn = xn",
+     "NormRope ignores w"),
+    ("rope.py", "out[:, :, offset:offset + L, :] = y", "out[:, :, 0:L, :] = y",
+     "cache written from row 0"),
+    ("rope.py", "xn = x / np.sqrt(mean_sq + f32_param(eps))", "xn = x / np.sqrt(mean_sq)",
+     "NormRope drops eps"),
+]
+
+
+def _load_mutant(tmp_path, k, fname, old, new):
+    name = f"oracle_mutant_{k}"
+    dst = tmp_path / name
+    shutil.copytree(ORACLE_DIR, dst, ignore=shutil.ignore_patterns("__pycache__"))
+    path = dst / fname
+    src = path.read_text()
+    assert src.count(old) >= 1, f"mutation text not found in {fname}: {old!r}"
+    path.write_text(src.replace(old, new, 1))
+    sys.path.insert(0, str(tmp_path))
+    try:
+        return importlib.import_module(name)
+    finally:
+        sys.path.remove(str(tmp_path))
+
+
+@pytest.mark.parametrize("k", range(len(MUTANTS)), ids=[m[3] for m in MUTANTS])
+def test_planted_mistake_fails_a_pin(tmp_path, k):
+    fname, old, new, what = MUTANTS[k]
+    mutant = _load_mutant(tmp_path, k, fname, old, new)
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError, IndexError):
+            return
+    pytest.fail(f"no pin caught the planted mistake: {what}")

@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for the row-wise normalisation ops.
+
+This module only draws random numbers and casts them to the storage dtypes; it holds none
+of the normalisation arithmetic. Both sides of every parity check (the fp64 oracle under
+``oracle/`` and the HIP library under ``transformer_row_wise_amd/``) receive the tensors
+built here, and neither of them imports the other.
+
+Recipe (the same for every workload):
+  * ``numpy.random.default_rng(seed)`` (PCG64), draws taken in float64 in the order
+    x, r, w, b;
+  * ``N(mean, std)`` means ``rng.normal(loc=mean, scale=std)`` (std, not variance);
+    ``U(lo, hi)`` is ``rng.uniform(lo, hi)``; Student-t(3) is ``rng.standard_t(3)``;
+  * the "1% of rows times 1e3" outlier rows are picked after x and r are drawn, with
+    ``rng.choice(rows, rows // 100, replace=False)``, and the same rows are scaled in x and r;
+  * float64 -> float32 by numpy's round-to-nearest-even cast, then float32 -> bfloat16 by
+    torch's round-to-nearest-even cast (CPU).
+
+Tensors are returned on the CPU; callers move them to the device themselves.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def cast(a64: np.ndarray, dtype: str) -> torch.Tensor:
+    """float64 draws -> float32 (RNE) -> bf16 (RNE, torch) as a CPU tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(a64, dtype=np.float32))
+    return t if dtype == "f32" else t.to(DTYPES[dtype])
+
+
+def draw(rng: np.random.Generator, spec, shape):
+    """One float64 draw. ``spec`` is ("normal", mean, std), ("uniform", lo, hi),
+    ("t3",) or ("const", value)."""
+    kind = spec[0]
+    if kind == "normal":
+        return rng.normal(spec[1], spec[2], size=shape)
+    if kind == "uniform":
+        return rng.uniform(spec[1], spec[2], size=shape)
+    if kind == "t3":
+        return rng.standard_t(3, size=shape)
+    if kind == "const":
+        return np.full(shape, float(spec[1]))
+    raise ValueError(f"unknown distribution {spec!r}")
+
+
+@dataclasses.dataclass
+class RowInputs:
+    """Inputs of one row-wise call: x (and r) of shape [rows, hidden]; w, b of [hidden]."""
+
+    x: torch.Tensor
+    r: torch.Tensor | None
+    w: torch.Tensor | None
+    b: torch.Tensor | None
+    eps: float
+
+
+def row_inputs(rows, hidden, dtype, *, seed=0, x=("normal", 0.0, 1.0), r=None,
+               w=("normal", 1.0, 0.1), b=None, w_dtype=None, eps=1e-5,
+               outlier_frac=0.0, outlier_scale=1e3) -> RowInputs:
+    """Draws x (and r, w, b when given a distribution) in the recipe's order."""
+    rng = np.random.default_rng(seed)
+    wd = w_dtype or dtype
+    x64 = draw(rng, x, (rows, hidden))
+    r64 = draw(rng, r, (rows, hidden)) if r is not None else None
+    w64 = draw(rng, w, (hidden,)) if w is not None else None
+    b64 = draw(rng, b, (hidden,)) if b is not None else None
+    if outlier_frac > 0 and rows > 0:
+        pick = rng.choice(rows, int(rows * outlier_frac), replace=False)
+        x64[pick] *= outlier_scale
+        if r64 is not None:
+            r64[pick] *= outlier_scale
+    return RowInputs(
+        x=cast(x64, dtype),
+        r=cast(r64, dtype) if r64 is not None else None,
+        w=cast(w64, wd) if w64 is not None else None,
+        b=cast(b64, wd) if b64 is not None else None,
+        eps=eps,
+    )
+
+
+@dataclasses.dataclass
+class RopeInputs:
+    """Inputs of one NormRope call: x [B, H, L, D], w [D] and the rotation settings."""
+
+    x: torch.Tensor
+    w: torch.Tensor | None
+    eps: float
+    dims: int
+    base: float
+    scale: float
+    offset: int
+
+
+def rope_inputs(B, H, L, D, dtype, *, seed=0, x=("normal", 0.0, 1.0),
+                w=("uniform", 0.5, 1.5), w_dtype=None, eps=1e-6, dims=None,
+                base=10000.0, scale=1.0, offset=0) -> RopeInputs:
+    rng = np.random.default_rng(seed)
+    x64 = draw(rng, x, (B, H, L, D))
+    w64 = draw(rng, w, (D,)) if w is not None else None
+    return RopeInputs(
+        x=cast(x64, dtype),
+        w=cast(w64, w_dtype or dtype) if w64 is not None else None,
+        eps=eps, dims=D if dims is None else dims, base=base, scale=scale, offset=offset,
+    )
+
+
+# ---------------------------------------------------------------------------------------
+# The named workloads. Sizes and distributions follow the five synthetic configurations
+# of the row-wise normalisation benchmark: small fp32 add-RMSNorm, bf16 add-RMSNorm at
+# 4096x4096, bf16 LayerNorm at 16384x8192 (affine and not), bf16 NormRope at
+# [8,32,512,128] (two pair modes, plain and cache output) and add-RMSNorm at scale with
+# heavy-tailed values.
+# ---------------------------------------------------------------------------------------
+
+def cfg_add_rms_small_f32(seed=0):
+    """add-RMSNorm fp32, x and r [64,512] ~N(0,1), w ~U(0.5,1.5), eps 1e-6."""
+    return row_inputs(64, 512, "f32", seed=seed, x=("normal", 0.0, 1.0),
+                      r=("normal", 0.0, 1.0), w=("uniform", 0.5, 1.5), eps=1e-6)
+
+
+def cfg_add_rms_4k_bf16(seed=0):
+    """add-RMSNorm bf16, x and r [4096,4096] ~N(0,1), w ~N(1,0.1), eps 1e-5."""
+    return row_inputs(4096, 4096, "bf16", seed=seed, x=("normal", 0.0, 1.0),
+                      r=("normal", 0.0, 1.0), w=("normal", 1.0, 0.1), eps=1e-5)
+
+
+def cfg_layer_norm_bf16(seed=0, affine=True, rows=16384, hidden=8192):
+    """LayerNorm bf16, x [16384,8192] ~N(0.5, std 2), w ~N(1,0.1), b ~N(0,0.1), eps 1e-5.
+    The no-affine case draws the same x (w and b are simply not drawn after it)."""
+    return row_inputs(rows, hidden, "bf16", seed=seed, x=("normal", 0.5, 2.0),
+                      w=("normal", 1.0, 0.1) if affine else None,
+                      b=("normal", 0.0, 0.1) if affine else None, eps=1e-5)
+
+
+def cfg_norm_rope_bf16(seed=0, offset=0):
+    """NormRope bf16, x [8,32,512,128] ~N(0,1), w[128] ~U(0.5,1.5), eps 1e-6, dims 128,
+    base 1e4, scale 1. The cache form writes [8,32,2048,128] at offset 1024."""
+    return rope_inputs(8, 32, 512, 128, "bf16", seed=seed, eps=1e-6, dims=128,
+                       base=10000.0, scale=1.0, offset=offset)
+
+
+NORM_ROPE_CACHE_LEN = 2048
+NORM_ROPE_CACHE_OFFSET = 1024
+
+
+def cfg_add_rms_scale(rows=16384, hidden=8192, dtype="bf16", seed=0):
+    """add-RMSNorm at scale: x and r Student-t(3), 1% of rows times 1e3, w ~N(1,0.1),
+    eps 1e-6. Shapes [16384,8192] and [65536,5120], bf16 and fp32."""
+    return row_inputs(rows, hidden, dtype, seed=seed, x=("t3",), r=("t3",),
+                      w=("normal", 1.0, 0.1), eps=1e-6, outlier_frac=0.01)
+
+
+# The headline measurement: add-RMSNorm, bf16, 16384 x 8192.
+METRIC_ROWS = 16384
+METRIC_HIDDEN = 8192
