@@ -1,0 +1,397 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused row-wise normalisation library on one MI355X.
+
+Default run: one JSON line on stdout for the headline workload, residual add-RMSNorm in bf16
+storage at [16384, 8192] (x and r Student-t(3) with 1% of rows scaled by 1e3, w ~ N(1, 0.1),
+eps 1e-6), inputs resident in HBM. A step is one nrm_add_rms_norm call: load x and r, add,
+round and store h, sum of squares, row scalar, normalise, scale by w, round and store out.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite] [--no-cpu-baseline]
+
+--suite        also prints one JSON line per synthetic workload (all four ops) to stderr,
+               rotating buffer sets when a call's working set would fit in the 256 MB
+               Infinity Cache.
+--profile      only warm-up and timed calls of the headline kernel plus the copy kernel
+               (for rocprofv3 runs); no CPU baseline.
+--summarize-pmc FETCH_CSV WRITE_CSV
+               turn two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter files of a
+               --profile run into profiles/traffic_add_rms_norm_bf16_16384x8192.json, scaled
+               by what the same counters read for the 16-byte copy kernel of known size.
+
+Fields beyond the contract: roofline (algorithmic bytes per launch over the average launch
+time measured with HIP events on the launch stream, against 8 TB/s), copy_ceiling_GBps (a
+plain 16-byte copy of the same byte count), and cpu_baseline (the fp64 oracle on a bounded
+sample of the same workload, in a process pool over the host's cores).
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) + rows/s, add-RMSNorm bf16 16384x8192"
+PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+ROWS, HIDDEN = 16384, 8192
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_add_rms_norm_bf16_16384x8192.json")
+HEADLINE_KERNEL = "row_regs<true, 1, 16, 1>"  # bf16, add-RMSNorm, 16 chunks/lane, 1 wave/row
+COPY_KERNEL = "copy16_kernel"
+CPU_SAMPLE_ROWS = 4096
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: a stored counter reading is used only for this exact code."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "transformer_row_wise_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def add_rms_bytes(rows, hidden, es, w_es):
+    """Algorithmic bytes of one add-RMSNorm call: read x and r, write out and h, read w."""
+    return 4 * rows * hidden * es + hidden * w_es
+
+
+# --------------------------------------------------------------------------- GPU timing
+
+def time_calls(fn, steps, warmup):
+    """Per-call durations (ms) from HIP events on torch's current stream (the stream the
+    library launches on), plus the host wall time per call over the whole timed region."""
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return per, wall_ms
+
+
+def copy_ceiling(nbytes, steps):
+    """GB/s of the library's 16-byte copy moving nbytes/2 bytes in and nbytes/2 out."""
+    import torch
+    import transformer_row_wise_amd as nrm
+
+    half = (nbytes // 2) // 16 * 16
+    src = torch.empty(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    per, _ = time_calls(lambda i: nrm.bench_copy(src, dst), steps, 3)
+    del src, dst
+    return 2 * half / (statistics.mean(per) * 1e-3) / 1e9
+
+
+def stored_traffic(nbytes):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def _oracle_chunk(args):
+    """One worker: the fp64 oracle on a slice of rows (bf16 bit patterns in, time out)."""
+    import numpy as np
+
+    import oracle
+
+    xb, rb, wb, eps = args
+
+    def decode(b):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    t = time.perf_counter()
+    oracle.add_rms_norm(decode(xb), decode(rb), decode(wb), eps, "bf16")
+    return time.perf_counter() - t
+
+
+def cpu_baseline(inp, rows):
+    """The oracle, as it is, on the first `rows` rows of the workload, spread over a process
+    pool with one process per available core (at most 16)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    xb, rb, wb = bits(inp.x[:rows]), bits(inp.r[:rows]), bits(inp.w)
+    step = 128
+    jobs = [(xb[i:i + step], rb[i:i + step], wb, inp.eps) for i in range(0, rows, step)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_chunk, jobs[:cores])  # start-up and imports, untimed
+        t0 = time.perf_counter()
+        busy = pool.map(_oracle_chunk, jobs)
+        wall = time.perf_counter() - t0
+    nbytes = add_rms_bytes(rows, inp.x.shape[1], 2, 2)
+    return {
+        "value": round(nbytes / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"first {rows} of {inp.x.shape[0]} rows of the same add-RMSNorm bf16 "
+                  f"[16384, 8192] inputs, fp64 oracle in a pool of {cores} processes "
+                  f"(chunks of {step} rows); {sum(busy):.1f} s of CPU work, {wall:.2f} s wall",
+        "rows_per_s": round(rows / wall, 1),
+        "wall_s": round(wall, 3),
+    }
+
+
+# --------------------------------------------------------------------------- headline
+
+def headline(args):
+    import torch
+
+    import transformer_row_wise_amd as nrm
+    import workloads
+
+    nrm.load()
+    print(f"# generating add-RMSNorm bf16 [{ROWS}, {HIDDEN}] inputs", file=sys.stderr, flush=True)
+    inp = workloads.cfg_add_rms_scale(ROWS, HIDDEN, "bf16")
+    x, r, w = inp.x.cuda(), inp.r.cuda(), inp.w.cuda()
+    out, h = torch.empty_like(x), torch.empty_like(x)
+    nbytes = add_rms_bytes(ROWS, HIDDEN, 2, 2)
+
+    def step(_):
+        nrm.add_rms_norm(x, r, w, inp.eps, out=out, h=h)
+
+    print(f"# timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    per, wall_ms = time_calls(step, args.steps, args.warmup)
+    avg_ms = statistics.mean(per)
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    value = nbytes / (wall_ms * 1e-3) / 1e9
+    ceiling = copy_ceiling(nbytes, max(10, args.steps // 2))
+    if args.profile:
+        print(json.dumps({"profile_run": True, "avg_launch_us": avg_ms * 1e3,
+                          "achieved_GBps": achieved, "copy_GBps": ceiling}), flush=True)
+        return
+    traffic = stored_traffic(nbytes)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "add-RMSNorm bf16 [16384, 8192]: x, r Student-t(3) with 1% of rows "
+                        "x1e3, w ~ N(1, 0.1) bf16, eps 1e-6",
+            "rows": ROWS, "hidden": HIDDEN, "io_dtype": "bf16", "parallelism": "none",
+        },
+        "pct_peak": round(100 * value / PEAK_GBPS, 2),
+        "rows_per_s": round(ROWS / (wall_ms * 1e-3), 1),
+        "bytes_per_step": nbytes,
+        "kernel_us": {"mean": round(avg_ms * 1e3, 2), "median": round(statistics.median(per) * 1e3, 2),
+                      "min": round(min(per) * 1e3, 2)},
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print(f"# cpu baseline: oracle on {CPU_SAMPLE_ROWS} rows", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, CPU_SAMPLE_ROWS)
+    print(json.dumps(res), flush=True)
+
+
+# --------------------------------------------------------------------------- suite
+
+def suite(args):
+    """One line per synthetic workload, to stderr. Working sets under 512 MB rotate through
+    enough buffer sets to exceed the 256 MB Infinity Cache."""
+    import torch
+
+    import transformer_row_wise_amd as nrm
+    import workloads
+
+    nrm.load()
+
+    def n_sets(bytes_per_call):
+        return max(1, min(16, -(-512 * 2**20 // bytes_per_call)))
+
+    def emit(cfg, op, shape, nbytes, rows, per):
+        avg = statistics.mean(per)
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        print(json.dumps({"cfg": cfg, "op": op, "shape": shape, "bytes": nbytes,
+                          "gpu_us_mean": round(avg * 1e3, 2),
+                          "gpu_us_median": round(statistics.median(per) * 1e3, 2),
+                          "gpu_us_min": round(min(per) * 1e3, 2),
+                          "gpu_GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 2),
+                          "rows_per_s": round(rows / (avg * 1e-3), 1)}), file=sys.stderr,
+              flush=True)
+
+    def run_add(cfg, inp):
+        rows, hidden = inp.x.shape
+        es = inp.x.element_size()
+        nbytes = add_rms_bytes(rows, hidden, es, inp.w.element_size())
+        sets = [(inp.x.cuda(), inp.r.cuda()) for _ in range(n_sets(nbytes))]
+        w = inp.w.cuda()
+        outs = [(torch.empty_like(s[0]), torch.empty_like(s[0])) for s in sets]
+        per, _ = time_calls(lambda i: nrm.add_rms_norm(*sets[i % len(sets)], w, inp.eps,
+                                                       out=outs[i % len(sets)][0],
+                                                       h=outs[i % len(sets)][1]),
+                            args.steps, args.warmup)
+        emit(cfg, "add_rms_norm", [rows, hidden, str(inp.x.dtype)], nbytes, rows, per)
+
+    run_add("1", workloads.cfg_add_rms_small_f32())
+    run_add("2", workloads.cfg_add_rms_4k_bf16())
+    for affine in (True, False):
+        inp = workloads.cfg_layer_norm_bf16(affine=affine)
+        rows, hidden = inp.x.shape
+        nbytes = 2 * rows * hidden * 2 + (2 * hidden * 2 if affine else 0)
+        x = inp.x.cuda()
+        w = inp.w.cuda() if affine else None
+        b = inp.b.cuda() if affine else None
+        out = torch.empty_like(x)
+        per, _ = time_calls(lambda i: nrm.layer_norm(x, w, b, inp.eps, out=out), args.steps,
+                            args.warmup)
+        emit("3a" if affine else "3b", "layer_norm", [rows, hidden], nbytes, rows, per)
+        del x, out
+    for cache in (False, True):
+        for trad in (False, True):
+            rp = workloads.cfg_norm_rope_bf16(offset=workloads.NORM_ROPE_CACHE_OFFSET if cache else 0)
+            B, H, L, D = rp.x.shape
+            nbytes = 2 * B * H * L * D * 2 + D * 2
+            k = n_sets(nbytes)
+            xs = [rp.x.cuda() for _ in range(k)]
+            w = rp.w.cuda()
+            if cache:
+                dsts = [torch.zeros(B, H, workloads.NORM_ROPE_CACHE_LEN, D, dtype=torch.bfloat16,
+                                    device="cuda") for _ in range(k)]
+            else:
+                dsts = [torch.empty_like(xs[0]) for _ in range(k)]
+            per, _ = time_calls(
+                lambda i: nrm.norm_rope(xs[i % k], w, eps=rp.eps, traditional=trad,
+                                        offset=rp.offset, cache=dsts[i % k] if cache else None,
+                                        out=None if cache else dsts[i % k]),
+                args.steps, args.warmup)
+            emit("4" + "abcd"[2 * cache + trad], "norm_rope" + ("_cache" if cache else "") +
+                 ("_interleaved" if trad else "_half"), [B, H, L, D], nbytes, B * H * L, per)
+            del xs, dsts
+    for shape, tag in (((16384, 8192), "5"), ((65536, 5120), "5")):
+        f32 = workloads.cfg_add_rms_scale(*shape, dtype="f32")
+        bf = workloads.RowInputs(x=f32.x.to(torch.bfloat16), r=f32.r.to(torch.bfloat16),
+                                 w=f32.w.to(torch.bfloat16), b=None, eps=f32.eps)
+        run_add(tag + ("a" if shape[1] == 8192 else "c"), bf)
+        run_add(tag + ("b" if shape[1] == 8192 else "d"), f32)
+        del f32, bf
+        torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- counters
+
+def _pmc_per_dispatch(csv_path, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv."""
+    import csv
+
+    out = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_bytes_half):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the headline kernel, each scaled by the
+    ratio of known bytes to the counter's reading for the 16-byte copy kernel."""
+    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        if not ks:
+            raise SystemExit(f"no dispatch of {key} in the counter file")
+        vals = d[ks[0]]
+        return statistics.median(vals), ks[0]
+
+    kf, kname = pick(f, HEADLINE_KERNEL)
+    kw, _ = pick(w, HEADLINE_KERNEL)
+    cf, _ = pick(f, COPY_KERNEL)
+    cw, _ = pick(w, COPY_KERNEL)
+    scale_f = copy_bytes_half / (cf * 1024)
+    scale_w = copy_bytes_half / (cw * 1024)
+    read_b = kf * 1024 * scale_f
+    write_b = kw * 1024 * scale_w
+    alg = add_rms_bytes(ROWS, HIDDEN, 2, 2)
+    summary = {
+        "kernel": kname,
+        "workload": "add-RMSNorm bf16 [16384, 8192]",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_KiB_per_dispatch": kf, "write_KiB_per_dispatch": kw,
+        "copy_fetch_KiB": cf, "copy_write_KiB": cw, "copy_bytes_each_way": copy_bytes_half,
+        "fetch_scale": scale_f, "write_scale": scale_w,
+        "hbm_read_bytes_per_launch": round(read_b), "hbm_write_bytes_per_launch": round(write_b),
+        "hbm_bytes_per_launch": round(read_b + write_b),
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round((read_b + write_b) / alg, 4),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    print(json.dumps(summary, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--suite", action="store_true")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        half = (add_rms_bytes(ROWS, HIDDEN, 2, 2) // 2) // 16 * 16
+        summarize_pmc(*args.summarize_pmc, copy_bytes_half=half)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (rows are "
+              f"independent, so N GPUs would each run this same kernel on their own rows); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        return 2
+    headline(args)
+    if args.suite:
+        suite(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

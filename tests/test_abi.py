@@ -1,0 +1,158 @@
+"""The C ABI without a GPU: the library loads, exports every function include/nrm.h declares,
+and rejects every bad argument on the host before any HIP call (so these calls need no
+device; the pointer values below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import transformer_row_wise_amd as nrm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nrm.h")
+
+OK, NULL, SHAPE, DTYPE, ALIAS, DEVICE = range(6)
+F32, BF16 = 0, 1
+P = 0x10000000  # a fake, 16-byte aligned address; nothing here dereferences it
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nrm.LIB_PATH):
+        pytest.fail("libnrm.so is not built (run __graft_entry__.build())")
+    return nrm.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nrm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_ops():
+    names = declared_functions()
+    for op in ("nrm_rms_norm", "nrm_add_rms_norm", "nrm_layer_norm", "nrm_norm_rope",
+               "nrm_last_error"):
+        assert op in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} is declared in nrm.h but not exported"
+
+
+def test_version_and_status_names(L):
+    assert L.nrm_version() == 100
+    names = [L.nrm_status_name(i).decode() for i in range(6)]
+    assert names == ["NRM_OK", "NRM_ERR_NULL", "NRM_ERR_SHAPE", "NRM_ERR_DTYPE", "NRM_ERR_ALIAS",
+                     "NRM_ERR_DEVICE"]
+
+
+def err(L):
+    return L.nrm_last_error().decode()
+
+
+def rms(L, x=P, w=None, out=P + 64 * MB, rows=4, hidden=8, eps=1e-5, dt=BF16, wdt=BF16):
+    return L.nrm_rms_norm(x, w, out, rows, hidden, eps, dt, wdt, None)
+
+
+def add(L, x=P, r=P + 64 * MB, w=None, out=P + 128 * MB, h=P + 192 * MB, rows=4, hidden=8,
+        dt=BF16, wdt=BF16):
+    return L.nrm_add_rms_norm(x, r, w, out, h, rows, hidden, 1e-5, dt, wdt, None)
+
+
+def ln(L, x=P, w=None, b=None, out=P + 64 * MB, rows=4, hidden=8, dt=BF16, wdt=BF16):
+    return L.nrm_layer_norm(x, w, b, out, rows, hidden, 1e-5, dt, wdt, None)
+
+
+def rope(L, x=P, w=None, out=P + 64 * MB, B=2, H=2, L_=4, D=16, normalize=1, dims=16, offset=0,
+         cache=0, cache_len=0, dt=BF16, wdt=BF16):
+    return L.nrm_norm_rope(x, w, out, B, H, L_, D, normalize, 1e-6, dims, 0, 10000.0, 1.0,
+                           offset, 1, cache, cache_len, dt, wdt, None)
+
+
+def test_null_pointers(L):
+    assert rms(L, x=None) == NULL and "x must not be NULL" in err(L)
+    assert rms(L, out=None) == NULL and "out must not be NULL" in err(L)
+    assert add(L, r=None) == NULL and "r must not be NULL" in err(L)
+    assert add(L, h=None) == NULL and "h_out must not be NULL" in err(L)
+    assert ln(L, x=None) == NULL
+    assert rope(L, out=None) == NULL and "out_or_cache" in err(L)
+    assert L.nrm_bench_copy(None, P, 16, None) == NULL
+
+
+def test_shapes(L):
+    assert rms(L, rows=-1) == SHAPE and "rows must be >= 0, got -1" in err(L)
+    assert rms(L, hidden=0) == SHAPE and "hidden must be in [1, 2147483647], got 0" in err(L)
+    assert rms(L, hidden=2**31) == SHAPE
+    assert rms(L, rows=2**62, hidden=2**20) == SHAPE and "overflows" in err(L)
+    assert ln(L, hidden=-3) == SHAPE
+    assert add(L, rows=-5) == SHAPE
+    assert rope(L, B=-1) == SHAPE and "B must be >= 0" in err(L)
+    assert rope(L, L_=-1) == SHAPE
+    assert rope(L, D=0) == SHAPE
+    assert rope(L, dims=15) == SHAPE and "dims must be even, got 15" in err(L)
+    assert rope(L, dims=18) == SHAPE and "dims must be in [0, D = 16], got 18" in err(L)
+    assert rope(L, dims=-2) == SHAPE
+    assert rope(L, offset=-1) == SHAPE and "offset must be >= 0" in err(L)
+    assert rope(L, cache=1, cache_len=10, offset=7, L_=4) == SHAPE
+    assert "offset + L must be <= cache_len (10), got 7 + 4" in err(L)
+    assert L.nrm_bench_copy(P, P + MB, 17, None) == SHAPE
+
+
+def test_dtypes(L):
+    assert rms(L, dt=2) == DTYPE and "dtype must be NRM_F32 (0) or NRM_BF16 (1), got 2" in err(L)
+    assert rms(L, dt=F32, wdt=BF16) == DTYPE and "w_dtype must equal dtype (0)" in err(L)
+    assert add(L, wdt=7) == DTYPE
+    assert ln(L, dt=-1) == DTYPE
+    assert rope(L, dt=3) == DTYPE
+
+
+def test_aliasing(L):
+    n = 4 * 8 * 2  # bytes of a [4, 8] bf16 array
+    # exact in-place use is allowed; zero rows keeps everything on the host
+    assert rms(L, out=P, rows=0) == OK
+    assert rms(L, out=P + 2, rows=4) == ALIAS and "partial overlap" in err(L)
+    assert rms(L, w=P + 64 * MB + 4) == ALIAS and "out must not overlap w" in err(L)
+    assert add(L, out=P + 128 * MB, h=P + 128 * MB) == ALIAS and "out must not overlap h_out" in err(L)
+    assert add(L, h=P + 16) == ALIAS and "h_out must be exactly or not overlap x" in err(L)
+    assert add(L, h=P + 64 * MB + n - 2) == ALIAS
+    assert add(L, out=P, h=P + 64 * MB, rows=0) == OK   # out == x, h == r: allowed
+    assert add(L, out=P + 64 * MB, h=P, rows=0) == OK   # out == r, h == x: allowed
+    assert ln(L, b=P + 64 * MB) == ALIAS and "out must not overlap b" in err(L)
+    assert rope(L, out=P + 8) == ALIAS
+    assert rope(L, out=P, B=0) == OK  # out == x: allowed
+    assert rope(L, out=P, cache=1, cache_len=8) == ALIAS and "cache must not overlap x" in err(L)
+    assert L.nrm_bench_copy(P, P + 8, 64, None) == ALIAS
+
+
+def test_zero_rows_is_a_noop(L):
+    assert rms(L, rows=0) == OK and err(L) == ""
+    assert add(L, rows=0) == OK
+    assert ln(L, rows=0) == OK
+    assert rope(L, B=0) == OK and rope(L, L_=0) == OK and rope(L, H=0) == OK
+    assert rope(L, L_=0, cache=1, cache_len=0) == OK
+    assert L.nrm_bench_copy(P, P + MB, 0, None) == OK
+
+
+def test_error_message_cleared_by_next_call(L):
+    assert rms(L, rows=-1) == SHAPE and err(L)
+    assert rms(L, rows=0) == OK and err(L) == ""
+
+
+def test_python_wrapper_refuses_host_tensors():
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        nrm.rms_norm(x)
+    with pytest.raises(ValueError, match="HIP device"):
+        nrm.norm_rope(x.view(1, 1, 4, 8))
+
+
+def test_python_error_type(L):
+    status = rms(L, rows=-1)
+    with pytest.raises(nrm.NrmError, match="NRM_ERR_SHAPE: nrm_rms_norm: rows must be >= 0"):
+        nrm._raise(status)

@@ -1,0 +1,315 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle, element by element,
+on shapes that span several tiles and ragged tails, with every kernel shape forced in turn.
+
+Bars: h and cache placement bit-exact; bf16 outputs within 1 ulp; fp32 outputs within
+1e-5 relative + 1e-6 absolute.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import compare
+import workloads
+from gpu_util import (DEV, check_add, check_ln, check_rms, check_rope, dev, f64, forced_path,
+                      run_rope, say)
+
+pytestmark = pytest.mark.gpu
+
+# widths: tiny, not a 16-byte multiple, one wave per row, one block per row, looping kernel
+HIDDEN = [1, 2, 7, 8, 64, 100, 512, 520, 1000, 4096, 5120, 8192, 8200, 12288, 16384, 32768,
+          40000, 70000]
+WEIGHTS = [("bf16", "bf16"), ("bf16", "f32"), ("bf16", None), ("f32", "f32"), ("f32", None)]
+
+
+def _row(rows, hidden, dt, wdt, seed, **kw):
+    return workloads.row_inputs(rows, hidden, dt, seed=seed,
+                                w=("normal", 1.0, 0.1) if wdt else None,
+                                w_dtype=wdt if wdt else None, **kw)
+
+
+@pytest.mark.parametrize("hidden", HIDDEN)
+@pytest.mark.parametrize("dt,wdt", WEIGHTS)
+def test_add_rms_norm_shapes(nrm_lib, hidden, dt, wdt):
+    say(f"add_rms_norm rows=5 hidden={hidden} {dt} w={wdt}")
+    inp = _row(5, hidden, dt, wdt, seed=hidden, r=("normal", 0.0, 1.0), eps=1e-6)
+    check_add(nrm_lib, inp)
+
+
+@pytest.mark.parametrize("hidden", HIDDEN)
+@pytest.mark.parametrize("dt,wdt", WEIGHTS)
+def test_rms_norm_shapes(nrm_lib, hidden, dt, wdt):
+    say(f"rms_norm rows=5 hidden={hidden} {dt} w={wdt}")
+    inp = _row(5, hidden, dt, wdt, seed=hidden + 1, x=("t3",), eps=1e-5)
+    check_rms(nrm_lib, inp)
+
+
+@pytest.mark.parametrize("hidden", HIDDEN)
+@pytest.mark.parametrize("dt,wdt", WEIGHTS)
+@pytest.mark.parametrize("affine", ["wb", "w", "b", "none"])
+def test_layer_norm_shapes(nrm_lib, hidden, dt, wdt, affine):
+    say(f"layer_norm rows=5 hidden={hidden} {dt} w={wdt} {affine}")
+    inp = workloads.row_inputs(5, hidden, dt, seed=hidden + 2, x=("normal", 0.5, 2.0),
+                               w=("normal", 1.0, 0.1), b=("normal", 0.0, 0.1),
+                               w_dtype=wdt or dt, eps=1e-5)
+    if "w" not in affine:
+        inp.w = None
+    if "b" not in affine:
+        inp.b = None
+    check_ln(nrm_lib, inp)
+
+
+@pytest.mark.parametrize("path", ["wave", "block", "chunked", "scalar"])
+@pytest.mark.parametrize("hidden", [512, 4096, 5120, 8192])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_forced_kernel_shapes(nrm_lib, path, hidden, dt):
+    """Every kernel shape gives oracle-parity results on the same inputs."""
+    say(f"forced path={path} hidden={hidden} {dt}")
+    with forced_path(path):
+        check_add(nrm_lib, _row(37, hidden, dt, dt, seed=7, r=("t3",), eps=1e-6))
+        check_rms(nrm_lib, _row(37, hidden, dt, dt, seed=8, eps=1e-6))
+        check_ln(nrm_lib, workloads.row_inputs(37, hidden, dt, seed=9, x=("normal", 0.5, 2.0),
+                                               b=("normal", 0.0, 0.1), eps=1e-5))
+
+
+@pytest.mark.parametrize("rows", [1, 3, 4, 5, 63, 257])
+def test_ragged_row_counts(nrm_lib, rows):
+    say(f"ragged rows={rows}")
+    check_add(nrm_lib, _row(rows, 4096, "bf16", "bf16", seed=rows, r=("normal", 0, 1)))
+
+
+# ------------------------------------------------------------------------------ NormRope
+
+ROPE_SHAPES = [
+    # (B, H, L, D, dims)
+    (2, 3, 5, 128, 128),
+    (1, 2, 7, 64, 64),
+    (2, 2, 4, 128, 64),
+    (1, 1, 3, 128, 32),
+    (1, 2, 3, 256, 256),
+    (1, 1, 2, 1024, 1024),
+    (1, 1, 2, 2048, 2048),
+    (2, 1, 3, 96, 96),
+    (1, 2, 4, 80, 80),
+    (1, 1, 3, 72, 72),
+    (1, 1, 3, 8, 4),
+    (1, 1, 2, 6, 6),
+    (1, 1, 2, 7, 6),
+    (1, 2, 3, 128, 0),
+    (3, 5, 33, 128, 128),
+]
+
+
+@pytest.mark.parametrize("shape", ROPE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("traditional", [False, True])
+def test_norm_rope_shapes(nrm_lib, shape, dt, traditional):
+    B, H, L, D, dims = shape
+    say(f"norm_rope {shape} {dt} traditional={traditional}")
+    rp = workloads.rope_inputs(B, H, L, D, dt, seed=D + L, dims=dims, offset=1021)
+    check_rope(nrm_lib, rp, traditional=traditional)
+
+
+@pytest.mark.parametrize("traditional", [False, True])
+@pytest.mark.parametrize("normalize", [True, False])
+@pytest.mark.parametrize("forward", [True, False])
+@pytest.mark.parametrize("path", [None, "scalar"])
+def test_norm_rope_modes(nrm_lib, traditional, normalize, forward, path):
+    say(f"norm_rope modes trad={traditional} norm={normalize} fwd={forward} path={path}")
+    with forced_path(path):
+        for dt, wdt in (("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")):
+            rp = workloads.rope_inputs(2, 4, 9, 128, dt, seed=11, w_dtype=wdt, offset=1530,
+                                       base=500000.0, scale=0.25)
+            check_rope(nrm_lib, rp, normalize=normalize, traditional=traditional, forward=forward)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 4096, 100000])
+def test_norm_rope_positions(nrm_lib, offset):
+    say(f"norm_rope offset={offset}")
+    rp = workloads.rope_inputs(1, 2, 16, 128, "bf16", seed=offset, offset=offset)
+    check_rope(nrm_lib, rp)
+    check_rope(nrm_lib, rp, traditional=True)
+
+
+@pytest.mark.parametrize("traditional", [False, True])
+@pytest.mark.parametrize("path", [None, "scalar"])
+def test_norm_rope_cache(nrm_lib, traditional, path):
+    """Cache mode: rows offset .. offset + L - 1 written, every other element keeps its bits."""
+    say(f"norm_rope cache trad={traditional} path={path}")
+    with forced_path(path):
+        rp = workloads.rope_inputs(2, 3, 6, 128, "bf16", seed=5, offset=9)
+        cache = workloads.cast(np.random.default_rng(3).standard_normal((2, 3, 20, 128)), "bf16")
+        check_rope(nrm_lib, rp, traditional=traditional, cache=cache)
+
+
+# ------------------------------------------------------------------------------ edge cases
+
+def test_in_place(nrm_lib):
+    """out == x for RMSNorm and LayerNorm; h == r and out == x for add-RMSNorm; out == x for
+    NormRope."""
+    say("in-place")
+    inp = _row(9, 4096, "bf16", "bf16", seed=1, r=("normal", 0, 1), eps=1e-6)
+    import oracle
+
+    x, r, w = dev(inp.x), dev(inp.r), dev(inp.w)
+    want_out, want_h = oracle.add_rms_norm(f64(inp.x), f64(inp.r), f64(inp.w), inp.eps, "bf16")
+    out, h = nrm_lib.add_rms_norm(x, r, w, inp.eps, out=x, h=r)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == x.data_ptr() and h.data_ptr() == r.data_ptr()
+    compare.check_bf16(x, want_out)
+    compare.check_exact_bits(r, compare.bits_of_values(want_h, "bf16").view(np.int16))
+
+    x = dev(inp.x)
+    nrm_lib.rms_norm(x, w, inp.eps, out=x)
+    torch.cuda.synchronize()
+    compare.check_bf16(x, oracle.rms_norm(f64(inp.x), f64(inp.w), inp.eps, "bf16"))
+
+    x = dev(inp.x)
+    nrm_lib.layer_norm(x, w, None, 1e-5, out=x)
+    torch.cuda.synchronize()
+    compare.check_bf16(x, oracle.layer_norm(f64(inp.x), f64(inp.w), None, 1e-5, "bf16"))
+
+    rp = workloads.rope_inputs(2, 2, 5, 128, "bf16", seed=4, offset=77)
+    for path in (None, "scalar"):
+        with forced_path(path):
+            xr = dev(rp.x)
+            nrm_lib.norm_rope(xr, dev(rp.w), eps=rp.eps, offset=rp.offset, out=xr)
+            torch.cuda.synchronize()
+            want = oracle.norm_rope(f64(rp.x), f64(rp.w), normalize=True, eps=rp.eps, dims=128,
+                                    traditional=False, base=1e4, scale=1.0, offset=77,
+                                    forward=True, dtype="bf16")
+            compare.check_bf16(xr, want)
+
+
+def _guarded(like, pad=4096):
+    """A contiguous view into a larger buffer whose margins hold a canary pattern."""
+    n = like.numel()
+    buf = torch.empty(n + 2 * pad, dtype=like.dtype, device=DEV)
+    buf.view(torch.int16 if like.element_size() == 2 else torch.int32).fill_(0x5A5A)
+    return buf, buf[pad:pad + n].view(like.shape), pad
+
+
+def _canary_ok(buf, pad, n):
+    b = buf.view(torch.int16 if buf.element_size() == 2 else torch.int32).cpu().numpy()
+    return np.all(b[:pad] == 0x5A5A) and np.all(b[pad + n:] == 0x5A5A)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("hidden", [100, 4096, 5120, 40000])
+def test_guard_bands(nrm_lib, dt, hidden):
+    """No kernel writes outside its output."""
+    say(f"guard bands {dt} hidden={hidden}")
+    inp = _row(7, hidden, dt, dt, seed=2, r=("normal", 0, 1), b=("normal", 0, 0.1))
+    x, r, w, b = dev(inp.x), dev(inp.r), dev(inp.w), dev(inp.b)
+    bo, out, pad = _guarded(x)
+    bh, h, _ = _guarded(x)
+    nrm_lib.add_rms_norm(x, r, w, 1e-6, out=out, h=h)
+    nrm_lib.rms_norm(x, w, 1e-6, out=out)
+    nrm_lib.layer_norm(x, w, b, 1e-5, out=out)
+    torch.cuda.synchronize()
+    assert _canary_ok(bo, pad, x.numel()) and _canary_ok(bh, pad, x.numel())
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 5, 128, 128), (1, 1, 3, 72, 72)])
+def test_norm_rope_guard_bands(nrm_lib, shape):
+    B, H, L, D, dims = shape
+    say(f"norm_rope guard bands {shape}")
+    rp = workloads.rope_inputs(B, H, L, D, "bf16", seed=1, dims=dims)
+    x = dev(rp.x)
+    for trad in (False, True):
+        bo, out, pad = _guarded(x)
+        nrm_lib.norm_rope(x, dev(rp.w), dims=dims, traditional=trad, out=out)
+        torch.cuda.synchronize()
+        assert _canary_ok(bo, pad, x.numel())
+
+
+def test_deterministic(nrm_lib):
+    """Two runs give the same bits (fixed reduction order)."""
+    say("determinism")
+    inp = _row(64, 8192, "bf16", "bf16", seed=3, r=("t3",), eps=1e-6)
+    x, r, w = dev(inp.x), dev(inp.r), dev(inp.w)
+    o1, h1 = nrm_lib.add_rms_norm(x, r, w, inp.eps)
+    o2, h2 = nrm_lib.add_rms_norm(x, r, w, inp.eps)
+    l1 = nrm_lib.layer_norm(x, w, w, 1e-5)
+    l2 = nrm_lib.layer_norm(x, w, w, 1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int16), l2.view(torch.int16))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("path", [None, "block", "scalar"])
+def test_scale_invariance_bit_exact(nrm_lib, dt, path):
+    """eps = 0 and alpha = 2^k: RMSNorm(alpha x) has the same bits as RMSNorm(x) (every step,
+    including the row scalar, scales exactly)."""
+    say(f"scale invariance {dt} path={path}")
+    inp = _row(16, 4096, dt, dt, seed=4)
+    x, w = dev(inp.x), dev(inp.w)
+    with forced_path(path):
+        base = nrm_lib.rms_norm(x, w, 0.0)
+        for k in (-9, -1, 3, 12):
+            got = nrm_lib.rms_norm(x * 2.0 ** k, w, 0.0)
+            torch.cuda.synchronize()
+            compare.check_exact_bits(got, base, what=f"2^{k}")
+
+
+def test_rope_identity_and_inverse(nrm_lib):
+    """Position 0 gives RMSNorm of the row; the inverse rotation undoes the forward one."""
+    say("rope identity / inverse")
+    rp = workloads.rope_inputs(2, 2, 4, 128, "bf16", seed=6, offset=0)
+    y = run_rope(nrm_lib, rp)
+    r0 = nrm_lib.rms_norm(dev(rp.x)[:, :, 0].contiguous(), dev(rp.w), rp.eps)
+    torch.cuda.synchronize()
+    compare.check_bf16(y[:, :, 0], f64(r0), what="position 0 vs rms_norm")
+    rp2 = workloads.rope_inputs(2, 2, 4, 128, "f32", seed=6, offset=1000)
+    y = run_rope(nrm_lib, rp2)
+    back = nrm_lib.norm_rope(y, eps=None, offset=1000, forward=False)
+    plain = nrm_lib.norm_rope(dev(rp2.x), dev(rp2.w), eps=rp2.eps, scale=0.0)
+    torch.cuda.synchronize()
+    compare.check_f32(f64(back), f64(plain), rtol=1e-5, atol=1e-6, what="inverse")
+
+
+def test_special_values(nrm_lib):
+    """NaN / inf stay in their row; an all-zero row gives 0 (eps > 0) or NaN (eps = 0)."""
+    say("special values")
+    import oracle
+
+    x = torch.randn(6, 4096, dtype=torch.float32).to(torch.bfloat16)
+    x[1, 17] = float("nan")
+    x[2, 5] = float("inf")
+    x[3] = 0
+    x[4, 4095] = -float("inf")
+    w = torch.ones(4096, dtype=torch.bfloat16)
+    for eps in (1e-6, 0.0):
+        got = nrm_lib.rms_norm(dev(x), dev(w), eps)
+        torch.cuda.synchronize()
+        want = oracle.rms_norm(f64(x), f64(w), eps, "bf16")
+        compare.check_bf16(got, want, what=f"rms eps={eps}")
+        got = nrm_lib.layer_norm(dev(x), dev(w), None, eps)
+        torch.cuda.synchronize()
+        with np.errstate(invalid="ignore"):
+            want = oracle.layer_norm(f64(x), f64(w), None, eps, "bf16")
+        compare.check_bf16(got, want, what=f"ln eps={eps}")
+
+
+def test_error_writes_nothing(nrm_lib):
+    """A rejected call (partial overlap) raises and leaves the output untouched."""
+    say("error path writes nothing")
+    buf = torch.zeros(2 * 4096 + 8, dtype=torch.bfloat16, device=DEV)
+    x = torch.randn(2, 4096, device=DEV).to(torch.bfloat16)
+    out = buf[8:8 + 2 * 4096].view(2, 4096)
+    h = buf[:2 * 4096].view(2, 4096)
+    with pytest.raises(nrm_lib.NrmError, match="NRM_ERR_ALIAS"):
+        nrm_lib.add_rms_norm(x, x, None, 1e-5, out=out, h=h)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(buf.view(torch.int16)) == 0
+
+
+def test_zero_rows(nrm_lib):
+    say("zero rows")
+    x = torch.empty(0, 4096, dtype=torch.bfloat16, device=DEV)
+    assert nrm_lib.rms_norm(x).shape == (0, 4096)
+    o, h = nrm_lib.add_rms_norm(x, x)
+    assert o.numel() == 0 and h.numel() == 0
+    assert nrm_lib.norm_rope(torch.empty(2, 0, 5, 128, dtype=torch.bfloat16, device=DEV)).numel() == 0

@@ -1,0 +1,227 @@
+"""Fused row-wise normalisation on AMD Instinct MI355X: the Python binding of libnrm.so.
+
+Every function here only marshals arguments (checks devices, dtypes, shapes and
+contiguity, allocates outputs with torch, passes raw device pointers and torch's current
+HIP stream) and calls the C ABI declared in ``include/nrm.h``; every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the library is not
+built, ``load()`` raises.
+
+    rms_norm(x, w=None, eps=1e-5)                -> out
+    add_rms_norm(x, r, w=None, eps=1e-5)         -> (out, h)   h = x + r
+    layer_norm(x, w=None, b=None, eps=1e-5)      -> out
+    norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, scale=1.0,
+              offset=0, forward=True, cache=None) -> out (or the cache, written in place)
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NrmError", "load", "lib", "rms_norm", "add_rms_norm", "layer_norm", "norm_rope",
+    "bench_copy", "NRM_F32", "NRM_BF16", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnrm.so")
+NRM_F32, NRM_BF16 = 0, 1
+_DTYPES = {torch.float32: NRM_F32, torch.bfloat16: NRM_BF16}
+_lib = None
+
+_i64, _f32, _int, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
+_SIGNATURES = {
+    "nrm_rms_norm": [_vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
+    "nrm_add_rms_norm": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
+    "nrm_layer_norm": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
+    "nrm_norm_rope": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _f32, _i64, _int, _f32, _f32,
+                      _i64, _int, _int, _i64, _int, _int, _vp],
+    "nrm_bench_copy": [_vp, _vp, _i64, _vp],
+    "nrm_last_error": [],
+    "nrm_status_name": [_int],
+    "nrm_version": [],
+}
+_RESTYPES = {"nrm_last_error": ctypes.c_char_p, "nrm_status_name": ctypes.c_char_p}
+
+
+class NrmError(RuntimeError):
+    """A failed nrm_* call: ``status`` is the nrm_status code, ``name`` its name."""
+
+    def __init__(self, status, name, message):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+def load(path=None):
+    """Load libnrm.so (once) and declare its C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is not built; run `python -m transformer_row_wise_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, args in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = _RESTYPES.get(name, ctypes.c_int)
+    _lib = lib
+    return lib
+
+
+def lib():
+    return load()
+
+
+def _raise(status):
+    L = load()
+    raise NrmError(status, L.nrm_status_name(status).decode(), L.nrm_last_error().decode())
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t, what):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"{what} must be float32 or bfloat16, got {t.dtype}") from None
+
+
+def _check_act(t, what, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _check_param(p, what, n, x):
+    if p is None:
+        return None, _DTYPES[x.dtype]
+    _check_act(p, what, x.device)
+    if p.dim() != 1 or p.shape[0] != n:
+        raise ValueError(f"{what} must have shape [{n}], got {list(p.shape)}")
+    if p.dtype not in (x.dtype, torch.float32):
+        raise TypeError(f"{what} must be {x.dtype} or float32, got {p.dtype}")
+    return p, _DTYPES[p.dtype]
+
+
+def _out_like(out, x, what):
+    if out is None:
+        return torch.empty_like(x)
+    _check_act(out, what, x.device)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError(f"{what} must be {x.dtype} of shape {list(x.shape)}, "
+                         f"got {out.dtype} {list(out.shape)}")
+    return out
+
+
+def _rows(x):
+    hidden = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // hidden if hidden else 0
+    return rows, hidden
+
+
+def rms_norm(x, w=None, eps=1e-5, out=None):
+    """x / sqrt(mean(x^2) + eps) * w over the last axis (nrm_rms_norm)."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    rows, hidden = _rows(x)
+    w, wdt = _check_param(w, "w", hidden, x)
+    out = _out_like(out, x, "out")
+    st = load().nrm_rms_norm(_ptr(x), _ptr(w), _ptr(out), rows, hidden, eps, dt, wdt, _stream())
+    if st:
+        _raise(st)
+    return out
+
+
+def add_rms_norm(x, r, w=None, eps=1e-5, out=None, h=None):
+    """(RMSNorm(x + r), x + r) in one pass (nrm_add_rms_norm). ``h`` may be ``x`` or ``r``
+    for an in-place residual update."""
+    _check_act(x, "x")
+    _check_act(r, "r", x.device)
+    dt = _dtype_code(x, "x")
+    if r.shape != x.shape or r.dtype != x.dtype:
+        raise ValueError(f"r must be {x.dtype} of shape {list(x.shape)}, got {r.dtype} "
+                         f"{list(r.shape)}")
+    rows, hidden = _rows(x)
+    w, wdt = _check_param(w, "w", hidden, x)
+    out = _out_like(out, x, "out")
+    h = _out_like(h, x, "h")
+    st = load().nrm_add_rms_norm(_ptr(x), _ptr(r), _ptr(w), _ptr(out), _ptr(h), rows, hidden,
+                                 eps, dt, wdt, _stream())
+    if st:
+        _raise(st)
+    return out, h
+
+
+def layer_norm(x, w=None, b=None, eps=1e-5, out=None):
+    """(x - mean) / sqrt(var + eps) * w + b over the last axis (nrm_layer_norm)."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    rows, hidden = _rows(x)
+    w, wdt = _check_param(w, "w", hidden, x)
+    b, bdt = _check_param(b, "b", hidden, x)
+    if w is not None and b is not None and wdt != bdt:
+        raise TypeError(f"w and b must share a dtype, got {w.dtype} and {b.dtype}")
+    pdt = wdt if w is not None else bdt
+    out = _out_like(out, x, "out")
+    st = load().nrm_layer_norm(_ptr(x), _ptr(w), _ptr(b), _ptr(out), rows, hidden, eps, dt,
+                               pdt, _stream())
+    if st:
+        _raise(st)
+    return out
+
+
+def norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, scale=1.0,
+              offset=0, forward=True, cache=None, out=None):
+    """NormRope over x [B, H, L, D] (nrm_norm_rope). ``eps=None`` skips the normalisation.
+    With ``cache`` ([B, H, cache_len, D]) rows offset .. offset + L - 1 of the cache are
+    written and the cache is returned; otherwise a new (or the given) [B, H, L, D] array."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    if x.dim() != 4:
+        raise ValueError(f"x must be [B, H, L, D], got {list(x.shape)}")
+    B, H, L, D = x.shape
+    dims = D if dims is None else int(dims)
+    normalize = eps is not None
+    w, wdt = _check_param(w, "w", D, x)
+    if cache is not None:
+        _check_act(cache, "cache", x.device)
+        if cache.dim() != 4 or list(cache.shape[:2]) != [B, H] or cache.shape[3] != D \
+                or cache.dtype != x.dtype:
+            raise ValueError(f"cache must be {x.dtype} [{B}, {H}, cache_len, {D}], got "
+                             f"{cache.dtype} {list(cache.shape)}")
+        dst, cache_len = cache, cache.shape[2]
+    else:
+        dst, cache_len = _out_like(out, x, "out"), 0
+    st = load().nrm_norm_rope(_ptr(x), _ptr(w), _ptr(dst), B, H, L, D, int(normalize),
+                              0.0 if eps is None else eps, dims, int(bool(traditional)), base,
+                              scale, int(offset), int(bool(forward)), int(cache is not None),
+                              cache_len, dt, wdt, _stream())
+    if st:
+        _raise(st)
+    return dst
+
+
+def bench_copy(src, dst):
+    """16-byte copy of src into dst (nrm_bench_copy): the bandwidth ceiling."""
+    _check_act(src, "src")
+    _check_act(dst, "dst", src.device)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    st = load().nrm_bench_copy(_ptr(src), _ptr(dst), n, _stream())
+    if st:
+        _raise(st)
+    return dst

@@ -1,0 +1,260 @@
+// C ABI of the row-wise normalisation library: argument validation, error reporting and
+// dispatch to the kernel launchers. Every argument check runs on the host before any HIP
+// call, so a failed call launches nothing and writes nothing.
+//
+// Error convention (after nuvec-nn's layers: an invalid argument gives a failure that names
+// the operation and states what was wrong, as Dropout does for a probability outside
+// [0, 1)): a non-zero nrm_status plus a thread-local message
+// "<function>: <argument> <reason>, got <value>".
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+#include "nrm.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+nrm_status fail(nrm_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int64_t esize(nrm_dtype d) { return d == NRM_BF16 ? 2 : 4; }
+
+struct Span {  // [lo, lo + bytes)
+  uintptr_t lo;
+  uintptr_t bytes;
+};
+Span span(const void* p, int64_t bytes) { return Span{(uintptr_t)p, (uintptr_t)bytes}; }
+bool overlap(Span a, Span b) {
+  return a.bytes > 0 && b.bytes > 0 && a.lo < b.lo + b.bytes && b.lo < a.lo + a.bytes;
+}
+bool same(Span a, Span b) { return a.lo == b.lo && a.bytes == b.bytes; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+nrm_status check_dtypes(const char* fn, nrm_dtype dtype, nrm_dtype w_dtype) {
+  if (dtype != NRM_F32 && dtype != NRM_BF16)
+    return fail(NRM_ERR_DTYPE, "%s: dtype must be NRM_F32 (0) or NRM_BF16 (1), got %d", fn,
+                (int)dtype);
+  if (w_dtype != dtype && w_dtype != NRM_F32)
+    return fail(NRM_ERR_DTYPE,
+                "%s: w_dtype must equal dtype (%d) or be NRM_F32 (0), got %d", fn, (int)dtype,
+                (int)w_dtype);
+  return NRM_OK;
+}
+
+nrm_status check_rows(const char* fn, int64_t rows, int64_t hidden, nrm_dtype dtype) {
+  if (rows < 0) return fail(NRM_ERR_SHAPE, "%s: rows must be >= 0, got %lld", fn, (long long)rows);
+  if (hidden < 1 || hidden > INT32_MAX)
+    return fail(NRM_ERR_SHAPE, "%s: hidden must be in [1, 2147483647], got %lld", fn,
+                (long long)hidden);
+  if (rows > 0 && rows > INT64_MAX / hidden / esize(dtype))
+    return fail(NRM_ERR_SHAPE, "%s: rows * hidden overflows the address range, got %lld x %lld",
+                fn, (long long)rows, (long long)hidden);
+  return NRM_OK;
+}
+
+// An output must either be exactly `in` (when allowed) or not overlap it at all.
+nrm_status check_out_vs(const char* fn, const char* out_name, Span out, const char* in_name,
+                        Span in, bool exact_ok) {
+  if (!overlap(out, in)) return NRM_OK;
+  if (exact_ok && same(out, in)) return NRM_OK;
+  return fail(NRM_ERR_ALIAS, "%s: %s must %s %s, got a %s overlap", fn, out_name,
+              exact_ok ? "be exactly or not overlap" : "not overlap", in_name,
+              same(out, in) ? "full" : "partial");
+}
+
+nrm_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(NRM_ERR_DEVICE, "%s: kernel launch failed: %s, got HIP error %d", fn,
+                hipGetErrorString(e), (int)e);
+  return NRM_OK;
+}
+
+nrm::RowArgs row_args(const void* x, const void* r, const void* w, const void* b, void* out,
+                      void* h, int64_t rows, int64_t hidden, float eps, nrm_dtype w_dtype) {
+  nrm::RowArgs a;
+  a.x = x; a.r = r; a.w = w; a.b = b; a.out = out; a.h = h;
+  a.rows = rows; a.hidden = hidden; a.eps = eps;
+  a.w_f32 = w_dtype == NRM_F32;
+  return a;
+}
+
+template <int OP>
+hipError_t dispatch_row(const nrm::RowArgs& a, nrm_dtype dtype, bool al, hipStream_t s) {
+  return dtype == NRM_BF16 ? nrm::launch_row<true, OP>(a, al, s)
+                           : nrm::launch_row<false, OP>(a, al, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+nrm_status nrm_rms_norm(const void* x, const void* w, void* out, int64_t rows, int64_t hidden,
+                        float eps, nrm_dtype dtype, nrm_dtype w_dtype, hipStream_t stream) {
+  static const char* fn = "nrm_rms_norm";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, w_dtype);
+  if (st) return st;
+  if ((st = check_rows(fn, rows, hidden, dtype))) return st;
+  if (rows == 0) return NRM_OK;  // empty: nothing to read or write, any pointers accepted
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  const int64_t nb = rows * hidden * esize(dtype);
+  const Span sx = span(x, nb), so = span(out, nb), sw = span(w, w ? hidden * esize(w_dtype) : 0);
+  if ((st = check_out_vs(fn, "out", so, "x", sx, true))) return st;
+  if ((st = check_out_vs(fn, "out", so, "w", sw, false))) return st;
+  const bool al = aligned16(x) && aligned16(out) && (!w || aligned16(w));
+  const nrm::RowArgs a = row_args(x, nullptr, w, nullptr, out, nullptr, rows, hidden, eps, w_dtype);
+  return launched(fn, dispatch_row<nrm::OP_RMS>(a, dtype, al, stream));
+}
+
+nrm_status nrm_add_rms_norm(const void* x, const void* r, const void* w, void* out, void* h_out,
+                            int64_t rows, int64_t hidden, float eps, nrm_dtype dtype,
+                            nrm_dtype w_dtype, hipStream_t stream) {
+  static const char* fn = "nrm_add_rms_norm";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, w_dtype);
+  if (st) return st;
+  if ((st = check_rows(fn, rows, hidden, dtype))) return st;
+  if (rows == 0) return NRM_OK;  // empty: nothing to read or write, any pointers accepted
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!r) return fail(NRM_ERR_NULL, "%s: r must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  if (!h_out) return fail(NRM_ERR_NULL, "%s: h_out must not be NULL, got NULL", fn);
+  const int64_t nb = rows * hidden * esize(dtype);
+  const Span sx = span(x, nb), sr = span(r, nb), so = span(out, nb), sh = span(h_out, nb);
+  const Span sw = span(w, w ? hidden * esize(w_dtype) : 0);
+  if ((st = check_out_vs(fn, "out", so, "h_out", sh, false))) return st;
+  if ((st = check_out_vs(fn, "out", so, "x", sx, true))) return st;
+  if ((st = check_out_vs(fn, "out", so, "r", sr, true))) return st;
+  if ((st = check_out_vs(fn, "h_out", sh, "x", sx, true))) return st;
+  if ((st = check_out_vs(fn, "h_out", sh, "r", sr, true))) return st;
+  if ((st = check_out_vs(fn, "out", so, "w", sw, false))) return st;
+  if ((st = check_out_vs(fn, "h_out", sh, "w", sw, false))) return st;
+  const bool al = aligned16(x) && aligned16(r) && aligned16(out) && aligned16(h_out) &&
+                  (!w || aligned16(w));
+  const nrm::RowArgs a = row_args(x, r, w, nullptr, out, h_out, rows, hidden, eps, w_dtype);
+  return launched(fn, dispatch_row<nrm::OP_ADD_RMS>(a, dtype, al, stream));
+}
+
+nrm_status nrm_layer_norm(const void* x, const void* w, const void* b, void* out, int64_t rows,
+                          int64_t hidden, float eps, nrm_dtype dtype, nrm_dtype w_dtype,
+                          hipStream_t stream) {
+  static const char* fn = "nrm_layer_norm";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, w_dtype);
+  if (st) return st;
+  if ((st = check_rows(fn, rows, hidden, dtype))) return st;
+  if (rows == 0) return NRM_OK;  // empty: nothing to read or write, any pointers accepted
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  const int64_t nb = rows * hidden * esize(dtype);
+  const int64_t pb = hidden * esize(w_dtype);
+  const Span sx = span(x, nb), so = span(out, nb);
+  const Span sw = span(w, w ? pb : 0), sb = span(b, b ? pb : 0);
+  if ((st = check_out_vs(fn, "out", so, "x", sx, true))) return st;
+  if ((st = check_out_vs(fn, "out", so, "w", sw, false))) return st;
+  if ((st = check_out_vs(fn, "out", so, "b", sb, false))) return st;
+  const bool al = aligned16(x) && aligned16(out) && (!w || aligned16(w)) && (!b || aligned16(b));
+  const nrm::RowArgs a = row_args(x, nullptr, w, b, out, nullptr, rows, hidden, eps, w_dtype);
+  return launched(fn, dispatch_row<nrm::OP_LN>(a, dtype, al, stream));
+}
+
+nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64_t B, int64_t H,
+                         int64_t L, int64_t D, int normalize, float eps, int64_t dims,
+                         int traditional, float base, float scale, int64_t offset, int forward,
+                         int cache, int64_t cache_len, nrm_dtype dtype, nrm_dtype w_dtype,
+                         hipStream_t stream) {
+  static const char* fn = "nrm_norm_rope";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, w_dtype);
+  if (st) return st;
+  if (B < 0) return fail(NRM_ERR_SHAPE, "%s: B must be >= 0, got %lld", fn, (long long)B);
+  if (H < 0) return fail(NRM_ERR_SHAPE, "%s: H must be >= 0, got %lld", fn, (long long)H);
+  if (L < 0) return fail(NRM_ERR_SHAPE, "%s: L must be >= 0, got %lld", fn, (long long)L);
+  if (D < 1 || D > INT32_MAX)
+    return fail(NRM_ERR_SHAPE, "%s: D must be in [1, 2147483647], got %lld", fn, (long long)D);
+  if (dims < 0 || dims > D)
+    return fail(NRM_ERR_SHAPE, "%s: dims must be in [0, D = %lld], got %lld", fn, (long long)D,
+                (long long)dims);
+  if (dims % 2) return fail(NRM_ERR_SHAPE, "%s: dims must be even, got %lld", fn, (long long)dims);
+  if (offset < 0)
+    return fail(NRM_ERR_SHAPE, "%s: offset must be >= 0, got %lld", fn, (long long)offset);
+  if (cache) {
+    if (cache_len < 0 || L > cache_len || offset > cache_len - L)
+      return fail(NRM_ERR_SHAPE, "%s: offset + L must be <= cache_len (%lld), got %lld + %lld", fn,
+                  (long long)cache_len, (long long)offset, (long long)L);
+  }
+  // Sizes in bytes, guarding against overflow of B * H * rows * D * element size.
+  const int64_t es = esize(dtype);
+  const int64_t out_rows = cache ? cache_len : L;
+  const int64_t lim = INT64_MAX / es / D;
+  if ((B && H > lim / B) || (B && H && L > lim / (B * H)) || (B && H && out_rows > lim / (B * H)))
+    return fail(NRM_ERR_SHAPE, "%s: B * H * L * D overflows the address range, got %lld x %lld", fn,
+                (long long)B, (long long)H);
+  const int64_t BH = B * H;
+  if (BH * L == 0) return NRM_OK;  // empty: nothing to read or write
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out_or_cache) return fail(NRM_ERR_NULL, "%s: out_or_cache must not be NULL, got NULL", fn);
+  const Span sx = span(x, BH * L * D * es), so = span(out_or_cache, BH * out_rows * D * es);
+  const Span sw = span(w, w ? D * esize(w_dtype) : 0);
+  if ((st = check_out_vs(fn, cache ? "cache" : "out", so, "x", sx, !cache))) return st;
+  if ((st = check_out_vs(fn, cache ? "cache" : "out", so, "w", sw, false))) return st;
+
+  nrm::RopeArgs a;
+  a.x = x; a.w = w; a.out = out_or_cache;
+  a.BH = BH; a.L = L; a.D = (int)D; a.dims = (int)dims;
+  a.normalize = normalize != 0; a.eps = eps; a.traditional = traditional != 0;
+  a.base = base; a.scale = scale; a.offset = offset; a.forward = forward != 0;
+  a.out_rows = out_rows; a.out_row0 = cache ? offset : 0;
+  a.w_f32 = w_dtype == NRM_F32;
+  a.iters = 1;
+  const bool al = aligned16(x) && aligned16(out_or_cache) && (!w || aligned16(w));
+  return launched(fn, dtype == NRM_BF16 ? nrm::launch_norm_rope<true>(a, al, stream)
+                                        : nrm::launch_norm_rope<false>(a, al, stream));
+}
+
+const char* nrm_last_error(void) { return g_err.c_str(); }
+
+const char* nrm_status_name(nrm_status status) {
+  switch (status) {
+    case NRM_OK: return "NRM_OK";
+    case NRM_ERR_NULL: return "NRM_ERR_NULL";
+    case NRM_ERR_SHAPE: return "NRM_ERR_SHAPE";
+    case NRM_ERR_DTYPE: return "NRM_ERR_DTYPE";
+    case NRM_ERR_ALIAS: return "NRM_ERR_ALIAS";
+    case NRM_ERR_DEVICE: return "NRM_ERR_DEVICE";
+  }
+  return "NRM_ERR_UNKNOWN";
+}
+
+int nrm_version(void) { return 100; }
+
+nrm_status nrm_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  static const char* fn = "nrm_bench_copy";
+  g_err.clear();
+  if (bytes < 0 || bytes % 16)
+    return fail(NRM_ERR_SHAPE, "%s: bytes must be a non-negative multiple of 16, got %lld", fn,
+                (long long)bytes);
+  if (bytes == 0) return NRM_OK;
+  if (!src) return fail(NRM_ERR_NULL, "%s: src must not be NULL, got NULL", fn);
+  if (!dst) return fail(NRM_ERR_NULL, "%s: dst must not be NULL, got NULL", fn);
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(NRM_ERR_ALIAS, "%s: src and dst must be 16-byte aligned, got %p and %p", fn, src,
+                dst);
+  if (overlap(span(src, bytes), span(dst, bytes)))
+    return fail(NRM_ERR_ALIAS, "%s: dst must not overlap src, got an overlap", fn);
+  return launched(fn, nrm::launch_copy16(src, dst, bytes / 16, stream));
+}
+
+}  // extern "C"

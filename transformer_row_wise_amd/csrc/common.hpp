@@ -1,0 +1,210 @@
+// Device helpers shared by the row-wise normalisation kernels (gfx950 / CDNA4, wave64).
+//
+// * bf16 values travel packed, two per 32-bit register (element 2k in the low half, 2k+1 in
+//   the high half, the little-endian memory order). Widening is a shift (exact); narrowing
+//   is v_cvt_pk_bf16_f32, round-to-nearest-even on two floats at once.
+// * Global memory is touched in 16-byte chunks (global_load_dwordx4 / global_store_dwordx4):
+//   8 bf16 or 4 fp32 elements per lane per instruction.
+// * Cross-lane sums use DPP within a 16-lane row (quad_perm, row_half_mirror, row_mirror)
+//   and v_readlane across the four rows of a wave. At every step a lane adds its partner's
+//   partial sum to its own, and fp addition is commutative, so every lane of a group ends
+//   with the same bits, and the order is fixed: results are identical run to run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nrm {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Elements per 16-byte chunk.
+template <bool BF16> struct Fmt;
+template <> struct Fmt<true> { static constexpr int VEC = 8; static constexpr int ESZ = 2; };
+template <> struct Fmt<false> { static constexpr int VEC = 4; static constexpr int ESZ = 4; };
+
+// ------------------------------------------------------------------ bf16 <-> fp32
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) {
+  return __builtin_bit_cast(float, u & 0xffff0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __builtin_bit_cast(float, (uint32_t)u << 16);
+}
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// ------------------------------------------------------------------ 16-byte chunks
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+// Unpack a 16-byte chunk into VEC floats.
+template <bool BF16>
+__device__ __forceinline__ void unpack(const u32x4& v, float (&f)[Fmt<BF16>::VEC]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = bf16lo(v[k]);
+      f[2 * k + 1] = bf16hi(v[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __builtin_bit_cast(float, v[k]);
+  }
+}
+
+// Pack VEC floats (rounded to the storage type) into a 16-byte chunk.
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack(const float (&f)[Fmt<BF16>::VEC]) {
+  u32x4 v;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = pack_bf16x2(f[2 * k], f[2 * k + 1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(unsigned, f[k]);
+  }
+  return v;
+}
+
+// V weights starting at element i: fp32 storage, or bf16 storage (only with bf16
+// activations). V is VEC (16-byte aligned chunk of activations) or 1 (scalar path).
+template <bool BF16, int V>
+__device__ __forceinline__ void load_param(const void* p, bool p_f32, int64_t i, float (&f)[V]) {
+  if (!BF16 || p_f32) {
+    const float* q = (const float*)p + i;
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < V / 4; ++k) {
+        f32x4 t = *(const f32x4*)(q + 4 * k);
+        f[4 * k] = t[0]; f[4 * k + 1] = t[1]; f[4 * k + 2] = t[2]; f[4 * k + 3] = t[3];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) f[k] = q[k];
+    }
+  } else {
+    const uint16_t* q = (const uint16_t*)p + i;
+    if constexpr (V == 8) {
+      float t[8];
+      unpack<true>(ld16(q), t);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) f[k] = t[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) f[k] = bf16_to_f32(q[k]);
+    }
+  }
+}
+
+// V activations at element i (16-byte chunk when V == VEC, else element by element).
+template <bool BF16, int V>
+__device__ __forceinline__ void load_act(const void* p, int64_t i, float (&f)[V]) {
+  if constexpr (V == Fmt<BF16>::VEC) {
+    unpack<BF16>(ld16((const char*)p + i * Fmt<BF16>::ESZ), f);
+  } else if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) f[k] = bf16_to_f32(((const uint16_t*)p)[i + k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) f[k] = ((const float*)p)[i + k];
+  }
+}
+
+template <bool BF16, int V>
+__device__ __forceinline__ void store_act(void* p, int64_t i, const float (&f)[V]) {
+  if constexpr (V == Fmt<BF16>::VEC) {
+    st16((char*)p + i * Fmt<BF16>::ESZ, pack<BF16>(f));
+  } else if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) ((uint16_t*)p)[i + k] = f32_to_bf16(f[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) ((float*)p)[i + k] = f[k];
+  }
+}
+
+// Round V floats to the storage type and back (the value that a store would keep).
+template <bool BF16, int V>
+__device__ __forceinline__ void round_to_storage(float (&f)[V]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) f[k] = bf16_to_f32(f32_to_bf16(f[k]));
+  }
+}
+
+// ------------------------------------------------------------------ DPP reductions
+
+// DPP control words (gfx9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over aligned groups of G lanes (G = 1, 2, 4, 8, 16, 32 or 64); every lane of a
+// group receives the group's sum.
+template <int G, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "G");
+  if constexpr (G >= 2) v += dpp<DPP_QUAD_XOR1>(v);
+  if constexpr (G >= 4) v += dpp<DPP_QUAD_XOR2>(v);
+  if constexpr (G >= 8) v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  if constexpr (G >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Sum over the whole wave, returned wave-uniform: DPP inside each 16-lane row, then the
+// four row sums read with v_readlane and added in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  v = group_sum<16>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// rstd = 1 / sqrt(sum / n + eps), formed in fp64 from an fp32 or fp64 sum (one row scalar).
+__device__ __forceinline__ double rstd_f64(double sum, int64_t n, float eps) {
+  return 1.0 / __builtin_sqrt(sum / (double)n + (double)eps);
+}
+
+}  // namespace nrm

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel launchers.
+#pragma once
+
+#include "common.hpp"
+#include "row_kernels.hpp"
+
+namespace nrm {
+
+struct RopeArgs {
+  const void* x;
+  const void* w;
+  void* out;
+  int64_t BH;        // B * H
+  int64_t L;
+  int D;
+  int dims;
+  int normalize;
+  float eps;
+  int traditional;
+  float base;
+  float scale;
+  int64_t offset;
+  int forward;
+  int64_t out_rows;  // rows per (b, h) in the output: L, or cache_len
+  int64_t out_row0;  // first output row of each (b, h): 0, or offset
+  int w_f32;
+  int iters;         // filled in by the launcher
+};
+
+// Kernel-shape override for tests, from the environment variable NRM_FORCE_PATH:
+// "wave" (one wave per row), "block" (one block per row), "chunked" (looping kernel,
+// 16-byte chunks), "scalar" (looping kernel element by element; for NormRope: the generic
+// kernel). Unset or anything else: automatic choice. A forced shape that cannot hold the
+// row falls back to the automatic choice.
+enum ForcePath : int { PATH_AUTO = 0, PATH_WAVE, PATH_BLOCK, PATH_CHUNKED, PATH_SCALAR };
+int forced_path();
+inline bool force_generic_path() { return forced_path() == PATH_SCALAR; }
+
+template <bool BF16, int OP>
+hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream);
+
+template <bool BF16>
+hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t stream);
+
+hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t stream);
+
+}  // namespace nrm

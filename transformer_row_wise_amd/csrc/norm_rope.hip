@@ -1,0 +1,287 @@
+// NormRope: RMS-normalise each [b, h, l] row of a [B, H, L, D] array (all D features, times
+// w), then rotate its first `dims` features at position offset + l; write the result as a
+// new [B, H, L, D] array or into rows offset + l of a [B, H, cache_len, D] cache.
+//
+// Source: nuvec-core 0.5.0 fast::FastOp, variants NormRope and Rope. The rotation is the
+// textbook RoPE (RoFormer, section 3.2): pair i turns by a = scale * position * theta_i with
+// theta_i = base^(-2i/dims); half mode pairs (i, i + dims/2), traditional mode (2i, 2i+1);
+// the inverse rotation (forward = 0) turns by -a.
+//
+// Precision: the angle, theta and sin/cos are fp64 (an fp32 angle at positions in the
+// thousands is off by ~1e-4 rad). The rotation u*c - v*s runs in fp64 on u = x*w (exact in
+// fp64), so cancellation between the two products costs nothing; the fp32 row statistic only
+// scales the result. Features at index >= dims get x * rstd * w in fp32.
+//
+// rope_fast: one block per (position l, chunk of b*h rows). The block first computes
+// (cos, sin) of every pair at its position into LDS, once, then each group of G lanes takes
+// a row: in half mode a lane loads the 16-byte chunk at feature j*VEC and its partner chunk
+// at dims/2 + j*VEC, so each rotated pair sits in one lane and no lane exchange is needed;
+// in traditional mode a chunk holds VEC/2 neighbouring pairs. The row's sum of squares is a
+// DPP reduction over the G lanes. Rows with the same l share the LDS table.
+// rope_generic: any D / dims / alignment, one wave per row, element at a time.
+#include "launch.hpp"
+
+namespace nrm {
+
+template <bool BF16, bool HALF, int G, int QC>
+__global__ void __launch_bounds__(256)
+rope_fast(RopeArgs a) {
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr int RPW = 64 / G;                 // rows per wave
+  constexpr int RPB = 4 * RPW;                // rows per block step
+  constexpr int PAIRS = HALF ? V : V / 2;     // rotated pairs per lane
+  constexpr int MAXP = G * PAIRS;             // pairs one group can hold
+  __shared__ double cs_c[MAXP];
+  __shared__ double cs_s[MAXP];
+
+  const int64_t l = blockIdx.x;
+  const int64_t pos = a.offset + l;
+  const int half = a.dims / 2;
+  for (int t = threadIdx.x; t < half; t += 256) {
+    const double theta = pow((double)a.base, (double)(-2 * t) / (double)a.dims);
+    const double ang = ((double)a.scale * (double)pos) * theta;
+    double s, c;
+    sincos(ang, &s, &c);
+    cs_c[t] = c;
+    cs_s[t] = a.forward ? s : -s;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / G, lj = lane % G;
+  const int npc = HALF ? half / V : a.dims / V;  // rotated chunks (pairs of chunks in half mode)
+  const int nqc = (a.D - a.dims) / V;            // pass-through chunks
+  const bool has_pc = lj < npc;
+  const bool norm = a.normalize != 0;
+  const bool has_w = norm && a.w != nullptr;
+
+  double c[PAIRS], s[PAIRS];
+  float wu[V], wv[V], wq[QC > 0 ? QC : 1][V];
+#pragma unroll
+  for (int e = 0; e < PAIRS; ++e) { c[e] = 1.0; s[e] = 0.0; }
+#pragma unroll
+  for (int e = 0; e < V; ++e) { wu[e] = 1.f; wv[e] = 1.f; }
+  const int off_u = lj * V;
+  const int off_v = HALF ? half + lj * V : 0;
+  if (has_pc) {
+#pragma unroll
+    for (int e = 0; e < PAIRS; ++e) {
+      const int p = HALF ? lj * V + e : lj * (V / 2) + e;
+      c[e] = cs_c[p];
+      s[e] = cs_s[p];
+    }
+    if (has_w) {
+      load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
+      if (HALF) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QC; ++q) {
+    if (has_w && lj + G * q < nqc) {
+      load_param<BF16, V>(a.w, a.w_f32, a.dims + (int64_t)(lj + G * q) * V, wq[q]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) wq[q][e] = 1.f;
+    }
+  }
+
+  const int64_t bh0 = (int64_t)blockIdx.y * a.iters * RPB;
+  for (int it = 0; it < a.iters; ++it) {
+    const int64_t bh = bh0 + (int64_t)it * RPB + wave * RPW + g;
+    if (bh >= a.BH) break;  // uniform over the group of G lanes that owns the row
+    const char* xrow = (const char*)a.x + ((bh * a.L + l) * a.D) * ESZ;
+    char* orow = (char*)a.out + ((bh * a.out_rows + a.out_row0 + l) * a.D) * ESZ;
+
+    u32x4 xu = {0, 0, 0, 0}, xv = {0, 0, 0, 0}, xq[QC > 0 ? QC : 1];
+    if (has_pc) {
+      xu = ld16(xrow + off_u * ESZ);
+      if (HALF) xv = ld16(xrow + off_v * ESZ);
+    }
+#pragma unroll
+    for (int q = 0; q < QC; ++q) {
+      xq[q] = u32x4{0, 0, 0, 0};
+      if (lj + G * q < nqc) xq[q] = ld16(xrow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ);
+    }
+
+    float fu[V], fv[V];
+    unpack<BF16>(xu, fu);
+    unpack<BF16>(xv, fv);
+    double rstd = 1.0;
+    if (norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fu[e], fu[e], ss);
+      if (HALF) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fv[e], fv[e], ss);
+      }
+#pragma unroll
+      for (int q = 0; q < QC; ++q) {
+        float fq[V];
+        unpack<BF16>(xq[q], fq);
+#pragma unroll
+        for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fq[e], fq[e], ss);
+      }
+      rstd = rstd_f64((double)group_sum<G>(ss), a.D, a.eps);
+    }
+
+    if (has_pc) {
+      if constexpr (HALF) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const double u = (double)fu[e] * (double)wu[e];
+          const double v = (double)fv[e] * (double)wv[e];
+          fu[e] = (float)((u * c[e] - v * s[e]) * rstd);
+          fv[e] = (float)((u * s[e] + v * c[e]) * rstd);
+        }
+        st16(orow + off_u * ESZ, pack<BF16>(fu));
+        st16(orow + off_v * ESZ, pack<BF16>(fv));
+      } else {
+#pragma unroll
+        for (int e = 0; e < V / 2; ++e) {
+          const double u = (double)fu[2 * e] * (double)wu[2 * e];
+          const double v = (double)fu[2 * e + 1] * (double)wu[2 * e + 1];
+          fu[2 * e] = (float)((u * c[e] - v * s[e]) * rstd);
+          fu[2 * e + 1] = (float)((u * s[e] + v * c[e]) * rstd);
+        }
+        st16(orow + off_u * ESZ, pack<BF16>(fu));
+      }
+    }
+    const float rstd_f = (float)rstd;
+#pragma unroll
+    for (int q = 0; q < QC; ++q) {
+      if (lj + G * q < nqc) {
+        float fq[V];
+        unpack<BF16>(xq[q], fq);
+#pragma unroll
+        for (int e = 0; e < V; ++e) fq[e] = norm ? (fq[e] * rstd_f) * wq[q][e] : fq[e];
+        st16(orow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ, pack<BF16>(fq));
+      }
+    }
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+rope_generic(RopeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = a.BH * a.L;
+  const int half = a.dims / 2;
+  const bool norm = a.normalize != 0;
+  const bool has_w = norm && a.w != nullptr;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < nrows;
+       row += (int64_t)gridDim.x * 4) {
+    const int64_t bh = row / a.L, l = row % a.L;
+    const int64_t xi = row * a.D;
+    const int64_t oi = (bh * a.out_rows + a.out_row0 + l) * a.D;
+    float ss = 0.f;
+    for (int e = lane; e < a.D; e += 64) {
+      float f[1];
+      load_act<BF16, 1>(a.x, xi + e, f);
+      ss = __builtin_fmaf(f[0], f[0], ss);
+    }
+    // The wave sum also orders every read of the row before the first write below.
+    const double rstd = norm ? rstd_f64((double)wave_sum(ss), a.D, a.eps) : 1.0;
+    const double pos = (double)(a.offset + l);
+    for (int p = lane; p < half; p += 64) {
+      const int iu = a.traditional ? 2 * p : p;
+      const int iv = a.traditional ? 2 * p + 1 : p + half;
+      float fu[1], fv[1], wu[1] = {1.f}, wv[1] = {1.f};
+      load_act<BF16, 1>(a.x, xi + iu, fu);
+      load_act<BF16, 1>(a.x, xi + iv, fv);
+      if (has_w) {
+        load_param<BF16, 1>(a.w, a.w_f32, iu, wu);
+        load_param<BF16, 1>(a.w, a.w_f32, iv, wv);
+      }
+      const double theta = pow((double)a.base, (double)(-2 * p) / (double)a.dims);
+      double s, c;
+      sincos(((double)a.scale * pos) * theta, &s, &c);
+      if (!a.forward) s = -s;
+      const double u = (double)fu[0] * (double)wu[0];
+      const double v = (double)fv[0] * (double)wv[0];
+      float ou[1] = {(float)((u * c - v * s) * rstd)};
+      float ov[1] = {(float)((u * s + v * c) * rstd)};
+      store_act<BF16, 1>(a.out, oi + iu, ou);
+      store_act<BF16, 1>(a.out, oi + iv, ov);
+    }
+    const float rstd_f = (float)rstd;
+    for (int e = a.dims + lane; e < a.D; e += 64) {
+      float f[1], wv[1] = {1.f};
+      load_act<BF16, 1>(a.x, xi + e, f);
+      if (has_w) load_param<BF16, 1>(a.w, a.w_f32, e, wv);
+      f[0] = norm ? (f[0] * rstd_f) * wv[0] : f[0];
+      store_act<BF16, 1>(a.out, oi + e, f);
+    }
+  }
+}
+
+namespace {
+
+template <bool BF16, bool HALF, int G, int QC>
+hipError_t go_fast(const RopeArgs& a0, hipStream_t stream) {
+  RopeArgs a = a0;
+  constexpr int RPB = 4 * (64 / G);
+  const int64_t steps = (a.BH + RPB - 1) / RPB;  // block steps to cover all b*h rows
+  // Enough blocks to fill the chip (>= ~2048) while keeping each block's sin/cos table
+  // shared by as many rows as possible.
+  int64_t chunks = (2048 + a.L - 1) / a.L;
+  if (chunks > steps) chunks = steps;
+  if (chunks > 65535) chunks = 65535;
+  if (chunks < 1) chunks = 1;
+  a.iters = (int)((steps + chunks - 1) / chunks);
+  chunks = (steps + a.iters - 1) / a.iters;
+  dim3 grid((unsigned)a.L, (unsigned)chunks);
+  rope_fast<BF16, HALF, G, QC><<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool HALF, int G>
+hipError_t pick_qc(const RopeArgs& a, int qc, hipStream_t stream) {
+  if (qc == 0) return go_fast<BF16, HALF, G, 0>(a, stream);
+  if (qc == 1) return go_fast<BF16, HALF, G, 1>(a, stream);
+  return go_fast<BF16, HALF, G, 2>(a, stream);
+}
+
+template <bool BF16, bool HALF>
+hipError_t pick_g(const RopeArgs& a, int g, int qc, hipStream_t stream) {
+  switch (g) {
+    case 8: return pick_qc<BF16, HALF, 8>(a, qc, stream);
+    case 16: return pick_qc<BF16, HALF, 16>(a, qc, stream);
+    case 32: return pick_qc<BF16, HALF, 32>(a, qc, stream);
+    default: return pick_qc<BF16, HALF, 64>(a, qc, stream);
+  }
+}
+
+}  // namespace
+
+// The fast kernel applies when every chunk is a whole 16-byte vector: D, the rotated
+// chunks and the pass-through chunks are VEC-multiples and the arrays are 16-byte aligned.
+template <bool BF16>
+hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t stream) {
+  constexpr int V = Fmt<BF16>::VEC;
+  const int half = a.dims / 2;
+  const bool chunks_ok = aligned16 && a.D % V == 0 && a.dims % V == 0 &&
+                         (a.traditional || half % V == 0) && a.L <= 0x7fffffff;
+  if (chunks_ok && !force_generic_path()) {
+    const int npc = a.traditional ? a.dims / V : half / V;
+    const int nqc = (a.D - a.dims) / V;
+    for (int g = 8; g <= 64; g *= 2) {
+      if (npc <= g && nqc <= 2 * g) {
+        const int qc = (nqc + g - 1) / g;
+        return a.traditional ? pick_g<BF16, false>(a, g, qc, stream)
+                             : pick_g<BF16, true>(a, g, qc, stream);
+      }
+    }
+  }
+  const int64_t nrows = a.BH * a.L;
+  int64_t blocks = (nrows + 3) / 4;
+  if (blocks > 1048576) blocks = 1048576;
+  rope_generic<BF16><<<(unsigned)blocks, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_norm_rope<true>(const RopeArgs&, bool, hipStream_t);
+template hipError_t launch_norm_rope<false>(const RopeArgs&, bool, hipStream_t);
+
+}  // namespace nrm

@@ -1,0 +1,292 @@
+// Row kernels for RMSNorm, residual add-RMSNorm and LayerNorm over the last axis.
+//
+// Operations (nuvec-core 0.5.0 fast::FastOp, variants RmsNorm, AddRmsNorm and LayerNorm):
+//   RMS      out = x * rstd * w,             rstd = 1 / sqrt(sum(x^2) / D + eps)
+//   ADD_RMS  h = RN(x + r); out = h * rstd * w, rstd from sum(h^2) of the rounded h
+//   LN       out = (x - mu) * rstd * w + b,  mu = sum(x) / D, rstd = 1 / sqrt(sum((x-mu)^2)/D + eps)
+//
+// Three shapes of the same arithmetic:
+//   row_regs<..., WPR = 1>  one wave64 per row, the whole row in registers (hidden <= 64*NV*VEC);
+//                           a block holds four independent waves (four rows);
+//   row_regs<..., WPR = 8>  one 512-thread block per row, row in registers, cross-wave sums
+//                           through LDS (hidden <= 512*NV*VEC);
+//   row_chunked             one 256-thread block per row looping over the row: any width, and
+//                           V = 1 for rows whose width or base addresses are not 16-byte
+//                           multiples. The row is re-read (L2) for the second pass.
+// Every element of x (and r) is read from HBM once and every output element written once;
+// w and b are small and come from L2.
+#pragma once
+
+#include "common.hpp"
+
+namespace nrm {
+
+enum RowOp : int { OP_RMS = 0, OP_ADD_RMS = 1, OP_LN = 2 };
+
+struct RowArgs {
+  const void* x;
+  const void* r;   // ADD_RMS only
+  const void* w;   // may be null (= 1)
+  const void* b;   // LN only, may be null (= 0)
+  void* out;
+  void* h;         // ADD_RMS only
+  int64_t rows;
+  int64_t hidden;  // elements per row, < 2^31
+  float eps;
+  int w_f32;       // w and b stored as fp32 (else bf16, only with bf16 activations)
+};
+
+// Cross-lane sum over the threads of one row: the wave itself (WPR == 1) or the block,
+// through `red` (one slot per wave) in LDS.
+template <int WPR, typename T>
+__device__ __forceinline__ T row_sum(T v, T* red) {
+  v = wave_sum(v);
+  if constexpr (WPR > 1) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    T t = red[0];
+#pragma unroll
+    for (int i = 1; i < WPR; ++i) t += red[i];
+    v = t;
+  }
+  return v;
+}
+
+// out = (x - mu) * rstd * w + b in fp64 for one chunk of V elements, with w / b optional.
+template <bool BF16, int V, bool HAS_W, bool HAS_B>
+__device__ __forceinline__ void ln_chunk_out(const float (&f)[V], const RowArgs& a, int64_t i,
+                                             double mu, double rstd, float (&y)[V]) {
+  float wv[V], bv[V];
+  if constexpr (HAS_W) load_param<BF16, V>(a.w, a.w_f32, i, wv);
+  if constexpr (HAS_B) load_param<BF16, V>(a.b, a.w_f32, i, bv);
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    double t = ((double)f[e] - mu) * rstd;
+    if constexpr (HAS_W && HAS_B) t = __builtin_fma(t, (double)wv[e], (double)bv[e]);
+    else if constexpr (HAS_W) t = t * (double)wv[e];
+    else if constexpr (HAS_B) t = t + (double)bv[e];
+    y[e] = (float)t;
+  }
+}
+
+template <bool BF16, int OP, int NV, int WPR>
+__global__ void __launch_bounds__(WPR == 1 ? 256 : 64 * WPR)
+row_regs(RowArgs a) {
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr int TPR = 64 * WPR;  // threads per row
+  __shared__ float red_f[WPR > 1 ? WPR : 1];
+  __shared__ double red_d[2][WPR > 1 ? WPR : 1];
+
+  const int64_t row = WPR == 1 ? (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6) : (int64_t)blockIdx.x;
+  const int tid = WPR == 1 ? (threadIdx.x & 63) : threadIdx.x;
+  if (row >= a.rows) return;  // uniform over the wave (WPR == 1) or the block (WPR > 1)
+
+  const int nvec = (int)(a.hidden / V);
+  const int64_t base = row * a.hidden * ESZ;  // byte offset of the row
+  const char* xr = (const char*)a.x + base;
+
+  // All loads of the row are issued before any store, so an output that is exactly an
+  // input (in-place use) is read before it is written.
+  u32x4 xv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int j = tid + k * TPR;
+    if (j < nvec) xv[k] = ld16(xr + (int64_t)j * 16);
+  }
+
+  if constexpr (OP == OP_RMS || OP == OP_ADD_RMS) {
+    float acc = 0.f;
+    if constexpr (OP == OP_ADD_RMS) {
+      const char* rr = (const char*)a.r + base;
+      u32x4 rv[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int j = tid + k * TPR;
+        if (j < nvec) rv[k] = ld16(rr + (int64_t)j * 16);
+      }
+      char* hr = (char*)a.h + base;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int j = tid + k * TPR;
+        if (j < nvec) {
+          float fx[V], fr[V];
+          unpack<BF16>(xv[k], fx);
+          unpack<BF16>(rv[k], fr);
+#pragma unroll
+          for (int e = 0; e < V; ++e) fx[e] = fx[e] + fr[e];
+          xv[k] = pack<BF16>(fx);  // h rounded to the storage type, kept for the output pass
+          st16(hr + (int64_t)j * 16, xv[k]);
+          unpack<BF16>(xv[k], fx);
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc = __builtin_fmaf(fx[e], fx[e], acc);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int j = tid + k * TPR;
+        if (j < nvec) {
+          float fx[V];
+          unpack<BF16>(xv[k], fx);
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc = __builtin_fmaf(fx[e], fx[e], acc);
+        }
+      }
+    }
+    const float ss = row_sum<WPR>(acc, red_f);
+    const float rstd = (float)rstd_f64((double)ss, a.hidden, a.eps);
+
+    char* orow = (char*)a.out + base;
+    const bool has_w = a.w != nullptr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int j = tid + k * TPR;
+      if (j < nvec) {
+        float f[V], wv[V];
+        unpack<BF16>(xv[k], f);
+        if (has_w) {
+          load_param<BF16, V>(a.w, a.w_f32, (int64_t)j * V, wv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) wv[e] = 1.f;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = (f[e] * rstd) * wv[e];
+        st16(orow + (int64_t)j * 16, pack<BF16>(f));
+      }
+    }
+  } else {  // OP_LN: fp64 statistics and output arithmetic
+    double s1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int j = tid + k * TPR;
+      if (j < nvec) {
+        float f[V];
+        unpack<BF16>(xv[k], f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) s1 += (double)f[e];
+      }
+    }
+    const double mu = row_sum<WPR>(s1, red_d[0]) / (double)a.hidden;
+    double s2 = 0.0;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int j = tid + k * TPR;
+      if (j < nvec) {
+        float f[V];
+        unpack<BF16>(xv[k], f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const double d = (double)f[e] - mu;
+          s2 = __builtin_fma(d, d, s2);
+        }
+      }
+    }
+    const double rstd = rstd_f64(row_sum<WPR>(s2, red_d[1]), a.hidden, a.eps);
+
+    char* orow = (char*)a.out + base;
+    const bool hw = a.w != nullptr, hb = a.b != nullptr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int j = tid + k * TPR;
+      if (j < nvec) {
+        float f[V], y[V];
+        unpack<BF16>(xv[k], f);
+        const int64_t i = (int64_t)j * V;
+        if (hw && hb) ln_chunk_out<BF16, V, true, true>(f, a, i, mu, rstd, y);
+        else if (hw) ln_chunk_out<BF16, V, true, false>(f, a, i, mu, rstd, y);
+        else if (hb) ln_chunk_out<BF16, V, false, true>(f, a, i, mu, rstd, y);
+        else ln_chunk_out<BF16, V, false, false>(f, a, i, mu, rstd, y);
+        st16(orow + (int64_t)j * 16, pack<BF16>(y));
+      }
+    }
+  }
+}
+
+// One block of 256 threads per row, looping over the row in chunks of V elements
+// (V = VEC for 16-byte aligned rows, 1 otherwise). Grid-strided over rows.
+template <bool BF16, int OP, int V>
+__global__ void __launch_bounds__(256)
+row_chunked(RowArgs a) {
+  constexpr int WPR = 4;
+  __shared__ float red_f[WPR];
+  __shared__ double red_d[2][WPR];
+  const int64_t nch = a.hidden / V;
+  const bool has_w = a.w != nullptr, has_b = a.b != nullptr;
+
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const int64_t e0 = row * a.hidden;  // element offset of the row
+    if constexpr (OP == OP_RMS || OP == OP_ADD_RMS) {
+      float acc = 0.f;
+      for (int64_t j = threadIdx.x; j < nch; j += 256) {
+        float f[V];
+        load_act<BF16, V>(a.x, e0 + j * V, f);
+        if constexpr (OP == OP_ADD_RMS) {
+          float fr[V];
+          load_act<BF16, V>(a.r, e0 + j * V, fr);
+#pragma unroll
+          for (int e = 0; e < V; ++e) f[e] = f[e] + fr[e];
+          round_to_storage<BF16, V>(f);
+          store_act<BF16, V>(a.h, e0 + j * V, f);
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
+      }
+      const float rstd = (float)rstd_f64((double)row_sum<WPR>(acc, red_f), a.hidden, a.eps);
+      // Each thread re-reads exactly the chunks it wrote or read in the first pass.
+      const void* src = OP == OP_ADD_RMS ? (const void*)a.h : a.x;
+      for (int64_t j = threadIdx.x; j < nch; j += 256) {
+        float f[V], wv[V];
+        load_act<BF16, V>(src, e0 + j * V, f);
+        if (has_w) {
+          load_param<BF16, V>(a.w, a.w_f32, j * V, wv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) wv[e] = 1.f;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = (f[e] * rstd) * wv[e];
+        store_act<BF16, V>(a.out, e0 + j * V, f);
+      }
+    } else {
+      double s1 = 0.0;
+      for (int64_t j = threadIdx.x; j < nch; j += 256) {
+        float f[V];
+        load_act<BF16, V>(a.x, e0 + j * V, f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) s1 += (double)f[e];
+      }
+      const double mu = row_sum<WPR>(s1, red_d[0]) / (double)a.hidden;
+      double s2 = 0.0;
+      for (int64_t j = threadIdx.x; j < nch; j += 256) {
+        float f[V];
+        load_act<BF16, V>(a.x, e0 + j * V, f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const double d = (double)f[e] - mu;
+          s2 = __builtin_fma(d, d, s2);
+        }
+      }
+      const double rstd = rstd_f64(row_sum<WPR>(s2, red_d[1]), a.hidden, a.eps);
+      for (int64_t j = threadIdx.x; j < nch; j += 256) {
+        float f[V], y[V];
+        load_act<BF16, V>(a.x, e0 + j * V, f);
+        if (has_w && has_b) ln_chunk_out<BF16, V, true, true>(f, a, j * V, mu, rstd, y);
+        else if (has_w) ln_chunk_out<BF16, V, true, false>(f, a, j * V, mu, rstd, y);
+        else if (has_b) ln_chunk_out<BF16, V, false, true>(f, a, j * V, mu, rstd, y);
+        else ln_chunk_out<BF16, V, false, false>(f, a, j * V, mu, rstd, y);
+        store_act<BF16, V>(a.out, e0 + j * V, y);
+      }
+    }
+    __syncthreads();  // the LDS slots are reused by the next row of this block
+  }
+}
+
+// Host-side launch of one row operation; picks the kernel shape from the row width and
+// alignment. Returns the HIP error of the launch.
+template <bool BF16, int OP>
+hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream);
+
+}  // namespace nrm
