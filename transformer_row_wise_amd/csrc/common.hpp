@@ -59,8 +59,13 @@ __device__ __forceinline__ void unpack(const u32x4& v, float (&f)[Fmt<BF16>::VEC
       f[2 * k + 1] = bf16hi(v[k]);
     }
   } else {
+    // Each element goes through a scalar first: __builtin_bit_cast applied directly to an
+    // ext_vector element reads element 0 whatever the index (seen with this hipcc).
 #pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = __builtin_bit_cast(float, v[k]);
+    for (int k = 0; k < 4; ++k) {
+      const unsigned u = v[k];
+      f[k] = __builtin_bit_cast(float, u);
+    }
   }
 }
 
