@@ -13,8 +13,9 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
                Infinity Cache.
 --profile      only warm-up and timed calls of the headline kernel plus the copy kernel
                (for rocprofv3 runs); no CPU baseline.
---summarize-pmc FETCH_CSV WRITE_CSV
-               turn two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter files of a
+--summarize-pmc FETCH_FILE WRITE_FILE
+               turn two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` outputs (rocpd .db or
+               counter_collection.csv) of a
                --profile run into profiles/traffic_add_rms_norm_bf16_16384x8192.json, scaled
                by what the same counters read for the 16-byte copy kernel of known size.
 
@@ -41,9 +42,8 @@ METRIC = "achieved HBM GB/s (% of peak) + rows/s, add-RMSNorm bf16 16384x8192"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 ROWS, HIDDEN = 16384, 8192
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_add_rms_norm_bf16_16384x8192.json")
-HEADLINE_KERNEL = "row_regs<true, 1, 16, 1>"  # bf16, add-RMSNorm, 16 chunks/lane, 1 wave/row
+HEADLINE_KERNEL = "row_block<true, 1, 2, 1, true>"  # bf16, add-RMSNorm, 2 chunks/thread, w bf16, exact
 COPY_KERNEL = "copy16_kernel"
-CPU_SAMPLE_ROWS = 4096
 
 
 def kernel_source_hash():
@@ -81,6 +81,36 @@ def time_calls(fn, steps, warmup):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return per, wall_ms
+
+
+def time_graph(fn, calls, replays=5):
+    """Per-call GPU time (ms) of `calls` back-to-back calls captured in one HIP graph and
+    replayed: no host time between kernels, which matters for calls of a few microseconds."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(replays):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        per.append(s.elapsed_time(e) / calls)
+    del g
+    return per
 
 
 def copy_ceiling(nbytes, steps):
@@ -128,35 +158,40 @@ def _oracle_chunk(args):
     return time.perf_counter() - t
 
 
-def cpu_baseline(inp, rows):
-    """The oracle, as it is, on the first `rows` rows of the workload, spread over a process
-    pool with one process per available core (at most 16)."""
+def cpu_baseline(inp, min_cpu_s=10.0, max_passes=3):
+    """The oracle, as it is, over all rows of the workload, spread over a process pool with
+    one process per available core (at most 16); whole passes are repeated until at least
+    `min_cpu_s` seconds of CPU work are done (at most `max_passes`)."""
     import multiprocessing as mp
 
     import numpy as np
     import torch
 
     cores = min(len(os.sched_getaffinity(0)), 16)
+    rows = inp.x.shape[0]
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
-    xb, rb, wb = bits(inp.x[:rows]), bits(inp.r[:rows]), bits(inp.w)
+    xb, rb, wb = bits(inp.x), bits(inp.r), bits(inp.w)
     step = 128
     jobs = [(xb[i:i + step], rb[i:i + step], wb, inp.eps) for i in range(0, rows, step)]
     ctx = mp.get_context("spawn")
+    busy, passes = 0.0, 0
     with ctx.Pool(cores) as pool:
         pool.map(_oracle_chunk, jobs[:cores])  # start-up and imports, untimed
         t0 = time.perf_counter()
-        busy = pool.map(_oracle_chunk, jobs)
+        while passes < max_passes and (passes == 0 or busy < min_cpu_s):
+            busy += sum(pool.map(_oracle_chunk, jobs))
+            passes += 1
         wall = time.perf_counter() - t0
-    nbytes = add_rms_bytes(rows, inp.x.shape[1], 2, 2)
+    nbytes = passes * add_rms_bytes(rows, inp.x.shape[1], 2, 2)
     return {
         "value": round(nbytes / wall / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"first {rows} of {inp.x.shape[0]} rows of the same add-RMSNorm bf16 "
-                  f"[16384, 8192] inputs, fp64 oracle in a pool of {cores} processes "
-                  f"(chunks of {step} rows); {sum(busy):.1f} s of CPU work, {wall:.2f} s wall",
-        "rows_per_s": round(rows / wall, 1),
+        "sample": f"all {rows} rows of the same add-RMSNorm bf16 [{rows}, {inp.x.shape[1]}] "
+                  f"inputs, {passes} pass(es); fp64 oracle in a pool of {cores} processes "
+                  f"(chunks of {step} rows); {busy:.1f} s of CPU work, {wall:.2f} s wall",
+        "rows_per_s": round(passes * rows / wall, 1),
         "wall_s": round(wall, 3),
     }
 
@@ -224,8 +259,8 @@ def headline(args):
         },
     }
     if not args.no_cpu_baseline:
-        print(f"# cpu baseline: oracle on {CPU_SAMPLE_ROWS} rows", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, CPU_SAMPLE_ROWS)
+        print("# cpu baseline: the oracle over the workload's rows", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(res), flush=True)
 
 
@@ -244,13 +279,17 @@ def suite(args):
     def n_sets(bytes_per_call):
         return max(1, min(16, -(-512 * 2**20 // bytes_per_call)))
 
+    def calls(bytes_per_call):
+        """Calls per graph: about 0.5 GB of traffic, between 8 and 400 calls."""
+        return max(8, min(400, (512 * 2**20) // bytes_per_call))
+
     def emit(cfg, op, shape, nbytes, rows, per):
-        avg = statistics.mean(per)
+        avg = statistics.median(per)
         gbps = nbytes / (avg * 1e-3) / 1e9
         print(json.dumps({"cfg": cfg, "op": op, "shape": shape, "bytes": nbytes,
-                          "gpu_us_mean": round(avg * 1e3, 2),
-                          "gpu_us_median": round(statistics.median(per) * 1e3, 2),
-                          "gpu_us_min": round(min(per) * 1e3, 2),
+                          "gpu_us_median": round(avg * 1e3, 3),
+                          "gpu_us_min": round(min(per) * 1e3, 3),
+                          "timing": "HIP graph of back-to-back calls, median of 5 replays",
                           "gpu_GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 2),
                           "rows_per_s": round(rows / (avg * 1e-3), 1)}), file=sys.stderr,
               flush=True)
@@ -262,10 +301,9 @@ def suite(args):
         sets = [(inp.x.cuda(), inp.r.cuda()) for _ in range(n_sets(nbytes))]
         w = inp.w.cuda()
         outs = [(torch.empty_like(s[0]), torch.empty_like(s[0])) for s in sets]
-        per, _ = time_calls(lambda i: nrm.add_rms_norm(*sets[i % len(sets)], w, inp.eps,
-                                                       out=outs[i % len(sets)][0],
-                                                       h=outs[i % len(sets)][1]),
-                            args.steps, args.warmup)
+        per = time_graph(lambda i: nrm.add_rms_norm(*sets[i % len(sets)], w, inp.eps,
+                                                    out=outs[i % len(sets)][0],
+                                                    h=outs[i % len(sets)][1]), calls(nbytes))
         emit(cfg, "add_rms_norm", [rows, hidden, str(inp.x.dtype)], nbytes, rows, per)
 
     run_add("1", workloads.cfg_add_rms_small_f32())
@@ -278,8 +316,7 @@ def suite(args):
         w = inp.w.cuda() if affine else None
         b = inp.b.cuda() if affine else None
         out = torch.empty_like(x)
-        per, _ = time_calls(lambda i: nrm.layer_norm(x, w, b, inp.eps, out=out), args.steps,
-                            args.warmup)
+        per = time_graph(lambda i: nrm.layer_norm(x, w, b, inp.eps, out=out), calls(nbytes))
         emit("3a" if affine else "3b", "layer_norm", [rows, hidden], nbytes, rows, per)
         del x, out
     for cache in (False, True):
@@ -295,11 +332,11 @@ def suite(args):
                                     device="cuda") for _ in range(k)]
             else:
                 dsts = [torch.empty_like(xs[0]) for _ in range(k)]
-            per, _ = time_calls(
+            per = time_graph(
                 lambda i: nrm.norm_rope(xs[i % k], w, eps=rp.eps, traditional=trad,
                                         offset=rp.offset, cache=dsts[i % k] if cache else None,
                                         out=None if cache else dsts[i % k]),
-                args.steps, args.warmup)
+                calls(nbytes))
             emit("4" + "abcd"[2 * cache + trad], "norm_rope" + ("_cache" if cache else "") +
                  ("_interleaved" if trad else "_half"), [B, H, L, D], nbytes, B * H * L, per)
             del xs, dsts
@@ -315,12 +352,22 @@ def suite(args):
 
 # --------------------------------------------------------------------------- counters
 
-def _pmc_per_dispatch(csv_path, counter):
-    """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv."""
+def _pmc_per_dispatch(path, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter file: the rocpd SQLite
+    database (its `counters_collection` view) or a counter_collection.csv."""
+    out = {}
+    if path.endswith(".db"):
+        import sqlite3
+
+        con = sqlite3.connect(path)
+        q = "select kernel_name, value from counters_collection where counter_name = ? order by id"
+        for name, value in con.execute(q, (counter,)):
+            out.setdefault(name, []).append(float(value))
+        con.close()
+        return out
     import csv
 
-    out = {}
-    with open(csv_path) as f:
+    with open(path) as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter:
                 continue
@@ -328,11 +375,11 @@ def _pmc_per_dispatch(csv_path, counter):
     return out
 
 
-def summarize_pmc(fetch_csv, write_csv, copy_bytes_half):
+def summarize_pmc(fetch_file, write_file, copy_bytes_half):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the headline kernel, each scaled by the
     ratio of known bytes to the counter's reading for the 16-byte copy kernel."""
-    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
-    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    f = _pmc_per_dispatch(fetch_file, "FETCH_SIZE")
+    w = _pmc_per_dispatch(write_file, "WRITE_SIZE")
 
     def pick(d, key):
         ks = [k for k in d if key in k]
@@ -371,12 +418,12 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes_half):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))
     args = ap.parse_args()
     if args.summarize_pmc:
         half = (add_rms_bytes(ROWS, HIDDEN, 2, 2) // 2) // 16 * 16

@@ -59,8 +59,8 @@ def test_layer_norm_shapes(nrm_lib, hidden, dt, wdt, affine):
     check_ln(nrm_lib, inp)
 
 
-@pytest.mark.parametrize("path", ["wave", "block", "chunked", "scalar"])
-@pytest.mark.parametrize("hidden", [512, 4096, 5120, 8192])
+@pytest.mark.parametrize("path", ["wave", "block", "rowblock", "chunked", "scalar"])
+@pytest.mark.parametrize("hidden", [512, 4096, 5120, 8192, 16384, 24576])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_forced_kernel_shapes(nrm_lib, path, hidden, dt):
     """Every kernel shape gives oracle-parity results on the same inputs."""
@@ -239,7 +239,7 @@ def test_deterministic(nrm_lib):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("path", [None, "block", "scalar"])
+@pytest.mark.parametrize("path", [None, "wave", "block", "scalar"])
 def test_scale_invariance_bit_exact(nrm_lib, dt, path):
     """eps = 0 and alpha = 2^k: RMSNorm(alpha x) has the same bits as RMSNorm(x) (every step,
     including the row scalar, scales exactly)."""
@@ -313,3 +313,26 @@ def test_zero_rows(nrm_lib):
     o, h = nrm_lib.add_rms_norm(x, x)
     assert o.numel() == 0 and h.numel() == 0
     assert nrm_lib.norm_rope(torch.empty(2, 0, 5, 128, dtype=torch.bfloat16, device=DEV)).numel() == 0
+
+
+@pytest.mark.parametrize("path", [None, "wave", "block", "chunked"])
+def test_in_place_many_rows(nrm_lib, path):
+    """In place over many rows, so persistent blocks prefetch the next row while writing the
+    current one: h == r and out == x for add-RMSNorm, out == x for LayerNorm."""
+    say(f"in-place many rows path={path}")
+    import oracle
+
+    inp = _row(3000, 4096, "bf16", "bf16", seed=12, r=("t3",), b=("normal", 0, 0.1), eps=1e-6)
+    want_out, want_h = oracle.add_rms_norm(f64(inp.x), f64(inp.r), f64(inp.w), inp.eps, "bf16")
+    want_ln = oracle.layer_norm(f64(inp.x), f64(inp.w), f64(inp.b), 1e-5, "bf16")
+    with forced_path(path):
+        x, r, w, b = dev(inp.x), dev(inp.r), dev(inp.w), dev(inp.b)
+        nrm_lib.add_rms_norm(x, r, w, inp.eps, out=x, h=r)
+        torch.cuda.synchronize()
+        compare.check_bf16(x, want_out, what="out in x")
+        compare.check_exact_bits(r, compare.bits_of_values(want_h, "bf16").view(np.int16),
+                                 what="h in r")
+        x = dev(inp.x)
+        nrm_lib.layer_norm(x, w, b, 1e-5, out=x)
+        torch.cuda.synchronize()
+        compare.check_bf16(x, want_ln, what="layer_norm in x")

@@ -49,6 +49,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
+// Streaming (non-temporal, `nt`) 16-byte access for data touched exactly once: on MI355X
+// this lifts a 50/50 read/write stream from ~6.0 to ~6.4 TB/s.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, (u32x4*)p);
+}
+
 // Unpack a 16-byte chunk into VEC floats.
 template <bool BF16>
 __device__ __forceinline__ void unpack(const u32x4& v, float (&f)[Fmt<BF16>::VEC]) {

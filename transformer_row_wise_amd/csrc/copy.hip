@@ -12,6 +12,7 @@ int forced_path() {
   if (!s) return PATH_AUTO;
   if (!std::strcmp(s, "wave")) return PATH_WAVE;
   if (!std::strcmp(s, "block")) return PATH_BLOCK;
+  if (!std::strcmp(s, "rowblock")) return PATH_ROWBLOCK;
   if (!std::strcmp(s, "chunked")) return PATH_CHUNKED;
   if (!std::strcmp(s, "scalar")) return PATH_SCALAR;
   return PATH_AUTO;
@@ -21,24 +22,16 @@ constexpr int64_t kMaxCopyGrid = 0x7fffffff;
 
 // ---------------------------------------------------------------- 16-byte copy
 
+// One 16-byte chunk per thread, non-temporal load and store: the fastest plain copy
+// measured on MI355X (~6.45 TB/s counting both directions; four chunks per thread without
+// the streaming hint reach ~5.6 TB/s).
 __global__ void __launch_bounds__(256) copy16_kernel(const u32x4* src, u32x4* dst, int64_t n) {
-  // Four 16-byte chunks per thread, 256 threads: a block moves 16 KiB.
-  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  u32x4 v[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t i = base + k * 256;
-    if (i < n) v[k] = src[i];
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t i = base + k * 256;
-    if (i < n) dst[i] = v[k];
-  }
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) st16_nt(dst + i, ld16_nt(src + i));
 }
 
 hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t stream) {
-  const int64_t blocks = (n16 + 1023) / 1024;
+  const int64_t blocks = (n16 + 255) / 256;
   if (blocks > kMaxCopyGrid) return hipErrorInvalidValue;
   copy16_kernel<<<(unsigned)blocks, 256, 0, stream>>>((const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError();

@@ -28,11 +28,11 @@ struct RopeArgs {
 };
 
 // Kernel-shape override for tests, from the environment variable NRM_FORCE_PATH:
-// "wave" (one wave per row), "block" (one block per row), "chunked" (looping kernel,
-// 16-byte chunks), "scalar" (looping kernel element by element; for NormRope: the generic
-// kernel). Unset or anything else: automatic choice. A forced shape that cannot hold the
-// row falls back to the automatic choice.
-enum ForcePath : int { PATH_AUTO = 0, PATH_WAVE, PATH_BLOCK, PATH_CHUNKED, PATH_SCALAR };
+// "wave" (one wave per row), "block" (one 512-thread block per row), "rowblock" (one block
+// of up to 1024 threads per row, the default shape), "chunked" (looping kernel, 16-byte chunks), "scalar" (looping kernel
+// element by element; for NormRope: the generic kernel). Unset or anything else: automatic
+// choice. A forced shape that cannot hold the row falls back to the automatic choice.
+enum ForcePath : int { PATH_AUTO = 0, PATH_WAVE, PATH_BLOCK, PATH_ROWBLOCK, PATH_CHUNKED, PATH_SCALAR };
 int forced_path();
 inline bool force_generic_path() { return forced_path() == PATH_SCALAR; }
 

@@ -95,13 +95,13 @@ rope_fast(RopeArgs a) {
 
     u32x4 xu = {0, 0, 0, 0}, xv = {0, 0, 0, 0}, xq[QC > 0 ? QC : 1];
     if (has_pc) {
-      xu = ld16(xrow + off_u * ESZ);
-      if (HALF) xv = ld16(xrow + off_v * ESZ);
+      xu = ld16_nt(xrow + off_u * ESZ);
+      if (HALF) xv = ld16_nt(xrow + off_v * ESZ);
     }
 #pragma unroll
     for (int q = 0; q < QC; ++q) {
       xq[q] = u32x4{0, 0, 0, 0};
-      if (lj + G * q < nqc) xq[q] = ld16(xrow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ);
+      if (lj + G * q < nqc) xq[q] = ld16_nt(xrow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ);
     }
 
     float fu[V], fv[V];
@@ -135,8 +135,8 @@ rope_fast(RopeArgs a) {
           fu[e] = (float)((u * c[e] - v * s[e]) * rstd);
           fv[e] = (float)((u * s[e] + v * c[e]) * rstd);
         }
-        st16(orow + off_u * ESZ, pack<BF16>(fu));
-        st16(orow + off_v * ESZ, pack<BF16>(fv));
+        st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
+        st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
       } else {
 #pragma unroll
         for (int e = 0; e < V / 2; ++e) {
@@ -145,7 +145,7 @@ rope_fast(RopeArgs a) {
           fu[2 * e] = (float)((u * c[e] - v * s[e]) * rstd);
           fu[2 * e + 1] = (float)((u * s[e] + v * c[e]) * rstd);
         }
-        st16(orow + off_u * ESZ, pack<BF16>(fu));
+        st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
       }
     }
     const float rstd_f = (float)rstd;
@@ -156,7 +156,7 @@ rope_fast(RopeArgs a) {
         unpack<BF16>(xq[q], fq);
 #pragma unroll
         for (int e = 0; e < V; ++e) fq[e] = norm ? (fq[e] * rstd_f) * wq[q][e] : fq[e];
-        st16(orow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ, pack<BF16>(fq));
+        st16_nt(orow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ, pack<BF16>(fq));
       }
     }
   }

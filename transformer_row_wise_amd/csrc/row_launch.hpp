@@ -1,13 +1,19 @@
 // Kernel-shape choice and launch of the row kernels (RMSNorm, add-RMSNorm, LayerNorm).
 //
-// For a row of n = hidden / VEC 16-byte chunks (VEC = 8 bf16 or 4 fp32):
-//   n <= 64 * NV      one wave per row, NV chunks per lane (hidden <= 8192 for bf16 and fp32)
-//   n <= 512 * NV     one 512-thread block per row (hidden <= 65536 bf16 / 32768 fp32)
+// For a row of n = hidden / VEC 16-byte chunks (VEC = 8 bf16 or 4 fp32), automatic choice:
+//   n <= 4096 (2048 for LayerNorm)   row_block: one block of T threads per row, NV chunks per
+//                                    thread, NV = max(2, ceil(n / 1024)), T = ceil(n / NV)
+//                                    rounded up to a wave (hidden 8192 bf16: 512 threads,
+//                                    2 chunks each);
 //   otherwise, or when hidden or a base address is not 16-byte granular: the looping
 //   kernel (16-byte chunks, or single elements).
-// NV is rounded up to the next instantiated size; lanes whose chunk index passes the row
-// end skip it. Each op instantiates this in its own translation unit.
+// Measured on MI355X for add-RMSNorm bf16 [16384, 8192]: row_block streams at ~6.25 TB/s,
+// one wave per row (the whole row in one wave's registers) at ~5.2 TB/s, the 512-thread
+// register kernel without streaming hints at ~5.9 TB/s. Those two stay available through
+// NRM_FORCE_PATH=wave / block.
 #pragma once
+
+#include <algorithm>
 
 #include "launch.hpp"
 
@@ -35,6 +41,50 @@ hipError_t go_chunked(const RowArgs& a, hipStream_t stream) {
   const int64_t blocks = a.rows < 1048576 ? a.rows : 1048576;
   row_chunked<BF16, OP, V><<<(unsigned)blocks, 256, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool BF16, int OP, int NV, int PK, bool EXACT>
+hipError_t go_rowblock(const RowArgs& a, int threads, hipStream_t stream) {
+  row_block<BF16, OP, NV, PK, EXACT><<<(unsigned)a.rows, threads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int OP, int NV>
+hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t stream) {
+  if (a.w == nullptr)
+    return exact ? go_rowblock<BF16, OP, NV, PK_NONE, true>(a, threads, stream)
+                 : go_rowblock<BF16, OP, NV, PK_NONE, false>(a, threads, stream);
+  if constexpr (BF16) {
+    if (a.w_f32)
+      return exact ? go_rowblock<BF16, OP, NV, PK_F32, true>(a, threads, stream)
+                   : go_rowblock<BF16, OP, NV, PK_F32, false>(a, threads, stream);
+  }
+  return exact ? go_rowblock<BF16, OP, NV, PK_SAME, true>(a, threads, stream)
+               : go_rowblock<BF16, OP, NV, PK_SAME, false>(a, threads, stream);
+}
+
+// One block per row: NV = max(2, ceil(n / 1024)) chunks per thread (at most 4; 2 for
+// LayerNorm, whose fp64 temporaries need the registers), T = ceil(n / NV) rounded up to a
+// wave. Two 16-byte chunks per thread measured best: at hidden 8192 bf16, 512 threads with
+// two chunks each beat 1024 threads with one (add-RMSNorm 172 vs 182 us, RMSNorm 86 vs
+// 95 us); four per thread gain nothing.
+template <bool BF16, int OP>
+hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* done) {
+  *done = false;
+  const int64_t nv = std::max<int64_t>(2, (n + 1023) / 1024);
+  if (nv > (OP == OP_LN ? 2 : 4) || a.rows > kMaxGrid) return hipSuccess;
+  const int threads = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
+  const bool exact = (int64_t)threads * nv == n;
+  *done = true;
+  switch (nv) {
+    case 1: return rowblock_pk<BF16, OP, 1>(a, threads, exact, stream);
+    case 2: return rowblock_pk<BF16, OP, 2>(a, threads, exact, stream);
+    case 3: if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 3>(a, threads, exact, stream); break;
+    case 4: if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 4>(a, threads, exact, stream); break;
+    default: break;
+  }
+  *done = false;
+  return hipSuccess;
 }
 
 // One wave per row: chunks per lane needed -> instantiated NV (0: does not fit).
@@ -99,14 +149,16 @@ hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream) {
   const int64_t n = a.hidden / V;
   bool done = false;
   hipError_t err = hipSuccess;
-  if (path == PATH_AUTO || path == PATH_WAVE) {
-    if ((a.rows + 3) / 4 <= kMaxGrid) {
-      err = try_wave<BF16, OP>(a, (int)((n + 63) / 64), stream, &done);
-      if (done) return err;
-    }
+  if (path == PATH_WAVE && (a.rows + 3) / 4 <= kMaxGrid) {
+    err = try_wave<BF16, OP>(a, (int)((n + 63) / 64), stream, &done);
+    if (done) return err;
   }
-  if (path != PATH_CHUNKED && a.rows <= kMaxGrid) {
+  if (path == PATH_BLOCK && a.rows <= kMaxGrid) {
     err = try_block<BF16, OP>(a, (int)((n + 511) / 512), stream, &done);
+    if (done) return err;
+  }
+  if (path == PATH_AUTO || path == PATH_ROWBLOCK || path == PATH_WAVE || path == PATH_BLOCK) {
+    err = try_rowblock<BF16, OP>(a, n, stream, &done);
     if (done) return err;
   }
   return go_chunked<BF16, OP, V>(a, stream);
