@@ -83,7 +83,7 @@ def time_calls(fn, steps, warmup):
     return per, wall_ms
 
 
-def time_graph(fn, calls, replays=5):
+def time_graph(fn, calls, replays=10):
     """Per-call GPU time (ms) of `calls` back-to-back calls captured in one HIP graph and
     replayed: no host time between kernels, which matters for calls of a few microseconds."""
     import torch
@@ -280,8 +280,8 @@ def suite(args):
         return max(1, min(16, -(-512 * 2**20 // bytes_per_call)))
 
     def calls(bytes_per_call):
-        """Calls per graph: about 0.5 GB of traffic, between 8 and 400 calls."""
-        return max(8, min(400, (512 * 2**20) // bytes_per_call))
+        """Calls per graph: about 2 GB of traffic, between 16 and 1000 calls."""
+        return max(16, min(1000, (2048 * 2**20) // bytes_per_call))
 
     def emit(cfg, op, shape, nbytes, rows, per):
         avg = statistics.median(per)
@@ -289,7 +289,7 @@ def suite(args):
         print(json.dumps({"cfg": cfg, "op": op, "shape": shape, "bytes": nbytes,
                           "gpu_us_median": round(avg * 1e3, 3),
                           "gpu_us_min": round(min(per) * 1e3, 3),
-                          "timing": "HIP graph of back-to-back calls, median of 5 replays",
+                          "timing": "HIP graph of back-to-back calls, median of 10 replays",
                           "gpu_GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 2),
                           "rows_per_s": round(rows / (avg * 1e-3), 1)}), file=sys.stderr,
               flush=True)
@@ -319,6 +319,16 @@ def suite(args):
         per = time_graph(lambda i: nrm.layer_norm(x, w, b, inp.eps, out=out), calls(nbytes))
         emit("3a" if affine else "3b", "layer_norm", [rows, hidden], nbytes, rows, per)
         del x, out
+    def run_copy(cfg, nbytes):
+        """The 16-byte copy moving the same bytes (half in, half out): the small-call ceiling."""
+        half = (nbytes // 2) // 16 * 16
+        k = n_sets(nbytes)
+        srcs = [torch.ones(half, dtype=torch.uint8, device="cuda") for _ in range(k)]
+        dsts = [torch.empty_like(srcs[0]) for _ in range(k)]
+        per = time_graph(lambda i: nrm.bench_copy(srcs[i % k], dsts[i % k]), calls(nbytes))
+        emit(cfg, "copy (ceiling)", [half], 2 * half, 0, per)
+
+    run_copy("4-copy", 2 * 8 * 32 * 512 * 128 * 2)
     for cache in (False, True):
         for trad in (False, True):
             rp = workloads.cfg_norm_rope_bf16(offset=workloads.NORM_ROPE_CACHE_OFFSET if cache else 0)

@@ -149,6 +149,18 @@ __device__ __forceinline__ void store_act(void* p, int64_t i, const float (&f)[V
   }
 }
 
+// fp64 -> fp32, round to nearest even, kept opaque to the optimiser (an empty asm with the
+// value in a VGPR; no memory access). Without it the compiler fuses a following fp32 ->
+// bf16 conversion into one exactly rounded fp64 -> bf16 conversion done by a round-to-odd
+// sequence of about eight instructions per element. Going through fp32 differs from direct
+// rounding only when the fp32 value lands exactly on a bf16 midpoint, and then by one unit
+// in the last place, which the one-ulp bar allows.
+__device__ __forceinline__ float f64_to_f32(double d) {
+  float f = (float)d;
+  __asm__ volatile("" : "+v"(f));
+  return f;
+}
+
 // Round V floats to the storage type and back (the value that a store would keep).
 template <bool BF16, int V>
 __device__ __forceinline__ void round_to_storage(float (&f)[V]) {

@@ -14,40 +14,34 @@
 //
 // rope_fast: one block per (position l, chunk of b*h rows). The block first computes
 // (cos, sin) of every pair at its position into LDS, once, then each group of G lanes takes
-// a row: in half mode a lane loads the 16-byte chunk at feature j*VEC and its partner chunk
+// rows: in half mode a lane loads the 16-byte chunk at feature j*VEC and its partner chunk
 // at dims/2 + j*VEC, so each rotated pair sits in one lane and no lane exchange is needed;
 // in traditional mode a chunk holds VEC/2 neighbouring pairs. The row's sum of squares is a
-// DPP reduction over the G lanes. Rows with the same l share the LDS table.
+// DPP reduction over the G lanes. Rows with the same l share the LDS table. A lane group
+// issues the loads of R rows before computing any of them (memory-level parallelism: a
+// 128-wide bf16 row is only 256 bytes), with clamped, unconditional addresses; the table
+// is built while the first rows are in flight.
 // rope_generic: any D / dims / alignment, one wave per row, element at a time.
 #include "launch.hpp"
 
 namespace nrm {
 
-template <bool BF16, bool HALF, int G, int QC>
+template <bool BF16, bool HALF, int G, int QC, int R>
 __global__ void __launch_bounds__(256)
 rope_fast(RopeArgs a) {
   constexpr int V = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
-  constexpr int RPW = 64 / G;                 // rows per wave
-  constexpr int RPB = 4 * RPW;                // rows per block step
+  constexpr int RPW = 64 / G;                 // row slots per wave
+  constexpr int RPB = 4 * RPW;                // row slots per block
   constexpr int PAIRS = HALF ? V : V / 2;     // rotated pairs per lane
   constexpr int MAXP = G * PAIRS;             // pairs one group can hold
+  constexpr int QN = QC > 0 ? QC : 1;
   __shared__ double cs_c[MAXP];
   __shared__ double cs_s[MAXP];
 
   const int64_t l = blockIdx.x;
   const int64_t pos = a.offset + l;
   const int half = a.dims / 2;
-  for (int t = threadIdx.x; t < half; t += 256) {
-    const double theta = pow((double)a.base, (double)(-2 * t) / (double)a.dims);
-    const double ang = ((double)a.scale * (double)pos) * theta;
-    double s, c;
-    sincos(ang, &s, &c);
-    cs_c[t] = c;
-    cs_s[t] = a.forward ? s : -s;
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane / G, lj = lane % G;
   const int npc = HALF ? half / V : a.dims / V;  // rotated chunks (pairs of chunks in half mode)
@@ -57,106 +51,142 @@ rope_fast(RopeArgs a) {
   const bool has_w = norm && a.w != nullptr;
 
   double c[PAIRS], s[PAIRS];
-  float wu[V], wv[V], wq[QC > 0 ? QC : 1][V];
+  float wu[V], wv[V], wq[QN][V];
 #pragma unroll
   for (int e = 0; e < PAIRS; ++e) { c[e] = 1.0; s[e] = 0.0; }
 #pragma unroll
   for (int e = 0; e < V; ++e) { wu[e] = 1.f; wv[e] = 1.f; }
-  const int off_u = lj * V;
-  const int off_v = HALF ? half + lj * V : 0;
-  if (has_pc) {
+  // Chunk offsets (in elements) within a row. A lane without a rotated chunk (lj >= npc)
+  // or without a pass-through chunk still loads a valid chunk of the row (clamped), so that
+  // every load is unconditional; it never stores it.
+  const int off_u = min(lj, max(npc - 1, 0)) * V;
+  const int off_v = HALF ? half + off_u : 0;
+  int off_q[QN];
+  bool has_q[QN];
 #pragma unroll
-    for (int e = 0; e < PAIRS; ++e) {
-      const int p = HALF ? lj * V + e : lj * (V / 2) + e;
-      c[e] = cs_c[p];
-      s[e] = cs_s[p];
-    }
-    if (has_w) {
-      load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
-      if (HALF) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
-    }
+  for (int q = 0; q < QN; ++q) {
+    has_q[q] = QC > 0 && lj + G * q < nqc;
+    off_q[q] = a.dims + min(lj + G * q, max(nqc - 1, 0)) * V;
   }
 #pragma unroll
-  for (int q = 0; q < QC; ++q) {
-    if (has_w && lj + G * q < nqc) {
-      load_param<BF16, V>(a.w, a.w_f32, a.dims + (int64_t)(lj + G * q) * V, wq[q]);
-    } else {
+  for (int q = 0; q < QN; ++q) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) wq[q][e] = 1.f;
-    }
+    for (int e = 0; e < V; ++e) wq[q][e] = 1.f;
   }
+  const bool any_pc = npc > 0;
+  const bool any_q = QC > 0 && nqc > 0;
 
-  const int64_t bh0 = (int64_t)blockIdx.y * a.iters * RPB;
+  // Each step handles R rows per lane group: all their loads are issued first.
+  const int64_t bh_blk = (int64_t)blockIdx.y * a.iters * RPB * R;
   for (int it = 0; it < a.iters; ++it) {
-    const int64_t bh = bh0 + (int64_t)it * RPB + wave * RPW + g;
-    if (bh >= a.BH) break;  // uniform over the group of G lanes that owns the row
-    const char* xrow = (const char*)a.x + ((bh * a.L + l) * a.D) * ESZ;
-    char* orow = (char*)a.out + ((bh * a.out_rows + a.out_row0 + l) * a.D) * ESZ;
-
-    u32x4 xu = {0, 0, 0, 0}, xv = {0, 0, 0, 0}, xq[QC > 0 ? QC : 1];
-    if (has_pc) {
-      xu = ld16_nt(xrow + off_u * ESZ);
-      if (HALF) xv = ld16_nt(xrow + off_v * ESZ);
-    }
+    u32x4 xu[R], xv[R], xq[R][QN];
+    int64_t bhr[R];
 #pragma unroll
-    for (int q = 0; q < QC; ++q) {
-      xq[q] = u32x4{0, 0, 0, 0};
-      if (lj + G * q < nqc) xq[q] = ld16_nt(xrow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ);
-    }
-
-    float fu[V], fv[V];
-    unpack<BF16>(xu, fu);
-    unpack<BF16>(xv, fv);
-    double rstd = 1.0;
-    if (norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fu[e], fu[e], ss);
-      if (HALF) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fv[e], fv[e], ss);
+    for (int r = 0; r < R; ++r) {
+      bhr[r] = bh_blk + ((int64_t)it * R + r) * RPB + wave * RPW + g;
+      const int64_t bhc = bhr[r] < a.BH ? bhr[r] : a.BH - 1;
+      const char* xrow = (const char*)a.x + ((bhc * a.L + l) * a.D) * ESZ;
+      xu[r] = u32x4{0, 0, 0, 0};
+      xv[r] = u32x4{0, 0, 0, 0};
+      if (any_pc) {
+        xu[r] = ld16_nt(xrow + off_u * ESZ);
+        if (HALF) xv[r] = ld16_nt(xrow + off_v * ESZ);
       }
 #pragma unroll
-      for (int q = 0; q < QC; ++q) {
-        float fq[V];
-        unpack<BF16>(xq[q], fq);
-#pragma unroll
-        for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fq[e], fq[e], ss);
+      for (int q = 0; q < QN; ++q) {
+        xq[r][q] = u32x4{0, 0, 0, 0};
+        if (any_q) xq[r][q] = ld16_nt(xrow + (int64_t)off_q[q] * ESZ);
       }
-      rstd = rstd_f64((double)group_sum<G>(ss), a.D, a.eps);
     }
-
-    if (has_pc) {
-      if constexpr (HALF) {
+    if (it == 0) {
+      // The (cos, sin) table of this position and the weights, built while the first
+      // rows are in flight (uniform over the block).
+      for (int t = threadIdx.x; t < half; t += 256) {
+        const double theta = pow((double)a.base, (double)(-2 * t) / (double)a.dims);
+        const double ang = ((double)a.scale * (double)pos) * theta;
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        cs_c[t] = cs;
+        cs_s[t] = a.forward ? sn : -sn;
+      }
+      __syncthreads();
+      if (has_pc) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const double u = (double)fu[e] * (double)wu[e];
-          const double v = (double)fv[e] * (double)wv[e];
-          fu[e] = (float)((u * c[e] - v * s[e]) * rstd);
-          fv[e] = (float)((u * s[e] + v * c[e]) * rstd);
+        for (int e = 0; e < PAIRS; ++e) {
+          const int p = HALF ? lj * V + e : lj * (V / 2) + e;
+          c[e] = cs_c[p];
+          s[e] = cs_s[p];
         }
-        st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
-        st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
-      } else {
-#pragma unroll
-        for (int e = 0; e < V / 2; ++e) {
-          const double u = (double)fu[2 * e] * (double)wu[2 * e];
-          const double v = (double)fu[2 * e + 1] * (double)wu[2 * e + 1];
-          fu[2 * e] = (float)((u * c[e] - v * s[e]) * rstd);
-          fu[2 * e + 1] = (float)((u * s[e] + v * c[e]) * rstd);
+        if (has_w) {
+          load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
+          if (HALF) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
         }
-        st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
       }
+#pragma unroll
+      for (int q = 0; q < QN; ++q)
+        if (has_w && has_q[q]) load_param<BF16, V>(a.w, a.w_f32, off_q[q], wq[q]);
     }
-    const float rstd_f = (float)rstd;
 #pragma unroll
-    for (int q = 0; q < QC; ++q) {
-      if (lj + G * q < nqc) {
-        float fq[V];
-        unpack<BF16>(xq[q], fq);
+    for (int r = 0; r < R; ++r) {
+      const bool live = bhr[r] < a.BH;  // uniform over the group of G lanes that owns the row
+      char* orow = (char*)a.out + ((bhr[r] * a.out_rows + a.out_row0 + l) * a.D) * ESZ;
+      float fu[V], fv[V];
+      unpack<BF16>(xu[r], fu);
+      unpack<BF16>(xv[r], fv);
+      double rstd = 1.0;
+      if (norm) {
+        float ss = 0.f;
+        if (has_pc) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) fq[e] = norm ? (fq[e] * rstd_f) * wq[q][e] : fq[e];
-        st16_nt(orow + (int64_t)(a.dims + (lj + G * q) * V) * ESZ, pack<BF16>(fq));
+          for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fu[e], fu[e], ss);
+          if (HALF) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fv[e], fv[e], ss);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+          if (has_q[q]) {
+            float fq[V];
+            unpack<BF16>(xq[r][q], fq);
+#pragma unroll
+            for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fq[e], fq[e], ss);
+          }
+        }
+        rstd = rstd_f64((double)group_sum<G>(ss), a.D, a.eps);
+      }
+      if (live && has_pc) {
+        if constexpr (HALF) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const double u = (double)fu[e] * (double)wu[e];
+            const double v = (double)fv[e] * (double)wv[e];
+            fu[e] = f64_to_f32((u * c[e] - v * s[e]) * rstd);
+            fv[e] = f64_to_f32((u * s[e] + v * c[e]) * rstd);
+          }
+          st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
+          st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
+        } else {
+#pragma unroll
+          for (int e = 0; e < V / 2; ++e) {
+            const double u = (double)fu[2 * e] * (double)wu[2 * e];
+            const double v = (double)fu[2 * e + 1] * (double)wu[2 * e + 1];
+            fu[2 * e] = f64_to_f32((u * c[e] - v * s[e]) * rstd);
+            fu[2 * e + 1] = f64_to_f32((u * s[e] + v * c[e]) * rstd);
+          }
+          st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
+        }
+      }
+      const float rstd_f = (float)rstd;
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        if (live && has_q[q]) {
+          float fq[V];
+          unpack<BF16>(xq[r][q], fq);
+#pragma unroll
+          for (int e = 0; e < V; ++e) fq[e] = norm ? (fq[e] * rstd_f) * wq[q][e] : fq[e];
+          st16_nt(orow + (int64_t)off_q[q] * ESZ, pack<BF16>(fq));
+        }
       }
     }
   }
@@ -200,8 +230,8 @@ rope_generic(RopeArgs a) {
       if (!a.forward) s = -s;
       const double u = (double)fu[0] * (double)wu[0];
       const double v = (double)fv[0] * (double)wv[0];
-      float ou[1] = {(float)((u * c - v * s) * rstd)};
-      float ov[1] = {(float)((u * s + v * c) * rstd)};
+      float ou[1] = {f64_to_f32((u * c - v * s) * rstd)};
+      float ov[1] = {f64_to_f32((u * s + v * c) * rstd)};
       store_act<BF16, 1>(a.out, oi + iu, ou);
       store_act<BF16, 1>(a.out, oi + iv, ov);
     }
@@ -218,29 +248,37 @@ rope_generic(RopeArgs a) {
 
 namespace {
 
-template <bool BF16, bool HALF, int G, int QC>
+template <bool BF16, bool HALF, int G, int QC, int R>
 hipError_t go_fast(const RopeArgs& a0, hipStream_t stream) {
   RopeArgs a = a0;
   constexpr int RPB = 4 * (64 / G);
-  const int64_t steps = (a.BH + RPB - 1) / RPB;  // block steps to cover all b*h rows
-  // Enough blocks to fill the chip (>= ~2048) while keeping each block's sin/cos table
-  // shared by as many rows as possible.
-  int64_t chunks = (2048 + a.L - 1) / a.L;
+  const int64_t steps = (a.BH + (int64_t)RPB * R - 1) / ((int64_t)RPB * R);
+  // Enough blocks for about one full round on the chip (~1024 blocks of 256 threads),
+  // while each block's sin/cos table is shared by as many rows as possible.
+  int64_t chunks = (1024 + a.L - 1) / a.L;
   if (chunks > steps) chunks = steps;
   if (chunks > 65535) chunks = 65535;
   if (chunks < 1) chunks = 1;
   a.iters = (int)((steps + chunks - 1) / chunks);
   chunks = (steps + a.iters - 1) / a.iters;
   dim3 grid((unsigned)a.L, (unsigned)chunks);
-  rope_fast<BF16, HALF, G, QC><<<grid, 256, 0, stream>>>(a);
+  rope_fast<BF16, HALF, G, QC, R><<<grid, 256, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+// R = 4 rows per lane group per step when there are enough b*h rows, else 1.
+template <bool BF16, bool HALF, int G, int QC>
+hipError_t pick_r(const RopeArgs& a, hipStream_t stream) {
+  constexpr int RPB = 4 * (64 / G);
+  if (a.BH >= 2 * RPB * 4) return go_fast<BF16, HALF, G, QC, 4>(a, stream);
+  return go_fast<BF16, HALF, G, QC, 1>(a, stream);
 }
 
 template <bool BF16, bool HALF, int G>
 hipError_t pick_qc(const RopeArgs& a, int qc, hipStream_t stream) {
-  if (qc == 0) return go_fast<BF16, HALF, G, 0>(a, stream);
-  if (qc == 1) return go_fast<BF16, HALF, G, 1>(a, stream);
-  return go_fast<BF16, HALF, G, 2>(a, stream);
+  if (qc == 0) return pick_r<BF16, HALF, G, 0>(a, stream);
+  if (qc == 1) return pick_r<BF16, HALF, G, 1>(a, stream);
+  return pick_r<BF16, HALF, G, 2>(a, stream);
 }
 
 template <bool BF16, bool HALF>

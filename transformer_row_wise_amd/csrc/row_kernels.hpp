@@ -68,7 +68,7 @@ __device__ __forceinline__ void ln_chunk_out(const float (&f)[V], const RowArgs&
     if constexpr (HAS_W && HAS_B) t = __builtin_fma(t, (double)wv[e], (double)bv[e]);
     else if constexpr (HAS_W) t = t * (double)wv[e];
     else if constexpr (HAS_B) t = t + (double)bv[e];
-    y[e] = (float)t;
+    y[e] = f64_to_f32(t);
   }
 }
 
@@ -307,36 +307,37 @@ row_block(RowArgs a) {
       if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   } else {  // OP_LN, fp64 statistics and output arithmetic
+    // x is widened to fp64 once; the second pass turns it into x - mu in place, which the
+    // output pass reuses. Four independent accumulators shorten the dependent add chains.
     const bool has_b = a.b != nullptr;
-    double s1 = 0.0;
+    double xd[NV][V];
+    double s1[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      if (ok[k]) {
-        float f[V];
-        unpack<BF16>(xv[k], f);
+      float f[V];
+      unpack<BF16>(xv[k], f);
 #pragma unroll
-        for (int e = 0; e < V; ++e) s1 += (double)f[e];
+      for (int e = 0; e < V; ++e) {
+        xd[k][e] = (double)f[e];
+        if (ok[k]) s1[e & 3] += xd[k][e];
       }
     }
-    const double mu = block_row_sum(s1, red_d[0], nw) / (double)a.hidden;
-    double s2 = 0.0;
+    const double mu =
+        block_row_sum((s1[0] + s1[1]) + (s1[2] + s1[3]), red_d[0], nw) / (double)a.hidden;
+    double s2[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      if (ok[k]) {
-        float f[V];
-        unpack<BF16>(xv[k], f);
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const double d = (double)f[e] - mu;
-          s2 = __builtin_fma(d, d, s2);
-        }
+      for (int e = 0; e < V; ++e) {
+        xd[k][e] -= mu;
+        if (ok[k]) s2[e & 3] = __builtin_fma(xd[k][e], xd[k][e], s2[e & 3]);
       }
     }
-    const double rstd = rstd_f64(block_row_sum(s2, red_d[1], nw), a.hidden, a.eps);
+    const double rstd = rstd_f64(block_row_sum((s2[0] + s2[1]) + (s2[2] + s2[3]), red_d[1], nw),
+                                 a.hidden, a.eps);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       float f[V], bv[V];
-      unpack<BF16>(xv[k], f);
       if (has_b) {
         load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv);
       } else {
@@ -345,7 +346,7 @@ row_block(RowArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        f[e] = (float)__builtin_fma(((double)f[e] - mu) * rstd, (double)wv[k][e], (double)bv[e]);
+        f[e] = f64_to_f32(__builtin_fma(xd[k][e] * rstd, (double)wv[k][e], (double)bv[e]));
       if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   }
