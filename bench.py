@@ -13,6 +13,9 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
                Infinity Cache.
 --profile      only warm-up and timed calls of the headline kernel plus the copy kernel
                (for rocprofv3 runs); no CPU baseline.
+--summarize-trace TRACE_DB
+               write profiles/add_rms_norm_bf16_16384x8192.md from the kernel trace of a
+               --profile run and the counter summary.
 --summarize-pmc FETCH_FILE WRITE_FILE
                turn two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` outputs (rocpd .db or
                counter_collection.csv) of a
@@ -63,24 +66,27 @@ def add_rms_bytes(rows, hidden, es, w_es):
 # --------------------------------------------------------------------------- GPU timing
 
 def time_calls(fn, steps, warmup):
-    """Per-call durations (ms) from HIP events on torch's current stream (the stream the
-    library launches on), plus the host wall time per call over the whole timed region."""
+    """Time `steps` back-to-back calls after `warmup` untimed ones.
+
+    Returns (gpu_ms_per_call, wall_ms_per_call). The GPU figure comes from two HIP events on
+    torch's current stream (the stream the library launches on) around the whole timed
+    region, so it is the average launch duration with nothing recorded between launches.
+    The wall figure is the host clock across the same region, bracketed by synchronisation.
+    """
     import torch
 
-    for _ in range(warmup):
-        fn(0)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    for i in range(warmup):
         fn(i)
-        ends[i].record()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return per, wall_ms
+    return start.elapsed_time(end) / steps, wall_ms
 
 
 def time_graph(fn, calls, replays=10):
@@ -99,7 +105,8 @@ def time_graph(fn, calls, replays=10):
     with torch.cuda.graph(g):
         for i in range(calls):
             fn(i)
-    g.replay()
+    for _ in range(3):  # untimed replays: let the clocks settle
+        g.replay()
     torch.cuda.synchronize()
     per = []
     for _ in range(replays):
@@ -122,9 +129,9 @@ def copy_ceiling(nbytes, steps):
     src = torch.empty(half, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
-    per, _ = time_calls(lambda i: nrm.bench_copy(src, dst), steps, 3)
+    gpu_ms, _ = time_calls(lambda i: nrm.bench_copy(src, dst), steps, steps)
     del src, dst
-    return 2 * half / (statistics.mean(per) * 1e-3) / 1e9
+    return 2 * half / (gpu_ms * 1e-3) / 1e9
 
 
 def stored_traffic(nbytes):
@@ -215,13 +222,12 @@ def headline(args):
         nrm.add_rms_norm(x, r, w, inp.eps, out=out, h=h)
 
     print(f"# timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
-    per, wall_ms = time_calls(step, args.steps, args.warmup)
-    avg_ms = statistics.mean(per)
-    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    gpu_ms, wall_ms = time_calls(step, args.steps, args.warmup)
+    achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = nbytes / (wall_ms * 1e-3) / 1e9
-    ceiling = copy_ceiling(nbytes, max(10, args.steps // 2))
+    ceiling = copy_ceiling(nbytes, max(100, args.steps // 2))
     if args.profile:
-        print(json.dumps({"profile_run": True, "avg_launch_us": avg_ms * 1e3,
+        print(json.dumps({"profile_run": True, "avg_launch_us": gpu_ms * 1e3,
                           "achieved_GBps": achieved, "copy_GBps": ceiling}), flush=True)
         return
     traffic = stored_traffic(nbytes)
@@ -246,8 +252,7 @@ def headline(args):
         "pct_peak": round(100 * value / PEAK_GBPS, 2),
         "rows_per_s": round(ROWS / (wall_ms * 1e-3), 1),
         "bytes_per_step": nbytes,
-        "kernel_us": {"mean": round(avg_ms * 1e3, 2), "median": round(statistics.median(per) * 1e3, 2),
-                      "min": round(min(per) * 1e3, 2)},
+        "kernel_us_mean": round(gpu_ms * 1e3, 2),
         "copy_ceiling_GBps": round(ceiling, 1),
         "roofline": {
             "bound": "hbm",
@@ -418,6 +423,7 @@ def summarize_pmc(fetch_file, write_file, copy_bytes_half):
         "hbm_bytes_per_launch": round(read_b + write_b),
         "algorithmic_bytes_per_launch": alg,
         "traffic_over_algorithmic": round((read_b + write_b) / alg, 4),
+        "commands": PMC_CMDS,
     }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
@@ -425,16 +431,92 @@ def summarize_pmc(fetch_file, write_file, copy_bytes_half):
     print(json.dumps(summary, indent=1))
 
 
+PROFILE_MD = os.path.join(ROOT, "profiles", "add_rms_norm_bf16_16384x8192.md")
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o trace -- "
+             "python3 bench.py --profile --steps 100 --warmup 1000")
+PMC_CMDS = [
+    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch -- "
+    "python3 bench.py --profile --steps 5 --warmup 2",
+    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write -- "
+    "python3 bench.py --profile --steps 5 --warmup 2",
+    "python3 bench.py --summarize-pmc gpurun_out/pmc_fetch/fetch_results.db "
+    "gpurun_out/pmc_write/write_results.db",
+]
+
+
+def summarize_trace(trace_db):
+    """Kernel-trace statistics (rocpd database of a --profile run) plus the counter summary,
+    written to profiles/add_rms_norm_bf16_16384x8192.md."""
+    import sqlite3
+
+    con = sqlite3.connect(trace_db)
+    rows = list(con.execute("select name, total_calls, total_duration, average from top_kernels"))
+    durs = {}
+    for name, d in con.execute("select name, duration from kernels order by start"):
+        durs.setdefault(name, []).append(d / 1000.0)
+    con.close()
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    alg = add_rms_bytes(ROWS, HIDDEN, 2, 2)
+    L = ["# add-RMSNorm bf16 [16384, 8192] on one MI355X: kernel trace and HBM traffic", "",
+         "Workload: x, r Student-t(3) with 1% of rows x1e3, w ~ N(1, 0.1) bf16, eps 1e-6. "
+         "`bench.py --profile` runs the headline kernel (1000 warm-up + 100 timed calls) and "
+         "then the 16-byte copy of the same byte count.", "",
+         f"Kernel sources hash (`bench.py` `kernel_source_hash`) of the counter runs: "
+         f"`{t['kernel_source_hash']}`.", "",
+         "## Kernel trace (`rocprofv3 --kernel-trace --stats`)", "",
+         "From the repository root, with `TMPDIR=/tmp`:", "", "```", TRACE_CMD,
+         f"python3 bench.py --summarize-trace gpurun_out/prof_trace/trace_results.db", "```", "",
+         "| kernel | calls | average us | last 100 average us | min us | max us |",
+         "|---|---|---|---|---|---|"]
+    for name, calls, _tot, avg in rows:
+        d = durs.get(name, [avg])
+        tail = d[-100:]
+        L.append(f"| `{name}` | {calls} | {avg:.2f} | {sum(tail) / len(tail):.2f} | "
+                 f"{min(d):.2f} | {max(d):.2f} |")
+    kavg = [r[3] for r in rows if HEADLINE_KERNEL in r[0]][0]
+    cavg = [r[3] for r in rows if COPY_KERNEL in r[0]][0]
+    cb = 2 * ((alg // 2) // 16 * 16)
+    L += ["", f"Headline kernel: {alg:,} algorithmic bytes / {kavg:.2f} us = "
+          f"{alg / (kavg * 1e-6) / 1e9:.0f} GB/s ({100 * alg / (kavg * 1e-6) / 8e12:.1f}% of 8 TB/s). "
+          f"Copy of the same byte count: {cb / (cavg * 1e-6) / 1e9:.0f} GB/s "
+          f"({100 * cb / (cavg * 1e-6) / 8e12:.1f}%).", "",
+          "## HBM bytes (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, one counter per run)",
+          "", "```", *PMC_CMDS, "```", "",
+          "| quantity | FETCH_SIZE | WRITE_SIZE |", "|---|---|---|",
+          f"| headline kernel, KiB per dispatch (median) | {t['fetch_KiB_per_dispatch']:.0f} | "
+          f"{t['write_KiB_per_dispatch']:.0f} |",
+          f"| copy16_kernel, KiB per dispatch (median) | {t['copy_fetch_KiB']:.1f} | "
+          f"{t['copy_write_KiB']:.1f} |",
+          f"| copy16_kernel, known bytes each way | {t['copy_bytes_each_way']:,} | "
+          f"{t['copy_bytes_each_way']:,} |",
+          f"| scale = known bytes / counter bytes | {t['fetch_scale']:.4f} | {t['write_scale']:.4f} |",
+          f"| headline kernel, scaled bytes per launch | {t['hbm_read_bytes_per_launch']:,} | "
+          f"{t['hbm_write_bytes_per_launch']:,} |",
+          f"| algorithmic bytes per launch | {2 * ROWS * HIDDEN * 2 + HIDDEN * 2:,} (x, r, w) | "
+          f"{2 * ROWS * HIDDEN * 2:,} (out, h) |", "",
+          f"Traffic / algorithmic = {t['traffic_over_algorithmic']}: x and r are read from HBM "
+          "once and out and h written once; w (16 KiB) comes from L2. On this GPU FETCH_SIZE "
+          "counts half of the copy's known read bytes, hence the x2 scale.", ""]
+    with open(PROFILE_MD, "w") as f:
+        f.write("\n".join(L))
+    print("\n".join(L))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DB")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return 0
     if args.summarize_pmc:
         half = (add_rms_bytes(ROWS, HIDDEN, 2, 2) // 2) // 16 * 16
         summarize_pmc(*args.summarize_pmc, copy_bytes_half=half)
