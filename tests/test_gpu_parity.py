@@ -123,12 +123,18 @@ def test_norm_rope_modes(nrm_lib, traditional, normalize, forward, path):
             check_rope(nrm_lib, rp, normalize=normalize, traditional=traditional, forward=forward)
 
 
-@pytest.mark.parametrize("offset", [0, 1, 4096, 100000])
-def test_norm_rope_positions(nrm_lib, offset):
-    say(f"norm_rope offset={offset}")
-    rp = workloads.rope_inputs(1, 2, 16, 128, "bf16", seed=offset, offset=offset)
-    check_rope(nrm_lib, rp)
-    check_rope(nrm_lib, rp, traditional=True)
+@pytest.mark.parametrize("offset", [0, 1, 4096, 100000, 3000000])
+@pytest.mark.parametrize("scale", [1.0, 0.125, 37.5])
+def test_norm_rope_positions(nrm_lib, offset, scale):
+    """Angles from 0 to ~1e8 rad: the in-kernel sin/cos range reduction across many
+    quadrants, in both kernels."""
+    say(f"norm_rope offset={offset} scale={scale}")
+    rp = workloads.rope_inputs(1, 2, 16, 128, "bf16", seed=offset % 1000, offset=offset,
+                               scale=scale)
+    for path in (None, "scalar"):
+        with forced_path(path):
+            check_rope(nrm_lib, rp)
+            check_rope(nrm_lib, rp, traditional=True)
 
 
 @pytest.mark.parametrize("traditional", [False, True])
@@ -336,3 +342,58 @@ def test_in_place_many_rows(nrm_lib, path):
         nrm_lib.layer_norm(x, w, b, 1e-5, out=x)
         torch.cuda.synchronize()
         compare.check_bf16(x, want_ln, what="layer_norm in x")
+
+
+def test_hip_graph_replays(nrm_lib):
+    """The library's launches capture into a HIP graph (torch.cuda.CUDAGraph) and every
+    replay matches the eager call on the inputs present at that replay; the inputs change
+    eagerly, with synchronisations, between replays."""
+    say("hip graph capture and replays")
+    import oracle
+
+    inp = _row(96, 4096, "bf16", "bf16", seed=21, r=("normal", 0, 1), b=("normal", 0, 0.1))
+    rp = workloads.rope_inputs(2, 4, 8, 128, "bf16", seed=22, offset=300)
+    x, r, w, b = dev(inp.x), dev(inp.r), dev(inp.w), dev(inp.b)
+    xr, wr = dev(rp.x), dev(rp.w)
+    out, h, ln_out = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    rope_out = torch.empty_like(xr)
+
+    def calls():
+        nrm_lib.add_rms_norm(x, r, w, 1e-6, out=out, h=h)
+        nrm_lib.layer_norm(x, w, b, 1e-5, out=ln_out)
+        nrm_lib.norm_rope(xr, wr, eps=rp.eps, offset=rp.offset, out=rope_out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    gen = torch.Generator().manual_seed(5)
+    for rep in range(4):
+        xs = torch.randn(x.shape, generator=gen).to(torch.bfloat16)
+        rs = torch.randn(r.shape, generator=gen).to(torch.bfloat16)
+        xrs = torch.randn(xr.shape, generator=gen).to(torch.bfloat16)
+        x.copy_(xs)
+        r.copy_(rs)
+        xr.copy_(xrs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want_out, want_h = oracle.add_rms_norm(f64(xs), f64(rs), f64(inp.w), 1e-6, "bf16")
+        compare.check_bf16(out, want_out, what=f"replay {rep} out")
+        compare.check_exact_bits(h, compare.bits_of_values(want_h, "bf16").view(np.int16),
+                                 what=f"replay {rep} h")
+        compare.check_bf16(ln_out, oracle.layer_norm(f64(xs), f64(inp.w), f64(inp.b), 1e-5,
+                                                     "bf16"), what=f"replay {rep} layer_norm")
+        want_rope = oracle.norm_rope(f64(xrs), f64(rp.w), normalize=True, eps=rp.eps, dims=128,
+                                     traditional=False, base=1e4, scale=1.0, offset=300,
+                                     forward=True, dtype="bf16")
+        compare.check_bf16(rope_out, want_rope, what=f"replay {rep} norm_rope")
+        # eager work between replays
+        e_out, _ = nrm_lib.add_rms_norm(x, r, w, 1e-6)
+        torch.cuda.synchronize()
+        compare.check_exact_bits(e_out, out, what=f"eager after replay {rep}")

@@ -26,6 +26,51 @@
 
 namespace nrm {
 
+// sin and cos of a rotation angle in fp64, with few registers (the general library sincos
+// carries a large-argument reduction whose registers, live next to a block's in-flight rows,
+// cost the kernel half its occupancy). Method: Cody-Waite reduction by pi/2 with pi/2 split
+// into three doubles and each step one fused multiply-add, so r = a - k*pi/2 is accurate
+// to ~1e-16 absolute for |k| < 2^40; then the Taylor series of sin and cos on
+// [-pi/4, pi/4] (terms to r^19 and r^18: truncation below 1e-20) and the quadrant k mod 4.
+// The angle itself carries a relative rounding of ~1e-16 from scale * position * theta.
+__device__ __forceinline__ void rope_sincos(double a, double* sn, double* cs) {
+  constexpr double kTwoOverPi = 0.6366197723675814;
+  constexpr double kPio2Hi = 1.5707963267948966;        // pi/2 = hi + mid + lo (to ~1e-49)
+  constexpr double kPio2Mid = 6.123233995736766e-17;
+  constexpr double kPio2Lo = -1.4973849048591698e-33;
+  const double k = __builtin_rint(a * kTwoOverPi);
+  double r = __builtin_fma(-k, kPio2Hi, a);
+  r = __builtin_fma(-k, kPio2Mid, r);
+  r = __builtin_fma(-k, kPio2Lo, r);
+  const double r2 = r * r;
+  // sin r = r (1 - r^2/3! + r^4/5! - ...),  cos r = 1 - r^2/2! + r^4/4! - ...
+  double ps = -1.0 / 121645100408832000.0;               // -1/19!
+  ps = __builtin_fma(ps, r2, 1.0 / 355687428096000.0);   //  1/17!
+  ps = __builtin_fma(ps, r2, -1.0 / 1307674368000.0);    // -1/15!
+  ps = __builtin_fma(ps, r2, 1.0 / 6227020800.0);        //  1/13!
+  ps = __builtin_fma(ps, r2, -1.0 / 39916800.0);         // -1/11!
+  ps = __builtin_fma(ps, r2, 1.0 / 362880.0);            //  1/9!
+  ps = __builtin_fma(ps, r2, -1.0 / 5040.0);             // -1/7!
+  ps = __builtin_fma(ps, r2, 1.0 / 120.0);               //  1/5!
+  ps = __builtin_fma(ps, r2, -1.0 / 6.0);                // -1/3!
+  const double sr = __builtin_fma(ps * r2, r, r);
+  double pc = -1.0 / 6402373705728000.0;                 // -1/18!
+  pc = __builtin_fma(pc, r2, 1.0 / 20922789888000.0);    //  1/16!
+  pc = __builtin_fma(pc, r2, -1.0 / 87178291200.0);      // -1/14!
+  pc = __builtin_fma(pc, r2, 1.0 / 479001600.0);         //  1/12!
+  pc = __builtin_fma(pc, r2, -1.0 / 3628800.0);          // -1/10!
+  pc = __builtin_fma(pc, r2, 1.0 / 40320.0);             //  1/8!
+  pc = __builtin_fma(pc, r2, -1.0 / 720.0);              // -1/6!
+  pc = __builtin_fma(pc, r2, 1.0 / 24.0);                //  1/4!
+  pc = __builtin_fma(pc, r2, -0.5);                      // -1/2!
+  const double cr = __builtin_fma(pc, r2, 1.0);
+  const int q = (int)((int64_t)k & 3);
+  const double s0 = (q & 1) ? cr : sr;
+  const double c0 = (q & 1) ? sr : cr;
+  *sn = (q & 2) ? -s0 : s0;
+  *cs = ((q + 1) & 2) ? -c0 : c0;
+}
+
 template <bool BF16, bool HALF, int G, int QC, int R>
 __global__ void __launch_bounds__(256)
 rope_fast(RopeArgs a) {
@@ -76,11 +121,14 @@ rope_fast(RopeArgs a) {
   const bool any_pc = npc > 0;
   const bool any_q = QC > 0 && nqc > 0;
 
-  // Each step handles R rows per lane group: all their loads are issued first.
+  // Each step handles R rows per lane group: all their loads are issued first. The loads
+  // of the first step are issued before the (cos, sin) table of this position is built,
+  // outside the step loop, so that the table's latency overlaps them and its constants
+  // are not kept live across the loop.
   const int64_t bh_blk = (int64_t)blockIdx.y * a.iters * RPB * R;
-  for (int it = 0; it < a.iters; ++it) {
-    u32x4 xu[R], xv[R], xq[R][QN];
-    int64_t bhr[R];
+  u32x4 xu[R], xv[R], xq[R][QN];
+  int64_t bhr[R];
+  auto load_step = [&](int it) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       bhr[r] = bh_blk + ((int64_t)it * R + r) * RPB + wave * RPW + g;
@@ -98,34 +146,35 @@ rope_fast(RopeArgs a) {
         if (any_q) xq[r][q] = ld16_nt(xrow + (int64_t)off_q[q] * ESZ);
       }
     }
-    if (it == 0) {
-      // The (cos, sin) table of this position and the weights, built while the first
-      // rows are in flight (uniform over the block).
-      for (int t = threadIdx.x; t < half; t += 256) {
-        const double theta = pow((double)a.base, (double)(-2 * t) / (double)a.dims);
-        const double ang = ((double)a.scale * (double)pos) * theta;
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        cs_c[t] = cs;
-        cs_s[t] = a.forward ? sn : -sn;
-      }
-      __syncthreads();
-      if (has_pc) {
+  };
+  load_step(0);
+  for (int t = threadIdx.x; t < half; t += 256) {
+    const double theta = pow((double)a.base, (double)(-2 * t) / (double)a.dims);
+    const double ang = ((double)a.scale * (double)pos) * theta;
+    double sn, cs;
+    rope_sincos(ang, &sn, &cs);
+    cs_c[t] = cs;
+    cs_s[t] = a.forward ? sn : -sn;
+  }
+  __syncthreads();
+  if (has_pc) {
 #pragma unroll
-        for (int e = 0; e < PAIRS; ++e) {
-          const int p = HALF ? lj * V + e : lj * (V / 2) + e;
-          c[e] = cs_c[p];
-          s[e] = cs_s[p];
-        }
-        if (has_w) {
-          load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
-          if (HALF) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < QN; ++q)
-        if (has_w && has_q[q]) load_param<BF16, V>(a.w, a.w_f32, off_q[q], wq[q]);
+    for (int e = 0; e < PAIRS; ++e) {
+      const int p = HALF ? lj * V + e : lj * (V / 2) + e;
+      c[e] = cs_c[p];
+      s[e] = cs_s[p];
     }
+    if (has_w) {
+      load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
+      if (HALF) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QN; ++q)
+    if (has_w && has_q[q]) load_param<BF16, V>(a.w, a.w_f32, off_q[q], wq[q]);
+
+  for (int it = 0; it < a.iters; ++it) {
+    if (it > 0) load_step(it);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool live = bhr[r] < a.BH;  // uniform over the group of G lanes that owns the row
@@ -226,7 +275,7 @@ rope_generic(RopeArgs a) {
       }
       const double theta = pow((double)a.base, (double)(-2 * p) / (double)a.dims);
       double s, c;
-      sincos(((double)a.scale * pos) * theta, &s, &c);
+      rope_sincos(((double)a.scale * pos) * theta, &s, &c);
       if (!a.forward) s = -s;
       const double u = (double)fu[0] * (double)wu[0];
       const double v = (double)fv[0] * (double)wv[0];
