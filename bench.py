@@ -29,7 +29,6 @@ sample of the same workload, in a process pool over the host's cores).
 """
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -49,12 +48,23 @@ HEADLINE_KERNEL = "row_block<true, 1, 2, 1, true>"  # bf16, add-RMSNorm, 2 chunk
 COPY_KERNEL = "copy16_kernel"
 
 
+# Files the headline kernel and the copy kernel that scales the counters are built from.
+HEADLINE_SOURCES = ("transformer_row_wise_amd/build.py",
+                    "transformer_row_wise_amd/csrc/common.hpp",
+                    "transformer_row_wise_amd/csrc/row_kernels.hpp",
+                    "transformer_row_wise_amd/csrc/row_launch.hpp",
+                    "transformer_row_wise_amd/csrc/launch.hpp",
+                    "transformer_row_wise_amd/csrc/add_rms.hip",
+                    "transformer_row_wise_amd/csrc/copy.hip")
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources: a stored counter reading is used only for this exact code."""
+    """Hash of the headline kernel's sources and build flags: a stored counter reading is used
+    only for this exact code."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "transformer_row_wise_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    for rel in HEADLINE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
