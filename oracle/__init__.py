@@ -16,6 +16,9 @@ What it computes, and where the pages define it:
                          ``LayerNorm`` (affine / ``without_bias`` / ``affine(false)``).
   * ``norm_rope``     -- ``fast::FastOp`` variants ``NormRope`` and ``Rope``; nuvec-nn
                          ``layers.rs``, ``Rope`` (defaults, positions ``offset + l``).
+  * ``rms_norm_vjp``, ``layer_norm_vjp`` -- ``fast::FastOp`` variants ``RmsNormVjp`` and
+                         ``LayerNormVjp``: the gradients of ``RmsNorm`` (for x, w) and of
+                         ``LayerNorm`` (for x, w, b) given the output cotangent g.
 
 Every value is computed in float64 from the exact input values (bf16 and fp32 decode
 exactly) and rounded once, round-to-nearest-even, to the output dtype. Parameters that the
@@ -29,9 +32,11 @@ invariants, library routines, brute force at 50 digits and hand-worked fixtures 
 from .rounding import round_bf16, round_f32, round_to, bf16_bits, f32_param
 from .norms import rms_norm, add_rms_norm, layer_norm
 from .rope import rope_frequencies, rope_angles, norm_rope
+from .vjp import rms_norm_vjp, layer_norm_vjp
 
 __all__ = [
     "round_bf16", "round_f32", "round_to", "bf16_bits", "f32_param",
     "rms_norm", "add_rms_norm", "layer_norm",
     "rope_frequencies", "rope_angles", "norm_rope",
+    "rms_norm_vjp", "layer_norm_vjp",
 ]

@@ -107,3 +107,53 @@ def rope_row(x, w, *, normalize, eps, dims, traditional, base, scale, pos, forwa
         out[iv] = u * s + v * c
     assert len(out) == d
     return out
+
+
+def _grad(f, point, k):
+    """d f / d point[k] at `point` (a list of mpf), by mpmath's high-precision numerical
+    differentiation: a finite-difference derivative, independent of any closed form."""
+    def fk(t):
+        q = list(point)
+        q[k] = t
+        return f(q)
+    return mpmath.diff(fk, point[k])
+
+
+def rms_vjp_rows(x, w, g, eps):
+    """(dx rows, dw) of RmsNorm for the rows x[i] with cotangents g[i]: the derivatives of
+    L = sum_i sum_j g[i][j] * RmsNorm(x)[i][j] with respect to x and to w (w None = ones)."""
+    d = len(x[0])
+    wv = [mpmath.mpf(1)] * d if w is None else [mpmath.mpf(v) for v in w]
+    dx = []
+    for xi, gi in zip(x, g):
+        gm = [mpmath.mpf(v) for v in gi]
+        loss = lambda q: mpmath.fsum(a * b for a, b in zip(gm, rms_row(q, wv, eps)))
+        pt = [mpmath.mpf(v) for v in xi]
+        dx.append([_grad(loss, pt, k) for k in range(d)])
+
+    def loss_w(q):
+        return mpmath.fsum(mpmath.fsum(mpmath.mpf(a) * b for a, b in zip(gi, rms_row(xi, q, eps)))
+                           for xi, gi in zip(x, g))
+    dw = [_grad(loss_w, wv, k) for k in range(d)]
+    return dx, dw
+
+
+def layer_vjp_rows(x, w, b, g, eps):
+    """(dx rows, dw, db) of LayerNorm, the same way (w None = ones, b None = zeros)."""
+    d = len(x[0])
+    wv = [mpmath.mpf(1)] * d if w is None else [mpmath.mpf(v) for v in w]
+    bv = [mpmath.mpf(0)] * d if b is None else [mpmath.mpf(v) for v in b]
+    dx = []
+    for xi, gi in zip(x, g):
+        gm = [mpmath.mpf(v) for v in gi]
+        loss = lambda q: mpmath.fsum(a * c for a, c in zip(gm, layer_row(q, wv, bv, eps)))
+        pt = [mpmath.mpf(v) for v in xi]
+        dx.append([_grad(loss, pt, k) for k in range(d)])
+
+    def total(wq, bq):
+        return mpmath.fsum(
+            mpmath.fsum(mpmath.mpf(a) * c for a, c in zip(gi, layer_row(xi, wq, bq, eps)))
+            for xi, gi in zip(x, g))
+    dw = [_grad(lambda q: total(q, bv), wv, k) for k in range(d)]
+    db = [_grad(lambda q: total(wv, q), bv, k) for k in range(d)]
+    return dx, dw, db

@@ -19,6 +19,11 @@ What pins what:
                      per-pair norm preservation, inverse undoes forward, half/interleaved
                      permutation, relative-position property, cache placement, RMS over
                      all D, 50-digit brute force.
+  * RmsNormVjp /  -- hand-worked fixtures, 50-digit numerical differentiation of the
+    LayerNormVjp     forward (brute force), torch autograd of ``rms_norm`` / ``layer_norm``
+                     in float64, and the invariances every gradient of these maps obeys
+                     (RMS: x . dx = 0 at eps = 0; LN: sum(dx) = 0, and x . dx = 0 at
+                     eps = 0; db = column sums of g).
 """
 
 import json
@@ -469,6 +474,133 @@ def pin_rope_brute(o):
                             want = [brute.round_mp(v, dt) for v in
                                     brute.rope_row(x[0, 0, l], w, pos=700 + l, **kw)]
                             _same_values(got[0, 0, l], want, f"{dt} {kw} l={l}")
+
+
+# --------------------------------------------------------------------- RmsNormVjp / LN
+
+def _rows_vals(rows):
+    return np.array([[float(Fraction(v)) for v in r] for r in rows])
+
+
+def pin_rms_vjp_golden(o):
+    g = _golden("rms_norm_vjp_hand.json")
+    for c in g["cases"]:
+        x, gg = _rows_vals(c["x"]), _rows_vals(c["g"])
+        w = _vals(c["w"])
+        want_dx, want_dw = _rows_vals(c["expect_dx"]), _vals(c["expect_dw"])
+        for dt in ("f64", "bf16", "f32"):
+            dx, dw = o.rms_norm_vjp(x, w, gg, c["eps"], dt)
+            _same_values(dx, want_dx, c["why"] + " dx " + dt)
+            _same_values(dw, want_dw, c["why"] + " dw " + dt)
+
+
+def pin_ln_vjp_golden(o):
+    g = _golden("layer_norm_vjp_hand.json")
+    for c in g["cases"]:
+        x, gg = _rows_vals(c["x"]), _rows_vals(c["g"])
+        w, b = _vals(c["w"]), _vals(c["b"])
+        want = (_rows_vals(c["expect_dx"]), _vals(c["expect_dw"]), _vals(c["expect_db"]))
+        for dt in ("f64", "bf16", "f32"):
+            got = o.layer_norm_vjp(x, w, b, gg, c["eps"], dt)
+            for name, a, e in zip(("dx", "dw", "db"), got, want):
+                _same_values(a, e, c["why"] + " " + name + " " + dt)
+
+
+def pin_rms_vjp_brute(o):
+    """2 x 8 inputs: 50-digit numerical derivatives of the brute-force forward, rounded
+    exactly, equal the oracle's rounded gradients."""
+    rng = _rng(21)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        for eps, with_w in ((1e-6, True), (0.3, False)):
+            x = cast(rng.standard_normal((2, 8)) * 2)
+            w = cast(rng.uniform(0.5, 1.5, 8)) if with_w else None
+            g = cast(rng.standard_normal((2, 8)))
+            dx, dw = o.rms_norm_vjp(x, w, g, eps, dt)
+            bdx, bdw = brute.rms_vjp_rows(x.tolist(), None if w is None else w.tolist(),
+                                          g.tolist(), eps)
+            for i in range(2):
+                _same_values(dx[i], [brute.round_mp(v, dt) for v in bdx[i]], f"{dt} dx {i}")
+            _same_values(dw, [brute.round_mp(v, dt) for v in bdw], f"{dt} dw")
+
+
+def pin_ln_vjp_brute(o):
+    rng = _rng(22)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        for eps, with_w in ((1e-5, True), (0.2, False)):
+            x = cast(rng.normal(0.5, 2, (2, 8)))
+            w = cast(rng.normal(1, 0.1, 8)) if with_w else None
+            b = cast(rng.normal(0, 0.1, 8)) if with_w else None
+            g = cast(rng.standard_normal((2, 8)))
+            dx, dw, db = o.layer_norm_vjp(x, w, b, g, eps, dt)
+            bdx, bdw, bdb = brute.layer_vjp_rows(x.tolist(), None if w is None else w.tolist(),
+                                                 None if b is None else b.tolist(), g.tolist(),
+                                                 eps)
+            for i in range(2):
+                _same_values(dx[i], [brute.round_mp(v, dt) for v in bdx[i]], f"{dt} dx {i}")
+            _same_values(dw, [brute.round_mp(v, dt) for v in bdw], f"{dt} dw")
+            _same_values(db, [brute.round_mp(v, dt) for v in bdb], f"{dt} db")
+
+
+def _torch_grads(fn, x, params, g):
+    xt = torch.from_numpy(x).requires_grad_(True)
+    ps = [None if p is None else torch.from_numpy(p).requires_grad_(True) for p in params]
+    fn(xt, *ps).backward(torch.from_numpy(g))
+    return [xt.grad.numpy()] + [None if p is None else p.grad.numpy() for p in ps]
+
+
+def pin_rms_vjp_torch(o):
+    """torch autograd of torch.nn.functional.rms_norm in float64 on the CPU."""
+    rng = _rng(23)
+    for d in (1, 7, 64, 1000):
+        x = rng.standard_normal((9, d)) * 3
+        w = rng.normal(1, 0.2, d)
+        g = rng.standard_normal((9, d))
+        for eps in (1e-6, 0.25):
+            e = float(np.float32(eps))
+            f = lambda xt, wt: torch.nn.functional.rms_norm(xt, (d,), wt, eps=e)
+            tdx, tdw = _torch_grads(f, x, [w], g)
+            dx, dw = o.rms_norm_vjp(x, w, g, eps, "f64")
+            _close(dx, tdx, 1e-11, 1e-13, f"d={d} dx")
+            _close(dw, tdw, 1e-11, 1e-13, f"d={d} dw")
+
+
+def pin_ln_vjp_torch(o):
+    """torch autograd of torch.nn.functional.layer_norm in float64 on the CPU."""
+    rng = _rng(24)
+    for d in (2, 33, 1024):
+        x = rng.normal(0.5, 2, (7, d))
+        w = rng.normal(1, 0.1, d)
+        b = rng.normal(0, 0.1, d)
+        g = rng.standard_normal((7, d))
+        for eps in (1e-5, 0.1):
+            e = float(np.float32(eps))
+            f = lambda xt, wt, bt: torch.nn.functional.layer_norm(xt, (d,), wt, bt, eps=e)
+            tdx, tdw, tdb = _torch_grads(f, x, [w, b], g)
+            dx, dw, db = o.layer_norm_vjp(x, w, b, g, eps, "f64")
+            _close(dx, tdx, 1e-11, 1e-13, f"d={d} dx")
+            _close(dw, tdw, 1e-11, 1e-13, f"d={d} dw")
+            _close(db, tdb, 1e-12, 1e-13, f"d={d} db")
+
+
+def pin_vjp_invariances(o):
+    """RMSNorm is scale invariant at eps = 0, so x . dx = 0 per row; LayerNorm is shift
+    invariant (sum dx = 0 for any eps) and scale invariant at eps = 0 (x . dx = 0); db is
+    the column sum of g. Checked relative to the sizes of the terms."""
+    rng = _rng(25)
+    x = rng.normal(0.3, 2, (6, 200))
+    w = rng.normal(1, 0.2, 200)
+    b = rng.normal(0, 0.1, 200)
+    g = rng.standard_normal((6, 200))
+    dx, _ = o.rms_norm_vjp(x, w, g, 0.0, "f64")
+    scale = np.sum(np.abs(x * dx), axis=-1)
+    assert np.all(np.abs(np.sum(x * dx, axis=-1)) <= 1e-13 * scale), "RMS x.dx"
+    for eps in (0.0, 0.5):
+        dx, _, db = o.layer_norm_vjp(x, w, b, g, eps, "f64")
+        assert np.all(np.abs(np.sum(dx, axis=-1)) <= 1e-13 * np.sum(np.abs(dx), axis=-1)), "LN sum"
+        _close(db, np.sum(g, axis=0), 1e-14, 1e-14, "db")
+        if eps == 0.0:
+            s = np.sum(np.abs(x * dx), axis=-1)
+            assert np.all(np.abs(np.sum(x * dx, axis=-1)) <= 1e-13 * s), "LN x.dx"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -70,6 +70,29 @@ MUTANTS = [
      "cache written from row 0"),
     ("rope.py", "xn = x / np.sqrt(mean_sq + f32_param(eps))", "xn = x / np.sqrt(mean_sq)",
      "NormRope drops eps"),
+    ("vjp.py", "x2 * (r ** 3) * dot / d", "x2 * (r ** 2) * dot / d", "RmsNormVjp r^2 for r^3"),
+    ("vjp.py", "dx = r * g2 * wv - x2 * (r ** 3) * dot / d", "dx = r * g2 * wv",
+     "RmsNormVjp drops the term through the statistic"),
+    ("vjp.py", "dot = np.sum(g2 * wv * x2", "dot = np.sum(g2 * x2", "RmsNormVjp dot ignores w"),
+    ("vjp.py", "dw = np.sum(g2 * x2 * r, axis=0)", "dw = np.sum(g2 * x2, axis=0)",
+     "RmsNormVjp dw not normalised"),
+    ("vjp.py", "dw = np.sum(g2 * x2 * r, axis=0)", "dw = np.mean(g2 * x2 * r, axis=0)",
+     "RmsNormVjp dw averages over rows"),
+    ("vjp.py", "x2 * x2, axis=-1, keepdims=True) / d + f32_param(eps)",
+     "x2 * x2, axis=-1, keepdims=True) / d", "RmsNormVjp drops eps"),
+    ("vjp.py", "dx = r * (dxh - m1 - xh * m2)", "dx = r * (dxh - m1 + xh * m2)",
+     "LayerNormVjp wrong sign on the variance term"),
+    ("vjp.py", "dx = r * (dxh - m1 - xh * m2)", "dx = r * (dxh - xh * m2)",
+     "LayerNormVjp drops the mean term"),
+    ("vjp.py", "dxh = g2 * wv", "dxh = g2", "LayerNormVjp dx ignores w"),
+    ("vjp.py", "dw = np.sum(g2 * xh, axis=0)", "dw = np.sum(g2 * c, axis=0)",
+     "LayerNormVjp dw uses the uncentred-unscaled x"),
+    ("vjp.py", "db = np.sum(g2, axis=0)", "db = np.sum(g2 * wv, axis=0)",
+     "LayerNormVjp db scaled by w"),
+    ("vjp.py", "np.sum(c * c, axis=-1, keepdims=True) / d", "np.sum(c * c, axis=-1, keepdims=True) / (d - 1)",
+     "LayerNormVjp unbiased variance"),
+    ("vjp.py", "m2 = np.sum(dxh * xh, axis=-1, keepdims=True) / d",
+     "m2 = np.sum(dxh * c, axis=-1, keepdims=True) / d", "LayerNormVjp m2 not normalised"),
 ]
 
 
