@@ -49,8 +49,7 @@ COPY_KERNEL = "copy16_kernel"
 
 
 # Files the headline kernel and the copy kernel that scales the counters are built from.
-HEADLINE_SOURCES = ("transformer_row_wise_amd/build.py",
-                    "transformer_row_wise_amd/csrc/common.hpp",
+HEADLINE_SOURCES = ("transformer_row_wise_amd/csrc/common.hpp",
                     "transformer_row_wise_amd/csrc/row_kernels.hpp",
                     "transformer_row_wise_amd/csrc/row_launch.hpp",
                     "transformer_row_wise_amd/csrc/launch.hpp",
@@ -59,9 +58,12 @@ HEADLINE_SOURCES = ("transformer_row_wise_amd/build.py",
 
 
 def kernel_source_hash():
-    """Hash of the headline kernel's sources and build flags: a stored counter reading is used
-    only for this exact code."""
+    """Hash of the headline kernel's sources and compiler flags: a stored counter reading is
+    used only for this exact code."""
+    from transformer_row_wise_amd import build as nrm_build
     h = hashlib.sha256()
+    flags = [f.replace(nrm_build.ROOT, ".") for f in nrm_build.FLAGS]
+    h.update(" ".join(flags).encode() + b"\0")
     for rel in HEADLINE_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
@@ -321,6 +323,35 @@ def suite(args):
                                                     h=outs[i % len(sets)][1]), calls(nbytes))
         emit(cfg, "add_rms_norm", [rows, hidden, str(inp.x.dtype)], nbytes, rows, per)
 
+    def run_vjp(cfg, inp, ln):
+        rows, hidden = inp.x.shape
+        es, pes = inp.x.element_size(), inp.w.element_size()
+        # read x and g, write dx; read w, write dw (and db)
+        nbytes = 3 * rows * hidden * es + hidden * pes * (3 if ln else 2)
+        x, g, w = inp.x.cuda(), inp.g.cuda(), inp.w.cuda()
+        dx, dw, db = torch.empty_like(x), torch.empty_like(w), torch.empty_like(w)
+        ws = torch.empty(nrm.vjp_workspace_bytes(rows, hidden, ln), dtype=torch.uint8,
+                         device="cuda")
+        if ln:
+            fn = lambda i: nrm.layer_norm_vjp(x, w, g, inp.eps, dx=dx, dw=dw, db=db, workspace=ws)
+        else:
+            fn = lambda i: nrm.rms_norm_vjp(x, w, g, inp.eps, dx=dx, dw=dw, workspace=ws)
+        per = time_graph(fn, calls(nbytes))
+        emit(cfg, "layer_norm_vjp" if ln else "rms_norm_vjp", [rows, hidden, str(inp.x.dtype)],
+             nbytes, rows, per)
+
+    groups = set(args.only.split(",")) if args.only else {"fwd", "vjp"}
+    if "vjp" in groups:
+        for ln, tag in ((False, "6"), (True, "7")):
+            f32 = workloads.cfg_ln_vjp(dtype="f32") if ln else workloads.cfg_rms_vjp(dtype="f32")
+            bf = workloads.RowInputs(x=f32.x.to(torch.bfloat16), r=None,
+                                     w=f32.w.to(torch.bfloat16), b=None, eps=f32.eps,
+                                     g=f32.g.to(torch.bfloat16))
+            run_vjp(tag + "a", bf, ln)
+            run_vjp(tag + "b", f32, ln)
+            del f32, bf
+    if "fwd" not in groups:
+        return
     run_add("1", workloads.cfg_add_rms_small_f32())
     run_add("2", workloads.cfg_add_rms_4k_bf16())
     for affine in (True, False):
@@ -519,6 +550,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--suite", action="store_true")
+    ap.add_argument("--only", metavar="GROUPS",
+                    help="with --suite: comma-separated groups among fwd, vjp (skips the "
+                         "headline line)")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))
@@ -536,8 +570,9 @@ def main():
               f"independent, so N GPUs would each run this same kernel on their own rows); "
               f"got --gpus {args.gpus}", file=sys.stderr)
         return 2
-    headline(args)
-    if args.suite:
+    if not args.only:
+        headline(args)
+    if args.suite or args.only:
         suite(args)
     return 0
 

@@ -1,17 +1,22 @@
 /*
  * nrm.h -- fused row-wise normalisation on AMD Instinct MI355X (gfx950): C ABI.
  *
- * Four operations over the last axis of a row-major array, each one HIP kernel launch:
- *   nrm_rms_norm      RMSNorm                      x / sqrt(mean(x^2) + eps) * w
- *   nrm_add_rms_norm  residual add + RMSNorm       h = x + r;  out = RMSNorm(h);  returns both
- *   nrm_layer_norm    LayerNorm                    (x - mean) / sqrt(var + eps) * w + b
- *   nrm_norm_rope     RMSNorm + rotary embedding   per [b, h, l] row, position offset + l
+ Operations over the last axis of a row-major array:
+ *   nrm_rms_norm        RMSNorm                     x / sqrt(mean(x^2) + eps) * w
+ *   nrm_add_rms_norm    residual add + RMSNorm      h = x + r;  out = RMSNorm(h);  returns both
+ *   nrm_layer_norm      LayerNorm                   (x - mean) / sqrt(var + eps) * w + b
+ *   nrm_norm_rope       RMSNorm + rotary embedding  per [b, h, l] row, position offset + l
+ *   nrm_rms_norm_vjp    RMSNorm backward            dx, dw from the output cotangent g
+ *   nrm_layer_norm_vjp  LayerNorm backward          dx, dw, db from the output cotangent g
+ * The forward operations are one HIP kernel launch each; the backward ones add a second,
+ * small launch that sums the per-block parameter-gradient partials.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.   Every array pointer is DEVICE memory on the current HIP device, owned by the
  *           caller, C-contiguous with the normalised axis innermost. The library allocates
- *           nothing and keeps no state beyond a thread-local error string.
+ *           nothing and keeps no state beyond a thread-local error string; the backward
+ *           operations take their scratch space as a caller-provided workspace.
  * Dtypes.   dtype is the storage type of the activations and of every output (x, r, out, h,
  *           cache). The weights w and b are stored either in dtype or in NRM_F32 (w_dtype);
  *           NRM_F32 activations take NRM_F32 weights. Arithmetic is fp32 with fp32
@@ -25,7 +30,8 @@
  *           nrm_last_error(), and launches nothing and writes nothing. Argument errors
  *           are found on the host, before any HIP call. An empty call (zero rows, or
  *           B * H * L == 0) with valid dtypes and sizes is a successful no-op whatever the
- *           pointers (an empty torch tensor may have a NULL data pointer).
+ *           pointers (an empty torch tensor may have a NULL data pointer), except that the
+ *           backward operations set a requested dw / db to zero.
  * Aliasing. An output may be exactly the same array as an input where stated (in-place
  *           use); any other overlap between an output and another array is NRM_ERR_ALIAS.
  * Threads.  Calls are thread-safe.
@@ -33,6 +39,7 @@
 #ifndef NRM_H
 #define NRM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -142,6 +149,68 @@ nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64
 /* The message of the last failed nrm_* call on this thread ("" if none): "<function>: <what>
  * <reason>, got <value>". Valid until the next nrm_* call on the same thread. */
 const char* nrm_last_error(void);
+
+/*
+ * Workspace bytes that nrm_rms_norm_vjp (layer_norm = 0) or nrm_layer_norm_vjp
+ * (layer_norm != 0) needs for `rows` rows of `hidden` features when a parameter gradient
+ * (dw or db) is requested: P * hidden * 8 for RMSNorm and twice that for LayerNorm, where
+ * P = ceil(rows / ceil(rows / 256)) <= 256 is the number of fp64 partial rows (one per
+ * block of consecutive rows). 0 for rows <= 0 or hidden < 1. Depends on the shape only,
+ * not on the device.
+ */
+size_t nrm_norm_vjp_workspace_bytes(int64_t rows, int64_t hidden, int layer_norm);
+
+/*
+ * RMSNorm backward: the gradients of RMSNorm (out = x / sqrt(mean(x^2) + eps) * w) for x and
+ * for w, given the output cotangent g.
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant RmsNormVjp, inputs (x, w, g), the gradients
+ * of RmsNorm for x and w; eps an f32. Per row, with r = 1 / sqrt(sum(x^2) / D + eps):
+ *   dx = r * g * w - x * r^3 * sum(g * w * x) / D,      dw = sum over rows of g * x * r.
+ * Row sums accumulate in fp32; r, the per-element dx and the dw column sums are evaluated in
+ * fp64 (dx is a difference that can cancel), so each result is within one unit of the last
+ * place of the exact value. dw is the same bits on every run (fixed summation order).
+ *
+ *   x, g       [rows, hidden] dtype, inputs
+ *   w          [hidden] w_dtype, or NULL (= 1)
+ *   dx         [rows, hidden] dtype output; may be exactly x or exactly g
+ *   dw         [hidden] w_dtype output, or NULL (not computed). With w == NULL it is the
+ *              gradient for a weight of ones. For rows == 0 it is set to zero.
+ *   workspace  device scratch of at least nrm_norm_vjp_workspace_bytes(rows, hidden, 0)
+ *              bytes, 16-byte aligned, overlapping no other argument; contents on return
+ *              are unspecified. Unused (may be NULL) when dw == NULL. Calls that share a
+ *              workspace must be ordered (the same stream).
+ * Errors: NULL x/g/dx (rows > 0), or NULL workspace with dw -> NRM_ERR_NULL; bad sizes or
+ * workspace_bytes too small -> NRM_ERR_SHAPE; dtypes -> NRM_ERR_DTYPE; dx partly overlapping
+ * x or g, any other overlap, or a misaligned workspace -> NRM_ERR_ALIAS; launch refused ->
+ * NRM_ERR_DEVICE.
+ */
+nrm_status nrm_rms_norm_vjp(const void* x, const void* w, const void* g, void* dx, void* dw,
+                            int64_t rows, int64_t hidden, float eps, nrm_dtype dtype,
+                            nrm_dtype w_dtype, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * LayerNorm backward: the gradients of LayerNorm (out = (x - mean) / sqrt(var + eps) * w + b)
+ * for x, w and b, given the output cotangent g.
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant LayerNormVjp, inputs (x, w, b, g), the
+ * gradients of LayerNorm for x, w and b; eps an f32. b does not enter any gradient, so it is
+ * not an argument. Per row, with xh = (x - mean) * r, r = 1 / sqrt(var + eps) (biased
+ * variance) and d = g * w:
+ *   dx = r * (d - mean(d) - xh * mean(d * xh)),   dw = sum over rows of g * xh,
+ *   db = sum over rows of g.
+ * Row statistics, dx and the column sums are evaluated in fp64; each result is within one
+ * unit of the last place of the exact value, and the same bits on every run.
+ *
+ *   x, g, w, dx as nrm_rms_norm_vjp
+ *   dw, db     [hidden] w_dtype outputs, each may be NULL (not computed); zero for rows == 0
+ *   workspace  at least nrm_norm_vjp_workspace_bytes(rows, hidden, 1) bytes when dw or db is
+ *              requested, as for nrm_rms_norm_vjp
+ * Errors: as nrm_rms_norm_vjp.
+ */
+nrm_status nrm_layer_norm_vjp(const void* x, const void* w, const void* g, void* dx, void* dw,
+                              void* db, int64_t rows, int64_t hidden, float eps,
+                              nrm_dtype dtype, nrm_dtype w_dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Name of a status code ("NRM_OK", "NRM_ERR_SHAPE", ...). */
 const char* nrm_status_name(nrm_status status);

@@ -122,3 +122,55 @@ def check_rope(nrm, rp, *, normalize=True, traditional=False, forward=True, cach
         w = compare.tensor_bits(cache)[:, :, keep]
         assert np.array_equal(g, w), "cache rows outside the written range changed"
     return res
+
+
+def run_vjp(nrm, inp, ln, want_dw=True, want_db=True):
+    x, w, g = dev(inp.x), dev(inp.w), dev(inp.g)
+    if ln:
+        res = nrm.layer_norm_vjp(x, w, g, inp.eps, want_dw=want_dw, want_db=want_db)
+    else:
+        res = nrm.rms_norm_vjp(x, w, g, inp.eps, want_dw=want_dw)
+    torch.cuda.synchronize()
+    return res
+
+
+def vjp_oracle(inp, ln, rows_sel=None, chunk=None):
+    """Oracle gradients. dx for rows_sel (all rows when None). dw (and db) always sum over
+    every row: with ``chunk`` the rows are taken in chunks whose unrounded float64 column
+    sums are added, then rounded once (the sum over rows, in pieces that fit in memory)."""
+    dt = DT[inp.x.dtype]
+    wdt = DT[inp.w.dtype] if inp.w is not None else dt
+    w = f64(inp.w)
+    xs = inp.x if rows_sel is None else inp.x[rows_sel]
+    gs = inp.g if rows_sel is None else inp.g[rows_sel]
+    if ln:
+        dx = oracle.layer_norm_vjp(f64(xs), w, None, f64(gs), inp.eps, dt, wdt)[0]
+    else:
+        dx = oracle.rms_norm_vjp(f64(xs), w, f64(gs), inp.eps, dt, wdt)[0]
+    rows = inp.x.shape[0]
+    step = chunk or max(rows, 1)
+    sums = None
+    for r0 in range(0, rows, step):
+        xc, gc = f64(inp.x[r0:r0 + step]), f64(inp.g[r0:r0 + step])
+        if ln:
+            part = oracle.layer_norm_vjp(xc, w, None, gc, inp.eps, "f64")[1:]
+        else:
+            part = oracle.rms_norm_vjp(xc, w, gc, inp.eps, "f64")[1:]
+        sums = list(part) if sums is None else [a + b for a, b in zip(sums, part)]
+    if sums is None:
+        sums = [np.zeros(inp.x.shape[-1])] * (2 if ln else 1)
+    params = [oracle.round_to(s, wdt) for s in sums]
+    return dx, params
+
+
+def check_vjp(nrm, inp, ln, rows_sel=None, chunk=None):
+    """Backward on the device against the oracle: dx (on rows_sel), dw (and db)."""
+    got = run_vjp(nrm, inp, ln)
+    want_dx, want_params = vjp_oracle(inp, ln, rows_sel, chunk)
+    dt = DT[inp.x.dtype]
+    wdt = DT[inp.w.dtype] if inp.w is not None else dt
+    gdx = got[0] if rows_sel is None else got[0][rows_sel]
+    res = [compare.check_output(gdx, want_dx, dt, what="dx")]
+    for name, g, wv in zip(("dw", "db"), got[1:], want_params):
+        res.append(compare.check_output(g, wv, wdt, what=name))
+    return res

@@ -156,3 +156,60 @@ def test_python_error_type(L):
     status = rms(L, rows=-1)
     with pytest.raises(nrm.NrmError, match="NRM_ERR_SHAPE: nrm_rms_norm: rows must be >= 0"):
         nrm._raise(status)
+
+
+# ------------------------------------------------------------------ backward entry points
+
+WS = P + 512 * MB  # fake workspace address
+
+
+def rvjp(L, x=P, w=None, g=P + 64 * MB, dx=P + 128 * MB, dw=P + 192 * MB, rows=4, hidden=8,
+         dt=BF16, wdt=BF16, ws=WS, ws_bytes=1 << 30):
+    return L.nrm_rms_norm_vjp(x, w, g, dx, dw, rows, hidden, 1e-5, dt, wdt, ws, ws_bytes, None)
+
+
+def lvjp(L, x=P, w=None, g=P + 64 * MB, dx=P + 128 * MB, dw=P + 192 * MB, db=P + 256 * MB,
+         rows=4, hidden=8, dt=BF16, wdt=BF16, ws=WS, ws_bytes=1 << 30):
+    return L.nrm_layer_norm_vjp(x, w, g, dx, dw, db, rows, hidden, 1e-5, dt, wdt, ws, ws_bytes,
+                                None)
+
+
+def test_vjp_workspace_bytes(L):
+    """P partial rows of fp64, P = ceil(rows / ceil(rows / 256)); LayerNorm needs two sets."""
+    for rows in (1, 7, 255, 256, 257, 1000, 16384, 65536, 100003):
+        rpb = -(-rows // 256)
+        parts = -(-rows // rpb)
+        assert parts <= 256
+        for hidden in (1, 8, 8192):
+            assert L.nrm_norm_vjp_workspace_bytes(rows, hidden, 0) == parts * hidden * 8
+            assert L.nrm_norm_vjp_workspace_bytes(rows, hidden, 1) == 2 * parts * hidden * 8
+    assert L.nrm_norm_vjp_workspace_bytes(0, 8, 0) == 0
+    assert L.nrm_norm_vjp_workspace_bytes(4, 0, 1) == 0
+
+
+def test_vjp_argument_errors(L):
+    assert rvjp(L, x=None) == NULL and "nrm_rms_norm_vjp: x must not be NULL" in err(L)
+    assert rvjp(L, g=None) == NULL and "g must not be NULL" in err(L)
+    assert lvjp(L, dx=None) == NULL and "nrm_layer_norm_vjp: dx must not be NULL" in err(L)
+    assert rvjp(L, ws=None) == NULL and "workspace must not be NULL" in err(L)
+    assert lvjp(L, ws=None, dw=P + 192 * MB, db=None) == NULL
+    assert rvjp(L, rows=-2) == SHAPE and "rows must be >= 0, got -2" in err(L)
+    assert lvjp(L, hidden=0) == SHAPE
+    need = L.nrm_norm_vjp_workspace_bytes(4, 8, 0)
+    assert rvjp(L, ws_bytes=need - 1) == SHAPE
+    assert f"workspace_bytes must be >= {need}, got {need - 1}" in err(L)
+    assert lvjp(L, ws_bytes=L.nrm_norm_vjp_workspace_bytes(4, 8, 1) - 8) == SHAPE
+    assert rvjp(L, dt=5) == DTYPE and lvjp(L, dt=F32, wdt=BF16) == DTYPE
+    n = 4 * 8 * 2
+    assert rvjp(L, dx=P + 2) == ALIAS and "dx must be exactly or not overlap x" in err(L)
+    assert rvjp(L, dx=P + 64 * MB + n - 2) == ALIAS
+    assert rvjp(L, dw=P + 4) == ALIAS and "dw must not overlap x" in err(L)
+    assert lvjp(L, db=P + 192 * MB) == ALIAS and "db must not overlap dw" in err(L)
+    assert lvjp(L, w=P + 256 * MB + 4) == ALIAS and "db must not overlap w" in err(L)
+    assert rvjp(L, ws=P + 128 * MB) == ALIAS and "workspace must not overlap dx" in err(L)
+    assert rvjp(L, ws=WS + 8) == ALIAS and "16-byte aligned" in err(L)
+
+
+def test_vjp_zero_rows_without_parameter_gradients_is_a_noop(L):
+    assert rvjp(L, rows=0, dw=None, x=None, g=None, dx=None, ws=None) == OK and err(L) == ""
+    assert lvjp(L, rows=0, dw=None, db=None, x=None, g=None, dx=None, ws=None) == OK

@@ -1,0 +1,179 @@
+"""GPU parity of the backward operations (RmsNormVjp, LayerNormVjp) through the C ABI against
+the fp64 oracle: dx element by element, dw and db (sums over every row) element by element.
+
+Bars as for the forward operations: bf16 within 1 ulp, fp32 within 1e-5 relative + 1e-6
+absolute, of the oracle's once-rounded values. The parameter gradients are the same bits on
+every run.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import compare
+import workloads
+from gpu_util import DEV, check_vjp, dev, f64, forced_path, run_vjp, say, vjp_oracle
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN = [1, 2, 7, 8, 64, 100, 512, 520, 1000, 4096, 5120, 8192, 8200, 12288, 16384]
+WEIGHTS = [("bf16", "bf16"), ("bf16", "f32"), ("bf16", None), ("f32", "f32"), ("f32", None)]
+
+
+def _inp(rows, hidden, dt, wdt, seed, ln, **kw):
+    x = ("normal", 0.5, 2.0) if ln else ("t3",)
+    return workloads.row_inputs(rows, hidden, dt, seed=seed, x=x,
+                                w=("normal", 1.0, 0.1) if wdt else None,
+                                g=("normal", 0.0, 1.0), w_dtype=wdt or None,
+                                eps=1e-5 if ln else 1e-6, **kw)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("hidden", HIDDEN)
+@pytest.mark.parametrize("dt,wdt", WEIGHTS)
+def test_vjp_shapes(nrm_lib, ln, hidden, dt, wdt):
+    say(f"vjp {'ln' if ln else 'rms'} rows=6 hidden={hidden} {dt} w={wdt}")
+    check_vjp(nrm_lib, _inp(6, hidden, dt, wdt, hidden + 40, ln), ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("rows", [1, 2, 3, 7, 255, 256, 257, 513, 1000, 4097])
+@pytest.mark.parametrize("hidden", [64, 512, 4096])
+def test_vjp_row_counts(nrm_lib, ln, rows, hidden):
+    """Row counts around the partial-row grid (256 blocks) and the teams per block."""
+    say(f"vjp {'ln' if ln else 'rms'} rows={rows} hidden={hidden}")
+    check_vjp(nrm_lib, _inp(rows, hidden, "bf16", "bf16", rows, ln), ln)
+
+
+@pytest.mark.parametrize("path", ["chunked", "scalar"])
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("hidden", [512, 4096, 8192])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_vjp_generic_kernel(nrm_lib, path, ln, hidden, dt):
+    """The looping kernel (16-byte chunks, or one element at a time) on rows the register
+    kernel would take."""
+    say(f"vjp forced {path} {'ln' if ln else 'rms'} hidden={hidden} {dt}")
+    with forced_path(path):
+        check_vjp(nrm_lib, _inp(300, hidden, dt, dt, 5, ln), ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_vjp_optional_gradients(nrm_lib, ln):
+    """Asking for fewer gradients leaves dx's bits unchanged, and each parameter gradient is
+    the same alone as together."""
+    say(f"vjp optional gradients {'ln' if ln else 'rms'}")
+    inp = _inp(700, 4096, "bf16", "bf16", 11, ln)
+    full = run_vjp(nrm_lib, inp, ln)
+    none = run_vjp(nrm_lib, inp, ln, want_dw=False, want_db=False)
+    compare.check_exact_bits(none[0], full[0], "dx without parameter gradients")
+    assert all(t is None for t in none[1:])
+    if ln:
+        only_w = run_vjp(nrm_lib, inp, ln, want_dw=True, want_db=False)
+        only_b = run_vjp(nrm_lib, inp, ln, want_dw=False, want_db=True)
+        compare.check_exact_bits(only_w[1], full[1], "dw alone")
+        compare.check_exact_bits(only_b[2], full[2], "db alone")
+        assert only_w[2] is None and only_b[1] is None
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_vjp_zero_rows_zero_parameter_gradients(nrm_lib, ln):
+    say(f"vjp zero rows {'ln' if ln else 'rms'}")
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(256, dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((256,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    if ln:
+        db = torch.full((256,), float("nan"), dtype=torch.bfloat16, device=DEV)
+        dx, dw, db = nrm_lib.layer_norm_vjp(x, w, x, 1e-5, dw=dw, db=db)
+        torch.cuda.synchronize()
+        assert torch.all(db == 0)
+    else:
+        dx, dw = nrm_lib.rms_norm_vjp(x, w, x, 1e-5, dw=dw)
+        torch.cuda.synchronize()
+    assert dx.numel() == 0 and torch.all(dw == 0)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("into", ["x", "g"])
+def test_vjp_in_place(nrm_lib, ln, into):
+    """dx written over x or over g gives the out-of-place bits (fast and generic kernels)."""
+    for path, hidden in ((None, 4096), ("chunked", 4096), ("scalar", 1000)):
+        say(f"vjp in place into {into} {'ln' if ln else 'rms'} path={path}")
+        inp = _inp(300, hidden, "bf16", "bf16", 12, ln)
+        with forced_path(path):
+            ref = run_vjp(nrm_lib, inp, ln)
+            x, w, g = dev(inp.x), dev(inp.w), dev(inp.g)
+            target = x if into == "x" else g
+            if ln:
+                got = nrm_lib.layer_norm_vjp(x, w, g, inp.eps, dx=target)
+            else:
+                got = nrm_lib.rms_norm_vjp(x, w, g, inp.eps, dx=target)
+            torch.cuda.synchronize()
+        compare.check_exact_bits(target, ref[0], f"dx in place over {into}")
+        for a, b in zip(got[1:], ref[1:]):
+            compare.check_exact_bits(a, b, "parameter gradient with dx in place")
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_vjp_deterministic(nrm_lib, ln):
+    say(f"vjp determinism {'ln' if ln else 'rms'}")
+    inp = _inp(3000, 8192, "bf16", "bf16", 13, ln)
+    a = run_vjp(nrm_lib, inp, ln)
+    b = run_vjp(nrm_lib, inp, ln)
+    for u, v in zip(a, b):
+        compare.check_exact_bits(u, v, "second run")
+
+
+def test_vjp_special_rows(nrm_lib):
+    """Constant rows (LayerNorm: x - mean is exactly 0, so they add nothing to dw) and
+    all-zero rows (RMSNorm: dx = g w / sqrt(eps), nothing to dw)."""
+    say("vjp special rows")
+    for ln in (False, True):
+        inp = _inp(40, 4096, "bf16", "bf16", 14, ln)
+        inp.x[::3] = 0.0
+        inp.x[1::3] = 2.5
+        check_vjp(nrm_lib, inp, ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_vjp_graph_replays(nrm_lib, ln):
+    """Captured in a HIP graph (row kernel + column sum), every replay matches eager."""
+    say(f"vjp graph {'ln' if ln else 'rms'}")
+    inp = _inp(1024, 4096, "bf16", "bf16", 15, ln)
+    x, w, g = dev(inp.x), dev(inp.w), dev(inp.g)
+    eager = run_vjp(nrm_lib, inp, ln)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    db = torch.empty_like(w) if ln else None
+    ws = torch.empty(nrm_lib.vjp_workspace_bytes(1024, 4096, ln), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            if ln:
+                nrm_lib.layer_norm_vjp(x, w, g, inp.eps, dx=dx, dw=dw, db=db, workspace=ws)
+            else:
+                nrm_lib.rms_norm_vjp(x, w, g, inp.eps, dx=dx, dw=dw, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        dx.fill_(float("nan"))
+        dw.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare.check_exact_bits(dx, eager[0], f"replay {rep} dx")
+        compare.check_exact_bits(dw, eager[1], f"replay {rep} dw")
+        if ln:
+            compare.check_exact_bits(db, eager[2], f"replay {rep} db")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+def test_vjp_full_size(nrm_lib, ln):
+    """[16384, 8192] bf16 in the benchmark's launch: dx on sampled rows, dw and db over all
+    rows (the oracle's float64 column sums taken in chunks of rows, rounded once)."""
+    say(f"vjp full size {'ln' if ln else 'rms'}")
+    inp = workloads.cfg_ln_vjp() if ln else workloads.cfg_rms_vjp()
+    rng = np.random.default_rng(99)
+    sel = torch.from_numpy(np.sort(rng.choice(inp.x.shape[0], 64, replace=False)))
+    check_vjp(nrm_lib, inp, ln, rows_sel=sel, chunk=1024)

@@ -11,6 +11,8 @@ built, ``load()`` raises.
     layer_norm(x, w=None, b=None, eps=1e-5)      -> out
     norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, scale=1.0,
               offset=0, forward=True, cache=None) -> out (or the cache, written in place)
+    rms_norm_vjp(x, w, g, eps=1e-5)              -> (dx, dw)
+    layer_norm_vjp(x, w, g, eps=1e-5)            -> (dx, dw, db)
 """
 
 import ctypes
@@ -20,7 +22,8 @@ import torch
 
 __all__ = [
     "NrmError", "load", "lib", "rms_norm", "add_rms_norm", "layer_norm", "norm_rope",
-    "bench_copy", "NRM_F32", "NRM_BF16", "LIB_PATH",
+    "rms_norm_vjp", "layer_norm_vjp", "vjp_workspace_bytes", "bench_copy", "NRM_F32",
+    "NRM_BF16", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnrm.so")
@@ -29,18 +32,24 @@ _DTYPES = {torch.float32: NRM_F32, torch.bfloat16: NRM_BF16}
 _lib = None
 
 _i64, _f32, _int, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
+_sz = ctypes.c_size_t
 _SIGNATURES = {
     "nrm_rms_norm": [_vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
     "nrm_add_rms_norm": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
     "nrm_layer_norm": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
     "nrm_norm_rope": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _f32, _i64, _int, _f32, _f32,
                       _i64, _int, _int, _i64, _int, _int, _vp],
+    "nrm_norm_vjp_workspace_bytes": [_i64, _i64, _int],
+    "nrm_rms_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz, _vp],
+    "nrm_layer_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz,
+                           _vp],
     "nrm_bench_copy": [_vp, _vp, _i64, _vp],
     "nrm_last_error": [],
     "nrm_status_name": [_int],
     "nrm_version": [],
 }
-_RESTYPES = {"nrm_last_error": ctypes.c_char_p, "nrm_status_name": ctypes.c_char_p}
+_RESTYPES = {"nrm_last_error": ctypes.c_char_p, "nrm_status_name": ctypes.c_char_p,
+             "nrm_norm_vjp_workspace_bytes": ctypes.c_size_t}
 
 
 class NrmError(RuntimeError):
@@ -212,6 +221,75 @@ def norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, s
     if st:
         _raise(st)
     return dst
+
+
+def vjp_workspace_bytes(rows, hidden, layer_norm):
+    """Workspace bytes for a backward call that computes a parameter gradient."""
+    return load().nrm_norm_vjp_workspace_bytes(rows, hidden, int(bool(layer_norm)))
+
+
+def _param_grad(want, given, n, x, pdtype, what):
+    if given is not None:
+        _check_act(given, what, x.device)
+        if given.dim() != 1 or given.shape[0] != n or given.dtype != pdtype:
+            raise ValueError(f"{what} must be {pdtype} of shape [{n}], got {given.dtype} "
+                             f"{list(given.shape)}")
+        return given
+    return torch.empty(n, dtype=pdtype, device=x.device) if want else None
+
+
+def _workspace(workspace, need, x):
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check_act(workspace, "workspace", x.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _vjp_common(x, w, g):
+    _check_act(x, "x")
+    _check_act(g, "g", x.device)
+    dt = _dtype_code(x, "x")
+    if g.shape != x.shape or g.dtype != x.dtype:
+        raise ValueError(f"g must be {x.dtype} of shape {list(x.shape)}, got {g.dtype} "
+                         f"{list(g.shape)}")
+    rows, hidden = _rows(x)
+    w, wdt = _check_param(w, "w", hidden, x)
+    pdtype = x.dtype if w is None else w.dtype
+    return dt, rows, hidden, w, wdt, pdtype
+
+
+def rms_norm_vjp(x, w, g, eps=1e-5, want_dw=True, dx=None, dw=None, workspace=None):
+    """Gradients of RMSNorm for x and w given the output cotangent g (nrm_rms_norm_vjp):
+    returns (dx, dw); dw is None when neither ``want_dw`` nor ``dw`` asks for it."""
+    dt, rows, hidden, w, wdt, pdtype = _vjp_common(x, w, g)
+    dx = _out_like(dx, x, "dx")
+    dw = _param_grad(want_dw, dw, hidden, x, pdtype, "dw")
+    need = vjp_workspace_bytes(rows, hidden, False) if dw is not None else 0
+    ws, ws_bytes = _workspace(workspace, need, x)
+    st = load().nrm_rms_norm_vjp(_ptr(x), _ptr(w), _ptr(g), _ptr(dx), _ptr(dw), rows, hidden,
+                                 eps, dt, wdt, _ptr(ws), ws_bytes, _stream())
+    if st:
+        _raise(st)
+    return dx, dw
+
+
+def layer_norm_vjp(x, w, g, eps=1e-5, want_dw=True, want_db=True, dx=None, dw=None, db=None,
+                   workspace=None):
+    """Gradients of LayerNorm for x, w and b given the output cotangent g
+    (nrm_layer_norm_vjp): returns (dx, dw, db), None for a gradient not asked for."""
+    dt, rows, hidden, w, wdt, pdtype = _vjp_common(x, w, g)
+    dx = _out_like(dx, x, "dx")
+    dw = _param_grad(want_dw, dw, hidden, x, pdtype, "dw")
+    db = _param_grad(want_db, db, hidden, x, pdtype, "db")
+    need = vjp_workspace_bytes(rows, hidden, True) if (dw is not None or db is not None) else 0
+    ws, ws_bytes = _workspace(workspace, need, x)
+    st = load().nrm_layer_norm_vjp(_ptr(x), _ptr(w), _ptr(g), _ptr(dx), _ptr(dw), _ptr(db), rows,
+                                   hidden, eps, dt, wdt, _ptr(ws), ws_bytes, _stream())
+    if st:
+        _raise(st)
+    return dx, dw, db
 
 
 def bench_copy(src, dst):

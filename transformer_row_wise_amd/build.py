@@ -8,6 +8,7 @@ does not know the feature, which is harmless); no fast-math.
 """
 
 import concurrent.futures
+import glob
 import os
 import subprocess
 import sys
@@ -21,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libnrm.so")
 ARCH = os.environ.get("NRM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "rms.hip", "add_rms.hip", "ln.hip", "norm_rope.hip", "copy.hip"]
+SOURCES = sorted(os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*.hip")))
 
 FLAGS = [
     f"--offload-arch={ARCH}",

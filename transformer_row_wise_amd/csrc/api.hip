@@ -13,6 +13,7 @@
 
 #include "launch.hpp"
 #include "nrm.h"
+#include "vjp.hpp"
 
 namespace {
 
@@ -222,6 +223,97 @@ nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64
   const bool al = aligned16(x) && aligned16(out_or_cache) && (!w || aligned16(w));
   return launched(fn, dtype == NRM_BF16 ? nrm::launch_norm_rope<true>(a, al, stream)
                                         : nrm::launch_norm_rope<false>(a, al, stream));
+}
+
+size_t nrm_norm_vjp_workspace_bytes(int64_t rows, int64_t hidden, int layer_norm) {
+  if (rows <= 0 || hidden < 1 || hidden > INT32_MAX) return 0;
+  return (size_t)nrm::vjp_partials(rows) * (size_t)hidden * sizeof(double) *
+         (layer_norm ? 2 : 1);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by the two backward entry points; db is always NULL for RMSNorm.
+nrm_status norm_vjp(const char* fn, bool ln, const void* x, const void* w, const void* g,
+                    void* dx, void* dw, void* db, int64_t rows, int64_t hidden, float eps,
+                    nrm_dtype dtype, nrm_dtype w_dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, w_dtype);
+  if (st) return st;
+  if ((st = check_rows(fn, rows, hidden, dtype))) return st;
+  const int64_t pb = hidden * esize(w_dtype);
+  const Span sw = span(w, w ? pb : 0), sdw = span(dw, dw ? pb : 0), sdb = span(db, db ? pb : 0);
+  if ((st = check_out_vs(fn, "dw", sdw, "w", sw, false))) return st;
+  if ((st = check_out_vs(fn, "db", sdb, "w", sw, false))) return st;
+  if ((st = check_out_vs(fn, "db", sdb, "dw", sdw, false))) return st;
+  nrm::VjpArgs a;
+  a.x = x; a.w = w; a.g = g; a.dx = dx;
+  a.part_w = a.part_b = nullptr;
+  a.rows = rows; a.hidden = hidden; a.rpb = 1; a.eps = eps;
+  a.w_f32 = w_dtype == NRM_F32; a.team = 64;
+  auto go = [&](bool al) {
+    if (ln)
+      return dtype == NRM_BF16 ? nrm::launch_vjp<true, nrm::VJP_LN>(a, dw, db, al, stream)
+                               : nrm::launch_vjp<false, nrm::VJP_LN>(a, dw, db, al, stream);
+    return dtype == NRM_BF16 ? nrm::launch_vjp<true, nrm::VJP_RMS>(a, dw, db, al, stream)
+                             : nrm::launch_vjp<false, nrm::VJP_RMS>(a, dw, db, al, stream);
+  };
+  if (rows == 0) return launched(fn, go(false));  // only zeroes dw / db
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!g) return fail(NRM_ERR_NULL, "%s: g must not be NULL, got NULL", fn);
+  if (!dx) return fail(NRM_ERR_NULL, "%s: dx must not be NULL, got NULL", fn);
+  const int64_t nb = rows * hidden * esize(dtype);
+  const Span sx = span(x, nb), sg = span(g, nb), sdx = span(dx, nb);
+  if ((st = check_out_vs(fn, "dx", sdx, "x", sx, true))) return st;
+  if ((st = check_out_vs(fn, "dx", sdx, "g", sg, true))) return st;
+  if ((st = check_out_vs(fn, "dx", sdx, "w", sw, false))) return st;
+  if ((st = check_out_vs(fn, "dw", sdw, "x", sx, false))) return st;
+  if ((st = check_out_vs(fn, "dw", sdw, "g", sg, false))) return st;
+  if ((st = check_out_vs(fn, "dw", sdw, "dx", sdx, false))) return st;
+  if ((st = check_out_vs(fn, "db", sdb, "x", sx, false))) return st;
+  if ((st = check_out_vs(fn, "db", sdb, "g", sg, false))) return st;
+  if ((st = check_out_vs(fn, "db", sdb, "dx", sdx, false))) return st;
+  if (dw || db) {
+    const size_t need = nrm_norm_vjp_workspace_bytes(rows, hidden, ln ? 1 : 0);
+    if (!workspace) return fail(NRM_ERR_NULL, "%s: workspace must not be NULL, got NULL", fn);
+    if (workspace_bytes < need)
+      return fail(NRM_ERR_SHAPE, "%s: workspace_bytes must be >= %zu, got %zu", fn, need,
+                  workspace_bytes);
+    if (!aligned16(workspace))
+      return fail(NRM_ERR_ALIAS, "%s: workspace must be 16-byte aligned, got %p", fn, workspace);
+    const Span sws = span(workspace, (int64_t)need);
+    const char* names[] = {"x", "g", "w", "dx", "dw", "db"};
+    const Span spans[] = {sx, sg, sw, sdx, sdw, sdb};
+    for (int i = 0; i < 6; ++i)
+      if ((st = check_out_vs(fn, "workspace", sws, names[i], spans[i], false))) return st;
+    a.part_w = (double*)workspace;
+    if (ln) a.part_b = a.part_w + nrm::vjp_partials(rows) * hidden;
+  }
+  const bool al = aligned16(x) && aligned16(g) && aligned16(dx) && (!w || aligned16(w));
+  return launched(fn, go(al));
+}
+
+}  // namespace
+
+extern "C" {
+
+nrm_status nrm_rms_norm_vjp(const void* x, const void* w, const void* g, void* dx, void* dw,
+                            int64_t rows, int64_t hidden, float eps, nrm_dtype dtype,
+                            nrm_dtype w_dtype, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return norm_vjp("nrm_rms_norm_vjp", false, x, w, g, dx, dw, nullptr, rows, hidden, eps, dtype,
+                  w_dtype, workspace, workspace_bytes, stream);
+}
+
+nrm_status nrm_layer_norm_vjp(const void* x, const void* w, const void* g, void* dx, void* dw,
+                              void* db, int64_t rows, int64_t hidden, float eps,
+                              nrm_dtype dtype, nrm_dtype w_dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return norm_vjp("nrm_layer_norm_vjp", true, x, w, g, dx, dw, db, rows, hidden, eps, dtype,
+                  w_dtype, workspace, workspace_bytes, stream);
 }
 
 const char* nrm_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,409 @@
+// Backward (vector-Jacobian products) of RMSNorm and LayerNorm over the last axis.
+//
+// Operations (nuvec-core 0.5.0 fast::FastOp, variants RmsNormVjp and LayerNormVjp): given the
+// cotangent g of the output, the gradients for x and for the scale w (and the shift b).
+// Per row of D features, with r the row's reciprocal standard deviation:
+//   RMS  r = 1/sqrt(sum(x^2)/D + eps), c = r^3 * sum(g w x) / D
+//        dx = r (g w) - x c,                 dw += g x r
+//   LN   mu = sum(x)/D, var = sum(x^2)/D - mu^2, r = 1/sqrt(var + eps), xh = (x - mu) r,
+//        d = g w, m1 = sum(d)/D, m2 = sum(d xh)/D = r (sum(d x) - mu sum(d)) / D
+//        dx = r (d - m1 - xh m2),            dw += g xh,   db += g
+// All row statistics come from one pass (LN's variance from the raw moments), accumulated in
+// fp64, so a row needs a single cross-thread reduction. The statistics and the per-element
+// outputs are fp64 because dx is a difference of two terms that can cancel, and the bar is
+// one unit in the last place of the result: an fp32 statistic would miss it on a few
+// elements per million.
+//
+// dw and db sum over rows. A block owns a contiguous run of rows and accumulates its column
+// sums in fp64 registers (each thread always holds the same columns); at the end the block
+// writes one fp64 partial row to the caller's workspace, and vjp_colsum adds the partial
+// rows in a fixed order. Results are therefore identical run to run.
+#pragma once
+
+#include "row_kernels.hpp"
+
+namespace nrm {
+
+enum VjpOp : int { VJP_RMS = 0, VJP_LN = 1 };
+
+// Partial rows of the column sums: one per block, at most this many. Fixed (not derived
+// from the device) so that the workspace size and the summation order depend only on the
+// problem shape.
+constexpr int64_t VJP_MAX_PARTIALS = 256;
+
+struct VjpArgs {
+  const void* x;
+  const void* w;      // may be null (= 1)
+  const void* g;
+  void* dx;
+  double* part_w;     // [blocks][hidden] partial sums for dw, or null (dw not wanted)
+  double* part_b;     // [blocks][hidden] partial sums for db (LN), or null
+  int64_t rows;
+  int64_t hidden;     // < 2^31
+  int64_t rpb;        // rows per block
+  float eps;
+  int w_f32;          // w stored as fp32 (else bf16, only with bf16 activations)
+  int team;           // threads per row (fast kernel): a multiple of 64
+};
+
+// Row scalars of one row, from its four sums.
+struct VjpRow {
+  double r;    // reciprocal standard deviation
+  double c;    // RMS: r^3 sum(g w x) / D
+  double mu;   // LN
+  double m1;   // LN: mean(d)
+  double m2;   // LN: mean(d xh)
+};
+
+__device__ __forceinline__ VjpRow vjp_rms_scalars(double ss, double dot, int64_t D, float eps) {
+  VjpRow s;
+  s.r = rstd_f64(ss, D, eps);
+  s.c = s.r * s.r * s.r * dot / (double)D;
+  s.mu = s.m1 = s.m2 = 0.0;
+  return s;
+}
+
+__device__ __forceinline__ VjpRow vjp_ln_scalars(double sx, double sxx, double sd, double sdx,
+                                                 int64_t D, float eps) {
+  VjpRow s;
+  const double n = (double)D;
+  s.mu = sx / n;
+  const double var = fmax(sxx / n - s.mu * s.mu, 0.0);
+  s.r = 1.0 / __builtin_sqrt(var + (double)eps);
+  s.c = 0.0;
+  s.m1 = sd / n;
+  s.m2 = s.r * (sdx - s.mu * sd) / n;
+  return s;
+}
+
+// Statistic sums of V elements, all accumulated in fp64: RMS (sum x^2, sum g w x), LN (sum x,
+// sum x^2, sum d, sum d x) with d = g w. XF: x, g and w are bf16 values (8 significant
+// bits), so x^2, g w and g w x are exact in fp32 and only need widening; otherwise the
+// products are formed in fp64 (exact up to one rounding of g w x).
+template <int OP, int V, bool XF>
+__device__ __forceinline__ void vjp_accumulate(const float (&f)[V], const float (&gv)[V],
+                                               const float (&wv)[V], double (&ds)[4]) {
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    if constexpr (OP == VJP_RMS) {
+      if constexpr (XF) {
+        ds[0] += (double)(f[e] * f[e]);
+        ds[1] += (double)((gv[e] * wv[e]) * f[e]);
+      } else {
+        const double xd = (double)f[e];
+        ds[0] = __builtin_fma(xd, xd, ds[0]);
+        ds[1] = __builtin_fma((double)gv[e] * (double)wv[e], xd, ds[1]);
+      }
+    } else {
+      const double xd = (double)f[e];
+      const double d = XF ? (double)(gv[e] * wv[e]) : (double)gv[e] * (double)wv[e];
+      ds[0] += xd;
+      ds[1] = __builtin_fma(xd, xd, ds[1]);
+      ds[2] += d;
+      ds[3] = __builtin_fma(d, xd, ds[3]);
+    }
+  }
+}
+
+// dx of V elements, and the dw / db column accumulators, in fp64.
+template <int OP, int V, bool DW, bool DB, bool XF>
+__device__ __forceinline__ void vjp_outputs(const float (&f)[V], const float (&gv)[V],
+                                            const float (&wv)[V], const VjpRow& s,
+                                            float (&dxv)[V], double* accw, double* accb) {
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const double xd = (double)f[e];
+    const double gd = (double)gv[e];
+    const double d = XF ? (double)(gv[e] * wv[e]) : gd * (double)wv[e];
+    if constexpr (OP == VJP_RMS) {
+      dxv[e] = f64_to_f32(__builtin_fma(s.r, d, -(xd * s.c)));
+      if constexpr (DW) {
+        const double gx = XF ? (double)(gv[e] * f[e]) : gd * xd;
+        accw[e] = __builtin_fma(gx, s.r, accw[e]);
+      }
+    } else {
+      // (d - m1) first: it is exactly 0 where d equals its row mean (a one-element row).
+      const double xh = (xd - s.mu) * s.r;
+      dxv[e] = f64_to_f32(__builtin_fma(-xh, s.m2, d - s.m1) * s.r);
+      if constexpr (DW) accw[e] = __builtin_fma(gd, xh, accw[e]);
+      if constexpr (DB) accb[e] += gd;
+    }
+  }
+}
+
+// Fast kernel: a block of G teams of T = a.team threads (G * T = blockDim.x); a team owns
+// one row at a time, thread t of a team keeping chunks t, t + T, ... (NV of them) of the
+// row in registers. Block b walks rows [b * rpb, min(rows, (b + 1) * rpb)), team i taking
+// rows b * rpb + i, + G, ...; every team runs the same number of iterations (a team past
+// the end reloads the last row and discards it), so the block barriers line up. The next
+// row's x and g are loaded before the current row is reduced. EXACT: T * NV chunks cover
+// the row; otherwise chunk indexes past the end are clamped for loads and their results
+// dropped. PG: parameter gradients wanted (dw for RMS; dw and db for LN).
+template <bool BF16, int OP, int NV, int PK, bool EXACT, bool PG>
+__global__ void __launch_bounds__(1024)
+vjp_rows(VjpArgs a) {
+  constexpr bool DW = PG, DB = PG && OP == VJP_LN;
+  constexpr bool XF = BF16 && PK != PK_F32;
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int NS = OP == VJP_RMS ? 2 : 4;  // sums per row
+  __shared__ double red[2][16][NS];          // [iteration parity][wave][sum]
+  extern __shared__ double comb[];           // (G - 1) * T * V doubles, team combine
+  const int T = a.team;
+  const int G = blockDim.x / T;
+  const int team = threadIdx.x / T;
+  const int tid = threadIdx.x - team * T;
+  const int nwt = T >> 6;                    // waves per team
+  const int wave0 = team * nwt;
+  const int nvec = (int)(a.hidden / V);
+  const int64_t row0 = (int64_t)blockIdx.x * a.rpb;
+  const int64_t row_end = min(a.rows, row0 + a.rpb);
+  const int iters = (int)((a.rpb + G - 1) / G);
+
+  int jj[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int j = tid + k * T;
+    ok[k] = EXACT || j < nvec;
+    jj[k] = EXACT ? j : min(j, nvec - 1);
+  }
+  float wv[NV][V];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+  double accw[NV][V], accb[NV][V];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < V; ++e) accw[k][e] = accb[k][e] = 0.0;
+
+  auto row_of = [&](int it) { return row0 + (int64_t)it * G + team; };
+  auto load_row = [&](int it, u32x4 (&xv)[NV], u32x4 (&gv)[NV]) {
+    const int64_t row = min(row_of(it), row_end - 1);
+    const char* xr = (const char*)a.x + row * a.hidden * Fmt<BF16>::ESZ;
+    const char* gr = (const char*)a.g + row * a.hidden * Fmt<BF16>::ESZ;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      xv[k] = ld16_nt(xr + (int64_t)jj[k] * 16);
+      gv[k] = ld16_nt(gr + (int64_t)jj[k] * 16);
+    }
+  };
+
+  auto process = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV]) {
+    const int64_t row = row_of(it);
+    const bool valid = row < row_end;
+    double ds[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (ok[k]) {
+        float f[V], gf[V];
+        unpack<BF16>(xv[k], f);
+        unpack<BF16>(gv[k], gf);
+        vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
+      }
+    }
+    // Team reduction: DPP within each wave, then the team's wave sums from LDS in order.
+    double v[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) v[i] = wave_sum(ds[i]);
+    const int par = it & 1;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) red[par][threadIdx.x >> 6][i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      double t = red[par][wave0][i];
+      for (int q = 1; q < nwt; ++q) t += red[par][wave0 + q][i];
+      v[i] = t;
+    }
+    VjpRow s;
+    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(v[0], v[1], a.hidden, a.eps);
+    else s = vjp_ln_scalars(v[0], v[1], v[2], v[3], a.hidden, a.eps);
+    if (!valid) return;
+    char* dr = (char*)a.dx + row * a.hidden * Fmt<BF16>::ESZ;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      // Re-derive the elements from the raw chunks: the opaque copy stops the compiler from
+      // keeping the statistic pass's fp64 conversions alive across the barrier, which
+      // costs more registers than converting again.
+      u32x4 xr = xv[k], gr = gv[k];
+      __asm__ volatile("" : "+v"(xr), "+v"(gr));
+      float f[V], gf[V], dxv[V];
+      unpack<BF16>(xr, f);
+      unpack<BF16>(gr, gf);
+      vjp_outputs<OP, V, DW, DB, XF>(f, gf, wv[k], s, dxv, accw[k], accb[k]);
+      if (ok[k]) st16_nt(dr + (int64_t)jj[k] * 16, pack<BF16>(dxv));
+    }
+  };
+
+  u32x4 xa[NV], ga[NV];
+  load_row(0, xa, ga);
+  for (int it = 0; it < iters - 1; ++it) {
+    u32x4 xb[NV], gb[NV];
+    load_row(it + 1, xb, gb);
+    process(it, xa, ga);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      xa[k] = xb[k];
+      ga[k] = gb[k];
+    }
+  }
+  process(iters - 1, xa, ga);
+
+  if constexpr (DW || DB) {
+    // Team 0 adds teams 1 .. G-1 (in that order) through LDS, one chunk slot at a time,
+    // then writes the block's partial row.
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((pass == 0 && !DW) || (pass == 1 && !DB)) continue;
+      double (&acc)[NV][V] = pass == 0 ? accw : accb;
+      double* part = (pass == 0 ? a.part_w : a.part_b) + (int64_t)blockIdx.x * a.hidden;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if (G > 1) {
+          __syncthreads();
+          if (team > 0) {
+            double* slot = comb + ((int64_t)(team - 1) * T + tid) * V;
+#pragma unroll
+            for (int e = 0; e < V; ++e) slot[e] = acc[k][e];
+          }
+          __syncthreads();
+          if (team == 0) {
+            for (int q = 1; q < G; ++q) {
+              const double* slot = comb + ((int64_t)(q - 1) * T + tid) * V;
+#pragma unroll
+              for (int e = 0; e < V; ++e) acc[k][e] += slot[e];
+            }
+          }
+        }
+        if (team == 0 && ok[k]) {
+          double* p = part + (int64_t)jj[k] * V;
+#pragma unroll
+          for (int e = 0; e < V; ++e) p[e] = acc[k][e];
+        }
+      }
+    }
+  }
+}
+
+// Generic kernel: any row width, V elements per access (VEC for 16-byte aligned rows, else
+// 1). One 256-thread block per run of rows; each row is read twice (the second pass mostly
+// from L2), and the block's partial row in the workspace is updated in place by the thread
+// that owns each column (the same thread for every row, so no other thread touches it).
+template <bool BF16, int OP, int V, bool PG>
+__global__ void __launch_bounds__(256)
+vjp_generic(VjpArgs a) {
+  constexpr bool DW = PG, DB = PG && OP == VJP_LN;
+  constexpr int NS = OP == VJP_RMS ? 2 : 4;
+  __shared__ double red[4][NS];
+  const int64_t nch = a.hidden / V;
+  const bool has_w = a.w != nullptr;
+  const bool xf = BF16 && !a.w_f32;  // exact fp32 products (see vjp_accumulate)
+  const int64_t row0 = (int64_t)blockIdx.x * a.rpb;
+  const int64_t row_end = min(a.rows, row0 + a.rpb);
+  double* pw = DW ? a.part_w + (int64_t)blockIdx.x * a.hidden : nullptr;
+  double* pb = DB ? a.part_b + (int64_t)blockIdx.x * a.hidden : nullptr;
+
+  for (int64_t row = row0; row < row_end; ++row) {
+    const int64_t e0 = row * a.hidden;
+    double ds[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int64_t j = threadIdx.x; j < nch; j += 256) {
+      float f[V], gf[V], wv[V];
+      load_act<BF16, V>(a.x, e0 + j * V, f);
+      load_act<BF16, V>(a.g, e0 + j * V, gf);
+      if (has_w) {
+        load_param<BF16, V>(a.w, a.w_f32, j * V, wv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) wv[e] = 1.f;
+      }
+      if (xf) vjp_accumulate<OP, V, BF16>(f, gf, wv, ds);
+      else vjp_accumulate<OP, V, false>(f, gf, wv, ds);
+    }
+    double v[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) v[i] = wave_sum(ds[i]);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) red[threadIdx.x >> 6][i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) v[i] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+    __syncthreads();  // red is rewritten by the next row
+    VjpRow s;
+    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(v[0], v[1], a.hidden, a.eps);
+    else s = vjp_ln_scalars(v[0], v[1], v[2], v[3], a.hidden, a.eps);
+    const bool first = row == row0;
+    for (int64_t j = threadIdx.x; j < nch; j += 256) {
+      float f[V], gf[V], wv[V], dxv[V];
+      load_act<BF16, V>(a.x, e0 + j * V, f);
+      load_act<BF16, V>(a.g, e0 + j * V, gf);
+      if (has_w) {
+        load_param<BF16, V>(a.w, a.w_f32, j * V, wv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) wv[e] = 1.f;
+      }
+      double aw[V], ab[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        aw[e] = (DW && !first) ? pw[j * V + e] : 0.0;
+        ab[e] = (DB && !first) ? pb[j * V + e] : 0.0;
+      }
+      if (xf) vjp_outputs<OP, V, DW, DB, BF16>(f, gf, wv, s, dxv, aw, ab);
+      else vjp_outputs<OP, V, DW, DB, false>(f, gf, wv, s, dxv, aw, ab);
+      store_act<BF16, V>(a.dx, e0 + j * V, dxv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if constexpr (DW) pw[j * V + e] = aw[e];
+        if constexpr (DB) pb[j * V + e] = ab[e];
+      }
+    }
+  }
+}
+
+// Column sums of the partial rows: out[c] = sum over p < nparts of part[p][c], added in a
+// fixed order (16 interleaved slices, then the slices in order), rounded once to the
+// parameter dtype. gridDim.y is the number of outputs (1 or 2); blockIdx.y picks the pair
+// (part0, out0) or (part1, out1). The host passes only outputs that were asked for.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256)
+vjp_colsum(const double* part0, void* out0, const double* part1, void* out1, int64_t nparts,
+           int64_t hidden) {
+  __shared__ double red[16][17];
+  const double* part = blockIdx.y == 0 ? part0 : part1;
+  void* out = blockIdx.y == 0 ? out0 : out1;
+  const int c = threadIdx.x & 15;
+  const int s = threadIdx.x >> 4;
+  const int64_t col = (int64_t)blockIdx.x * 16 + c;
+  double acc = 0.0;
+  if (col < hidden) {
+    for (int64_t p = s; p < nparts; p += 16) acc += part[p * hidden + col];
+  }
+  red[s][c] = acc;
+  __syncthreads();
+  if (s == 0 && col < hidden) {
+    double t = red[0][c];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) t += red[q][c];
+    if constexpr (OUT_BF16) ((uint16_t*)out)[col] = f32_to_bf16(f64_to_f32(t));
+    else ((float*)out)[col] = (float)t;
+  }
+}
+
+// Host-side launch: picks the kernel and writes dx, and dw / db (either may be null) through
+// the workspace. With rows == 0 it only zeroes dw / db.
+template <bool BF16, int OP>
+hipError_t launch_vjp(const VjpArgs& a, void* dw, void* db, bool aligned16, hipStream_t stream);
+
+// Number of partial rows (and blocks) for `rows` rows: ceil(rows / ceil(rows / 256)).
+inline int64_t vjp_partials(int64_t rows) {
+  if (rows <= 0) return 0;
+  const int64_t p = rows < VJP_MAX_PARTIALS ? rows : VJP_MAX_PARTIALS;
+  const int64_t rpb = (rows + p - 1) / p;
+  return (rows + rpb - 1) / rpb;
+}
+
+}  // namespace nrm

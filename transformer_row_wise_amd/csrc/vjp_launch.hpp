@@ -1,0 +1,161 @@
+// Kernel-shape choice and launch of the RMSNorm / LayerNorm backward kernels.
+//
+// For rows of n = hidden / VEC 16-byte chunks (VEC = 8 bf16, 4 fp32), when hidden and the
+// base addresses are 16-byte granular and a thread's share fits in registers (NV * VEC <= 8
+// elements, so hidden <= 8192 for bf16 and fp32):
+//   vjp_rows, a team of T = ceil(n / NV) threads (rounded up to a wave) per row, NV the
+//   smallest chunk count per thread that keeps T <= 1024; G = min(1024 / T, 8) teams per
+//   block. With parameter gradients the grid is vjp_partials(rows) blocks of rpb rows each
+//   (one partial row per block); without, each team takes one row.
+// Otherwise vjp_generic (256 threads, 16-byte chunks or single elements, any width).
+// The partial rows are then added by vjp_colsum.
+#pragma once
+
+#include <algorithm>
+
+#include "launch.hpp"
+#include "vjp.hpp"
+
+namespace nrm {
+
+namespace {
+
+constexpr int64_t kVjpMaxGrid = 0x7fffffff;
+
+__global__ void vjp_zero_kernel(unsigned char* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+hipError_t zero_bytes(void* p, int64_t n, hipStream_t stream) {
+  if (p == nullptr || n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  vjp_zero_kernel<<<(unsigned)blocks, 256, 0, stream>>>((unsigned char*)p, n);
+  return hipGetLastError();
+}
+
+template <bool BF16, int OP, int NV, int PK, bool EXACT, bool PG>
+hipError_t go_vjp_rows(const VjpArgs& a, int64_t blocks, int threads, hipStream_t stream) {
+  constexpr int V = Fmt<BF16>::VEC;
+  const int G = threads / a.team;
+  const size_t lds = PG && G > 1 ? (size_t)(G - 1) * a.team * V * sizeof(double) : 0;
+  vjp_rows<BF16, OP, NV, PK, EXACT, PG><<<(unsigned)blocks, threads, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int OP, int NV, bool PG>
+hipError_t vjp_rows_pk(const VjpArgs& a, int64_t blocks, int threads, bool exact,
+                       hipStream_t stream) {
+  if (a.w == nullptr)
+    return exact ? go_vjp_rows<BF16, OP, NV, PK_NONE, true, PG>(a, blocks, threads, stream)
+                 : go_vjp_rows<BF16, OP, NV, PK_NONE, false, PG>(a, blocks, threads, stream);
+  if constexpr (BF16) {
+    if (a.w_f32)
+      return exact ? go_vjp_rows<BF16, OP, NV, PK_F32, true, PG>(a, blocks, threads, stream)
+                   : go_vjp_rows<BF16, OP, NV, PK_F32, false, PG>(a, blocks, threads, stream);
+  }
+  return exact ? go_vjp_rows<BF16, OP, NV, PK_SAME, true, PG>(a, blocks, threads, stream)
+               : go_vjp_rows<BF16, OP, NV, PK_SAME, false, PG>(a, blocks, threads, stream);
+}
+
+template <bool BF16, int OP, int NV>
+hipError_t vjp_rows_pg(const VjpArgs& a, bool pg, int64_t blocks, int threads, bool exact,
+                       hipStream_t stream) {
+  return pg ? vjp_rows_pk<BF16, OP, NV, true>(a, blocks, threads, exact, stream)
+            : vjp_rows_pk<BF16, OP, NV, false>(a, blocks, threads, exact, stream);
+}
+
+// Fast path; *done = false when the row does not fit it.
+template <bool BF16, int OP>
+hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool* done) {
+  constexpr int V = Fmt<BF16>::VEC;
+  // At most 8 elements per thread: the fp64 column accumulators of 16 (LN: dw and db, 64
+  // registers) push the kernel past 128 registers, into scratch.
+  constexpr int MAX_NV = 8 / V;  // 1 for bf16, 2 for fp32
+  *done = false;
+  int nv = 1;
+  while (nv <= MAX_NV && (n + nv - 1) / nv > 1024) nv *= 2;
+  if (nv > MAX_NV) return hipSuccess;
+  const int team = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
+  const bool exact = (int64_t)team * nv == n;
+  const int gmax = std::max(1, std::min(8, 1024 / team));
+  int64_t blocks;
+  int G;
+  if (pg) {
+    blocks = vjp_partials(a.rows);
+    a.rpb = (a.rows + blocks - 1) / blocks;
+    G = (int)std::min<int64_t>(gmax, a.rpb);
+  } else {
+    G = (int)std::min<int64_t>(gmax, a.rows);
+    a.rpb = G;
+    blocks = (a.rows + G - 1) / G;
+  }
+  if (blocks > kVjpMaxGrid) return hipSuccess;
+  a.team = team;
+  *done = true;
+  const int threads = G * team;
+  switch (nv) {
+    case 1: return vjp_rows_pg<BF16, OP, 1>(a, pg, blocks, threads, exact, stream);
+    case 2: if constexpr (!BF16) return vjp_rows_pg<BF16, OP, 2>(a, pg, blocks, threads, exact, stream); break;
+    default: break;
+  }
+  *done = false;
+  return hipSuccess;
+}
+
+template <bool BF16, int OP, int V>
+hipError_t go_vjp_generic(VjpArgs a, bool pg, hipStream_t stream) {
+  int64_t blocks;
+  if (pg) {
+    blocks = vjp_partials(a.rows);
+    a.rpb = (a.rows + blocks - 1) / blocks;
+  } else {
+    a.rpb = 1;
+    blocks = a.rows;
+  }
+  if (blocks > kVjpMaxGrid) return hipErrorInvalidConfiguration;
+  if (pg) vjp_generic<BF16, OP, V, true><<<(unsigned)blocks, 256, 0, stream>>>(a);
+  else vjp_generic<BF16, OP, V, false><<<(unsigned)blocks, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <bool BF16, int OP>
+hipError_t launch_vjp(const VjpArgs& a, void* dw, void* db, bool aligned16, hipStream_t stream) {
+  constexpr int V = Fmt<BF16>::VEC;
+  const int pbytes = (!BF16 || a.w_f32) ? 4 : 2;  // parameter element size
+  if (a.rows == 0) {
+    hipError_t e = zero_bytes(dw, a.hidden * pbytes, stream);
+    if (e == hipSuccess) e = zero_bytes(db, a.hidden * pbytes, stream);
+    return e;
+  }
+  const bool pg = dw != nullptr || db != nullptr;
+  const int path = forced_path();
+  const bool vec = aligned16 && a.hidden % V == 0 && path != PATH_SCALAR;
+  hipError_t err = hipSuccess;
+  bool done = false;
+  if (vec && path != PATH_CHUNKED) err = try_vjp_rows<BF16, OP>(a, pg, a.hidden / V, stream, &done);
+  if (!done) err = vec ? go_vjp_generic<BF16, OP, V>(a, pg, stream)
+                       : go_vjp_generic<BF16, OP, 1>(a, pg, stream);
+  if (err != hipSuccess || !pg) return err;
+  // Only the requested outputs are passed: (part_w, dw) and/or (part_b, db).
+  const double* parts[2];
+  void* outs[2];
+  int n = 0;
+  if (dw != nullptr) { parts[n] = a.part_w; outs[n] = dw; ++n; }
+  if (OP == VJP_LN && db != nullptr) { parts[n] = a.part_b; outs[n] = db; ++n; }
+  if (n == 1) { parts[1] = parts[0]; outs[1] = outs[0]; }
+  const int64_t nparts = vjp_partials(a.rows);
+  const dim3 grid((unsigned)((a.hidden + 15) / 16), (unsigned)n);
+  if (BF16 && !a.w_f32)
+    vjp_colsum<true><<<grid, 256, 0, stream>>>(parts[0], outs[0], parts[1], outs[1], nparts,
+                                               a.hidden);
+  else
+    vjp_colsum<false><<<grid, 256, 0, stream>>>(parts[0], outs[0], parts[1], outs[1], nparts,
+                                                a.hidden);
+  return hipGetLastError();
+}
+
+}  // namespace nrm

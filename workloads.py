@@ -7,10 +7,10 @@ built here, and neither of them imports the other.
 
 Recipe (the same for every workload):
   * ``numpy.random.default_rng(seed)`` (PCG64), draws taken in float64 in the order
-    x, r, w, b;
+    x, r, w, b, g (g: the output cotangent of a backward call);
   * ``N(mean, std)`` means ``rng.normal(loc=mean, scale=std)`` (std, not variance);
     ``U(lo, hi)`` is ``rng.uniform(lo, hi)``; Student-t(3) is ``rng.standard_t(3)``;
-  * the "1% of rows times 1e3" outlier rows are picked after x and r are drawn, with
+  * the "1% of rows times 1e3" outlier rows are picked after every draw, with
     ``rng.choice(rows, rows // 100, replace=False)``, and the same rows are scaled in x and r;
   * float64 -> float32 by numpy's round-to-nearest-even cast, then float32 -> bfloat16 by
     torch's round-to-nearest-even cast (CPU).
@@ -51,25 +51,27 @@ def draw(rng: np.random.Generator, spec, shape):
 
 @dataclasses.dataclass
 class RowInputs:
-    """Inputs of one row-wise call: x (and r) of shape [rows, hidden]; w, b of [hidden]."""
+    """Inputs of one row-wise call: x (and r, g) of shape [rows, hidden]; w, b of [hidden]."""
 
     x: torch.Tensor
     r: torch.Tensor | None
     w: torch.Tensor | None
     b: torch.Tensor | None
     eps: float
+    g: torch.Tensor | None = None
 
 
 def row_inputs(rows, hidden, dtype, *, seed=0, x=("normal", 0.0, 1.0), r=None,
-               w=("normal", 1.0, 0.1), b=None, w_dtype=None, eps=1e-5,
+               w=("normal", 1.0, 0.1), b=None, g=None, w_dtype=None, eps=1e-5,
                outlier_frac=0.0, outlier_scale=1e3) -> RowInputs:
-    """Draws x (and r, w, b when given a distribution) in the recipe's order."""
+    """Draws x (and r, w, b, g when given a distribution) in the recipe's order."""
     rng = np.random.default_rng(seed)
     wd = w_dtype or dtype
     x64 = draw(rng, x, (rows, hidden))
     r64 = draw(rng, r, (rows, hidden)) if r is not None else None
     w64 = draw(rng, w, (hidden,)) if w is not None else None
     b64 = draw(rng, b, (hidden,)) if b is not None else None
+    g64 = draw(rng, g, (rows, hidden)) if g is not None else None
     if outlier_frac > 0 and rows > 0:
         pick = rng.choice(rows, int(rows * outlier_frac), replace=False)
         x64[pick] *= outlier_scale
@@ -81,6 +83,7 @@ def row_inputs(rows, hidden, dtype, *, seed=0, x=("normal", 0.0, 1.0), r=None,
         w=cast(w64, wd) if w64 is not None else None,
         b=cast(b64, wd) if b64 is not None else None,
         eps=eps,
+        g=cast(g64, dtype) if g64 is not None else None,
     )
 
 
@@ -159,3 +162,19 @@ def cfg_add_rms_scale(rows=16384, hidden=8192, dtype="bf16", seed=0):
 # The headline measurement: add-RMSNorm, bf16, 16384 x 8192.
 METRIC_ROWS = 16384
 METRIC_HIDDEN = 8192
+
+
+# Backward workloads (RmsNormVjp, LayerNormVjp): the forward inputs of the add-RMSNorm and
+# LayerNorm workloads at [16384, 8192] bf16 with a cotangent g ~ N(0, 1) of the same shape.
+
+def cfg_rms_vjp(rows=16384, hidden=8192, dtype="bf16", seed=0):
+    """RMSNorm backward: x Student-t(3) with 1% of rows x1e3, w ~N(1,0.1), g ~N(0,1),
+    eps 1e-6."""
+    return row_inputs(rows, hidden, dtype, seed=seed, x=("t3",), w=("normal", 1.0, 0.1),
+                      g=("normal", 0.0, 1.0), eps=1e-6, outlier_frac=0.01)
+
+
+def cfg_ln_vjp(rows=16384, hidden=8192, dtype="bf16", seed=0):
+    """LayerNorm backward: x ~N(0.5, std 2), w ~N(1,0.1), g ~N(0,1), eps 1e-5."""
+    return row_inputs(rows, hidden, dtype, seed=seed, x=("normal", 0.5, 2.0),
+                      w=("normal", 1.0, 0.1), g=("normal", 0.0, 1.0), eps=1e-5)
