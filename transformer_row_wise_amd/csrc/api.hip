@@ -252,7 +252,7 @@ nrm_status norm_vjp(const char* fn, bool ln, const void* x, const void* w, const
   nrm::VjpArgs a;
   a.x = x; a.w = w; a.g = g; a.dx = dx;
   a.part_w = a.part_b = nullptr;
-  a.rows = rows; a.hidden = hidden; a.rpb = 1; a.eps = eps;
+  a.rows = rows; a.hidden = hidden; a.rpb = 1; a.eps = eps; a.inv_n = 1.0 / (double)hidden;
   a.w_f32 = w_dtype == NRM_F32; a.team = 64;
   auto go = [&](bool al) {
     if (ln)

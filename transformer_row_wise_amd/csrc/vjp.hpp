@@ -41,6 +41,7 @@ struct VjpArgs {
   int64_t rows;
   int64_t hidden;     // < 2^31
   int64_t rpb;        // rows per block
+  double inv_n;       // 1 / hidden
   float eps;
   int w_f32;          // w stored as fp32 (else bf16, only with bf16 activations)
   int team;           // threads per row (fast kernel): a multiple of 64
@@ -55,24 +56,23 @@ struct VjpRow {
   double m2;   // LN: mean(d xh)
 };
 
-__device__ __forceinline__ VjpRow vjp_rms_scalars(double ss, double dot, int64_t D, float eps) {
+__device__ __forceinline__ VjpRow vjp_rms_scalars(double ss, double dot, double inv_n, float eps) {
   VjpRow s;
-  s.r = rstd_f64(ss, D, eps);
-  s.c = s.r * s.r * s.r * dot / (double)D;
+  s.r = 1.0 / __builtin_sqrt(ss * inv_n + (double)eps);
+  s.c = s.r * s.r * s.r * (dot * inv_n);
   s.mu = s.m1 = s.m2 = 0.0;
   return s;
 }
 
 __device__ __forceinline__ VjpRow vjp_ln_scalars(double sx, double sxx, double sd, double sdx,
-                                                 int64_t D, float eps) {
+                                                 double inv_n, float eps) {
   VjpRow s;
-  const double n = (double)D;
-  s.mu = sx / n;
-  const double var = fmax(sxx / n - s.mu * s.mu, 0.0);
+  s.mu = sx * inv_n;
+  const double var = fmax(sxx * inv_n - s.mu * s.mu, 0.0);
   s.r = 1.0 / __builtin_sqrt(var + (double)eps);
   s.c = 0.0;
-  s.m1 = sd / n;
-  s.m2 = s.r * (sdx - s.mu * sd) / n;
+  s.m1 = sd * inv_n;
+  s.m2 = s.r * ((sdx - s.mu * sd) * inv_n);
   return s;
 }
 
@@ -131,6 +131,46 @@ __device__ __forceinline__ void vjp_outputs(const float (&f)[V], const float (&g
   }
 }
 
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+// Sum over the 64 lanes of a wave, every lane ending with a total (the lanes need not agree
+// bit for bit; callers read a fixed lane): rotations by 4 and 8 inside each 16-lane row keep
+// a lane's index mod 4, and so do the xor-16 / xor-32 exchanges across rows.
+__device__ __forceinline__ double lanes_sum_mod4(double v) {
+  v += dpp<DPP_ROW_ROR4>(v);
+  v += dpp<DPP_ROW_ROR8>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Four fp64 row sums over a team of nwt waves, with one barrier. Within a quad of lanes the
+// four sums are transposed (lane l keeps sum l & 3 of the quad), so the rest of the wave
+// reduction handles one value per lane instead of four; each wave's four totals go to LDS
+// (red: 4 slots per wave of the block), and after the barrier lane l of every wave adds up
+// sum l & 3 of team wave l >> 2. The order of every addition is fixed: results are the same
+// on every run, and the same in every thread of the team (they are read from lanes 0..3).
+__device__ __forceinline__ void team_sum4(double (&s)[4], double* red, int wave0, int nwt) {
+  const int lane = threadIdx.x & 63;
+  const bool b = lane & 1, c = lane & 2;
+  double k0 = b ? s[1] : s[0], u0 = b ? s[0] : s[1];
+  double k1 = b ? s[3] : s[2], u1 = b ? s[2] : s[3];
+  k0 += dpp<DPP_QUAD_XOR1>(u0);  // sum b of the lane pair
+  k1 += dpp<DPP_QUAD_XOR1>(u1);  // sum 2 + b
+  double k = c ? k1 : k0;
+  const double u = c ? k0 : k1;
+  k += dpp<DPP_QUAD_XOR2>(u);    // sum lane & 3 of the quad
+  k = lanes_sum_mod4(k);         // ... of the wave
+  if (lane < 4) red[(threadIdx.x >> 6) * 4 + lane] = k;
+  __syncthreads();
+  const int w = lane >> 2;
+  double t = w < nwt ? red[(wave0 + w) * 4 + (lane & 3)] : 0.0;
+  t = lanes_sum_mod4(t);         // sum lane & 3 of the team
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = readlane_f64(t, i);
+}
+
 // Fast kernel: a block of G teams of T = a.team threads (G * T = blockDim.x); a team owns
 // one row at a time, thread t of a team keeping chunks t, t + T, ... (NV of them) of the
 // row in registers. Block b walks rows [b * rpb, min(rows, (b + 1) * rpb)), team i taking
@@ -145,8 +185,7 @@ vjp_rows(VjpArgs a) {
   constexpr bool DW = PG, DB = PG && OP == VJP_LN;
   constexpr bool XF = BF16 && PK != PK_F32;
   constexpr int V = Fmt<BF16>::VEC;
-  constexpr int NS = OP == VJP_RMS ? 2 : 4;  // sums per row
-  __shared__ double red[2][16][NS];          // [iteration parity][wave][sum]
+  __shared__ double red[2][16 * 4];          // [iteration parity][wave * 4 + sum]
   extern __shared__ double comb[];           // (G - 1) * T * V doubles, team combine
   const int T = a.team;
   const int G = blockDim.x / T;
@@ -201,25 +240,10 @@ vjp_rows(VjpArgs a) {
         vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
       }
     }
-    // Team reduction: DPP within each wave, then the team's wave sums from LDS in order.
-    double v[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) v[i] = wave_sum(ds[i]);
-    const int par = it & 1;
-    if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i) red[par][threadIdx.x >> 6][i] = v[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      double t = red[par][wave0][i];
-      for (int q = 1; q < nwt; ++q) t += red[par][wave0 + q][i];
-      v[i] = t;
-    }
+    team_sum4(ds, red[it & 1], wave0, nwt);
     VjpRow s;
-    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(v[0], v[1], a.hidden, a.eps);
-    else s = vjp_ln_scalars(v[0], v[1], v[2], v[3], a.hidden, a.eps);
+    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
+    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
     if (!valid) return;
     char* dr = (char*)a.dx + row * a.hidden * Fmt<BF16>::ESZ;
 #pragma unroll
@@ -295,8 +319,7 @@ template <bool BF16, int OP, int V, bool PG>
 __global__ void __launch_bounds__(256)
 vjp_generic(VjpArgs a) {
   constexpr bool DW = PG, DB = PG && OP == VJP_LN;
-  constexpr int NS = OP == VJP_RMS ? 2 : 4;
-  __shared__ double red[4][NS];
+  __shared__ double red[4 * 4];
   const int64_t nch = a.hidden / V;
   const bool has_w = a.w != nullptr;
   const bool xf = BF16 && !a.w_f32;  // exact fp32 products (see vjp_accumulate)
@@ -321,20 +344,11 @@ vjp_generic(VjpArgs a) {
       if (xf) vjp_accumulate<OP, V, BF16>(f, gf, wv, ds);
       else vjp_accumulate<OP, V, false>(f, gf, wv, ds);
     }
-    double v[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) v[i] = wave_sum(ds[i]);
-    if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i) red[threadIdx.x >> 6][i] = v[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NS; ++i) v[i] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+    team_sum4(ds, red, 0, 4);
     __syncthreads();  // red is rewritten by the next row
     VjpRow s;
-    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(v[0], v[1], a.hidden, a.eps);
-    else s = vjp_ln_scalars(v[0], v[1], v[2], v[3], a.hidden, a.eps);
+    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
+    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
     const bool first = row == row0;
     for (int64_t j = threadIdx.x; j < nch; j += 256) {
       float f[V], gf[V], wv[V], dxv[V];

@@ -5,8 +5,8 @@
 // elements, so hidden <= 8192 for bf16 and fp32):
 //   vjp_rows, a team of T = ceil(n / NV) threads (rounded up to a wave) per row, NV the
 //   smallest chunk count per thread that keeps T <= 1024; G = min(1024 / T, 8) teams per
-//   block. With parameter gradients the grid is vjp_partials(rows) blocks of rpb rows each
-//   (one partial row per block); without, each team takes one row.
+//   block. The grid is vjp_partials(rows) blocks of rpb consecutive rows each (with
+//   parameter gradients, one partial row per block).
 // Otherwise vjp_generic (256 threads, 16-byte chunks or single elements, any width).
 // The partial rows are then added by vjp_colsum.
 #pragma once
@@ -80,18 +80,12 @@ hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool*
   const int team = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
   const bool exact = (int64_t)team * nv == n;
   const int gmax = std::max(1, std::min(8, 1024 / team));
-  int64_t blocks;
-  int G;
-  if (pg) {
-    blocks = vjp_partials(a.rows);
-    a.rpb = (a.rows + blocks - 1) / blocks;
-    G = (int)std::min<int64_t>(gmax, a.rpb);
-  } else {
-    G = (int)std::min<int64_t>(gmax, a.rows);
-    a.rpb = G;
-    blocks = (a.rows + G - 1) / G;
-  }
-  if (blocks > kVjpMaxGrid) return hipSuccess;
+  // The same persistent grid with or without parameter gradients: at [16384, 8192] bf16 it
+  // streams dx-only work faster (RMSNorm ~155 us) than one short-lived block per row
+  // (~211 us), since a block keeps loading its next row while it reduces the current one.
+  const int64_t blocks = vjp_partials(a.rows);
+  a.rpb = (a.rows + blocks - 1) / blocks;
+  const int G = (int)std::min<int64_t>(gmax, a.rpb);
   a.team = team;
   *done = true;
   const int threads = G * team;
