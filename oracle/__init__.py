@@ -16,6 +16,11 @@ What it computes, and where the pages define it:
                          ``LayerNorm`` (affine / ``without_bias`` / ``affine(false)``).
   * ``norm_rope``     -- ``fast::FastOp`` variants ``NormRope`` and ``Rope``; nuvec-nn
                          ``layers.rs``, ``Rope`` (defaults, positions ``offset + l``).
+  * ``rope_positions`` -- the positions-tensor form of RoPE on [T, H, D] rows (MinivLLM API
+                         reference, "Layers", ``RotaryEmbedding.forward``).
+  * ``rope_scaling``  -- frequency scalings named by nuvec-nn ``layers.rs``, ``Rope``
+                         (Llama 3 NTK-by-parts, YaRN, LongRoPE "su"), each after its
+                         published method.
   * ``rms_norm_vjp``, ``layer_norm_vjp`` -- ``fast::FastOp`` variants ``RmsNormVjp`` and
                          ``LayerNormVjp``: the gradients of ``RmsNorm`` (for x, w) and of
                          ``LayerNorm`` (for x, w, b) given the output cotangent g.
@@ -31,12 +36,13 @@ invariants, library routines, brute force at 50 digits and hand-worked fixtures 
 
 from .rounding import round_bf16, round_f32, round_to, bf16_bits, f32_param
 from .norms import rms_norm, add_rms_norm, layer_norm
-from .rope import rope_frequencies, rope_angles, norm_rope
+from .rope import rope_frequencies, rope_angles, norm_rope, rope_positions
+from . import rope_scaling
 from .vjp import rms_norm_vjp, layer_norm_vjp
 
 __all__ = [
     "round_bf16", "round_f32", "round_to", "bf16_bits", "f32_param",
     "rms_norm", "add_rms_norm", "layer_norm",
-    "rope_frequencies", "rope_angles", "norm_rope",
+    "rope_frequencies", "rope_angles", "norm_rope", "rope_positions", "rope_scaling",
     "rms_norm_vjp", "layer_norm_vjp",
 ]

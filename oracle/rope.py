@@ -14,6 +14,17 @@ section 3.2): pair i of the rotated features has frequency theta_i = base^(-2i/d
 angle a = scale * position * theta_i, and the pair (u, v) turns counter-clockwise,
 (u, v) -> (u cos a - v sin a, u sin a + v cos a); the inverse uses -a. The RMS statistic
 spans all D features; features at index >= dims are normalised but not rotated.
+
+``freqs`` (the optional input of ``Rope`` and ``NormRope``, which the pages say replaces
+``base``): read in the convention of the fast rope the pages name (MLX's ``fast::rope``),
+freqs[i] is the period divisor of pair i, theta_i = 1 / freqs[i]; with the defaults
+freqs[i] = base^(2i/dims). ``mscale`` multiplies the rotated features (the attention factor
+of the scaled variants: mlx-lm's YarnRoPE and SuScaledRoPE scale x[..., :dims] before the
+rotation); 1 for plain RoPE.
+
+``rope_positions`` is the positions-tensor form of the MinivLLM API reference
+(``RotaryEmbedding.forward(positions, query, key)``): rows of [T, H, D] arrays, token t at
+position positions[t], the same rotation for every head of the token.
 """
 
 import numpy as np
@@ -21,16 +32,36 @@ import numpy as np
 from .rounding import f32_param, round_to
 
 
-def rope_frequencies(dims, base):
-    """theta_i = base^(-2 i / dims) for i = 0 .. dims/2 - 1, in float64."""
+def rope_frequencies(dims, base, freqs=None):
+    """theta_i for i = 0 .. dims/2 - 1 in float64: base^(-2 i / dims), or 1 / freqs[i]."""
+    if freqs is not None:
+        f = np.asarray(freqs, dtype=np.float64)
+        assert f.shape == (dims // 2,), f.shape
+        return 1.0 / f
     i = np.arange(dims // 2, dtype=np.float64)
     return np.power(f32_param(base), (-2.0 * i) / dims)
 
 
-def rope_angles(positions, dims, base, scale):
+def rope_angles(positions, dims, base, scale, freqs=None):
     """Angles [len(positions), dims/2]: scale * position * theta_i."""
     p = np.asarray(positions, dtype=np.float64)
-    return (f32_param(scale) * p)[:, None] * rope_frequencies(dims, base)[None, :]
+    return (f32_param(scale) * p)[:, None] * rope_frequencies(dims, base, freqs)[None, :]
+
+
+def _rotate(xn, a, dims, traditional, forward, mscale):
+    """Rotate the first dims features of rows xn [..., P, D] by angles a [P, dims/2]."""
+    c = np.cos(a)
+    s = np.sin(a)
+    if not forward:
+        s = -s
+    iu, iv = _pair_index(dims, traditional)
+    u = xn[..., iu]
+    v = xn[..., iv]
+    y = xn.copy()
+    m = f32_param(mscale)
+    y[..., iu] = m * (u * c - v * s)
+    y[..., iv] = m * (u * s + v * c)
+    return y
 
 
 def _pair_index(dims, traditional):
@@ -43,7 +74,7 @@ def _pair_index(dims, traditional):
 
 
 def norm_rope(x, w, *, normalize, eps, dims, traditional, base, scale, offset, forward,
-              dtype, cache=None):
+              dtype, cache=None, freqs=None, mscale=1.0):
     """x: [B, H, L, D] float64 values. Returns the rotated [B, H, L, D] array rounded to
     ``dtype``; with ``cache`` ([B, H, Lc, D] values) returns a copy of the cache with rows
     offset .. offset + L - 1 of every (b, h) replaced by the result and the rest untouched.
@@ -58,21 +89,21 @@ def norm_rope(x, w, *, normalize, eps, dims, traditional, base, scale, offset, f
     else:
         xn = x.copy()
 
-    a = rope_angles(offset + np.arange(L), dims, base, scale)  # [L, dims/2]
-    c = np.cos(a)
-    s = np.sin(a)
-    if not forward:
-        s = -s
-    iu, iv = _pair_index(dims, traditional)
-    u = xn[..., iu]
-    v = xn[..., iv]
-    y = xn.copy()
-    y[..., iu] = u * c - v * s
-    y[..., iv] = u * s + v * c
-    y = round_to(y, dtype)
+    a = rope_angles(offset + np.arange(L), dims, base, scale, freqs)  # [L, dims/2]
+    y = round_to(_rotate(xn, a, dims, traditional, forward, mscale), dtype)
 
     if cache is None:
         return y
     out = np.array(cache, dtype=np.float64, copy=True)
     out[:, :, offset:offset + L, :] = y
     return out
+
+
+def rope_positions(x, positions, *, dims, traditional, base, scale, forward, dtype,
+                   freqs=None, mscale=1.0):
+    """x: [T, H, D] float64 values, positions: [T] integers. Every head of token t turns at
+    position positions[t]; returns [T, H, D] rounded to ``dtype``."""
+    x = np.asarray(x, dtype=np.float64)
+    a = rope_angles(np.asarray(positions), dims, base, scale, freqs)  # [T, dims/2]
+    y = _rotate(x, a[:, None, :], dims, traditional, forward, mscale)
+    return round_to(y, dtype)

@@ -89,22 +89,28 @@ def layer_row(x, w, b, eps):
     return out
 
 
-def rope_row(x, w, *, normalize, eps, dims, traditional, base, scale, pos, forward):
-    """One [D] row rotated at integer position ``pos``."""
+def rope_row(x, w, *, normalize, eps, dims, traditional, base, scale, pos, forward,
+             freqs=None, mscale=1.0):
+    """One [D] row rotated at integer position ``pos`` (pair i at frequency 1 / freqs[i]
+    when freqs is given; rotated features times mscale)."""
     d = len(x)
     xs = rms_row(x, w, eps) if normalize else [mpmath.mpf(v) for v in x]
     out = list(xs)
     half = dims // 2
+    m = mpmath.mpf(f32(mscale))
     for i in range(half):
-        theta = mpmath.power(mpmath.mpf(f32(base)), mpmath.mpf(-2 * i) / dims)
+        if freqs is None:
+            theta = mpmath.power(mpmath.mpf(f32(base)), mpmath.mpf(-2 * i) / dims)
+        else:
+            theta = 1 / mpmath.mpf(freqs[i])
         a = mpmath.mpf(f32(scale)) * pos * theta
         c, s = mpmath.cos(a), mpmath.sin(a)
         if not forward:
             s = -s
         iu, iv = (2 * i, 2 * i + 1) if traditional else (i, i + half)
         u, v = xs[iu], xs[iv]
-        out[iu] = u * c - v * s
-        out[iv] = u * s + v * c
+        out[iu] = m * (u * c - v * s)
+        out[iv] = m * (u * s + v * c)
     assert len(out) == d
     return out
 

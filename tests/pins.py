@@ -19,6 +19,12 @@ What pins what:
                      per-pair norm preservation, inverse undoes forward, half/interleaved
                      permutation, relative-position property, cache placement, RMS over
                      all D, 50-digit brute force.
+  * Rope freqs /  -- 50-digit brute force with freqs and mscale, freqs = base^(2i/dims)
+    positions        reproduces the base form, mscale is a plain factor, the positions form
+                     equals the offset form row by row;
+  * scaled freqs  -- band properties of each published method (pairs kept, pairs scaled by
+                     the factor, the blend in between and its continuity at the band edges,
+                     ramp ends, closed-form attention factors), identity at factor 1;
   * RmsNormVjp /  -- hand-worked fixtures, 50-digit numerical differentiation of the
     LayerNormVjp     forward (brute force), torch autograd of ``rms_norm`` / ``layer_norm``
                      in float64, and the invariances every gradient of these maps obeys
@@ -344,9 +350,12 @@ def pin_rope_golden(o):
     g = _golden("rope_hand.json")
     for c in g["cases"]:
         x = _vals(c["x"]).reshape(1, 1, 1, -1)
+        extra = {}
+        if "freqs" in c:
+            extra = dict(freqs=_vals(c["freqs"]), mscale=c["mscale"])
         got = _rope(o, x, None, normalize=c["normalize"], eps=c.get("eps", 0.0), dims=c["dims"],
                     traditional=c["traditional"], base=c["base"], scale=c["scale"],
-                    offset=c["offset"], forward=c["forward"])[0, 0, 0]
+                    offset=c["offset"], forward=c["forward"], **extra)[0, 0, 0]
         if "expect" in c:
             _close(got, _vals(c["expect"]), 1e-15, 1e-300, c["why"])
         else:
@@ -474,6 +483,141 @@ def pin_rope_brute(o):
                             want = [brute.round_mp(v, dt) for v in
                                     brute.rope_row(x[0, 0, l], w, pos=700 + l, **kw)]
                             _same_values(got[0, 0, l], want, f"{dt} {kw} l={l}")
+
+
+# ------------------------------------------------------------- Rope freqs / positions
+
+def pin_rope_freqs_brute(o):
+    """Rotation with a freqs vector and an mscale against the 50-digit evaluation."""
+    rng = _rng(31)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        for trad in (False, True):
+            x = cast(rng.standard_normal((1, 1, 2, 8)))
+            freqs = _f32_values(rng.uniform(0.5, 300.0, 2))
+            got = o.norm_rope(x, None, normalize=False, eps=1e-6, dims=4, traditional=trad,
+                              base=10000.0, scale=0.5, offset=37, forward=True, dtype=dt,
+                              freqs=freqs, mscale=1.25)
+            for l in range(2):
+                want = brute.rope_row(x[0, 0, l], None, normalize=False, eps=1e-6, dims=4,
+                                      traditional=trad, base=10000.0, scale=0.5, pos=37 + l,
+                                      forward=True, freqs=freqs.tolist(), mscale=1.25)
+                _same_values(got[0, 0, l], [brute.round_mp(v, dt) for v in want], f"{dt} {l}")
+
+
+def pin_rope_freqs_reproduce_base(o):
+    """freqs[i] = base^(2i/dims) (rounded to f32) gives the base form, to the angle change
+    that rounding makes (relative 2^-24 of an angle of at most 40 rad here)."""
+    rng = _rng(32)
+    x = rng.standard_normal((2, 3, 40, 16))
+    f = np.power(10000.0, 2.0 * np.arange(6) / 12).astype(np.float32).astype(np.float64)
+    kw = dict(normalize=False, eps=1e-6, dims=12, base=10000.0, scale=1.0, offset=0,
+              forward=True, dtype="f64")
+    for trad in (False, True):
+        a = o.norm_rope(x, None, traditional=trad, **kw)
+        b = o.norm_rope(x, None, traditional=trad, freqs=f, **kw)
+        _close(b, a, 0, 40 * 2.0 ** -23 * np.max(np.abs(x)) * 2, "freqs vs base")
+
+
+def pin_rope_mscale_is_a_factor(o):
+    rng = _rng(33)
+    x = rng.standard_normal((1, 2, 5, 10))
+    kw = dict(normalize=False, eps=1e-6, dims=6, traditional=False, base=500.0, scale=1.0,
+              offset=3, forward=True, dtype="f64")
+    a = o.norm_rope(x, None, **kw)
+    b = o.norm_rope(x, None, mscale=2.0, **kw)
+    _same_values(b[..., :6], 2.0 * a[..., :6], "rotated features doubled")
+    _same_values(b[..., 6:], a[..., 6:], "pass-through features unchanged")
+
+
+def pin_rope_positions_form(o):
+    """[T, H, D] rows with positions p[t] equal the [B, H, L, D] form at offset p[t] (one
+    row each), head by head."""
+    rng = _rng(34)
+    T, H, D = 5, 3, 8
+    x = _bf16_values(rng.standard_normal((T, H, D)))
+    pos = np.array([7, 0, 3000, 7, 42])
+    f = _f32_values(rng.uniform(1.0, 50.0, 3))
+    for trad in (False, True):
+        for freqs in (None, f):
+            got = o.rope_positions(x, pos, dims=6, traditional=trad, base=100.0, scale=0.75,
+                                   forward=False, dtype="bf16", freqs=freqs, mscale=1.5)
+            for t in range(T):
+                want = o.norm_rope(x[t][None, :, None, :], None, normalize=False, eps=1e-6,
+                                   dims=6, traditional=trad, base=100.0, scale=0.75,
+                                   offset=int(pos[t]), forward=False, dtype="bf16",
+                                   freqs=freqs, mscale=1.5)
+                _same_values(got[t], want[0, :, 0, :], f"token {t}")
+
+
+# ------------------------------------------------------------------ scaled frequencies
+
+def pin_llama3_bands(o):
+    """Pairs with wavelength 2 pi f below original_max / high_freq_factor keep f, above
+    original_max / low_freq_factor get factor * f, in between lie strictly between and grow
+    with the wavelength; factor 1 changes nothing."""
+    S = o.rope_scaling
+    for dims, base, orig in ((128, 500000.0, 8192), (64, 10000.0, 2048), (8, 65536.0, 4096)):
+        f = _f32_values(np.power(np.float64(np.float32(base)), 2.0 * np.arange(dims // 2) / dims))
+        fexact = np.power(np.float64(np.float32(base)), 2.0 * np.arange(dims // 2) / dims)
+        got, ms = S.llama3_freqs(dims, base, factor=32.0, low_freq_factor=1.0,
+                                 high_freq_factor=4.0, original_max=orig)
+        assert ms == 1.0
+        wl = 2 * np.pi * fexact
+        lo, hi = wl < orig / 4.0, wl > orig / 1.0
+        _same_values(got[lo], f[lo], "high-frequency pairs kept")
+        _same_values(got[hi], _f32_values(32.0 * fexact[hi]), "low-frequency pairs scaled")
+        mid = ~lo & ~hi
+        if mid.any():
+            assert np.all(got[mid] > f[mid]) and np.all(got[mid] < 32.0 * f[mid])
+            ratio = got[mid] / fexact[mid]
+            assert np.all(np.diff(ratio) > 0), "blend must grow with the wavelength"
+        same, _ = S.llama3_freqs(dims, base, factor=1.0, original_max=orig)
+        _close(same, fexact, 2.0 ** -23, 0, "factor 1")
+
+
+def pin_llama3_blend_is_continuous(o):
+    """At the band edges the blend meets the two outer rules: a pair just inside the high
+    edge keeps ~f, one just inside the low edge gets ~factor * f."""
+    S = o.rope_scaling
+    for target, want_ratio in ((8192 / 4.0 * (1 + 1e-9), 1.0), (8192 / 1.0 * (1 - 1e-9), 8.0)):
+        # with dims = 4, pair 1 has f = base^(1/2): pick base so that 2 pi f = target
+        base = (target / (2 * np.pi)) ** 2
+        got, _ = S.llama3_freqs(4, base, factor=8.0, original_max=8192)
+        fexact = np.sqrt(np.float64(np.float32(base)))
+        _close(got[1] / fexact, want_ratio, 1e-5, 0, f"edge {target}")
+
+
+def pin_yarn_ramp(o):
+    """Pairs below floor(d(beta_fast)) keep f, pairs from ceil(d(beta_slow)) on get
+    factor * f, with d(r) the pair index whose wavelength fits r turns in original_max;
+    factor 1 changes nothing; the attention factor is 0.1 ln(factor) + 1 by default."""
+    S = o.rope_scaling
+    dims, base, orig = 64, 10000.0, 4096
+    fexact = np.power(10000.0, 2.0 * np.arange(dims // 2) / dims)
+    d = lambda r: dims * np.log(orig / (r * 2 * np.pi)) / (2 * np.log(base))
+    lo, hi = int(np.floor(d(32.0))), int(np.ceil(d(1.0)))
+    got, ms = S.yarn_freqs(dims, base, factor=8.0, original_max=orig)
+    _close(got[:lo + 1], fexact[:lo + 1], 2.0 ** -23, 0, "extrapolated pairs")
+    _close(got[hi:], 8.0 * fexact[hi:], 2.0 ** -23, 0, "interpolated pairs")
+    assert np.all(got[lo + 1:hi] > fexact[lo + 1:hi]) and np.all(got[lo + 1:hi] < 8 * fexact[lo + 1:hi])
+    _close(ms, 0.1 * np.log(8.0) + 1.0, 1e-15, 0, "attention factor")
+    one, ms1 = S.yarn_freqs(dims, base, factor=1.0, original_max=orig)
+    _close(one, fexact, 2.0 ** -23, 0, "factor 1")
+    assert ms1 == 1.0
+    _, ms2 = S.yarn_freqs(dims, base, factor=np.e ** 5, mscale=1.0, mscale_all_dim=1.0)
+    assert ms2 == 1.0, "equal mscale and mscale_all_dim cancel"
+
+
+def pin_su_scaling(o):
+    S = o.rope_scaling
+    dims, base = 16, 10000.0
+    lf = np.linspace(1.0, 40.0, 8)
+    fexact = np.power(10000.0, 2.0 * np.arange(8) / 16)
+    got, ms = S.su_freqs(dims, base, lf, max_position=4096 ** 2, original_max=4096)
+    _close(got / fexact, lf, 2.0 ** -23, 0, "per-pair factors")
+    _close(ms, np.sqrt(2.0), 1e-15, 0, "max = original^2 gives sqrt 2")
+    _, ms1 = S.su_freqs(dims, base, np.ones(8), max_position=4096, original_max=4096)
+    assert ms1 == 1.0
 
 
 # --------------------------------------------------------------------- RmsNormVjp / LN

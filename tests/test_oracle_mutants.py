@@ -47,8 +47,9 @@ MUTANTS = [
     ("rounding.py", "_BF16_MIN_QUANTUM_EXP = -133", "_BF16_MIN_QUANTUM_EXP = -126",
      "bf16 subnormals flushed"),
     ("rounding.py", "_BF16_SIG_BITS = 8", "_BF16_SIG_BITS = 7", "bf16 keeps one bit too few"),
-    ("rope.py", "y[..., iu] = u * c - v * s\n    y[..., iv] = u * s + v * c",
-     "y[..., iu] = u * c + v * s\n    y[..., iv] = -u * s + v * c", "rotation turns clockwise"),
+    ("rope.py", "y[..., iu] = m * (u * c - v * s)\n    y[..., iv] = m * (u * s + v * c)",
+     "y[..., iu] = m * (u * c + v * s)\n    y[..., iv] = m * (-u * s + v * c)",
+     "rotation turns clockwise"),
     ("rope.py", "    if traditional:\n        return 2 * i, 2 * i + 1",
      "    if not traditional:\n        return 2 * i, 2 * i + 1", "pair modes swapped"),
     ("rope.py", "return i, i + half", "return i, i + half - 1", "half-mode partner off by one"),
@@ -70,6 +71,30 @@ MUTANTS = [
      "cache written from row 0"),
     ("rope.py", "xn = x / np.sqrt(mean_sq + f32_param(eps))", "xn = x / np.sqrt(mean_sq)",
      "NormRope drops eps"),
+    ("rope.py", "return 1.0 / f", "return f", "freqs taken as frequencies, not divisors"),
+    ("rope.py", "m = f32_param(mscale)", "m = 1.0", "mscale ignored"),
+    ("rope.py", "y[..., iv] = m * (u * s + v * c)", "y[..., iv] = u * s + v * c",
+     "mscale on one half of each pair only"),
+    ("rope.py", "a = rope_angles(np.asarray(positions), dims, base, scale, freqs)",
+     "a = rope_angles(np.arange(len(positions)), dims, base, scale, freqs)",
+     "positions tensor ignored"),
+    ("rope_scaling.py", "out[wavelen > low_wavelen] = f[wavelen > low_wavelen] * factor",
+     "out[wavelen > low_wavelen] = f[wavelen > low_wavelen] / factor",
+     "Llama 3 low-frequency pairs divided by the factor"),
+    ("rope_scaling.py", "high_wavelen = original_max / high_freq_factor",
+     "high_wavelen = original_max / low_freq_factor / 2", "Llama 3 high edge misplaced"),
+    ("rope_scaling.py", "out[mid] = f[mid] / ((1.0 - s) / factor + s)",
+     "out[mid] = f[mid] / (s / factor + (1.0 - s))", "Llama 3 blend weights swapped"),
+    ("rope_scaling.py", "keep = 1.0 - ramp", "keep = ramp", "YaRN ramp reversed"),
+    ("rope_scaling.py", "low = max(math.floor(corr_dim(beta_fast)), 0)",
+     "low = max(math.floor(corr_dim(beta_slow)), 0)", "YaRN ramp start from beta_slow"),
+    ("rope_scaling.py", "return 1.0 if s <= 1 else 0.1 * m * math.log(s) + 1.0",
+     "return 1.0 if s <= 1 else 0.1 * m * math.log10(s) + 1.0", "YaRN attention factor log10"),
+    ("rope_scaling.py", "ms = math.sqrt(1.0 + math.log(max_position / original_max) / math.log(original_max))",
+     "ms = 1.0 + math.log(max_position / original_max) / math.log(original_max)",
+     "su attention factor without the root"),
+    ("rope_scaling.py", "out = round_to(lf * _base_periods(dims, base), \"f32\")",
+     "out = round_to(lf / _base_periods(dims, base), \"f32\")", "su factors divide"),
     ("vjp.py", "x2 * (r ** 3) * dot / d", "x2 * (r ** 2) * dot / d", "RmsNormVjp r^2 for r^3"),
     ("vjp.py", "dx = r * g2 * wv - x2 * (r ** 3) * dot / d", "dx = r * g2 * wv",
      "RmsNormVjp drops the term through the statistic"),
