@@ -340,7 +340,32 @@ def suite(args):
         emit(cfg, "layer_norm_vjp" if ln else "rms_norm_vjp", [rows, hidden, str(inp.x.dtype)],
              nbytes, rows, per)
 
-    groups = set(args.only.split(",")) if args.only else {"fwd", "vjp"}
+    groups = set(args.only.split(",")) if args.only else {"fwd", "vjp", "rope"}
+    if "rope" in groups:
+        inp = workloads.cfg_rope_qk_bf16()
+        T, Hq, Hk, D = workloads.ROPE_QK_SHAPE
+        freqs, ms = nrm.rope_freqs_llama3(D, workloads.ROPE_QK_BASE)
+        nbytes = 2 * T * (Hq + Hk) * D * 2 + T * 8 + D // 2 * 4
+        k = n_sets(nbytes)
+        qs = [inp.q.cuda() for _ in range(k)]
+        ks = [inp.k.cuda() for _ in range(k)]
+        pos, fr = inp.positions.cuda(), freqs.cuda()
+        outs = [(torch.empty_like(qs[0]), torch.empty_like(ks[0])) for _ in range(k)]
+        per = time_graph(lambda i: nrm.rope_positions(pos, qs[i % k], ks[i % k],
+                                                      base=workloads.ROPE_QK_BASE, freqs=fr,
+                                                      mscale=ms, q_out=outs[i % k][0],
+                                                      k_out=outs[i % k][1]), calls(nbytes))
+        emit("8a", "rope_positions_llama3", [T, Hq, Hk, D], nbytes, T * (Hq + Hk), per)
+        del qs, ks, outs
+        rp = workloads.cfg_norm_rope_bf16()
+        B, H, L, D = rp.x.shape
+        nbytes = 2 * B * H * L * D * 2
+        k = n_sets(nbytes)
+        xs = [rp.x.cuda() for _ in range(k)]
+        dsts = [torch.empty_like(xs[0]) for _ in range(k)]
+        per = time_graph(lambda i: nrm.rope(xs[i % k], out=dsts[i % k]), calls(nbytes))
+        emit("8b", "rope", [B, H, L, D], nbytes, B * H * L, per)
+        del xs, dsts
     if "vjp" in groups:
         for ln, tag in ((False, "6"), (True, "7")):
             f32 = workloads.cfg_ln_vjp(dtype="f32") if ln else workloads.cfg_rms_vjp(dtype="f32")
@@ -551,8 +576,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--only", metavar="GROUPS",
-                    help="with --suite: comma-separated groups among fwd, vjp (skips the "
-                         "headline line)")
+                    help="with --suite: comma-separated groups among fwd, vjp, rope (skips "
+                         "the headline line)")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))

@@ -6,6 +6,8 @@
  *   nrm_add_rms_norm    residual add + RMSNorm      h = x + r;  out = RMSNorm(h);  returns both
  *   nrm_layer_norm      LayerNorm                   (x - mean) / sqrt(var + eps) * w + b
  *   nrm_norm_rope       RMSNorm + rotary embedding  per [b, h, l] row, position offset + l
+ *   nrm_rope            rotary embedding            per [n, l] row, position offset + l
+ *   nrm_rope_positions  rotary embedding of query and key rows at per-token positions
  *   nrm_rms_norm_vjp    RMSNorm backward            dx, dw from the output cotangent g
  *   nrm_layer_norm_vjp  LayerNorm backward          dx, dw, db from the output cotangent g
  * The forward operations are one HIP kernel launch each; the backward ones add a second,
@@ -119,9 +121,11 @@ nrm_status nrm_layer_norm(const void* x, const void* w, const void* b, void* out
  * normalisation; result returned as a new [B, H, L, D] array or written into a cache at the
  * rows' positions) and Rope (dims even; traditional rotates neighbouring pairs (2i, 2i+1),
  * otherwise the halves (i, i + dims/2); base and scale are f32, scale multiplies the
- * position; forward = 0 is the inverse rotation). nuvec-nn 0.4.0 layers.rs, Rope: defaults
- * half pairs, base 10000, scale 1; frequencies are computed, never loaded.
- * Formula (textbook RoPE, RoFormer section 3.2): theta_i = base^(-2i/dims), angle
+ * position; forward = 0 is the inverse rotation; an optional freqs vector replaces base).
+ * nuvec-nn 0.4.0 layers.rs, Rope: defaults half pairs, base 10000, scale 1.
+ * Formula (textbook RoPE, RoFormer section 3.2): theta_i = base^(-2i/dims), or
+ * theta_i = 1 / freqs[i] with freqs (freqs[i] divides the position, the convention of the
+ * fast rope the pages name; the defaults correspond to freqs[i] = base^(2i/dims)), angle
  * a = scale * (offset + l) * theta_i, (u, v) -> (u cos a - v sin a, u sin a + v cos a);
  * the inverse uses -a. Angles and sin/cos are computed in the kernel in fp64; features at
  * index >= dims are normalised but not rotated.
@@ -135,6 +139,7 @@ nrm_status nrm_layer_norm(const void* x, const void* w, const void* b, void* out
  *   normalize  0: rotation only (eps and w unused);  eps: added to the mean square
  *   dims       even, 0 <= dims <= D (0: normalisation only)
  *   traditional, base, scale, offset (>= 0), forward (0 = inverse) as above
+ *   freqs      [dims / 2] fp32 device array, or NULL (use base); must not overlap the output
  *   cache_len  used only with cache != 0; needs offset + L <= cache_len
  * Errors: NULL x/out_or_cache -> NRM_ERR_NULL; negative B/H/L/offset, D < 1, odd dims,
  * dims > D, offset + L > cache_len -> NRM_ERR_SHAPE; dtypes -> NRM_ERR_DTYPE; overlaps ->
@@ -143,8 +148,81 @@ nrm_status nrm_layer_norm(const void* x, const void* w, const void* b, void* out
 nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64_t B, int64_t H,
                          int64_t L, int64_t D, int normalize, float eps, int64_t dims,
                          int traditional, float base, float scale, int64_t offset, int forward,
-                         int cache, int64_t cache_len, nrm_dtype dtype, nrm_dtype w_dtype,
-                         hipStream_t stream);
+                         const float* freqs, int cache, int64_t cache_len, nrm_dtype dtype,
+                         nrm_dtype w_dtype, hipStream_t stream);
+
+/*
+ * Rope: rotary position embedding of the first dims features of each row of x [N, L, D]
+ * (N = the product of the leading axes), row l at position offset + l.
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant Rope, inputs (x, offset[, freqs]), fields
+ * dims, traditional, base, scale, forward; nuvec-nn 0.4.0 layers.rs, Rope (x as
+ * [..., sequence, features], positions offset, offset + 1, ...; optionally scaled
+ * frequencies, see nrm_rope_freqs_*). The rotation is NormRope's without the
+ * normalisation; mscale multiplies the rotated features (the attention factor of YaRN and
+ * LongRoPE scaling; 1 for plain RoPE). Features at index >= dims are copied.
+ *
+ *   x          [N, L, D] dtype, input;  out [N, L, D] dtype, may be exactly x
+ *   freqs      [dims / 2] fp32 device array, or NULL (use base)
+ * Errors: as nrm_norm_rope.
+ */
+nrm_status nrm_rope(const void* x, void* out, int64_t N, int64_t L, int64_t D, int64_t dims,
+                    int traditional, float base, float scale, int64_t offset, int forward,
+                    const float* freqs, float mscale, nrm_dtype dtype, hipStream_t stream);
+
+/*
+ * Rope on query and key rows at per-token positions, both tensors in one launch.
+ * Source: MinivLLM API reference, "Layers", RotaryEmbedding: forward(positions, query, key)
+ * rotates query [total_tokens, num_heads, head_dim] and key [total_tokens, num_kv_heads,
+ * head_dim] for the 1-D integer positions of the tokens (batched [B, seq, heads, head_dim]
+ * inputs are the same rows with T = B * seq and positions repeated per sequence), optionally
+ * with Llama 3 frequency scaling (pass its freqs from nrm_rope_freqs_llama3). Every head of
+ * token t turns at position positions[t]; otherwise as nrm_rope.
+ *
+ *   q          [T, Hq, D] dtype;  q_out [T, Hq, D], may be exactly q
+ *   k          [T, Hk, D] dtype, or NULL when Hk == 0;  k_out likewise, may be exactly k
+ *   positions  [T] int32 (pos_int64 == 0) or int64 (pos_int64 != 0) device array
+ *   freqs      [dims / 2] fp32 device array, or NULL (use base)
+ * Errors: as nrm_rope; NULL positions with T > 0 -> NRM_ERR_NULL.
+ */
+nrm_status nrm_rope_positions(const void* q, const void* k, void* q_out, void* k_out,
+                              const void* positions, int pos_int64, int64_t T, int64_t Hq,
+                              int64_t Hk, int64_t D, int64_t dims, int traditional, float base,
+                              float scale, int forward, const float* freqs, float mscale,
+                              nrm_dtype dtype, hipStream_t stream);
+
+/*
+ * Frequency scalings for long contexts: fill freqs_out (HOST memory, dims / 2 floats) with
+ * the per-pair divisors to pass as `freqs`, and *mscale_out (when not NULL) with the factor
+ * on the rotated features. All arithmetic is fp64, each divisor rounded once to fp32.
+ * Source: nuvec-nn 0.4.0 layers.rs, Rope (Rope::scaled: mlx-lm's Llama3RoPE, YarnRoPE,
+ * SuScaledRoPE, ProportionalRoPE; frequencies computed from the settings); the MinivLLM API
+ * reference, RotaryEmbedding (Llama 3 settings and defaults). The formulas are those of the
+ * published methods (the pages print none); ProportionalRoPE is not provided.
+ * With f_i = base^(2i/dims):
+ *   llama3  Meta's Llama 3.1 scaling: wavelength 2 pi f_i below original_max /
+ *           high_freq_factor keeps f_i; above original_max / low_freq_factor gives
+ *           factor * f_i; between, with s = (original_max / wavelength - low_freq_factor) /
+ *           (high_freq_factor - low_freq_factor), f_i / ((1 - s) / factor + s). mscale 1.
+ *   yarn    YaRN (Peng et al. 2023): a linear ramp over pair indices from
+ *           floor(d(beta_fast)) to ceil(d(beta_slow)) (clamped to [0, dims - 1]),
+ *           d(r) = dims ln(original_max / (2 pi r)) / (2 ln base), blends 1/f_i (below the
+ *           ramp) into 1/(factor f_i) (above it); mscale = g(factor, mscale) /
+ *           g(factor, mscale_all_dim), g(s, m) = 0.1 m ln s + 1 (1 for s <= 1).
+ *   su      LongRoPE (Phi-3 "su" scaling): long_factor[i] * f_i (long_factor in HOST
+ *           memory); mscale = sqrt(1 + ln(max_position / original_max) / ln(original_max)).
+ * Errors: NULL outputs (or long_factor) -> NRM_ERR_NULL; dims < 2 or odd, base <= 1,
+ * factor <= 0, a non-positive length or a low_freq_factor >= high_freq_factor ->
+ * NRM_ERR_SHAPE. Host-only: no HIP call.
+ */
+nrm_status nrm_rope_freqs_llama3(int64_t dims, float base, float factor, float low_freq_factor,
+                                 float high_freq_factor, int64_t original_max,
+                                 float* freqs_out, float* mscale_out);
+nrm_status nrm_rope_freqs_yarn(int64_t dims, float base, float factor, int64_t original_max,
+                               float beta_fast, float beta_slow, float mscale,
+                               float mscale_all_dim, float* freqs_out, float* mscale_out);
+nrm_status nrm_rope_freqs_su(int64_t dims, float base, const float* long_factor,
+                             int64_t max_position, int64_t original_max, float* freqs_out,
+                             float* mscale_out);
 
 /* The message of the last failed nrm_* call on this thread ("" if none): "<function>: <what>
  * <reason>, got <value>". Valid until the next nrm_* call on the same thread. */

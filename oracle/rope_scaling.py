@@ -12,7 +12,9 @@ definition in the pages or in a publication this module can follow, so it is abs
 Every strategy returns ``(freqs, mscale)``: freqs[i] (float32 values, as float64) is the
 divisor of the position for rotated pair i (theta_i = 1 / freqs[i], the convention of the
 ``freqs`` input of ``Rope``), and mscale multiplies the rotated features (1 when the method
-has none). All arithmetic is float64; freqs are rounded once to float32.
+has none). Every real-valued setting enters as its float32 value (the interface takes
+them as f32, like eps, base and scale); all arithmetic is float64; freqs are rounded once
+to float32.
 """
 
 import math
@@ -41,6 +43,8 @@ def llama3_freqs(dims, base, factor=32.0, low_freq_factor=1.0, high_freq_factor=
     low_freq_factor get f * factor; in between, with s = (original_max / wavelength -
     low_freq_factor) / (high_freq_factor - low_freq_factor), the inverse frequencies are
     blended, 1/f' = (1 - s) / (factor f) + s / f."""
+    factor, low_freq_factor, high_freq_factor = (f32_param(v) for v in
+                                                 (factor, low_freq_factor, high_freq_factor))
     f = _base_periods(dims, base)
     wavelen = 2.0 * math.pi * f
     low_wavelen = original_max / low_freq_factor
@@ -64,6 +68,8 @@ def yarn_freqs(dims, base, factor=4.0, original_max=4096, beta_fast=32.0, beta_s
     (extrapolation), above it they get factor * f (interpolation), and on it the inverse
     frequencies blend linearly. mscale = g(factor, mscale) / g(factor, mscale_all_dim),
     g(s, m) = 0.1 m ln s + 1 (1 when s <= 1)."""
+    factor, beta_fast, beta_slow, mscale, mscale_all_dim = (
+        f32_param(v) for v in (factor, beta_fast, beta_slow, mscale, mscale_all_dim))
     f = _base_periods(dims, base)
 
     def corr_dim(rotations):
@@ -88,7 +94,7 @@ def su_freqs(dims, base, long_factor, max_position=131072, original_max=4096):
     mlx-lm's SuScaledRoPE): per-pair rescale factors multiply the divisors,
     freqs[i] = long_factor[i] * base^(2i/dims), and the rotated features are scaled by
     sqrt(1 + ln(max_position / original_max) / ln(original_max))."""
-    lf = np.asarray(long_factor, dtype=np.float64)
+    lf = np.asarray(long_factor, dtype=np.float32).astype(np.float64)
     assert lf.shape == (dims // 2,)
     out = round_to(lf * _base_periods(dims, base), "f32")
     ms = math.sqrt(1.0 + math.log(max_position / original_max) / math.log(original_max))

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -70,9 +71,9 @@ def ln(L, x=P, w=None, b=None, out=P + 64 * MB, rows=4, hidden=8, dt=BF16, wdt=B
 
 
 def rope(L, x=P, w=None, out=P + 64 * MB, B=2, H=2, L_=4, D=16, normalize=1, dims=16, offset=0,
-         cache=0, cache_len=0, dt=BF16, wdt=BF16):
+         cache=0, cache_len=0, dt=BF16, wdt=BF16, freqs=None):
     return L.nrm_norm_rope(x, w, out, B, H, L_, D, normalize, 1e-6, dims, 0, 10000.0, 1.0,
-                           offset, 1, cache, cache_len, dt, wdt, None)
+                           offset, 1, freqs, cache, cache_len, dt, wdt, None)
 
 
 def test_null_pointers(L):
@@ -213,3 +214,82 @@ def test_vjp_argument_errors(L):
 def test_vjp_zero_rows_without_parameter_gradients_is_a_noop(L):
     assert rvjp(L, rows=0, dw=None, x=None, g=None, dx=None, ws=None) == OK and err(L) == ""
     assert lvjp(L, rows=0, dw=None, db=None, x=None, g=None, dx=None, ws=None) == OK
+
+
+# ------------------------------------------------------------------------ rope variants
+
+def rope1(L, x=P, out=P + 64 * MB, N=2, L_=4, D=16, dims=16, offset=0, freqs=None, dt=BF16):
+    return L.nrm_rope(x, out, N, L_, D, dims, 0, 10000.0, 1.0, offset, 1, freqs, 1.0, dt, None)
+
+
+def ropeqk(L, q=P, k=P + 64 * MB, qo=P + 128 * MB, ko=P + 192 * MB, pos=P + 256 * MB, T=4,
+           Hq=4, Hk=2, D=16, dims=16, freqs=None, dt=BF16, i64=1):
+    return L.nrm_rope_positions(q, k, qo, ko, pos, i64, T, Hq, Hk, D, dims, 0, 10000.0, 1.0, 1,
+                                freqs, 1.0, dt, None)
+
+
+def test_rope_variant_argument_errors(L):
+    assert rope(L, freqs=P + 64 * MB + 8) == ALIAS and "out must not overlap freqs" in err(L)
+    assert rope1(L, x=None) == NULL and "nrm_rope: x must not be NULL" in err(L)
+    assert rope1(L, dims=3) == SHAPE and rope1(L, offset=-1) == SHAPE and rope1(L, N=-1) == SHAPE
+    assert rope1(L, out=P + 2) == ALIAS
+    assert rope1(L, N=0) == OK and rope1(L, L_=0, x=None) == OK
+    assert rope1(L, dt=9) == DTYPE
+    assert ropeqk(L, pos=None) == NULL and "positions must not be NULL" in err(L)
+    assert ropeqk(L, k=None) == NULL and "k must not be NULL" in err(L)
+    assert ropeqk(L, k=None, ko=None, Hk=0, T=0) == OK
+    assert ropeqk(L, T=-1) == SHAPE and ropeqk(L, Hk=-1) == SHAPE and ropeqk(L, dims=17) == SHAPE
+    assert ropeqk(L, qo=P + 64 * MB) == ALIAS and "q_out must not overlap k" in err(L)
+    assert ropeqk(L, ko=P + 8) == ALIAS and "k_out must not overlap q" in err(L)
+    assert ropeqk(L, qo=P + 256 * MB) == ALIAS and "q_out must not overlap positions" in err(L)
+    assert ropeqk(L, qo=P, ko=P + 64 * MB, T=0) == OK  # in place: allowed
+
+
+def _host(L, name, dims, *args):
+    out = (ctypes.c_float * (dims // 2))()
+    ms = ctypes.c_float(0.0)
+    st = getattr(L, name)(dims, *args, ctypes.cast(out, ctypes.c_void_p), ctypes.byref(ms))
+    return st, np.array(out[:], dtype=np.float64), float(ms.value)
+
+
+def _f32_ulps(a, b):
+    a32 = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    b32 = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a32 - b32)
+
+
+def test_rope_freqs_host_match_the_oracle(L):
+    """The host generators against the fp64 oracle: each divisor within 1 fp32 ulp (both
+    round one fp64 value; libm and numpy may differ in the last fp64 bit), mscale to fp32."""
+    import oracle
+    S = oracle.rope_scaling
+    for dims, base, fac, lo, hi, orig in ((128, 500000.0, 32.0, 1.0, 4.0, 8192),
+                                          (64, 10000.0, 8.0, 1.0, 4.0, 2048),
+                                          (8, 65536.0, 4.0, 0.5, 3.0, 4096)):
+        st, got, ms = _host(L, "nrm_rope_freqs_llama3", dims, base, fac, lo, hi, orig)
+        want, wms = S.llama3_freqs(dims, base, fac, lo, hi, orig)
+        assert st == OK and ms == wms and _f32_ulps(got, want).max() <= 1
+    for dims, base, fac, orig, bf, bs, m, mad in ((128, 10000.0, 4.0, 4096, 32.0, 1.0, 1.0, 0.0),
+                                                  (64, 1e6, 16.0, 8192, 16.0, 2.0, 0.707, 0.5),
+                                                  (32, 10000.0, 1.0, 2048, 32.0, 1.0, 1.0, 0.0)):
+        st, got, ms = _host(L, "nrm_rope_freqs_yarn", dims, base, fac, orig, bf, bs, m, mad)
+        want, wms = S.yarn_freqs(dims, base, fac, orig, bf, bs, m, mad)
+        assert st == OK and _f32_ulps(got, want).max() <= 1
+        assert abs(ms - wms) <= 2.0 ** -23 * abs(wms)
+    lf = np.linspace(1.0, 60.0, 48).astype(np.float32)
+    st, got, ms = _host(L, "nrm_rope_freqs_su", 96, 10000.0,
+                        ctypes.c_void_p(lf.ctypes.data), 131072, 4096)
+    want, wms = S.su_freqs(96, 10000.0, lf, 131072, 4096)
+    assert st == OK and _f32_ulps(got, want).max() <= 1 and abs(ms - wms) <= 2.0 ** -23 * wms
+
+
+def test_rope_freqs_host_errors(L):
+    st, _, _ = _host(L, "nrm_rope_freqs_llama3", 7, 10000.0, 8.0, 1.0, 4.0, 8192)
+    assert st == SHAPE and "dims must be even" in err(L)
+    st, _, _ = _host(L, "nrm_rope_freqs_llama3", 8, 10000.0, 8.0, 4.0, 1.0, 8192)
+    assert st == SHAPE and "low_freq_factor < high_freq_factor" in err(L)
+    st, _, _ = _host(L, "nrm_rope_freqs_yarn", 8, 1.0, 8.0, 4096, 32.0, 1.0, 1.0, 0.0)
+    assert st == SHAPE and "base must be > 1" in err(L)
+    assert L.nrm_rope_freqs_su(8, 10000.0, None, 4096, 1024, None, None) == NULL
+    st, _, _ = _host(L, "nrm_rope_freqs_llama3", 8, 10000.0, 8.0, 1.0, 4.0, 8192)
+    assert st == OK and err(L) == ""

@@ -10,7 +10,12 @@ built, ``load()`` raises.
     add_rms_norm(x, r, w=None, eps=1e-5)         -> (out, h)   h = x + r
     layer_norm(x, w=None, b=None, eps=1e-5)      -> out
     norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, scale=1.0,
-              offset=0, forward=True, cache=None) -> out (or the cache, written in place)
+              offset=0, forward=True, cache=None, freqs=None)
+                                                 -> out (or the cache, written in place)
+    rope(x, dims=None, traditional=False, base=10000.0, scale=1.0, offset=0, forward=True,
+         freqs=None, mscale=1.0)                 -> out
+    rope_positions(positions, q, k=None, ...)    -> (q_out, k_out)
+    rope_freqs_llama3 / rope_freqs_yarn / rope_freqs_su(...) -> (freqs, mscale) on the host
     rms_norm_vjp(x, w, g, eps=1e-5)              -> (dx, dw)
     layer_norm_vjp(x, w, g, eps=1e-5)            -> (dx, dw, db)
 """
@@ -22,7 +27,8 @@ import torch
 
 __all__ = [
     "NrmError", "load", "lib", "rms_norm", "add_rms_norm", "layer_norm", "norm_rope",
-    "rms_norm_vjp", "layer_norm_vjp", "vjp_workspace_bytes", "bench_copy", "NRM_F32",
+    "rms_norm_vjp", "layer_norm_vjp", "vjp_workspace_bytes", "rope", "rope_positions",
+    "rope_freqs_llama3", "rope_freqs_yarn", "rope_freqs_su", "bench_copy", "NRM_F32",
     "NRM_BF16", "LIB_PATH",
 ]
 
@@ -38,7 +44,14 @@ _SIGNATURES = {
     "nrm_add_rms_norm": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
     "nrm_layer_norm": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp],
     "nrm_norm_rope": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _f32, _i64, _int, _f32, _f32,
-                      _i64, _int, _int, _i64, _int, _int, _vp],
+                      _i64, _int, _vp, _int, _i64, _int, _int, _vp],
+    "nrm_rope": [_vp, _vp, _i64, _i64, _i64, _i64, _int, _f32, _f32, _i64, _int, _vp, _f32, _int,
+                 _vp],
+    "nrm_rope_positions": [_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _int,
+                           _f32, _f32, _int, _vp, _f32, _int, _vp],
+    "nrm_rope_freqs_llama3": [_i64, _f32, _f32, _f32, _f32, _i64, _vp, _vp],
+    "nrm_rope_freqs_yarn": [_i64, _f32, _f32, _i64, _f32, _f32, _f32, _f32, _vp, _vp],
+    "nrm_rope_freqs_su": [_i64, _f32, _vp, _i64, _i64, _vp, _vp],
     "nrm_norm_vjp_workspace_bytes": [_i64, _i64, _int],
     "nrm_rms_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz, _vp],
     "nrm_layer_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz,
@@ -192,8 +205,19 @@ def layer_norm(x, w=None, b=None, eps=1e-5, out=None):
     return out
 
 
+def _freqs_arg(freqs, dims, x):
+    """Device float32 [dims / 2] divisors, or None."""
+    if freqs is None:
+        return None
+    _check_act(freqs, "freqs", x.device)
+    if freqs.dtype != torch.float32 or freqs.dim() != 1 or freqs.shape[0] != dims // 2:
+        raise ValueError(f"freqs must be float32 of shape [{dims // 2}], got {freqs.dtype} "
+                         f"{list(freqs.shape)}")
+    return freqs
+
+
 def norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, scale=1.0,
-              offset=0, forward=True, cache=None, out=None):
+              offset=0, forward=True, cache=None, out=None, freqs=None):
     """NormRope over x [B, H, L, D] (nrm_norm_rope). ``eps=None`` skips the normalisation.
     With ``cache`` ([B, H, cache_len, D]) rows offset .. offset + L - 1 of the cache are
     written and the cache is returned; otherwise a new (or the given) [B, H, L, D] array."""
@@ -205,6 +229,7 @@ def norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, s
     dims = D if dims is None else int(dims)
     normalize = eps is not None
     w, wdt = _check_param(w, "w", D, x)
+    freqs = _freqs_arg(freqs, dims, x)
     if cache is not None:
         _check_act(cache, "cache", x.device)
         if cache.dim() != 4 or list(cache.shape[:2]) != [B, H] or cache.shape[3] != D \
@@ -216,8 +241,8 @@ def norm_rope(x, w=None, eps=1e-6, dims=None, traditional=False, base=10000.0, s
         dst, cache_len = _out_like(out, x, "out"), 0
     st = load().nrm_norm_rope(_ptr(x), _ptr(w), _ptr(dst), B, H, L, D, int(normalize),
                               0.0 if eps is None else eps, dims, int(bool(traditional)), base,
-                              scale, int(offset), int(bool(forward)), int(cache is not None),
-                              cache_len, dt, wdt, _stream())
+                              scale, int(offset), int(bool(forward)), _ptr(freqs),
+                              int(cache is not None), cache_len, dt, wdt, _stream())
     if st:
         _raise(st)
     return dst
@@ -290,6 +315,98 @@ def layer_norm_vjp(x, w, g, eps=1e-5, want_dw=True, want_db=True, dx=None, dw=No
     if st:
         _raise(st)
     return dx, dw, db
+
+
+def rope(x, dims=None, traditional=False, base=10000.0, scale=1.0, offset=0, forward=True,
+         freqs=None, mscale=1.0, out=None):
+    """Rope over x [..., L, D] (nrm_rope): row l of every leading index at offset + l."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    if x.dim() < 2:
+        raise ValueError(f"x must be [..., L, D], got {list(x.shape)}")
+    L, D = x.shape[-2], x.shape[-1]
+    N = x.numel() // (L * D) if L * D else 0
+    dims = D if dims is None else int(dims)
+    freqs = _freqs_arg(freqs, dims, x)
+    out = _out_like(out, x, "out")
+    st = load().nrm_rope(_ptr(x), _ptr(out), N, L, D, dims, int(bool(traditional)), base, scale,
+                         int(offset), int(bool(forward)), _ptr(freqs), mscale, dt, _stream())
+    if st:
+        _raise(st)
+    return out
+
+
+def rope_positions(positions, q, k=None, dims=None, traditional=False, base=10000.0, scale=1.0,
+                   forward=True, freqs=None, mscale=1.0, q_out=None, k_out=None):
+    """Rotate query [..., Hq, D] and key [..., Hk, D] rows at per-token positions in one
+    launch (nrm_rope_positions). The leading axes flatten to T tokens; positions holds T
+    integers, or one sequence's positions (repeated for every sequence of a batch)."""
+    _check_act(q, "q")
+    dt = _dtype_code(q, "q")
+    if q.dim() < 3:
+        raise ValueError(f"q must be [..., T, Hq, D], got {list(q.shape)}")
+    Hq, D = q.shape[-2], q.shape[-1]
+    T = q.numel() // (Hq * D) if Hq * D else 0
+    Hk = 0
+    if k is not None:
+        _check_act(k, "k", q.device)
+        if k.dtype != q.dtype or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != D:
+            raise ValueError(f"k must be {q.dtype} [..., Hk, {D}] with q's leading axes, got "
+                             f"{k.dtype} {list(k.shape)}")
+        Hk = k.shape[-2]
+    _check_act(positions, "positions", q.device)
+    if positions.dtype not in (torch.int32, torch.int64) or positions.dim() != 1:
+        raise ValueError(f"positions must be a 1-D int32 or int64 tensor, got {positions.dtype} "
+                         f"{list(positions.shape)}")
+    if positions.shape[0] != T:
+        if T and positions.shape[0] and T % positions.shape[0] == 0:
+            positions = positions.repeat(T // positions.shape[0])
+        else:
+            raise ValueError(f"positions must hold {T} positions (or one sequence's), got "
+                             f"{positions.shape[0]}")
+    dims = D if dims is None else int(dims)
+    freqs = _freqs_arg(freqs, dims, q)
+    q_out = _out_like(q_out, q, "q_out")
+    k_out = _out_like(k_out, k, "k_out") if k is not None else None
+    st = load().nrm_rope_positions(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(positions),
+                                   int(positions.dtype == torch.int64), T, Hq, Hk, D, dims,
+                                   int(bool(traditional)), base, scale, int(bool(forward)),
+                                   _ptr(freqs), mscale, dt, _stream())
+    if st:
+        _raise(st)
+    return q_out, k_out
+
+
+def _host_freqs(fn, dims, *args):
+    out = torch.empty(dims // 2, dtype=torch.float32)
+    ms = ctypes.c_float(0.0)
+    st = fn(dims, *args, ctypes.c_void_p(out.data_ptr()), ctypes.byref(ms))
+    if st:
+        _raise(st)
+    return out, ms.value
+
+
+def rope_freqs_llama3(dims, base, factor=32.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                      original_max=8192):
+    """Llama 3 scaled divisors (nrm_rope_freqs_llama3): (CPU float32 [dims / 2], mscale)."""
+    return _host_freqs(load().nrm_rope_freqs_llama3, dims, base, factor, low_freq_factor,
+                       high_freq_factor, original_max)
+
+
+def rope_freqs_yarn(dims, base, factor=4.0, original_max=4096, beta_fast=32.0, beta_slow=1.0,
+                    mscale=1.0, mscale_all_dim=0.0):
+    """YaRN scaled divisors and attention factor (nrm_rope_freqs_yarn)."""
+    return _host_freqs(load().nrm_rope_freqs_yarn, dims, base, factor, original_max, beta_fast,
+                       beta_slow, mscale, mscale_all_dim)
+
+
+def rope_freqs_su(dims, base, long_factor, max_position=131072, original_max=4096):
+    """LongRoPE ("su") scaled divisors and attention factor (nrm_rope_freqs_su)."""
+    lf = torch.as_tensor(long_factor, dtype=torch.float32).contiguous()
+    if lf.dim() != 1 or lf.shape[0] != dims // 2:
+        raise ValueError(f"long_factor must hold {dims // 2} values, got {list(lf.shape)}")
+    return _host_freqs(load().nrm_rope_freqs_su, dims, base, ctypes.c_void_p(lf.data_ptr()),
+                       max_position, original_max)
 
 
 def bench_copy(src, dst):

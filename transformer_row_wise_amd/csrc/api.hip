@@ -13,6 +13,7 @@
 
 #include "launch.hpp"
 #include "nrm.h"
+#include "rope.hpp"
 #include "vjp.hpp"
 
 namespace {
@@ -74,6 +75,32 @@ nrm_status check_out_vs(const char* fn, const char* out_name, Span out, const ch
               same(out, in) ? "full" : "partial");
 }
 
+// Rope arguments with no second tensor, no positions array, no freqs and mscale 1.
+nrm::RopeArgs rope_defaults() {
+  nrm::RopeArgs a;
+  a.x = a.w = a.x2 = nullptr;
+  a.out = a.out2 = nullptr;
+  a.BH = a.BH1 = a.L = 0;
+  a.x_sbh = a.x_sl = a.o_sbh = a.o_sl = a.o_row0 = 0;
+  a.x2_sbh = a.x2_sl = a.o2_sbh = a.o2_sl = 0;
+  a.D = a.dims = 0;
+  a.normalize = 0; a.eps = 0.f; a.traditional = 0; a.base = 10000.f; a.scale = 1.f;
+  a.offset = 0; a.forward = 1; a.freqs = nullptr; a.positions = nullptr; a.pos_i64 = 0;
+  a.mscale = 1.f; a.w_f32 = 0; a.iters = 1;
+  return a;
+}
+
+// Checks shared by the rope entry points: D, dims (even, <= D).
+nrm_status check_rope_dims(const char* fn, int64_t D, int64_t dims) {
+  if (D < 1 || D > INT32_MAX)
+    return fail(NRM_ERR_SHAPE, "%s: D must be in [1, 2147483647], got %lld", fn, (long long)D);
+  if (dims < 0 || dims > D)
+    return fail(NRM_ERR_SHAPE, "%s: dims must be in [0, D = %lld], got %lld", fn, (long long)D,
+                (long long)dims);
+  if (dims % 2) return fail(NRM_ERR_SHAPE, "%s: dims must be even, got %lld", fn, (long long)dims);
+  return NRM_OK;
+}
+
 nrm_status launched(const char* fn, hipError_t e) {
   if (e != hipSuccess)
     return fail(NRM_ERR_DEVICE, "%s: kernel launch failed: %s, got HIP error %d", fn,
@@ -97,6 +124,10 @@ hipError_t dispatch_row(const nrm::RowArgs& a, nrm_dtype dtype, bool al, hipStre
 }
 
 }  // namespace
+
+namespace nrm {
+void set_last_error(const char* msg) { g_err = msg; }
+}  // namespace nrm
 
 extern "C" {
 
@@ -174,8 +205,8 @@ nrm_status nrm_layer_norm(const void* x, const void* w, const void* b, void* out
 nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64_t B, int64_t H,
                          int64_t L, int64_t D, int normalize, float eps, int64_t dims,
                          int traditional, float base, float scale, int64_t offset, int forward,
-                         int cache, int64_t cache_len, nrm_dtype dtype, nrm_dtype w_dtype,
-                         hipStream_t stream) {
+                         const float* freqs, int cache, int64_t cache_len, nrm_dtype dtype,
+                         nrm_dtype w_dtype, hipStream_t stream) {
   static const char* fn = "nrm_norm_rope";
   g_err.clear();
   nrm_status st = check_dtypes(fn, dtype, w_dtype);
@@ -183,12 +214,7 @@ nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64
   if (B < 0) return fail(NRM_ERR_SHAPE, "%s: B must be >= 0, got %lld", fn, (long long)B);
   if (H < 0) return fail(NRM_ERR_SHAPE, "%s: H must be >= 0, got %lld", fn, (long long)H);
   if (L < 0) return fail(NRM_ERR_SHAPE, "%s: L must be >= 0, got %lld", fn, (long long)L);
-  if (D < 1 || D > INT32_MAX)
-    return fail(NRM_ERR_SHAPE, "%s: D must be in [1, 2147483647], got %lld", fn, (long long)D);
-  if (dims < 0 || dims > D)
-    return fail(NRM_ERR_SHAPE, "%s: dims must be in [0, D = %lld], got %lld", fn, (long long)D,
-                (long long)dims);
-  if (dims % 2) return fail(NRM_ERR_SHAPE, "%s: dims must be even, got %lld", fn, (long long)dims);
+  if ((st = check_rope_dims(fn, D, dims))) return st;
   if (offset < 0)
     return fail(NRM_ERR_SHAPE, "%s: offset must be >= 0, got %lld", fn, (long long)offset);
   if (cache) {
@@ -209,17 +235,20 @@ nrm_status nrm_norm_rope(const void* x, const void* w, void* out_or_cache, int64
   if (!out_or_cache) return fail(NRM_ERR_NULL, "%s: out_or_cache must not be NULL, got NULL", fn);
   const Span sx = span(x, BH * L * D * es), so = span(out_or_cache, BH * out_rows * D * es);
   const Span sw = span(w, w ? D * esize(w_dtype) : 0);
+  const Span sf = span(freqs, freqs ? dims / 2 * 4 : 0);
   if ((st = check_out_vs(fn, cache ? "cache" : "out", so, "x", sx, !cache))) return st;
   if ((st = check_out_vs(fn, cache ? "cache" : "out", so, "w", sw, false))) return st;
+  if ((st = check_out_vs(fn, cache ? "cache" : "out", so, "freqs", sf, false))) return st;
 
-  nrm::RopeArgs a;
+  nrm::RopeArgs a = rope_defaults();
   a.x = x; a.w = w; a.out = out_or_cache;
-  a.BH = BH; a.L = L; a.D = (int)D; a.dims = (int)dims;
+  a.BH = a.BH1 = BH; a.L = L; a.D = (int)D; a.dims = (int)dims;
+  a.x_sbh = L; a.x_sl = 1;
+  a.o_sbh = out_rows; a.o_sl = 1; a.o_row0 = cache ? offset : 0;
   a.normalize = normalize != 0; a.eps = eps; a.traditional = traditional != 0;
   a.base = base; a.scale = scale; a.offset = offset; a.forward = forward != 0;
-  a.out_rows = out_rows; a.out_row0 = cache ? offset : 0;
+  a.freqs = freqs;
   a.w_f32 = w_dtype == NRM_F32;
-  a.iters = 1;
   const bool al = aligned16(x) && aligned16(out_or_cache) && (!w || aligned16(w));
   return launched(fn, dtype == NRM_BF16 ? nrm::launch_norm_rope<true>(a, al, stream)
                                         : nrm::launch_norm_rope<false>(a, al, stream));
@@ -314,6 +343,94 @@ nrm_status nrm_layer_norm_vjp(const void* x, const void* w, const void* g, void*
                               size_t workspace_bytes, hipStream_t stream) {
   return norm_vjp("nrm_layer_norm_vjp", true, x, w, g, dx, dw, db, rows, hidden, eps, dtype,
                   w_dtype, workspace, workspace_bytes, stream);
+}
+
+nrm_status nrm_rope(const void* x, void* out, int64_t N, int64_t L, int64_t D, int64_t dims,
+                    int traditional, float base, float scale, int64_t offset, int forward,
+                    const float* freqs, float mscale, nrm_dtype dtype, hipStream_t stream) {
+  static const char* fn = "nrm_rope";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, dtype);
+  if (st) return st;
+  if (N < 0) return fail(NRM_ERR_SHAPE, "%s: N must be >= 0, got %lld", fn, (long long)N);
+  if (L < 0) return fail(NRM_ERR_SHAPE, "%s: L must be >= 0, got %lld", fn, (long long)L);
+  if ((st = check_rope_dims(fn, D, dims))) return st;
+  if (offset < 0)
+    return fail(NRM_ERR_SHAPE, "%s: offset must be >= 0, got %lld", fn, (long long)offset);
+  const int64_t es = esize(dtype);
+  if (N && L > INT64_MAX / es / D / N)
+    return fail(NRM_ERR_SHAPE, "%s: N * L * D overflows the address range, got %lld x %lld", fn,
+                (long long)N, (long long)L);
+  if (N * L == 0) return NRM_OK;
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  const Span sx = span(x, N * L * D * es), so = span(out, N * L * D * es);
+  const Span sf = span(freqs, freqs ? dims / 2 * 4 : 0);
+  if ((st = check_out_vs(fn, "out", so, "x", sx, true))) return st;
+  if ((st = check_out_vs(fn, "out", so, "freqs", sf, false))) return st;
+  nrm::RopeArgs a = rope_defaults();
+  a.x = x; a.out = out;
+  a.BH = a.BH1 = N; a.L = L; a.D = (int)D; a.dims = (int)dims;
+  a.x_sbh = L; a.x_sl = 1; a.o_sbh = L; a.o_sl = 1;
+  a.traditional = traditional != 0; a.base = base; a.scale = scale; a.offset = offset;
+  a.forward = forward != 0; a.freqs = freqs; a.mscale = mscale;
+  const bool al = aligned16(x) && aligned16(out);
+  return launched(fn, dtype == NRM_BF16 ? nrm::launch_norm_rope<true>(a, al, stream)
+                                        : nrm::launch_norm_rope<false>(a, al, stream));
+}
+
+nrm_status nrm_rope_positions(const void* q, const void* k, void* q_out, void* k_out,
+                              const void* positions, int pos_int64, int64_t T, int64_t Hq,
+                              int64_t Hk, int64_t D, int64_t dims, int traditional, float base,
+                              float scale, int forward, const float* freqs, float mscale,
+                              nrm_dtype dtype, hipStream_t stream) {
+  static const char* fn = "nrm_rope_positions";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, dtype);
+  if (st) return st;
+  if (T < 0) return fail(NRM_ERR_SHAPE, "%s: T must be >= 0, got %lld", fn, (long long)T);
+  if (Hq < 0) return fail(NRM_ERR_SHAPE, "%s: Hq must be >= 0, got %lld", fn, (long long)Hq);
+  if (Hk < 0) return fail(NRM_ERR_SHAPE, "%s: Hk must be >= 0, got %lld", fn, (long long)Hk);
+  if ((st = check_rope_dims(fn, D, dims))) return st;
+  const int64_t es = esize(dtype);
+  const int64_t lim = INT64_MAX / es / D;
+  if ((T && Hq > lim / T) || (T && Hk > lim / T) || (Hq > INT64_MAX - Hk))
+    return fail(NRM_ERR_SHAPE, "%s: T * H * D overflows the address range, got %lld x %lld", fn,
+                (long long)T, (long long)(Hq > Hk ? Hq : Hk));
+  if (T == 0 || Hq + Hk == 0) return NRM_OK;
+  if (!positions) return fail(NRM_ERR_NULL, "%s: positions must not be NULL, got NULL", fn);
+  if (Hq && !q) return fail(NRM_ERR_NULL, "%s: q must not be NULL, got NULL", fn);
+  if (Hq && !q_out) return fail(NRM_ERR_NULL, "%s: q_out must not be NULL, got NULL", fn);
+  if (Hk && !k) return fail(NRM_ERR_NULL, "%s: k must not be NULL, got NULL", fn);
+  if (Hk && !k_out) return fail(NRM_ERR_NULL, "%s: k_out must not be NULL, got NULL", fn);
+  const Span sq = span(q, T * Hq * D * es), sqo = span(q_out, T * Hq * D * es);
+  const Span sk = span(k, T * Hk * D * es), sko = span(k_out, T * Hk * D * es);
+  const Span sp = span(positions, T * (pos_int64 ? 8 : 4));
+  const Span sf = span(freqs, freqs ? dims / 2 * 4 : 0);
+  if ((st = check_out_vs(fn, "q_out", sqo, "q", sq, true))) return st;
+  if ((st = check_out_vs(fn, "q_out", sqo, "k", sk, false))) return st;
+  if ((st = check_out_vs(fn, "q_out", sqo, "k_out", sko, false))) return st;
+  if ((st = check_out_vs(fn, "k_out", sko, "k", sk, true))) return st;
+  if ((st = check_out_vs(fn, "k_out", sko, "q", sq, false))) return st;
+  const char* in_names[] = {"positions", "freqs"};
+  const Span in_spans[] = {sp, sf};
+  for (int i = 0; i < 2; ++i) {
+    if ((st = check_out_vs(fn, "q_out", sqo, in_names[i], in_spans[i], false))) return st;
+    if ((st = check_out_vs(fn, "k_out", sko, in_names[i], in_spans[i], false))) return st;
+  }
+  nrm::RopeArgs a = rope_defaults();
+  // Tensor A is the query (Hq rows per token), tensor B the key (Hk rows per token).
+  a.x = q; a.out = q_out; a.x2 = k; a.out2 = k_out;
+  a.BH = Hq + Hk; a.BH1 = Hq; a.L = T; a.D = (int)D; a.dims = (int)dims;
+  a.x_sbh = 1; a.x_sl = Hq; a.o_sbh = 1; a.o_sl = Hq;
+  a.x2_sbh = 1; a.x2_sl = Hk; a.o2_sbh = 1; a.o2_sl = Hk;
+  a.traditional = traditional != 0; a.base = base; a.scale = scale;
+  a.forward = forward != 0; a.freqs = freqs; a.mscale = mscale;
+  a.positions = positions; a.pos_i64 = pos_int64 != 0;
+  const bool al = (!Hq || (aligned16(q) && aligned16(q_out))) &&
+                  (!Hk || (aligned16(k) && aligned16(k_out)));
+  return launched(fn, dtype == NRM_BF16 ? nrm::launch_norm_rope<true>(a, al, stream)
+                                        : nrm::launch_norm_rope<false>(a, al, stream));
 }
 
 const char* nrm_last_error(void) { return g_err.c_str(); }

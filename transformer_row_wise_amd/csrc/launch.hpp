@@ -6,27 +6,6 @@
 
 namespace nrm {
 
-struct RopeArgs {
-  const void* x;
-  const void* w;
-  void* out;
-  int64_t BH;        // B * H
-  int64_t L;
-  int D;
-  int dims;
-  int normalize;
-  float eps;
-  int traditional;
-  float base;
-  float scale;
-  int64_t offset;
-  int forward;
-  int64_t out_rows;  // rows per (b, h) in the output: L, or cache_len
-  int64_t out_row0;  // first output row of each (b, h): 0, or offset
-  int w_f32;
-  int iters;         // filled in by the launcher
-};
-
 // Kernel-shape override for tests, from the environment variable NRM_FORCE_PATH:
 // "wave" (one wave per row), "block" (one 512-thread block per row), "rowblock" (one block
 // of up to 1024 threads per row, the default shape), "chunked" (looping kernel, 16-byte chunks), "scalar" (looping kernel
@@ -38,9 +17,6 @@ inline bool force_generic_path() { return forced_path() == PATH_SCALAR; }
 
 template <bool BF16, int OP>
 hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream);
-
-template <bool BF16>
-hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t stream);
 
 hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t stream);
 

@@ -1,18 +1,26 @@
-// NormRope: RMS-normalise each [b, h, l] row of a [B, H, L, D] array (all D features, times
-// w), then rotate its first `dims` features at position offset + l; write the result as a
-// new [B, H, L, D] array or into rows offset + l of a [B, H, cache_len, D] cache.
+// Rotary position embeddings over rows of D features, three layouts sharing one kernel:
+//   NormRope  RMS-normalise each [b, h, l] row of a [B, H, L, D] array (all D features, times
+//             w), then rotate its first `dims` features at position offset + l; write a new
+//             [B, H, L, D] array or rows offset + l of a [B, H, cache_len, D] cache;
+//   Rope      the rotation alone on [N, L, D] rows, position offset + l;
+//   positions query [T, Hq, D] and key [T, Hk, D] rows rotated in one launch, every head of
+//             token t at position positions[t].
 //
-// Source: nuvec-core 0.5.0 fast::FastOp, variants NormRope and Rope. The rotation is the
-// textbook RoPE (RoFormer, section 3.2): pair i turns by a = scale * position * theta_i with
-// theta_i = base^(-2i/dims); half mode pairs (i, i + dims/2), traditional mode (2i, 2i+1);
-// the inverse rotation (forward = 0) turns by -a.
+// Sources: nuvec-core 0.5.0 fast::FastOp, variants NormRope and Rope (optional freqs that
+// replace base); the MinivLLM API reference, "Layers", RotaryEmbedding.forward(positions,
+// query, key). The rotation is the textbook RoPE (RoFormer, section 3.2): pair i turns by
+// a = scale * position * theta_i with theta_i = base^(-2i/dims), or 1 / freqs[i] when a
+// freqs vector is given (it holds the divisor of the position for each pair, as in the fast
+// rope the pages name); half mode pairs (i, i + dims/2), traditional mode (2i, 2i+1); the
+// inverse rotation (forward = 0) turns by -a. mscale multiplies the rotated features (the
+// attention factor of the scaled variants; 1 otherwise).
 //
 // Precision: the angle, theta and sin/cos are fp64 (an fp32 angle at positions in the
 // thousands is off by ~1e-4 rad). The rotation u*c - v*s runs in fp64 on u = x*w (exact in
 // fp64), so cancellation between the two products costs nothing; the fp32 row statistic only
 // scales the result. Features at index >= dims get x * rstd * w in fp32.
 //
-// rope_fast: one block per (position l, chunk of b*h rows). The block first computes
+// rope_fast: one block per (position l, chunk of rows at that position). The block first computes
 // (cos, sin) of every pair at its position into LDS, once, then each group of G lanes takes
 // rows: in half mode a lane loads the 16-byte chunk at feature j*VEC and its partner chunk
 // at dims/2 + j*VEC, so each rotated pair sits in one lane and no lane exchange is needed;
@@ -22,9 +30,36 @@
 // 128-wide bf16 row is only 256 bytes), with clamped, unconditional addresses; the table
 // is built while the first rows are in flight.
 // rope_generic: any D / dims / alignment, one wave per row, element at a time.
-#include "launch.hpp"
+#include "rope.hpp"
 
 namespace nrm {
+
+namespace {
+
+// Position of index l: positions[l] when a positions array is given, else offset + l.
+__device__ __forceinline__ int64_t rope_position(const RopeArgs& a, int64_t l) {
+  if (a.positions == nullptr) return a.offset + l;
+  return a.pos_i64 ? ((const int64_t*)a.positions)[l] : (int64_t)((const int32_t*)a.positions)[l];
+}
+
+// Frequency of pair t: 1 / freqs[t], or base^(-2t/dims).
+__device__ __forceinline__ double rope_theta(const RopeArgs& a, int t) {
+  if (a.freqs != nullptr) return 1.0 / (double)a.freqs[t];
+  return pow((double)a.base, (double)(-2 * t) / (double)a.dims);
+}
+
+// Element offset of row (bh, l) in the input, and in the output.
+__device__ __forceinline__ const char* rope_in_row(const RopeArgs& a, int64_t bh, int64_t l,
+                                                   int esz) {
+  if (bh < a.BH1) return (const char*)a.x + (bh * a.x_sbh + l * a.x_sl) * a.D * esz;
+  return (const char*)a.x2 + ((bh - a.BH1) * a.x2_sbh + l * a.x2_sl) * a.D * esz;
+}
+__device__ __forceinline__ char* rope_out_row(const RopeArgs& a, int64_t bh, int64_t l, int esz) {
+  if (bh < a.BH1) return (char*)a.out + (bh * a.o_sbh + (a.o_row0 + l) * a.o_sl) * a.D * esz;
+  return (char*)a.out2 + ((bh - a.BH1) * a.o2_sbh + l * a.o2_sl) * a.D * esz;
+}
+
+}  // namespace
 
 // sin and cos of a rotation angle in fp64, with few registers (the general library sincos
 // carries a large-argument reduction whose registers, live next to a block's in-flight rows,
@@ -85,7 +120,7 @@ rope_fast(RopeArgs a) {
   __shared__ double cs_s[MAXP];
 
   const int64_t l = blockIdx.x;
-  const int64_t pos = a.offset + l;
+  const int64_t pos = rope_position(a, l);
   const int half = a.dims / 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane / G, lj = lane % G;
@@ -133,7 +168,7 @@ rope_fast(RopeArgs a) {
     for (int r = 0; r < R; ++r) {
       bhr[r] = bh_blk + ((int64_t)it * R + r) * RPB + wave * RPW + g;
       const int64_t bhc = bhr[r] < a.BH ? bhr[r] : a.BH - 1;
-      const char* xrow = (const char*)a.x + ((bhc * a.L + l) * a.D) * ESZ;
+      const char* xrow = rope_in_row(a, bhc, l, ESZ);
       xu[r] = u32x4{0, 0, 0, 0};
       xv[r] = u32x4{0, 0, 0, 0};
       if (any_pc) {
@@ -149,7 +184,7 @@ rope_fast(RopeArgs a) {
   };
   load_step(0);
   for (int t = threadIdx.x; t < half; t += 256) {
-    const double theta = pow((double)a.base, (double)(-2 * t) / (double)a.dims);
+    const double theta = rope_theta(a, t);
     const double ang = ((double)a.scale * (double)pos) * theta;
     double sn, cs;
     rope_sincos(ang, &sn, &cs);
@@ -178,7 +213,7 @@ rope_fast(RopeArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool live = bhr[r] < a.BH;  // uniform over the group of G lanes that owns the row
-      char* orow = (char*)a.out + ((bhr[r] * a.out_rows + a.out_row0 + l) * a.D) * ESZ;
+      char* orow = rope_out_row(a, live ? bhr[r] : 0, l, ESZ);
       float fu[V], fv[V];
       unpack<BF16>(xu[r], fu);
       unpack<BF16>(xv[r], fv);
@@ -204,14 +239,15 @@ rope_fast(RopeArgs a) {
         }
         rstd = rstd_f64((double)group_sum<G>(ss), a.D, a.eps);
       }
+      const double rs = rstd * (double)a.mscale;  // scale of the rotated features
       if (live && has_pc) {
         if constexpr (HALF) {
 #pragma unroll
           for (int e = 0; e < V; ++e) {
             const double u = (double)fu[e] * (double)wu[e];
             const double v = (double)fv[e] * (double)wv[e];
-            fu[e] = f64_to_f32((u * c[e] - v * s[e]) * rstd);
-            fv[e] = f64_to_f32((u * s[e] + v * c[e]) * rstd);
+            fu[e] = f64_to_f32((u * c[e] - v * s[e]) * rs);
+            fv[e] = f64_to_f32((u * s[e] + v * c[e]) * rs);
           }
           st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
           st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
@@ -220,8 +256,8 @@ rope_fast(RopeArgs a) {
           for (int e = 0; e < V / 2; ++e) {
             const double u = (double)fu[2 * e] * (double)wu[2 * e];
             const double v = (double)fu[2 * e + 1] * (double)wu[2 * e + 1];
-            fu[2 * e] = f64_to_f32((u * c[e] - v * s[e]) * rstd);
-            fu[2 * e + 1] = f64_to_f32((u * s[e] + v * c[e]) * rstd);
+            fu[2 * e] = f64_to_f32((u * c[e] - v * s[e]) * rs);
+            fu[2 * e + 1] = f64_to_f32((u * s[e] + v * c[e]) * rs);
           }
           st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
         }
@@ -252,45 +288,46 @@ rope_generic(RopeArgs a) {
   for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < nrows;
        row += (int64_t)gridDim.x * 4) {
     const int64_t bh = row / a.L, l = row % a.L;
-    const int64_t xi = row * a.D;
-    const int64_t oi = (bh * a.out_rows + a.out_row0 + l) * a.D;
+    const char* xr = rope_in_row(a, bh, l, Fmt<BF16>::ESZ);
+    char* orow = rope_out_row(a, bh, l, Fmt<BF16>::ESZ);
     float ss = 0.f;
     for (int e = lane; e < a.D; e += 64) {
       float f[1];
-      load_act<BF16, 1>(a.x, xi + e, f);
+      load_act<BF16, 1>(xr, e, f);
       ss = __builtin_fmaf(f[0], f[0], ss);
     }
     // The wave sum also orders every read of the row before the first write below.
     const double rstd = norm ? rstd_f64((double)wave_sum(ss), a.D, a.eps) : 1.0;
-    const double pos = (double)(a.offset + l);
+    const double rs = rstd * (double)a.mscale;
+    const double pos = (double)rope_position(a, l);
     for (int p = lane; p < half; p += 64) {
       const int iu = a.traditional ? 2 * p : p;
       const int iv = a.traditional ? 2 * p + 1 : p + half;
       float fu[1], fv[1], wu[1] = {1.f}, wv[1] = {1.f};
-      load_act<BF16, 1>(a.x, xi + iu, fu);
-      load_act<BF16, 1>(a.x, xi + iv, fv);
+      load_act<BF16, 1>(xr, iu, fu);
+      load_act<BF16, 1>(xr, iv, fv);
       if (has_w) {
         load_param<BF16, 1>(a.w, a.w_f32, iu, wu);
         load_param<BF16, 1>(a.w, a.w_f32, iv, wv);
       }
-      const double theta = pow((double)a.base, (double)(-2 * p) / (double)a.dims);
+      const double theta = rope_theta(a, p);
       double s, c;
       rope_sincos(((double)a.scale * pos) * theta, &s, &c);
       if (!a.forward) s = -s;
       const double u = (double)fu[0] * (double)wu[0];
       const double v = (double)fv[0] * (double)wv[0];
-      float ou[1] = {f64_to_f32((u * c - v * s) * rstd)};
-      float ov[1] = {f64_to_f32((u * s + v * c) * rstd)};
-      store_act<BF16, 1>(a.out, oi + iu, ou);
-      store_act<BF16, 1>(a.out, oi + iv, ov);
+      float ou[1] = {f64_to_f32((u * c - v * s) * rs)};
+      float ov[1] = {f64_to_f32((u * s + v * c) * rs)};
+      store_act<BF16, 1>(orow, iu, ou);
+      store_act<BF16, 1>(orow, iv, ov);
     }
     const float rstd_f = (float)rstd;
     for (int e = a.dims + lane; e < a.D; e += 64) {
       float f[1], wv[1] = {1.f};
-      load_act<BF16, 1>(a.x, xi + e, f);
+      load_act<BF16, 1>(xr, e, f);
       if (has_w) load_param<BF16, 1>(a.w, a.w_f32, e, wv);
       f[0] = norm ? (f[0] * rstd_f) * wv[0] : f[0];
-      store_act<BF16, 1>(a.out, oi + e, f);
+      store_act<BF16, 1>(orow, e, f);
     }
   }
 }

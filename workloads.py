@@ -178,3 +178,49 @@ def cfg_ln_vjp(rows=16384, hidden=8192, dtype="bf16", seed=0):
     """LayerNorm backward: x ~N(0.5, std 2), w ~N(1,0.1), g ~N(0,1), eps 1e-5."""
     return row_inputs(rows, hidden, dtype, seed=seed, x=("normal", 0.5, 2.0),
                       w=("normal", 1.0, 0.1), g=("normal", 0.0, 1.0), eps=1e-5)
+
+
+@dataclasses.dataclass
+class RopeQKInputs:
+    """Query [T, Hq, D] and key [T, Hk, D] rows with their token positions [T] (int64)."""
+
+    q: torch.Tensor
+    k: torch.Tensor | None
+    positions: torch.Tensor
+
+
+def rope_qk_inputs(T, Hq, Hk, D, dtype, *, seed=0, positions="arange", max_position=None):
+    """q then k ~ N(0, 1); positions 0 .. T-1 ("arange", a prefill) or uniform integers in
+    [0, max_position) ("random", a decode batch of independent sequences)."""
+    rng = np.random.default_rng(seed)
+    q64 = rng.standard_normal((T, Hq, D))
+    k64 = rng.standard_normal((T, Hk, D)) if Hk else None
+    if positions == "arange":
+        pos = np.arange(T, dtype=np.int64)
+    else:
+        pos = rng.integers(0, max_position, size=T, dtype=np.int64)
+    return RopeQKInputs(q=cast(q64, dtype), k=cast(k64, dtype) if k64 is not None else None,
+                        positions=torch.from_numpy(pos))
+
+
+def rope_freqs_draw(dims, kind, seed=0):
+    """Synthetic per-pair divisors for the freqs input, float32 [dims / 2]: "uniform" in
+    [0.5, 5000), or "loguniform" in [1, 1e7) (the span of long-context scaled divisors)."""
+    rng = np.random.default_rng(seed)
+    if kind == "uniform":
+        f = rng.uniform(0.5, 5000.0, dims // 2)
+    else:
+        f = np.exp(rng.uniform(0.0, np.log(1e7), dims // 2))
+    return torch.from_numpy(f.astype(np.float32))
+
+
+# Positions-form workload: a Llama-3-8B-shaped prefill of 16384 tokens, 32 query and 8 key
+# heads of 128 features, bf16, Llama 3 scaled frequencies (base 500000, the MinivLLM
+# defaults factor 32, low 1, high 4, original context 8192).
+ROPE_QK_SHAPE = (16384, 32, 8, 128)
+ROPE_QK_BASE = 500000.0
+
+
+def cfg_rope_qk_bf16(seed=0):
+    T, Hq, Hk, D = ROPE_QK_SHAPE
+    return rope_qk_inputs(T, Hq, Hk, D, "bf16", seed=seed)
