@@ -21,6 +21,8 @@ What it computes, and where the pages define it:
   * ``rope_scaling``  -- frequency scalings named by nuvec-nn ``layers.rs``, ``Rope``
                          (Llama 3 NTK-by-parts, YaRN, LongRoPE "su"), each after its
                          published method.
+  * ``softmax``       -- ``fast::FastOp`` variants ``Softmax``, ``CausalSoftmax``,
+                         ``LogSumExp``, ``CrossEntropy``, ``CrossEntropyVjp``.
   * ``rms_norm_vjp``, ``layer_norm_vjp`` -- ``fast::FastOp`` variants ``RmsNormVjp`` and
                          ``LayerNormVjp``: the gradients of ``RmsNorm`` (for x, w) and of
                          ``LayerNorm`` (for x, w, b) given the output cotangent g.
@@ -38,11 +40,12 @@ from .rounding import round_bf16, round_f32, round_to, bf16_bits, f32_param
 from .norms import rms_norm, add_rms_norm, layer_norm
 from .rope import rope_frequencies, rope_angles, norm_rope, rope_positions
 from . import rope_scaling
+from . import softmax
 from .vjp import rms_norm_vjp, layer_norm_vjp
 
 __all__ = [
     "round_bf16", "round_f32", "round_to", "bf16_bits", "f32_param",
     "rms_norm", "add_rms_norm", "layer_norm",
     "rope_frequencies", "rope_angles", "norm_rope", "rope_positions", "rope_scaling",
-    "rms_norm_vjp", "layer_norm_vjp",
+    "rms_norm_vjp", "layer_norm_vjp", "softmax",
 ]

@@ -163,3 +163,22 @@ def layer_vjp_rows(x, w, b, g, eps):
     dw = [_grad(lambda q: total(q, bv), wv, k) for k in range(d)]
     db = [_grad(lambda q: total(wv, q), bv, k) for k in range(d)]
     return dx, dw, db
+
+
+def softmax_row(x):
+    xs = [mpmath.mpf(v) for v in x]
+    e = [mpmath.exp(v) for v in xs]
+    s = mpmath.fsum(e)
+    return [v / s for v in e]
+
+
+def logsumexp_row(x):
+    return mpmath.log(mpmath.fsum(mpmath.exp(mpmath.mpf(v)) for v in x))
+
+
+def cross_entropy_vjp_row(x, t, g):
+    """Numerical derivatives of g * (logsumexp(x) - x[t]) with respect to each x_j."""
+    gm = mpmath.mpf(g)
+    loss = lambda q: gm * (mpmath.log(mpmath.fsum(mpmath.exp(v) for v in q)) - q[t])
+    pt = [mpmath.mpf(v) for v in x]
+    return [_grad(loss, pt, k) for k in range(len(x))]

@@ -25,6 +25,11 @@ What pins what:
   * scaled freqs  -- band properties of each published method (pairs kept, pairs scaled by
                      the factor, the blend in between and its continuity at the band edges,
                      ramp ends, closed-form attention factors), identity at factor 1;
+  * softmax family -- hand-worked fixtures (equal shares, underflow, causal rows with and
+                     without survivors, ln 4), 50-digit brute force (the gradient by numerical
+                     differentiation of the loss), torch's softmax / logsumexp /
+                     cross_entropy and its autograd in float64, invariants (rows sum to 1,
+                     shift invariance, LSE(x + c) = LSE(x) + c, gradient rows sum to 0);
   * RmsNormVjp /  -- hand-worked fixtures, 50-digit numerical differentiation of the
     LayerNormVjp     forward (brute force), torch autograd of ``rms_norm`` / ``layer_norm``
                      in float64, and the invariances every gradient of these maps obeys
@@ -41,6 +46,7 @@ import numpy as np
 import torch
 
 import brute
+import mpmath
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -618,6 +624,97 @@ def pin_su_scaling(o):
     _close(ms, np.sqrt(2.0), 1e-15, 0, "max = original^2 gives sqrt 2")
     _, ms1 = S.su_freqs(dims, base, np.ones(8), max_position=4096, original_max=4096)
     assert ms1 == 1.0
+
+
+# ---------------------------------------------------------------------- softmax family
+
+def pin_softmax_golden(o):
+    g = _golden("softmax_hand.json")
+    S = o.softmax
+    for c in g["softmax"]:
+        x = _vals(c["x"])[None]
+        _close(S.softmax(x, "f64")[0], _vals(c["expect"]), 1e-15, 1e-300, c["why"])
+        for dt in ("bf16", "f32"):
+            want = [brute.round_fraction(Fraction(v), dt) for v in c["expect"]]
+            _same_values(S.softmax(x, dt)[0], want, c["why"])
+    for c in g["causal"]:
+        x = np.array([[float(Fraction(v)) for v in r] for r in c["x"]])
+        want = np.array([[float(Fraction(v)) for v in r] for r in c["expect"]])
+        for dt in ("bf16", "f32"):
+            _close(S.causal_softmax(x, c["rows"], dt), want, 2.0 ** -7, 0, c["why"])
+        _close(S.causal_softmax(x, c["rows"], "f64"), want, 1e-15, 0, c["why"])
+    for c in g["logsumexp"]:
+        got = S.logsumexp(_vals(c["x"])[None], "f64")[0, 0]
+        _close(got, float(c["expect_decimal"]), 1e-15, 0, c["why"])
+    for c in g["cross_entropy"]:
+        got = S.cross_entropy(_vals(c["x"])[None], [c["t"]])[0]
+        _close(got, np.float32(float(c["expect_decimal"])), 0, 0, c["why"])
+    for c in g["cross_entropy_vjp"]:
+        got = S.cross_entropy_vjp(_vals(c["x"])[None], [c["t"]], [float(Fraction(c["g"]))],
+                                  "f64")[0]
+        _close(got, _vals(c["expect"]), 1e-15, 1e-300, c["why"])
+
+
+def pin_softmax_brute(o):
+    """Softmax, logsumexp, cross-entropy and its gradient on short rows against 50 digits
+    (the gradient by numerical differentiation of g * loss)."""
+    S = o.softmax
+    rng = _rng(41)
+    for dt, cast in (("bf16", _bf16_values), ("f32", _f32_values)):
+        x = cast(rng.standard_normal((3, 9)) * 4)
+        got = S.softmax(x, dt)
+        lse = S.logsumexp(x, dt)
+        t = rng.integers(0, 9, 3)
+        g = _f32_values(rng.standard_normal(3))
+        ce = S.cross_entropy(x, t)
+        dx = S.cross_entropy_vjp(x, t, g, dt)
+        for i in range(3):
+            _same_values(got[i], [brute.round_mp(v, dt) for v in brute.softmax_row(x[i])], "sm")
+            _same_values(lse[i], [brute.round_mp(brute.logsumexp_row(x[i]), dt)], "lse")
+            want = brute.logsumexp_row(x[i]) - mpmath.mpf(x[i][t[i]])
+            _same_values(ce[i:i + 1], [brute.round_mp(want, "f32")], "ce")
+            bd = brute.cross_entropy_vjp_row(x[i], int(t[i]), g[i])
+            _same_values(dx[i], [brute.round_mp(v, dt) for v in bd], "ce vjp")
+
+
+def pin_softmax_torch(o):
+    """torch's softmax, logsumexp, cross_entropy (reduction none) and autograd, float64."""
+    S = o.softmax
+    rng = _rng(42)
+    for V in (1, 7, 1000):
+        x = rng.standard_normal((6, V)) * 3
+        xt = torch.from_numpy(x)
+        _close(S.softmax(x, "f64"), torch.softmax(xt, -1).numpy(), 1e-13, 1e-300, "softmax")
+        _close(S.logsumexp(x, "f64"), torch.logsumexp(xt, -1, keepdim=True).numpy(), 1e-14,
+               1e-14, "logsumexp")
+        t = rng.integers(0, V, 6)
+        want = torch.nn.functional.cross_entropy(xt, torch.from_numpy(t), reduction="none")
+        _close(S.cross_entropy(x, t), want.numpy().astype(np.float32), 2.0 ** -23, 1e-7, "ce")
+        g = rng.standard_normal(6)
+        xr = xt.clone().requires_grad_(True)
+        torch.nn.functional.cross_entropy(xr, torch.from_numpy(t), reduction="none").backward(
+            torch.from_numpy(g))
+        _close(S.cross_entropy_vjp(x, t, g, "f64"), xr.grad.numpy(), 1e-12, 1e-15, "ce vjp")
+
+
+def pin_softmax_invariants(o):
+    S = o.softmax
+    rng = _rng(43)
+    x = _bf16_values(rng.standard_normal((5, 300)) * 6)
+    p = S.softmax(x, "f64")
+    _close(np.sum(p, axis=-1), np.ones(5), 1e-14, 0, "rows sum to 1")
+    for c in (1.0, -37.0, 1024.0):  # x + c is exact in float64 for these bf16 values
+        _same_values(S.softmax(x + c, "f64"), p, f"shift {c}")
+        _close(S.logsumexp(x + c, "f64"), S.logsumexp(x, "f64") + c, 1e-15, 1e-12, "lse shift")
+    big = x * 100 + 1e4  # exp of these overflows unless the maximum is taken out first
+    assert np.all(np.isfinite(S.softmax(big, "f64"))) and np.all(np.isfinite(S.logsumexp(big, "f64")))
+    t = rng.integers(0, 300, 5)
+    g = rng.standard_normal(5)
+    d = S.cross_entropy_vjp(x, t, g, "f64")
+    _close(np.sum(d, axis=-1), np.zeros(5), 0, 1e-13, "gradient rows sum to 0")
+    assert np.all(S.cross_entropy(x, t) >= 0)
+    bad = S.cross_entropy(x[:2], [-1, 300])
+    assert np.all(np.isnan(bad)) and np.all(np.isnan(S.cross_entropy_vjp(x[:1], [300], [1.0], "f64")))
 
 
 # --------------------------------------------------------------------- RmsNormVjp / LN

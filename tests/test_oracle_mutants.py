@@ -95,6 +95,22 @@ MUTANTS = [
      "su attention factor without the root"),
     ("rope_scaling.py", "out = round_to(lf * _base_periods(dims, base), \"f32\")",
      "out = round_to(lf / _base_periods(dims, base), \"f32\")", "su factors divide"),
+    ("softmax.py", "    return c <= r + L - rows", "    return c <= r + L - rows - 1",
+     "causal mask one column short"),
+    ("softmax.py", "    return c <= r + L - rows", "    return c <= r", "causal mask not aligned at the end"),
+    ("softmax.py", "    e = np.exp(x - m)\n    return e / np.sum(e, axis=-1, keepdims=True)",
+     "    e = np.exp(x)\n    return e / np.sum(e, axis=-1, keepdims=True)",
+     "softmax without the maximum taken out"),
+    ("softmax.py", "return softmax(np.where(keep, x, LOWEST[dtype]), dtype)",
+     "return softmax(np.where(keep, x, -np.inf), dtype)", "masked scores as -inf"),
+    ("softmax.py", "out = finite_m + np.log(np.sum(np.exp(x - finite_m), axis=-1, keepdims=True))",
+     "out = np.log(np.sum(np.exp(x - finite_m), axis=-1, keepdims=True))",
+     "logsumexp drops the maximum"),
+    ("softmax.py", "loss = lse - x[np.arange(x.shape[0]), t]", "loss = x[np.arange(x.shape[0]), t] - lse",
+     "cross-entropy sign"),
+    ("softmax.py", "    d[np.arange(x.shape[0]), t] -= 1.0\n", "", "gradient without the one-hot"),
+    ("softmax.py", "    d = d * np.asarray(g, dtype=np.float64).reshape(-1, 1)\n", "",
+     "gradient ignores g"),
     ("vjp.py", "x2 * (r ** 3) * dot / d", "x2 * (r ** 2) * dot / d", "RmsNormVjp r^2 for r^3"),
     ("vjp.py", "dx = r * g2 * wv - x2 * (r ** 3) * dot / d", "dx = r * g2 * wv",
      "RmsNormVjp drops the term through the statistic"),
