@@ -340,7 +340,37 @@ def suite(args):
         emit(cfg, "layer_norm_vjp" if ln else "rms_norm_vjp", [rows, hidden, str(inp.x.dtype)],
              nbytes, rows, per)
 
-    groups = set(args.only.split(",")) if args.only else {"fwd", "vjp", "rope"}
+    groups = set(args.only.split(",")) if args.only else {"fwd", "vjp", "rope", "sm"}
+    if "sm" in groups:
+        x = workloads.scores((16384, 8192), "bf16").cuda()
+        out = torch.empty_like(x)
+        nbytes = 2 * x.numel() * 2
+        per = time_graph(lambda i: nrm.softmax(x, out=out), calls(nbytes))
+        emit("9a", "softmax", list(x.shape), nbytes, x.shape[0], per)
+        del x, out
+        B, H, L = 8, 32, 512
+        xs = workloads.scores((B * H, L, L), "bf16", seed=1)
+        k = n_sets(2 * xs.numel() * 2)
+        xl = [xs.cuda() for _ in range(k)]
+        ol = [torch.empty_like(xl[0]) for _ in range(k)]
+        nbytes = 2 * xs.numel() * 2
+        per = time_graph(lambda i: nrm.causal_softmax(xl[i % k], L, out=ol[i % k]), calls(nbytes))
+        emit("9b", "causal_softmax", [B * H, L, L], nbytes, B * H * L, per)
+        del xl, ol
+        inp = workloads.cfg_ce_bf16()
+        rows, V = workloads.CE_SHAPE
+        lg, tg, g = inp.logits.cuda(), inp.targets.cuda(), inp.g.cuda()
+        lse = torch.empty(rows, 1, dtype=torch.bfloat16, device="cuda")
+        loss = torch.empty(rows, dtype=torch.float32, device="cuda")
+        dl = torch.empty_like(lg)
+        nb_in = rows * V * 2
+        per = time_graph(lambda i: nrm.logsumexp(lg, out=lse), calls(nb_in))
+        emit("9c", "logsumexp", [rows, V], nb_in + rows * 2, rows, per)
+        per = time_graph(lambda i: nrm.cross_entropy(lg, tg, loss=loss), calls(nb_in))
+        emit("9d", "cross_entropy", [rows, V], nb_in + rows * 12, rows, per)
+        per = time_graph(lambda i: nrm.cross_entropy_vjp(lg, tg, g, dlogits=dl), calls(2 * nb_in))
+        emit("9e", "cross_entropy_vjp", [rows, V], 2 * nb_in + rows * 12, rows, per)
+        del lg, dl
     if "rope" in groups:
         inp = workloads.cfg_rope_qk_bf16()
         T, Hq, Hk, D = workloads.ROPE_QK_SHAPE
@@ -576,8 +606,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--only", metavar="GROUPS",
-                    help="with --suite: comma-separated groups among fwd, vjp, rope (skips "
-                         "the headline line)")
+                    help="with --suite: comma-separated groups among fwd, vjp, rope, sm "
+                         "(skips the headline line)")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))

@@ -8,6 +8,11 @@
  *   nrm_norm_rope       RMSNorm + rotary embedding  per [b, h, l] row, position offset + l
  *   nrm_rope            rotary embedding            per [n, l] row, position offset + l
  *   nrm_rope_positions  rotary embedding of query and key rows at per-token positions
+ *   nrm_softmax         softmax                     exp(x - max) / sum, fp32 accumulation
+ *   nrm_causal_softmax  softmax of causally masked scores (blocked attention mask)
+ *   nrm_logsumexp       log(sum(exp(x)))            the last axis becomes size 1
+ *   nrm_cross_entropy   logsumexp(logits) - logits[target], fp32 per row
+ *   nrm_cross_entropy_vjp  its gradient for the logits
  *   nrm_rms_norm_vjp    RMSNorm backward            dx, dw from the output cotangent g
  *   nrm_layer_norm_vjp  LayerNorm backward          dx, dw, db from the output cotangent g
  * The forward operations are one HIP kernel launch each; the backward ones add a second,
@@ -289,6 +294,76 @@ nrm_status nrm_layer_norm_vjp(const void* x, const void* w, const void* g, void*
                               void* db, int64_t rows, int64_t hidden, float eps,
                               nrm_dtype dtype, nrm_dtype w_dtype, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Softmax over the last axis of x [rows, n]: out = exp(x - max) / sum(exp(x - max)).
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant Softmax ((x): softmax over the last axis,
+ * accumulated in float32). Arithmetic fp32; the result is rounded once to dtype; every
+ * element is within one unit in the last place (bf16) or 1e-5 relative + 1e-6 absolute
+ * (fp32) of the exact value. NaN or +inf in a row makes the row NaN.
+ *
+ *   x, out     [rows, n] dtype; out may be exactly x
+ * Errors: NULL x/out (rows > 0) -> NRM_ERR_NULL; rows < 0, n outside [1, 2^31) ->
+ * NRM_ERR_SHAPE; dtype -> NRM_ERR_DTYPE; out partly overlapping x -> NRM_ERR_ALIAS.
+ */
+nrm_status nrm_softmax(const void* x, void* out, int64_t rows, int64_t n, nrm_dtype dtype,
+                       hipStream_t stream);
+
+/*
+ * Softmax of causally masked scores x [N, R, L] (R a multiple of rows_per_block): row r of
+ * the R axis keeps the columns c <= r % rows_per_block + L - rows_per_block; the other scores
+ * are replaced by the dtype's lowest finite value (so they come out 0, unless a row keeps no
+ * column at all: then every score is that value and the row is uniform).
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant CausalSoftmax (field rows: rows per block;
+ * MLX's blocked attention mask). Otherwise as nrm_softmax.
+ * Errors: as nrm_softmax; rows_per_block < 1 or R not a multiple of it -> NRM_ERR_SHAPE.
+ */
+nrm_status nrm_causal_softmax(const void* x, void* out, int64_t N, int64_t R, int64_t L,
+                              int64_t rows_per_block, nrm_dtype dtype, hipStream_t stream);
+
+/*
+ * LogSumExp over the last axis: out[row] = log(sum_j exp(x[row, j])), computed as
+ * max + log(sum exp(x - max)) in fp32 and rounded once to dtype.
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant LogSumExp ((x): the last axis becomes
+ * size 1).
+ *   x [rows, n] dtype;  out [rows] dtype (the [rows, 1] result), must not overlap x
+ * Errors: as nrm_softmax (out may not overlap x at all).
+ */
+nrm_status nrm_logsumexp(const void* x, void* out, int64_t rows, int64_t n, nrm_dtype dtype,
+                         hipStream_t stream);
+
+/*
+ * Cross-entropy per row: loss[row] = logsumexp(logits[row]) - logits[row, targets[row]],
+ * fp32. Computed as log1p(R / e_t) with e_t = exp(x_t - max) and R the sum of the other
+ * columns' exp(x - max), so small losses keep their relative precision. A target outside
+ * [0, V) gives NaN.
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant CrossEntropy ((logits, targets):
+ * logsumexp(logits) - logits[target] per row, in float32).
+ *   logits     [rows, V] dtype
+ *   targets    [rows] int32 (targets_int64 == 0) or int64 device array
+ *   loss       [rows] fp32 output; must not overlap logits or targets
+ * Errors: as nrm_softmax; NULL targets/loss -> NRM_ERR_NULL.
+ */
+nrm_status nrm_cross_entropy(const void* logits, const void* targets, int targets_int64,
+                             float* loss, int64_t rows, int64_t V, nrm_dtype dtype,
+                             hipStream_t stream);
+
+/*
+ * Gradient of nrm_cross_entropy for the logits: dlogits[row, j] = g[row] * (softmax(
+ * logits[row])_j - [j == target]); the target's entry is formed as -g R / (R + e_t) (no
+ * cancellation). Rounded once to dtype; a target outside [0, V) gives a NaN row.
+ * Source: nuvec-core 0.5.0 fast::FastOp, variant CrossEntropyVjp ((logits, targets, loss,
+ * g): the gradient of CrossEntropy for the logits).
+ *   logits, targets as nrm_cross_entropy
+ *   loss       [rows] fp32 forward output: accepted, not read (the kernel rebuilds the row's
+ *              normaliser from the logits it reads anyway); may be NULL
+ *   g          [rows] fp32 cotangent of the loss
+ *   dlogits    [rows, V] dtype output; may be exactly logits
+ * Errors: as nrm_cross_entropy; NULL g/dlogits -> NRM_ERR_NULL.
+ */
+nrm_status nrm_cross_entropy_vjp(const void* logits, const void* targets, int targets_int64,
+                                 const float* loss, const float* g, void* dlogits,
+                                 int64_t rows, int64_t V, nrm_dtype dtype, hipStream_t stream);
 
 /* Name of a status code ("NRM_OK", "NRM_ERR_SHAPE", ...). */
 const char* nrm_status_name(nrm_status status);

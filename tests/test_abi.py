@@ -293,3 +293,26 @@ def test_rope_freqs_host_errors(L):
     assert L.nrm_rope_freqs_su(8, 10000.0, None, 4096, 1024, None, None) == NULL
     st, _, _ = _host(L, "nrm_rope_freqs_llama3", 8, 10000.0, 8.0, 1.0, 4.0, 8192)
     assert st == OK and err(L) == ""
+
+
+# ----------------------------------------------------------------------- softmax family
+
+def test_softmax_family_argument_errors(L):
+    assert L.nrm_softmax(None, P, 4, 8, BF16, None) == NULL
+    assert L.nrm_softmax(P, P + 2, 4, 8, BF16, None) == ALIAS
+    assert L.nrm_softmax(P, P, 0, 8, BF16, None) == OK
+    assert L.nrm_softmax(P, P, 4, 0, BF16, None) == SHAPE
+    assert L.nrm_softmax(P, P, 4, 8, 7, None) == DTYPE
+    assert L.nrm_causal_softmax(P, P, 2, 6, 8, 4, BF16, None) == SHAPE
+    assert "R must be a multiple of rows_per_block (4), got 6" in err(L)
+    assert L.nrm_causal_softmax(P, P, 2, 8, 8, 0, BF16, None) == SHAPE
+    assert L.nrm_causal_softmax(P, P, 0, 8, 8, 4, BF16, None) == OK
+    assert L.nrm_logsumexp(P, P + 8, 4, 8, BF16, None) == ALIAS
+    assert L.nrm_cross_entropy(P, None, 1, P + MB, 4, 8, BF16, None) == NULL
+    assert L.nrm_cross_entropy(P, P + MB, 1, P + 4, 4, 8, BF16, None) == ALIAS
+    assert "loss must not overlap logits" in err(L)
+    assert L.nrm_cross_entropy_vjp(P, P + MB, 1, None, None, P + 2 * MB, 4, 8, BF16, None) == NULL
+    assert "g must not be NULL" in err(L)
+    assert L.nrm_cross_entropy_vjp(P, P + MB, 1, None, P + 3 * MB, P + 2, 4, 8, BF16,
+                                   None) == ALIAS
+    assert L.nrm_cross_entropy_vjp(P, P + MB, 1, None, P + 3 * MB, P, 0, 8, BF16, None) == OK

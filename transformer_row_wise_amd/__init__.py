@@ -16,6 +16,10 @@ built, ``load()`` raises.
          freqs=None, mscale=1.0)                 -> out
     rope_positions(positions, q, k=None, ...)    -> (q_out, k_out)
     rope_freqs_llama3 / rope_freqs_yarn / rope_freqs_su(...) -> (freqs, mscale) on the host
+    softmax(x) / causal_softmax(x, rows)         -> out
+    logsumexp(x)                                 -> [..., 1]
+    cross_entropy(logits, targets)               -> fp32 loss per row
+    cross_entropy_vjp(logits, targets, g)        -> dlogits
     rms_norm_vjp(x, w, g, eps=1e-5)              -> (dx, dw)
     layer_norm_vjp(x, w, g, eps=1e-5)            -> (dx, dw, db)
 """
@@ -28,7 +32,8 @@ import torch
 __all__ = [
     "NrmError", "load", "lib", "rms_norm", "add_rms_norm", "layer_norm", "norm_rope",
     "rms_norm_vjp", "layer_norm_vjp", "vjp_workspace_bytes", "rope", "rope_positions",
-    "rope_freqs_llama3", "rope_freqs_yarn", "rope_freqs_su", "bench_copy", "NRM_F32",
+    "rope_freqs_llama3", "rope_freqs_yarn", "rope_freqs_su", "softmax", "causal_softmax",
+    "logsumexp", "cross_entropy", "cross_entropy_vjp", "bench_copy", "NRM_F32",
     "NRM_BF16", "LIB_PATH",
 ]
 
@@ -56,6 +61,11 @@ _SIGNATURES = {
     "nrm_rms_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz, _vp],
     "nrm_layer_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz,
                            _vp],
+    "nrm_softmax": [_vp, _vp, _i64, _i64, _int, _vp],
+    "nrm_causal_softmax": [_vp, _vp, _i64, _i64, _i64, _i64, _int, _vp],
+    "nrm_logsumexp": [_vp, _vp, _i64, _i64, _int, _vp],
+    "nrm_cross_entropy": [_vp, _vp, _int, _vp, _i64, _i64, _int, _vp],
+    "nrm_cross_entropy_vjp": [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, _int, _vp],
     "nrm_bench_copy": [_vp, _vp, _i64, _vp],
     "nrm_last_error": [],
     "nrm_status_name": [_int],
@@ -407,6 +417,93 @@ def rope_freqs_su(dims, base, long_factor, max_position=131072, original_max=409
         raise ValueError(f"long_factor must hold {dims // 2} values, got {list(lf.shape)}")
     return _host_freqs(load().nrm_rope_freqs_su, dims, base, ctypes.c_void_p(lf.data_ptr()),
                        max_position, original_max)
+
+
+def softmax(x, out=None):
+    """Softmax over the last axis (nrm_softmax); ``out`` may be ``x``."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    rows, n = _rows(x)
+    out = _out_like(out, x, "out")
+    st = load().nrm_softmax(_ptr(x), _ptr(out), rows, n, dt, _stream())
+    if st:
+        _raise(st)
+    return out
+
+
+def causal_softmax(x, rows, out=None):
+    """Softmax of x [..., R, L] with MLX's blocked causal mask of ``rows`` rows per block
+    (nrm_causal_softmax)."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    if x.dim() < 2:
+        raise ValueError(f"x must be [..., R, L], got {list(x.shape)}")
+    R, L = x.shape[-2], x.shape[-1]
+    N = x.numel() // (R * L) if R * L else 0
+    out = _out_like(out, x, "out")
+    st = load().nrm_causal_softmax(_ptr(x), _ptr(out), N, R, L, int(rows), dt, _stream())
+    if st:
+        _raise(st)
+    return out
+
+
+def logsumexp(x, out=None):
+    """log(sum(exp(x))) over the last axis, kept as a size-1 axis (nrm_logsumexp)."""
+    _check_act(x, "x")
+    dt = _dtype_code(x, "x")
+    rows, n = _rows(x)
+    shape = list(x.shape[:-1]) + [1]
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _check_act(out, "out", x.device)
+    if list(out.shape) != shape or out.dtype != x.dtype:
+        raise ValueError(f"out must be {x.dtype} {shape}, got {out.dtype} {list(out.shape)}")
+    st = load().nrm_logsumexp(_ptr(x), _ptr(out), rows, n, dt, _stream())
+    if st:
+        _raise(st)
+    return out
+
+
+def _ce_common(logits, targets):
+    _check_act(logits, "logits")
+    dt = _dtype_code(logits, "logits")
+    rows, V = _rows(logits)
+    _check_act(targets, "targets", logits.device)
+    if targets.dtype not in (torch.int32, torch.int64) or targets.numel() != rows:
+        raise ValueError(f"targets must hold {rows} int32 or int64 values, got "
+                         f"{targets.dtype} {list(targets.shape)}")
+    return dt, rows, V, int(targets.dtype == torch.int64)
+
+
+def cross_entropy(logits, targets, loss=None):
+    """logsumexp(logits) - logits[target] per row, float32 (nrm_cross_entropy)."""
+    dt, rows, V, i64 = _ce_common(logits, targets)
+    shape = list(logits.shape[:-1])
+    if loss is None:
+        loss = torch.empty(shape, dtype=torch.float32, device=logits.device)
+    _check_act(loss, "loss", logits.device)
+    if loss.dtype != torch.float32 or loss.numel() != rows:
+        raise ValueError(f"loss must be float32 with {rows} values")
+    st = load().nrm_cross_entropy(_ptr(logits), _ptr(targets), i64, _ptr(loss), rows, V, dt,
+                                  _stream())
+    if st:
+        _raise(st)
+    return loss
+
+
+def cross_entropy_vjp(logits, targets, g, loss=None, dlogits=None):
+    """Gradient of cross_entropy for the logits given the loss cotangent g (float32 per
+    row) (nrm_cross_entropy_vjp); ``dlogits`` may be ``logits``."""
+    dt, rows, V, i64 = _ce_common(logits, targets)
+    _check_act(g, "g", logits.device)
+    if g.dtype != torch.float32 or g.numel() != rows:
+        raise ValueError(f"g must be float32 with {rows} values")
+    dlogits = _out_like(dlogits, logits, "dlogits")
+    st = load().nrm_cross_entropy_vjp(_ptr(logits), _ptr(targets), i64, _ptr(loss), _ptr(g),
+                                      _ptr(dlogits), rows, V, dt, _stream())
+    if st:
+        _raise(st)
+    return dlogits
 
 
 def bench_copy(src, dst):

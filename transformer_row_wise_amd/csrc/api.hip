@@ -14,6 +14,7 @@
 #include "launch.hpp"
 #include "nrm.h"
 #include "rope.hpp"
+#include "softmax.hpp"
 #include "vjp.hpp"
 
 namespace {
@@ -431,6 +432,140 @@ nrm_status nrm_rope_positions(const void* q, const void* k, void* q_out, void* k
                   (!Hk || (aligned16(k) && aligned16(k_out)));
   return launched(fn, dtype == NRM_BF16 ? nrm::launch_norm_rope<true>(a, al, stream)
                                         : nrm::launch_norm_rope<false>(a, al, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+nrm::SmArgs sm_args(const void* x, void* out, int64_t rows, int64_t n) {
+  nrm::SmArgs a;
+  a.x = x; a.out = out; a.targets = nullptr; a.tgt_i64 = 0; a.g = nullptr; a.loss = nullptr;
+  a.rows = rows; a.n = n; a.causal_R = 1; a.causal_rows = 1; a.team = 64;
+  return a;
+}
+
+template <int OP>
+hipError_t dispatch_sm(const nrm::SmArgs& a, nrm_dtype dtype, bool al, hipStream_t s) {
+  return dtype == NRM_BF16 ? nrm::launch_softmax<true, OP>(a, al, s)
+                           : nrm::launch_softmax<false, OP>(a, al, s);
+}
+
+// Shared checks of the softmax family: dtype, rows >= 0, 1 <= n < 2^31, no overflow.
+nrm_status check_sm(const char* fn, int64_t rows, int64_t n, nrm_dtype dtype) {
+  nrm_status st = check_dtypes(fn, dtype, dtype);
+  if (st) return st;
+  return check_rows(fn, rows, n, dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+nrm_status nrm_softmax(const void* x, void* out, int64_t rows, int64_t n, nrm_dtype dtype,
+                       hipStream_t stream) {
+  static const char* fn = "nrm_softmax";
+  g_err.clear();
+  nrm_status st = check_sm(fn, rows, n, dtype);
+  if (st) return st;
+  if (rows == 0) return NRM_OK;
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  const int64_t nb = rows * n * esize(dtype);
+  if ((st = check_out_vs(fn, "out", span(out, nb), "x", span(x, nb), true))) return st;
+  return launched(fn, dispatch_sm<nrm::SM_SOFTMAX>(sm_args(x, out, rows, n), dtype,
+                                                   aligned16(x) && aligned16(out), stream));
+}
+
+nrm_status nrm_causal_softmax(const void* x, void* out, int64_t N, int64_t R, int64_t L,
+                              int64_t rows_per_block, nrm_dtype dtype, hipStream_t stream) {
+  static const char* fn = "nrm_causal_softmax";
+  g_err.clear();
+  if (N < 0) return fail(NRM_ERR_SHAPE, "%s: N must be >= 0, got %lld", fn, (long long)N);
+  if (R < 0) return fail(NRM_ERR_SHAPE, "%s: R must be >= 0, got %lld", fn, (long long)R);
+  if (rows_per_block < 1)
+    return fail(NRM_ERR_SHAPE, "%s: rows_per_block must be >= 1, got %lld", fn,
+                (long long)rows_per_block);
+  if (R % rows_per_block)
+    return fail(NRM_ERR_SHAPE, "%s: R must be a multiple of rows_per_block (%lld), got %lld", fn,
+                (long long)rows_per_block, (long long)R);
+  if (N && R > INT64_MAX / N)
+    return fail(NRM_ERR_SHAPE, "%s: N * R overflows, got %lld x %lld", fn, (long long)N,
+                (long long)R);
+  nrm_status st = check_sm(fn, N * R, L, dtype);
+  if (st) return st;
+  if (N * R == 0) return NRM_OK;
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  const int64_t nb = N * R * L * esize(dtype);
+  if ((st = check_out_vs(fn, "out", span(out, nb), "x", span(x, nb), true))) return st;
+  nrm::SmArgs a = sm_args(x, out, N * R, L);
+  a.causal_R = R;
+  a.causal_rows = rows_per_block;
+  return launched(fn, dispatch_sm<nrm::SM_CAUSAL>(a, dtype, aligned16(x) && aligned16(out),
+                                                  stream));
+}
+
+nrm_status nrm_logsumexp(const void* x, void* out, int64_t rows, int64_t n, nrm_dtype dtype,
+                         hipStream_t stream) {
+  static const char* fn = "nrm_logsumexp";
+  g_err.clear();
+  nrm_status st = check_sm(fn, rows, n, dtype);
+  if (st) return st;
+  if (rows == 0) return NRM_OK;
+  if (!x) return fail(NRM_ERR_NULL, "%s: x must not be NULL, got NULL", fn);
+  if (!out) return fail(NRM_ERR_NULL, "%s: out must not be NULL, got NULL", fn);
+  const int64_t es = esize(dtype);
+  if ((st = check_out_vs(fn, "out", span(out, rows * es), "x", span(x, rows * n * es), false)))
+    return st;
+  return launched(fn, dispatch_sm<nrm::SM_LSE>(sm_args(x, out, rows, n), dtype, aligned16(x),
+                                               stream));
+}
+
+nrm_status nrm_cross_entropy(const void* logits, const void* targets, int targets_int64,
+                             float* loss, int64_t rows, int64_t V, nrm_dtype dtype,
+                             hipStream_t stream) {
+  static const char* fn = "nrm_cross_entropy";
+  g_err.clear();
+  nrm_status st = check_sm(fn, rows, V, dtype);
+  if (st) return st;
+  if (rows == 0) return NRM_OK;
+  if (!logits) return fail(NRM_ERR_NULL, "%s: logits must not be NULL, got NULL", fn);
+  if (!targets) return fail(NRM_ERR_NULL, "%s: targets must not be NULL, got NULL", fn);
+  if (!loss) return fail(NRM_ERR_NULL, "%s: loss must not be NULL, got NULL", fn);
+  const Span sx = span(logits, rows * V * esize(dtype));
+  const Span st_ = span(targets, rows * (targets_int64 ? 8 : 4)), sl = span(loss, rows * 4);
+  if ((st = check_out_vs(fn, "loss", sl, "logits", sx, false))) return st;
+  if ((st = check_out_vs(fn, "loss", sl, "targets", st_, false))) return st;
+  nrm::SmArgs a = sm_args(logits, nullptr, rows, V);
+  a.targets = targets; a.tgt_i64 = targets_int64 != 0; a.loss = loss;
+  return launched(fn, dispatch_sm<nrm::SM_CE>(a, dtype, aligned16(logits), stream));
+}
+
+nrm_status nrm_cross_entropy_vjp(const void* logits, const void* targets, int targets_int64,
+                                 const float* loss, const float* g, void* dlogits,
+                                 int64_t rows, int64_t V, nrm_dtype dtype, hipStream_t stream) {
+  static const char* fn = "nrm_cross_entropy_vjp";
+  g_err.clear();
+  (void)loss;  // not needed: see nrm.h
+  nrm_status st = check_sm(fn, rows, V, dtype);
+  if (st) return st;
+  if (rows == 0) return NRM_OK;
+  if (!logits) return fail(NRM_ERR_NULL, "%s: logits must not be NULL, got NULL", fn);
+  if (!targets) return fail(NRM_ERR_NULL, "%s: targets must not be NULL, got NULL", fn);
+  if (!g) return fail(NRM_ERR_NULL, "%s: g must not be NULL, got NULL", fn);
+  if (!dlogits) return fail(NRM_ERR_NULL, "%s: dlogits must not be NULL, got NULL", fn);
+  const int64_t nb = rows * V * esize(dtype);
+  const Span sx = span(logits, nb), sd = span(dlogits, nb);
+  const Span st_ = span(targets, rows * (targets_int64 ? 8 : 4)), sg = span(g, rows * 4);
+  if ((st = check_out_vs(fn, "dlogits", sd, "logits", sx, true))) return st;
+  if ((st = check_out_vs(fn, "dlogits", sd, "targets", st_, false))) return st;
+  if ((st = check_out_vs(fn, "dlogits", sd, "g", sg, false))) return st;
+  nrm::SmArgs a = sm_args(logits, dlogits, rows, V);
+  a.targets = targets; a.tgt_i64 = targets_int64 != 0; a.g = g;
+  return launched(fn, dispatch_sm<nrm::SM_CE_VJP>(a, dtype,
+                                                  aligned16(logits) && aligned16(dlogits),
+                                                  stream));
 }
 
 const char* nrm_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,409 @@
+// Softmax family over the last axis: Softmax, CausalSoftmax, LogSumExp, CrossEntropy and its
+// gradient for the logits.
+//
+// Sources: nuvec-core 0.5.0 fast::FastOp, variants Softmax ((x): softmax over the last axis,
+// accumulated in float32), CausalSoftmax ((x), field rows: row r of the second-to-last axis
+// keeps the columns c <= r % rows + L - rows, the others become the dtype's lowest finite
+// value and so 0), LogSumExp ((x): log(sum(exp(x))), the last axis becomes size 1),
+// CrossEntropy ((logits, targets): logsumexp(logits) - logits[target] per row, float32) and
+// CrossEntropyVjp ((logits, targets, loss, g): its gradient for the logits).
+//
+// Arithmetic: fp32 throughout (the pages' float32 accumulation). Per row, m = max and
+// S = sum exp(x - m) over the row; exp(t) = 2^(t log2 e) on the hardware exp2, with the
+// argument shifted up by 64 and the result scaled by 2^-64 where it would fall below the
+// normal range (so tiny probabilities keep their subnormal values). Cross-entropy keeps the
+// target's term apart: with e_t = exp(x_t - m) and R = the sum over the other columns,
+//   loss = log1p(R / e_t)                      (= logsumexp - x_t, no cancellation)
+//   d loss / d x_t = -R / (R + e_t),   d loss / d x_j = exp(x_j - m) / (R + e_t)
+// so a confident row (loss near 0) still gets its small loss and gradient to full relative
+// precision; the gradient is then scaled by g. The loss input of the gradient is not needed
+// (the row is read anyway) and is not read. A target outside [0, V) gives NaN.
+//
+// sm_rows: a team of T threads per row (T a multiple of 64, at most 1024), G = blockDim / T
+// teams per block, each thread keeping NV 16-byte chunks of its row in registers: the row is
+// read from HBM once, then max, sum and output passes run over registers. Rows of up to
+// 16 * 1024 chunks (131072 bf16 or 65536 fp32 values) take it.
+// sm_stream: 256 threads per row looping over the row in chunks (16-byte or single
+// elements), an online (max, sum) per thread (the sum rescaled when the maximum grows), then
+// a second pass over the row for the outputs: any width.
+#include "softmax.hpp"
+
+namespace nrm {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp(t) for t <= 0 (or NaN), fp32.
+__device__ __forceinline__ float sm_exp(float t) {
+  const float y = t * kLog2e;
+  const bool tiny = y < -126.0f;
+  const float r = __builtin_amdgcn_exp2f(tiny ? y + 64.0f : y);
+  return tiny ? r * 5.421010862427522e-20f : r;  // 2^-64
+}
+
+__device__ __forceinline__ float lowest_of(bool bf16) {
+  return bf16 ? -3.3895313892515355e38f : -3.4028234663852886e38f;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) { return dpp<CTRL>(v); }
+
+// Max or sum over a wave, returned wave-uniform (DPP in each row of 16, then the four row
+// results read with readlane and combined in a fixed order).
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = op(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = op(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = op(v, dpp_f<DPP_ROW_MIRROR>(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
+// Max or sum over a team of nwt waves starting at wave0; red holds one slot per wave of the
+// block. Every team of the block calls this the same number of times (one barrier each).
+template <bool MAX>
+__device__ __forceinline__ float team_reduce(float v, float* red, int wave0, int nwt) {
+  v = wave_reduce<MAX>(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[wave0];
+  for (int q = 1; q < nwt; ++q) t = MAX ? fmaxf(t, red[wave0 + q]) : t + red[wave0 + q];
+  return t;
+}
+
+// Per-row context shared by both kernels.
+struct SmRow {
+  int64_t row;
+  int64_t cut;     // CAUSAL: last kept column (may be negative); others: n - 1
+  int64_t target;  // CE: target column, or -1 when out of range
+  bool bad;        // CE: target out of range
+  float g;         // CE_VJP: cotangent
+};
+
+template <int OP>
+__device__ __forceinline__ SmRow sm_row(const SmArgs& a, int64_t row) {
+  SmRow r;
+  r.row = row;
+  r.cut = a.n - 1;
+  if constexpr (OP == SM_CAUSAL) {
+    const int64_t rr = (row % a.causal_R) % a.causal_rows;
+    r.cut = rr + a.n - a.causal_rows;
+  }
+  r.target = -1;
+  r.bad = false;
+  r.g = 1.f;
+  if constexpr (OP == SM_CE || OP == SM_CE_VJP) {
+    const int64_t t = a.tgt_i64 ? ((const int64_t*)a.targets)[row]
+                                : (int64_t)((const int32_t*)a.targets)[row];
+    r.bad = t < 0 || t >= a.n;
+    r.target = r.bad ? -1 : t;
+  }
+  if constexpr (OP == SM_CE_VJP) r.g = a.g[row];
+  return r;
+}
+
+// log(sum exp(x)) from the row's maximum m and S = sum exp(x - m); an infinite maximum is
+// the result itself (+inf: some score is +inf; -inf: every score is -inf, the sum is 0).
+__device__ __forceinline__ float lse_of(float m, float s) {
+  if (__builtin_isinf(m)) return m;
+  return m + __builtin_amdgcn_logf(s) * 0.6931471805599453f;
+}
+
+// The loss from the row's maximum m, the target's logit x_t, e_t = exp(x_t - m) and the sum
+// R of the other columns' exponentials.
+__device__ __forceinline__ float ce_loss(float m, float x_t, float e_t, float rest) {
+  if (m - x_t < 60.f) return log1pf(rest / e_t);
+  return (m - x_t) + logf(rest + e_t);
+}
+
+}  // namespace
+
+template <bool BF16, int OP, int NV, bool EXACT>
+__global__ void __launch_bounds__(1024)
+sm_rows(SmArgs a) {
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr bool CE = OP == SM_CE || OP == SM_CE_VJP;
+  __shared__ float red_m[16], red_s[16], xt_s[8];
+  const int T = a.team;
+  const int team = threadIdx.x / T;
+  const int tid = threadIdx.x - team * T;
+  const int nwt = T >> 6, wave0 = team * nwt;
+  const int nvec = (int)(a.n / V);
+  const int64_t row_raw = (int64_t)blockIdx.x * (blockDim.x / T) + team;
+  const bool live = row_raw < a.rows;
+  const int64_t row = live ? row_raw : a.rows - 1;
+  const SmRow r = sm_row<OP>(a, row);
+  const float lowest = lowest_of(BF16);
+
+  // Chunk k of this thread is chunk tid + k * T of the row; past the row's end (only when
+  // not EXACT) its loads are clamped to the last chunk and its results dropped. Indices are
+  // recomputed where used rather than kept in registers.
+  auto chunk = [&](int k) { return tid + k * T; };
+  auto ok = [&](int k) { return EXACT || chunk(k) < nvec; };
+  const int cut = (int)r.cut;
+  // The target's chunk and its element within the chunk (team-uniform): per chunk one
+  // vector compare says whether this thread owns it, per element a scalar compare.
+  const int tgt_chunk = r.target < 0 ? -1 : (int)(r.target / V);
+  const int tgt_e = r.target < 0 ? -1 : (int)(r.target % V);
+  auto is_tgt = [&](int k, int e) { return e == tgt_e && chunk(k) == tgt_chunk; };
+  const char* xr = (const char*)a.x + row * a.n * ESZ;
+  u32x4 xv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    xv[k] = ld16_nt(xr + (int64_t)(EXACT ? chunk(k) : min(chunk(k), nvec - 1)) * 16);
+
+  // Score of element e of chunk k as the operation sees it (masked, or -inf when absent).
+  auto score = [&](int k, int e, float f) {
+    if (!ok(k)) return -__builtin_inff();
+    if constexpr (OP == SM_CAUSAL) return chunk(k) * V + e <= cut ? f : lowest;
+    return f;
+  };
+
+  float m = -__builtin_inff();
+  float xt = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float f[V];
+    unpack<BF16>(xv[k], f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float v = score(k, e, f[e]);
+      m = fmaxf(m, v);
+      if constexpr (CE) {
+        // The one thread that holds the target's logit publishes it; the barrier of the
+        // maximum's reduction orders the write before every read.
+        if (is_tgt(k, e)) xt_s[team] = f[e];
+      }
+    }
+  }
+  m = team_reduce<true>(m, red_m, wave0, nwt);
+  if constexpr (CE) xt = r.bad ? 0.f : xt_s[team];
+  // A row whose every score is NaN-free and -inf (only with -inf inputs) keeps m = -inf;
+  // exp(x - m) is then NaN, as exp(-inf + inf) is in the definition.
+
+  // Each pass widens the raw chunks again: the opaque redefinition keeps the compiler from
+  // holding a previous pass's widened values (two floats per bf16 pair) across the barrier.
+#pragma unroll
+  for (int k = 0; k < NV; ++k) __asm__ volatile("" : "+v"(xv[k]));
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float f[V];
+    unpack<BF16>(xv[k], f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float v = score(k, e, f[e]);
+      float ex = sm_exp(v - m);
+      if (!ok(k)) ex = 0.f;
+      if constexpr (CE) {
+        if (is_tgt(k, e)) ex = 0.f;  // R excludes the target
+      }
+      s += ex;
+    }
+  }
+  s = team_reduce<false>(s, red_s, wave0, nwt);
+
+  if constexpr (OP == SM_LSE) {
+    if (live && tid == 0) {
+      float o[1] = {lse_of(m, s)};
+      store_act<BF16, 1>(a.out, row, o);
+    }
+    return;
+  }
+  if constexpr (OP == SM_CE) {
+    if (live && tid == 0) {
+      const float e_t = sm_exp(xt - m);
+      a.loss[row] = r.bad ? __builtin_nanf("") : ce_loss(m, xt, e_t, s);
+    }
+    return;
+  }
+  // Softmax, CausalSoftmax, CrossEntropyVjp: the output row.
+  float inv, gt = 0.f;
+  if constexpr (OP == SM_CE_VJP) {
+    const float e_t = sm_exp(xt - m);
+    const float tot = s + e_t;
+    inv = r.g / tot;
+    gt = -r.g * (s / tot);  // d loss / d x_t, times g
+    if (r.bad) inv = gt = __builtin_nanf("");
+  } else {
+    inv = 1.f / s;
+  }
+  if (!live) return;
+  char* orow = (char*)a.out + row * a.n * ESZ;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) __asm__ volatile("" : "+v"(xv[k]));
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float f[V];
+    unpack<BF16>(xv[k], f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float v = score(k, e, f[e]);
+      float p = sm_exp(v - m) * inv;
+      if constexpr (OP == SM_CE_VJP) {
+        if (is_tgt(k, e)) p = gt;
+      }
+      f[e] = p;
+    }
+    if (ok(k)) st16_nt(orow + (int64_t)chunk(k) * 16, pack<BF16>(f));
+  }
+}
+
+template <bool BF16, int OP, int V>
+__global__ void __launch_bounds__(256)
+sm_stream(SmArgs a) {
+  constexpr bool CE = OP == SM_CE || OP == SM_CE_VJP;
+  __shared__ float red_m[4], red_s[4], xt_s[1];
+  const int64_t row = blockIdx.x;
+  const SmRow r = sm_row<OP>(a, row);
+  const float lowest = lowest_of(BF16);
+  const int64_t nch = a.n / V;
+  const int64_t e0 = row * a.n;
+  auto score = [&](int64_t c, float f) {
+    if constexpr (OP == SM_CAUSAL) return c <= r.cut ? f : lowest;
+    return f;
+  };
+  // Pass 1: online maximum and rescaled sum per thread (while a thread's maximum is still
+  // -inf every score it has seen is -inf, and contributes 0).
+  float m = -__builtin_inff(), s = 0.f, xt = 0.f;
+  for (int64_t j = threadIdx.x; j < nch; j += 256) {
+    float f[V];
+    load_act<BF16, V>(a.x, e0 + j * V, f);
+    float cm = m;
+#pragma unroll
+    for (int e = 0; e < V; ++e) cm = fmaxf(cm, score(j * V + e, f[e]));
+    if (cm > m) {
+      s = s * sm_exp(m - cm);
+      m = cm;
+    }
+    const float mm = m == -__builtin_inff() ? 0.f : m;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int64_t c = j * V + e;
+      float ex = sm_exp(score(c, f[e]) - mm);
+      if constexpr (CE) {
+        if (c == r.target) {
+          xt_s[0] = f[e];  // published by the barrier of the maximum's reduction
+          ex = 0.f;
+        }
+      }
+      s += ex;
+    }
+  }
+  const float M = team_reduce<true>(m, red_m, 0, 4);
+  if constexpr (CE) xt = r.bad ? 0.f : xt_s[0];
+  // Rescale each thread's sum to the row maximum, then add in a fixed order.
+  const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_exp(m - M), red_s, 0, 4);
+
+  if constexpr (OP == SM_LSE) {
+    if (threadIdx.x == 0) {
+      float o[1] = {lse_of(M, S)};
+      store_act<BF16, 1>(a.out, row, o);
+    }
+    return;
+  }
+  if constexpr (OP == SM_CE) {
+    if (threadIdx.x == 0)
+      a.loss[row] = r.bad ? __builtin_nanf("") : ce_loss(M, xt, sm_exp(xt - M), S);
+    return;
+  }
+  float inv, gt = 0.f;
+  if constexpr (OP == SM_CE_VJP) {
+    const float e_t = sm_exp(xt - M);
+    const float tot = S + e_t;
+    inv = r.g / tot;
+    gt = -r.g * (S / tot);
+    if (r.bad) inv = gt = __builtin_nanf("");
+  } else {
+    inv = 1.f / S;
+  }
+  // Pass 2: each thread re-reads the chunks it read in pass 1 (so in-place use is safe).
+  for (int64_t j = threadIdx.x; j < nch; j += 256) {
+    float f[V];
+    load_act<BF16, V>(a.x, e0 + j * V, f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int64_t c = j * V + e;
+      float p = sm_exp(score(c, f[e]) - M) * inv;
+      if constexpr (OP == SM_CE_VJP) {
+        if (c == r.target) p = gt;
+      }
+      f[e] = p;
+    }
+    store_act<BF16, V>(a.out, e0 + j * V, f);
+  }
+}
+
+namespace {
+
+constexpr int64_t kSmMaxGrid = 0x7fffffff;
+
+template <bool BF16, int OP, int NV, bool EXACT>
+hipError_t go_sm_rows(const SmArgs& a0, int team, hipStream_t stream) {
+  SmArgs a = a0;
+  a.team = team;
+  const int G = std::max(1, std::min(8, 1024 / team));
+  const int64_t blocks = (a.rows + G - 1) / G;
+  if (blocks > kSmMaxGrid) return hipErrorInvalidConfiguration;
+  sm_rows<BF16, OP, NV, EXACT><<<(unsigned)blocks, G * team, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int OP, int NV>
+hipError_t sm_exact(const SmArgs& a, int team, bool exact, hipStream_t stream) {
+  return exact ? go_sm_rows<BF16, OP, NV, true>(a, team, stream)
+               : go_sm_rows<BF16, OP, NV, false>(a, team, stream);
+}
+
+template <bool BF16, int OP, int V>
+hipError_t go_sm_stream(const SmArgs& a, hipStream_t stream) {
+  if (a.rows > kSmMaxGrid) return hipErrorInvalidConfiguration;
+  sm_stream<BF16, OP, V><<<(unsigned)a.rows, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <bool BF16, int OP>
+hipError_t launch_softmax(const SmArgs& a, bool aligned16, hipStream_t stream) {
+  constexpr int V = Fmt<BF16>::VEC;
+  const int path = forced_path();
+  const bool vec = aligned16 && a.n % V == 0 && path != PATH_SCALAR;
+  if (!vec) return go_sm_stream<BF16, OP, 1>(a, stream);
+  if (path != PATH_CHUNKED) {
+    const int64_t n = a.n / V;
+    int nv = 1;
+    while (nv <= 16 && (n + nv - 1) / nv > 1024) nv *= 2;
+    if (nv <= 16) {
+      const int team = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
+      const bool exact = (int64_t)team * nv == n;
+      switch (nv) {
+        case 1: return sm_exact<BF16, OP, 1>(a, team, exact, stream);
+        case 2: return sm_exact<BF16, OP, 2>(a, team, exact, stream);
+        case 4: return sm_exact<BF16, OP, 4>(a, team, exact, stream);
+        case 8: return sm_exact<BF16, OP, 8>(a, team, exact, stream);
+        default: return sm_exact<BF16, OP, 16>(a, team, exact, stream);
+      }
+    }
+  }
+  return go_sm_stream<BF16, OP, V>(a, stream);
+}
+
+#define NRM_SM_INST(OP)                                                                     \
+  template hipError_t launch_softmax<true, OP>(const SmArgs&, bool, hipStream_t);          \
+  template hipError_t launch_softmax<false, OP>(const SmArgs&, bool, hipStream_t);
+NRM_SM_INST(SM_SOFTMAX)
+NRM_SM_INST(SM_CAUSAL)
+NRM_SM_INST(SM_LSE)
+NRM_SM_INST(SM_CE)
+NRM_SM_INST(SM_CE_VJP)
+#undef NRM_SM_INST
+
+}  // namespace nrm

@@ -224,3 +224,37 @@ ROPE_QK_BASE = 500000.0
 def cfg_rope_qk_bf16(seed=0):
     T, Hq, Hk, D = ROPE_QK_SHAPE
     return rope_qk_inputs(T, Hq, Hk, D, "bf16", seed=seed)
+
+
+# Softmax-family workloads: scores of one attention layer's prefill ([8 * 32 heads, 512, 512]
+# bf16, N(0, 3)) for the causal softmax; a [16384, 8192] bf16 softmax; and the language-model
+# head's loss over a Llama-3-sized vocabulary: logits [4096, 128256] bf16 ~ N(0, 2), targets
+# uniform over the vocabulary, loss cotangent 1 / 4096 (a mean over the rows).
+CE_SHAPE = (4096, 128256)
+
+
+@dataclasses.dataclass
+class CEInputs:
+    logits: torch.Tensor
+    targets: torch.Tensor   # int64
+    g: torch.Tensor         # float32 loss cotangent per row
+
+
+def ce_inputs(rows, V, dtype, *, seed=0, std=2.0, g="mean"):
+    """logits ~ N(0, std) then targets ~ U{0 .. V-1}, then g (1 / rows, or ~ N(0, 1))."""
+    rng = np.random.default_rng(seed)
+    x64 = rng.normal(0.0, std, size=(rows, V))
+    t = rng.integers(0, V, size=rows, dtype=np.int64)
+    g64 = np.full(rows, 1.0 / rows) if g == "mean" else rng.standard_normal(rows)
+    return CEInputs(logits=cast(x64, dtype), targets=torch.from_numpy(t),
+                    g=torch.from_numpy(g64.astype(np.float32)))
+
+
+def cfg_ce_bf16(seed=0):
+    return ce_inputs(*CE_SHAPE, "bf16", seed=seed)
+
+
+def scores(shape, dtype, *, seed=0, std=3.0):
+    """Attention-like scores ~ N(0, std)."""
+    rng = np.random.default_rng(seed)
+    return cast(rng.normal(0.0, std, size=shape), dtype)
