@@ -19,13 +19,17 @@
 // precision; the gradient is then scaled by g. The loss input of the gradient is not needed
 // (the row is read anyway) and is not read. A target outside [0, V) gives NaN.
 //
-// sm_rows: a team of T threads per row (T a multiple of 64, at most 1024), G = blockDim / T
-// teams per block, each thread keeping NV 16-byte chunks of its row in registers: the row is
-// read from HBM once, then max, sum and output passes run over registers. Rows of up to
-// 16 * 1024 chunks (131072 bf16 or 65536 fp32 values) take it.
-// sm_stream: 256 threads per row looping over the row in chunks (16-byte or single
-// elements), an online (max, sum) per thread (the sum rescaled when the maximum grows), then
-// a second pass over the row for the outputs: any width.
+// sm_rows: a team of T threads per row, each thread keeping NV 16-byte chunks of the row in
+// registers: the row is read from HBM once, then max, sum and output passes run over
+// registers. T is 16 or 32 lanes (SUB: the team's reductions are DPP exchanges inside a
+// wave, no barrier) or a multiple of 64 (reductions through LDS, one barrier each); NV is at
+// least 4 where the row allows, so that every thread keeps 64 bytes in flight. Rows of up
+// to 2048 chunks (16384 bf16 or 8192 fp32 values) take it.
+// sm_stream: 256 threads per row looping over the row, U = 4 chunks (16-byte or single
+// elements) per step loaded together, an online (max, sum) per thread (the sum rescaled when
+// the maximum grows), then, for the operations with a row output, a second pass over the
+// row (which the first pass left in the caches where it fits). Any width; the vocabulary-
+// sized rows of the loss (128256 columns) take it at 8 blocks per compute unit.
 #include "softmax.hpp"
 
 namespace nrm {
@@ -77,6 +81,19 @@ __device__ __forceinline__ float team_reduce(float v, float* red, int wave0, int
   return t;
 }
 
+// Max or sum over aligned groups of G lanes (G = 16 or 32) of a wave; every lane of a
+// group gets the same bits (each exchange pairs lanes symmetrically).
+template <bool MAX, int G>
+__device__ __forceinline__ float group_reduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = op(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = op(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = op(v, dpp_f<DPP_ROW_MIRROR>(v));
+  if constexpr (G == 32) v = op(v, __shfl_xor(v, 16, 64));
+  return v;
+}
+
 // Per-row context shared by both kernels.
 struct SmRow {
   int64_t row;
@@ -124,23 +141,31 @@ __device__ __forceinline__ float ce_loss(float m, float x_t, float e_t, float re
 
 }  // namespace
 
-template <bool BF16, int OP, int NV, bool EXACT>
+template <bool BF16, int OP, int NV, bool EXACT, int SUB>
 __global__ void __launch_bounds__(1024)
 sm_rows(SmArgs a) {
   constexpr int V = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr bool CE = OP == SM_CE || OP == SM_CE_VJP;
-  __shared__ float red_m[16], red_s[16], xt_s[8];
-  const int T = a.team;
+  __shared__ float red_m[16], red_s[16], xt_s[64];
+  const int T = SUB ? SUB : a.team;
   const int team = threadIdx.x / T;
   const int tid = threadIdx.x - team * T;
-  const int nwt = T >> 6, wave0 = team * nwt;
+  const int nwt = SUB ? 1 : T >> 6, wave0 = SUB ? 0 : team * nwt;
   const int nvec = (int)(a.n / V);
   const int64_t row_raw = (int64_t)blockIdx.x * (blockDim.x / T) + team;
   const bool live = row_raw < a.rows;
   const int64_t row = live ? row_raw : a.rows - 1;
   const SmRow r = sm_row<OP>(a, row);
   const float lowest = lowest_of(BF16);
+  auto reduce_max = [&](float v) {
+    if constexpr (SUB) return group_reduce<true, SUB>(v);
+    else return team_reduce<true>(v, red_m, wave0, nwt);
+  };
+  auto reduce_sum = [&](float v) {
+    if constexpr (SUB) return group_reduce<false, SUB>(v);
+    else return team_reduce<false>(v, red_s, wave0, nwt);
+  };
 
   // Chunk k of this thread is chunk tid + k * T of the row; past the row's end (only when
   // not EXACT) its loads are clamped to the last chunk and its results dropped. Indices are
@@ -174,19 +199,27 @@ sm_rows(SmArgs a) {
     unpack<BF16>(xv[k], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const float v = score(k, e, f[e]);
-      m = fmaxf(m, v);
+      m = fmaxf(m, score(k, e, f[e]));
       if constexpr (CE) {
-        // The one thread that holds the target's logit publishes it; the barrier of the
-        // maximum's reduction orders the write before every read.
-        if (is_tgt(k, e)) xt_s[team] = f[e];
+        if (is_tgt(k, e)) xt = f[e];
       }
     }
   }
-  m = team_reduce<true>(m, red_m, wave0, nwt);
-  if constexpr (CE) xt = r.bad ? 0.f : xt_s[team];
-  // A row whose every score is NaN-free and -inf (only with -inf inputs) keeps m = -inf;
-  // exp(x - m) is then NaN, as exp(-inf + inf) is in the definition.
+  if constexpr (CE) {
+    // The one thread that holds the target's logit publishes it (team slot in LDS); a
+    // barrier (block teams) or the group's own lanes (sub-wave teams) order the read.
+    if constexpr (SUB) {
+      // The owner is lane tgt_chunk % SUB of this team's lanes of the wave.
+      const int base = (threadIdx.x & 63) - tid;
+      xt = __shfl(xt, base + (tgt_chunk < 0 ? 0 : tgt_chunk % SUB), 64);
+    } else {
+      if (tgt_chunk >= 0 && tgt_chunk % T == tid) xt_s[team] = xt;
+    }
+  }
+  m = reduce_max(m);
+  if constexpr (CE && !SUB) xt = r.bad ? 0.f : xt_s[team];
+  // A row whose scores are all -inf keeps m = -inf; exp(x - m) is then NaN, as
+  // exp(-inf + inf) is in the definition.
 
   // Each pass widens the raw chunks again: the opaque redefinition keeps the compiler from
   // holding a previous pass's widened values (two floats per bf16 pair) across the barrier.
@@ -199,8 +232,7 @@ sm_rows(SmArgs a) {
     unpack<BF16>(xv[k], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const float v = score(k, e, f[e]);
-      float ex = sm_exp(v - m);
+      float ex = sm_exp(score(k, e, f[e]) - m);
       if (!ok(k)) ex = 0.f;
       if constexpr (CE) {
         if (is_tgt(k, e)) ex = 0.f;  // R excludes the target
@@ -208,7 +240,7 @@ sm_rows(SmArgs a) {
       s += ex;
     }
   }
-  s = team_reduce<false>(s, red_s, wave0, nwt);
+  s = reduce_sum(s);
 
   if constexpr (OP == SM_LSE) {
     if (live && tid == 0) {
@@ -245,8 +277,7 @@ sm_rows(SmArgs a) {
     unpack<BF16>(xv[k], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const float v = score(k, e, f[e]);
-      float p = sm_exp(v - m) * inv;
+      float p = sm_exp(score(k, e, f[e]) - m) * inv;
       if constexpr (OP == SM_CE_VJP) {
         if (is_tgt(k, e)) p = gt;
       }
@@ -260,6 +291,8 @@ template <bool BF16, int OP, int V>
 __global__ void __launch_bounds__(256)
 sm_stream(SmArgs a) {
   constexpr bool CE = OP == SM_CE || OP == SM_CE_VJP;
+  constexpr int U = 4;  // chunks loaded together per step
+  constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CAUSAL || OP == SM_CE_VJP;
   __shared__ float red_m[4], red_s[4], xt_s[1];
   const int64_t row = blockIdx.x;
   const SmRow r = sm_row<OP>(a, row);
@@ -271,33 +304,57 @@ sm_stream(SmArgs a) {
     return f;
   };
   // Pass 1: online maximum and rescaled sum per thread (while a thread's maximum is still
-  // -inf every score it has seen is -inf, and contributes 0).
-  float m = -__builtin_inff(), s = 0.f, xt = 0.f;
-  for (int64_t j = threadIdx.x; j < nch; j += 256) {
-    float f[V];
-    load_act<BF16, V>(a.x, e0 + j * V, f);
+  // -inf every score it has seen is -inf, and contributes 0). Each step loads U chunks
+  // (clamped to the row, unconditional) before using any.
+  float m = -__builtin_inff(), s = 0.f;
+  for (int64_t j0 = threadIdx.x; j0 < nch; j0 += 256 * U) {
+    float f[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = min(j0 + (int64_t)u * 256, nch - 1);
+      if constexpr (V == Fmt<BF16>::VEC) {
+        const void* p = (const char*)a.x + (e0 + j * V) * Fmt<BF16>::ESZ;
+        // Rows with an output pass are read with cached loads, so that the second read
+        // of this block's row finds it in the caches.
+        unpack<BF16>(OUT ? ld16(p) : ld16_nt(p), f[u]);
+      } else {
+        load_act<BF16, V>(a.x, e0 + j * V, f[u]);
+      }
+    }
     float cm = m;
 #pragma unroll
-    for (int e = 0; e < V; ++e) cm = fmaxf(cm, score(j * V + e, f[e]));
+    for (int u = 0; u < U; ++u) {
+      if (j0 + (int64_t)u * 256 < nch) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) cm = fmaxf(cm, score((j0 + u * 256) * V + e, f[u][e]));
+      }
+    }
     if (cm > m) {
       s = s * sm_exp(m - cm);
       m = cm;
     }
     const float mm = m == -__builtin_inff() ? 0.f : m;
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const int64_t c = j * V + e;
-      float ex = sm_exp(score(c, f[e]) - mm);
-      if constexpr (CE) {
-        if (c == r.target) {
-          xt_s[0] = f[e];  // published by the barrier of the maximum's reduction
-          ex = 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + (int64_t)u * 256;
+      if (j < nch) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int64_t c = j * V + e;
+          float ex = sm_exp(score(c, f[u][e]) - mm);
+          if constexpr (CE) {
+            if (c == r.target) {
+              xt_s[0] = f[u][e];  // published by the barrier of the maximum's reduction
+              ex = 0.f;
+            }
+          }
+          s += ex;
         }
       }
-      s += ex;
     }
   }
   const float M = team_reduce<true>(m, red_m, 0, 4);
+  float xt = 0.f;
   if constexpr (CE) xt = r.bad ? 0.f : xt_s[0];
   // Rescale each thread's sum to the row maximum, then add in a fixed order.
   const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_exp(m - M), red_s, 0, 4);
@@ -324,20 +381,39 @@ sm_stream(SmArgs a) {
   } else {
     inv = 1.f / S;
   }
-  // Pass 2: each thread re-reads the chunks it read in pass 1 (so in-place use is safe).
-  for (int64_t j = threadIdx.x; j < nch; j += 256) {
-    float f[V];
-    load_act<BF16, V>(a.x, e0 + j * V, f);
+  // Pass 2: each thread re-reads exactly the chunks it read in pass 1 (so in-place use is
+  // safe: no thread writes a chunk another thread still has to read).
+  for (int64_t j0 = threadIdx.x; j0 < nch; j0 += 256 * U) {
+    float f[U][V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const int64_t c = j * V + e;
-      float p = sm_exp(score(c, f[e]) - M) * inv;
-      if constexpr (OP == SM_CE_VJP) {
-        if (c == r.target) p = gt;
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = min(j0 + (int64_t)u * 256, nch - 1);
+      if constexpr (V == Fmt<BF16>::VEC) {
+        unpack<BF16>(ld16_nt((const char*)a.x + (e0 + j * V) * Fmt<BF16>::ESZ), f[u]);
+      } else {
+        load_act<BF16, V>(a.x, e0 + j * V, f[u]);
       }
-      f[e] = p;
     }
-    store_act<BF16, V>(a.out, e0 + j * V, f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + (int64_t)u * 256;
+      if (j < nch) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int64_t c = j * V + e;
+          float p = sm_exp(score(c, f[u][e]) - M) * inv;
+          if constexpr (OP == SM_CE_VJP) {
+            if (c == r.target) p = gt;
+          }
+          f[u][e] = p;
+        }
+        if constexpr (V == Fmt<BF16>::VEC) {
+          st16_nt((char*)a.out + (e0 + j * V) * Fmt<BF16>::ESZ, pack<BF16>(f[u]));
+        } else {
+          store_act<BF16, V>(a.out, e0 + j * V, f[u]);
+        }
+      }
+    }
   }
 }
 
@@ -345,21 +421,28 @@ namespace {
 
 constexpr int64_t kSmMaxGrid = 0x7fffffff;
 
-template <bool BF16, int OP, int NV, bool EXACT>
+template <bool BF16, int OP, int NV, bool EXACT, int SUB>
 hipError_t go_sm_rows(const SmArgs& a0, int team, hipStream_t stream) {
   SmArgs a = a0;
   a.team = team;
-  const int G = std::max(1, std::min(8, 1024 / team));
+  const int threads = team >= 256 ? team : 256;
+  const int G = threads / team;
   const int64_t blocks = (a.rows + G - 1) / G;
   if (blocks > kSmMaxGrid) return hipErrorInvalidConfiguration;
-  sm_rows<BF16, OP, NV, EXACT><<<(unsigned)blocks, G * team, 0, stream>>>(a);
+  sm_rows<BF16, OP, NV, EXACT, SUB><<<(unsigned)blocks, threads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <bool BF16, int OP, int NV>
-hipError_t sm_exact(const SmArgs& a, int team, bool exact, hipStream_t stream) {
-  return exact ? go_sm_rows<BF16, OP, NV, true>(a, team, stream)
-               : go_sm_rows<BF16, OP, NV, false>(a, team, stream);
+hipError_t sm_team(const SmArgs& a, int team, bool exact, hipStream_t stream) {
+  if (team == 16)
+    return exact ? go_sm_rows<BF16, OP, NV, true, 16>(a, 16, stream)
+                 : go_sm_rows<BF16, OP, NV, false, 16>(a, 16, stream);
+  if (team == 32)
+    return exact ? go_sm_rows<BF16, OP, NV, true, 32>(a, 32, stream)
+                 : go_sm_rows<BF16, OP, NV, false, 32>(a, 32, stream);
+  return exact ? go_sm_rows<BF16, OP, NV, true, 0>(a, team, stream)
+               : go_sm_rows<BF16, OP, NV, false, 0>(a, team, stream);
 }
 
 template <bool BF16, int OP, int V>
@@ -371,26 +454,29 @@ hipError_t go_sm_stream(const SmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Register kernel for rows of up to 2048 chunks: NV = ceil(chunks / 256) (at most 8), raised
+// towards 4 as far as the team keeps 16 lanes; T = ceil(chunks / NV), rounded up to 16, 32
+// or a multiple of 64. Longer rows and unaligned rows: the streaming kernel.
 template <bool BF16, int OP>
 hipError_t launch_softmax(const SmArgs& a, bool aligned16, hipStream_t stream) {
   constexpr int V = Fmt<BF16>::VEC;
   const int path = forced_path();
   const bool vec = aligned16 && a.n % V == 0 && path != PATH_SCALAR;
   if (!vec) return go_sm_stream<BF16, OP, 1>(a, stream);
-  if (path != PATH_CHUNKED) {
-    const int64_t n = a.n / V;
-    int nv = 1;
-    while (nv <= 16 && (n + nv - 1) / nv > 1024) nv *= 2;
-    if (nv <= 16) {
-      const int team = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
-      const bool exact = (int64_t)team * nv == n;
-      switch (nv) {
-        case 1: return sm_exact<BF16, OP, 1>(a, team, exact, stream);
-        case 2: return sm_exact<BF16, OP, 2>(a, team, exact, stream);
-        case 4: return sm_exact<BF16, OP, 4>(a, team, exact, stream);
-        case 8: return sm_exact<BF16, OP, 8>(a, team, exact, stream);
-        default: return sm_exact<BF16, OP, 16>(a, team, exact, stream);
-      }
+  const int64_t n = a.n / V;
+  if (path != PATH_CHUNKED && n <= 2048) {
+    int nv = (int)std::min<int64_t>(8, (n + 255) / 256);
+    if (nv < 4) nv = (int)std::max<int64_t>(nv, std::min<int64_t>(4, n / 16));
+    if (nv < 1) nv = 1;
+    nv = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : 8;
+    const int64_t per = (n + nv - 1) / nv;
+    const int team = per <= 16 ? 16 : per <= 32 ? 32 : (int)((per + 63) / 64 * 64);
+    const bool exact = (int64_t)team * nv == n;
+    switch (nv) {
+      case 1: return sm_team<BF16, OP, 1>(a, team, exact, stream);
+      case 2: return sm_team<BF16, OP, 2>(a, team, exact, stream);
+      case 4: return sm_team<BF16, OP, 4>(a, team, exact, stream);
+      default: return sm_team<BF16, OP, 8>(a, team, exact, stream);
     }
   }
   return go_sm_stream<BF16, OP, V>(a, stream);
