@@ -228,6 +228,46 @@ __device__ __forceinline__ double wave_sum(double v) {
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+// Sum over the 64 lanes of a wave, every lane ending with a total (the lanes need not agree
+// bit for bit; callers read a fixed lane): rotations by 4 and 8 inside each 16-lane row keep
+// a lane's index mod 4, and so do the xor-16 / xor-32 exchanges across rows.
+__device__ __forceinline__ double lanes_sum_mod4(double v) {
+  v += dpp<DPP_ROW_ROR4>(v);
+  v += dpp<DPP_ROW_ROR8>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Four fp64 row sums over a team of nwt waves, with one barrier. Within a quad of lanes the
+// four sums are transposed (lane l keeps sum l & 3 of the quad), so the rest of the wave
+// reduction handles one value per lane instead of four; each wave's four totals go to LDS
+// (red: 4 slots per wave of the block), and after the barrier lane l of every wave adds up
+// sum l & 3 of team wave l >> 2. The order of every addition is fixed: results are the same
+// on every run, and the same in every thread of the team (they are read from lanes 0..3).
+__device__ __forceinline__ void team_sum4(double (&s)[4], double* red, int wave0, int nwt) {
+  const int lane = threadIdx.x & 63;
+  const bool b = lane & 1, c = lane & 2;
+  double k0 = b ? s[1] : s[0], u0 = b ? s[0] : s[1];
+  double k1 = b ? s[3] : s[2], u1 = b ? s[2] : s[3];
+  k0 += dpp<DPP_QUAD_XOR1>(u0);  // sum b of the lane pair
+  k1 += dpp<DPP_QUAD_XOR1>(u1);  // sum 2 + b
+  double k = c ? k1 : k0;
+  const double u = c ? k0 : k1;
+  k += dpp<DPP_QUAD_XOR2>(u);    // sum lane & 3 of the quad
+  k = lanes_sum_mod4(k);         // ... of the wave
+  if (lane < 4) red[(threadIdx.x >> 6) * 4 + lane] = k;
+  __syncthreads();
+  const int w = lane >> 2;
+  double t = w < nwt ? red[(wave0 + w) * 4 + (lane & 3)] : 0.0;
+  t = lanes_sum_mod4(t);         // sum lane & 3 of the team
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = readlane_f64(t, i);
+}
+
 // rstd = 1 / sqrt(sum / n + eps), formed in fp64 from an fp32 or fp64 sum (one row scalar).
 __device__ __forceinline__ double rstd_f64(double sum, int64_t n, float eps) {
   return 1.0 / __builtin_sqrt(sum / (double)n + (double)eps);

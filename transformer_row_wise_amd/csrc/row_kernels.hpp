@@ -250,7 +250,7 @@ row_block(RowArgs a) {
   constexpr int V = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   __shared__ float red_f[16];
-  __shared__ double red_d[2][16];
+  __shared__ double red4[16 * 4];
   const int T = blockDim.x;
   const int nw = T >> 6;
   const int tid = threadIdx.x;
@@ -307,46 +307,56 @@ row_block(RowArgs a) {
       if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   } else {  // OP_LN, fp64 statistics and output arithmetic
-    // x is widened to fp64 once; the second pass turns it into x - mu in place, which the
-    // output pass reuses. Four independent accumulators shorten the dependent add chains.
+    // One pass: sum x and sum x^2 in fp64 (for bf16, x^2 is exact in fp32 and only widened),
+    // reduced together with one barrier; var = sum x^2 / n - mu^2 (fp64 keeps the
+    // cancellation harmless unless |mu| / sigma exceeds ~1e6). A constant row gets var = 0
+    // and x - mu = 0 exactly, so its output is exactly b. b (like w) is loaded before the
+    // row's statistics, kept packed when it is bf16.
     const bool has_b = a.b != nullptr;
-    double xd[NV][V];
-    double s1[4] = {0.0, 0.0, 0.0, 0.0};
+    float bv[NV][V];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (has_b) {
+        load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) bv[k][e] = 0.f;
+      }
+    }
+    double ds[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       float f[V];
       unpack<BF16>(xv[k], f);
+      if (ok[k]) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        xd[k][e] = (double)f[e];
-        if (ok[k]) s1[e & 3] += xd[k][e];
+        for (int e = 0; e < V; ++e) {
+          ds[e & 1] += (double)f[e];
+          if constexpr (BF16) ds[2 + (e & 1)] += (double)(f[e] * f[e]);
+          else ds[2 + (e & 1)] = __builtin_fma((double)f[e], (double)f[e], ds[2 + (e & 1)]);
+        }
       }
     }
-    const double mu =
-        block_row_sum((s1[0] + s1[1]) + (s1[2] + s1[3]), red_d[0], nw) / (double)a.hidden;
-    double s2[4] = {0.0, 0.0, 0.0, 0.0};
+    ds[0] += ds[1];
+    ds[1] = ds[2] + ds[3];
+    ds[2] = ds[3] = 0.0;
+    team_sum4(ds, red4, 0, nw);
+    const double inv_n = 1.0 / (double)a.hidden;
+    const double mu = ds[0] * inv_n;
+    // Clamp rounding below zero, but keep a NaN (an infinite row gives inf - inf).
+    const double v0 = ds[1] * inv_n - mu * mu;
+    const double var = v0 < 0.0 ? 0.0 : v0;
+    const double rstd = 1.0 / __builtin_sqrt(var + (double)a.eps);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        xd[k][e] -= mu;
-        if (ok[k]) s2[e & 3] = __builtin_fma(xd[k][e], xd[k][e], s2[e & 3]);
-      }
-    }
-    const double rstd = rstd_f64(block_row_sum((s2[0] + s2[1]) + (s2[2] + s2[3]), red_d[1], nw),
-                                 a.hidden, a.eps);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      float f[V], bv[V];
-      if (has_b) {
-        load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) bv[e] = 0.f;
-      }
+      u32x4 xr = xv[k];
+      __asm__ volatile("" : "+v"(xr));  // widen again rather than hold fp64 copies
+      float f[V];
+      unpack<BF16>(xr, f);
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        f[e] = f64_to_f32(__builtin_fma(xd[k][e] * rstd, (double)wv[k][e], (double)bv[e]));
+        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wv[k][e],
+                                        (double)bv[k][e]));
       if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   }
