@@ -599,6 +599,46 @@ def summarize_trace(trace_db):
     print("\n".join(L))
 
 
+SUITE_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_suite -o suite -- "
+                   "python3 bench.py --only vjp,rope,sm")
+SUITE_TRACE_MD = os.path.join(ROOT, "profiles", "suite_kernels_backward_rope_softmax.md")
+
+
+def summarize_suite_trace(trace_db):
+    """Per-kernel statistics of a kernel-trace run of the backward, rope and softmax suite
+    groups, written to profiles/suite_kernels_backward_rope_softmax.md."""
+    import re
+    import sqlite3
+
+    con = sqlite3.connect(trace_db)
+    rows = list(con.execute("select name, total_calls, average from top_kernels"))
+    mins = {n: (lo / 1000.0, hi / 1000.0) for n, lo, hi in
+            con.execute("select name, min(duration), max(duration) from kernels group by name")}
+    con.close()
+
+    def short(n):
+        n = re.sub(r"\(nrm::\w+\)$", "", n.replace("void ", ""))
+        return n if len(n) < 90 else n[:87] + "..."
+
+    L = ["# Backward, Rope and softmax-family kernels on one MI355X: kernel trace", "",
+         "`bench.py --only vjp,rope,sm` times each workload of those groups from captured HIP "
+         "graphs (cfg 6a-9e); under the profiler every kernel launch of those graphs (and of "
+         "their warm-up replays) is traced. Average durations here are per launch and "
+         "agree with the suite's per-call figures, which add the small column-sum kernel of "
+         "the backward.", "", "From the repository root, with `TMPDIR=/tmp`:", "", "```",
+         SUITE_TRACE_CMD, "python3 bench.py --summarize-suite-trace "
+         "gpurun_out/prof_suite/suite_results.db", "```", "",
+         "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for name, calls, avg in rows:
+        if not name.startswith("void nrm::") and not name.startswith("nrm::"):
+            continue
+        lo, hi = mins.get(name, (avg, avg))
+        L.append(f"| `{short(name)}` | {calls} | {avg:.2f} | {lo:.2f} | {hi:.2f} |")
+    with open(SUITE_TRACE_MD, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -612,9 +652,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DB")
+    ap.add_argument("--summarize-suite-trace", metavar="TRACE_DB")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return 0
+    if args.summarize_suite_trace:
+        summarize_suite_trace(args.summarize_suite_trace)
         return 0
     if args.summarize_pmc:
         half = (add_rms_bytes(ROWS, HIDDEN, 2, 2) // 2) // 16 * 16
