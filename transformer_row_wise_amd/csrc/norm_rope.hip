@@ -106,14 +106,23 @@ __device__ __forceinline__ void rope_sincos(double a, double* sn, double* cs) {
   *cs = ((q + 1) & 2) ? -c0 : c0;
 }
 
-template <bool BF16, bool HALF, int G, int QC, int R>
+// Lane layouts of the rotated features. HALF: a lane holds chunk j of the first half and
+// chunk j of the second half (pairs (i, i + dims/2) across the two). TRAD2: a lane holds the
+// same two chunks, each a run of whole neighbouring pairs (2i, 2i+1), so interleaved rows
+// keep two chunks (32 bytes of bf16) per lane in flight like half-split ones. TRAD1: one
+// chunk per lane (interleaved rows whose half is not a whole number of chunks).
+enum RopeMode : int { M_HALF = 0, M_TRAD1 = 1, M_TRAD2 = 2 };
+
+template <bool BF16, int MODE, int G, int QC, int R>
 __global__ void __launch_bounds__(256)
 rope_fast(RopeArgs a) {
+  constexpr bool HALF = MODE == M_HALF;
+  constexpr bool TWO = MODE != M_TRAD1;       // two chunks per lane
   constexpr int V = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr int RPW = 64 / G;                 // row slots per wave
   constexpr int RPB = 4 * RPW;                // row slots per block
-  constexpr int PAIRS = HALF ? V : V / 2;     // rotated pairs per lane
+  constexpr int PAIRS = TWO ? V : V / 2;      // rotated pairs per lane
   constexpr int MAXP = G * PAIRS;             // pairs one group can hold
   constexpr int QN = QC > 0 ? QC : 1;
   __shared__ double cs_c[MAXP];
@@ -124,7 +133,7 @@ rope_fast(RopeArgs a) {
   const int half = a.dims / 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane / G, lj = lane % G;
-  const int npc = HALF ? half / V : a.dims / V;  // rotated chunks (pairs of chunks in half mode)
+  const int npc = TWO ? half / V : a.dims / V;  // lanes' rotated chunks (or chunk pairs)
   const int nqc = (a.D - a.dims) / V;            // pass-through chunks
   const bool has_pc = lj < npc;
   const bool norm = a.normalize != 0;
@@ -140,7 +149,7 @@ rope_fast(RopeArgs a) {
   // or without a pass-through chunk still loads a valid chunk of the row (clamped), so that
   // every load is unconditional; it never stores it.
   const int off_u = min(lj, max(npc - 1, 0)) * V;
-  const int off_v = HALF ? half + off_u : 0;
+  const int off_v = TWO ? half + off_u : 0;
   int off_q[QN];
   bool has_q[QN];
 #pragma unroll
@@ -173,7 +182,7 @@ rope_fast(RopeArgs a) {
       xv[r] = u32x4{0, 0, 0, 0};
       if (any_pc) {
         xu[r] = ld16_nt(xrow + off_u * ESZ);
-        if (HALF) xv[r] = ld16_nt(xrow + off_v * ESZ);
+        if (TWO) xv[r] = ld16_nt(xrow + off_v * ESZ);
       }
 #pragma unroll
       for (int q = 0; q < QN; ++q) {
@@ -195,13 +204,14 @@ rope_fast(RopeArgs a) {
   if (has_pc) {
 #pragma unroll
     for (int e = 0; e < PAIRS; ++e) {
-      const int p = HALF ? lj * V + e : lj * (V / 2) + e;
+      const int p = HALF ? lj * V + e
+                  : (e < V / 2 ? lj * (V / 2) + e : half / 2 + lj * (V / 2) + (e - V / 2));
       c[e] = cs_c[p];
       s[e] = cs_s[p];
     }
     if (has_w) {
       load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
-      if (HALF) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
+      if (TWO) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
     }
   }
 #pragma unroll
@@ -223,7 +233,7 @@ rope_fast(RopeArgs a) {
         if (has_pc) {
 #pragma unroll
           for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fu[e], fu[e], ss);
-          if (HALF) {
+          if (TWO) {
 #pragma unroll
             for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fv[e], fv[e], ss);
           }
@@ -258,8 +268,15 @@ rope_fast(RopeArgs a) {
             const double v = (double)fu[2 * e + 1] * (double)wu[2 * e + 1];
             fu[2 * e] = f64_to_f32((u * c[e] - v * s[e]) * rs);
             fu[2 * e + 1] = f64_to_f32((u * s[e] + v * c[e]) * rs);
+            if constexpr (TWO) {
+              const double u2 = (double)fv[2 * e] * (double)wv[2 * e];
+              const double v2 = (double)fv[2 * e + 1] * (double)wv[2 * e + 1];
+              fv[2 * e] = f64_to_f32((u2 * c[V / 2 + e] - v2 * s[V / 2 + e]) * rs);
+              fv[2 * e + 1] = f64_to_f32((u2 * s[V / 2 + e] + v2 * c[V / 2 + e]) * rs);
+            }
           }
           st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
+          if constexpr (TWO) st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
         }
       }
       const float rstd_f = (float)rstd;
@@ -334,7 +351,7 @@ rope_generic(RopeArgs a) {
 
 namespace {
 
-template <bool BF16, bool HALF, int G, int QC, int R>
+template <bool BF16, int MODE, int G, int QC, int R>
 hipError_t go_fast(const RopeArgs& a0, hipStream_t stream) {
   RopeArgs a = a0;
   constexpr int RPB = 4 * (64 / G);
@@ -348,32 +365,32 @@ hipError_t go_fast(const RopeArgs& a0, hipStream_t stream) {
   a.iters = (int)((steps + chunks - 1) / chunks);
   chunks = (steps + a.iters - 1) / a.iters;
   dim3 grid((unsigned)a.L, (unsigned)chunks);
-  rope_fast<BF16, HALF, G, QC, R><<<grid, 256, 0, stream>>>(a);
+  rope_fast<BF16, MODE, G, QC, R><<<grid, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 // R = 4 rows per lane group per step when there are enough b*h rows, else 1.
-template <bool BF16, bool HALF, int G, int QC>
+template <bool BF16, int MODE, int G, int QC>
 hipError_t pick_r(const RopeArgs& a, hipStream_t stream) {
   constexpr int RPB = 4 * (64 / G);
-  if (a.BH >= 2 * RPB * 4) return go_fast<BF16, HALF, G, QC, 4>(a, stream);
-  return go_fast<BF16, HALF, G, QC, 1>(a, stream);
+  if (a.BH >= 2 * RPB * 4) return go_fast<BF16, MODE, G, QC, 4>(a, stream);
+  return go_fast<BF16, MODE, G, QC, 1>(a, stream);
 }
 
-template <bool BF16, bool HALF, int G>
+template <bool BF16, int MODE, int G>
 hipError_t pick_qc(const RopeArgs& a, int qc, hipStream_t stream) {
-  if (qc == 0) return pick_r<BF16, HALF, G, 0>(a, stream);
-  if (qc == 1) return pick_r<BF16, HALF, G, 1>(a, stream);
-  return pick_r<BF16, HALF, G, 2>(a, stream);
+  if (qc == 0) return pick_r<BF16, MODE, G, 0>(a, stream);
+  if (qc == 1) return pick_r<BF16, MODE, G, 1>(a, stream);
+  return pick_r<BF16, MODE, G, 2>(a, stream);
 }
 
-template <bool BF16, bool HALF>
+template <bool BF16, int MODE>
 hipError_t pick_g(const RopeArgs& a, int g, int qc, hipStream_t stream) {
   switch (g) {
-    case 8: return pick_qc<BF16, HALF, 8>(a, qc, stream);
-    case 16: return pick_qc<BF16, HALF, 16>(a, qc, stream);
-    case 32: return pick_qc<BF16, HALF, 32>(a, qc, stream);
-    default: return pick_qc<BF16, HALF, 64>(a, qc, stream);
+    case 8: return pick_qc<BF16, MODE, 8>(a, qc, stream);
+    case 16: return pick_qc<BF16, MODE, 16>(a, qc, stream);
+    case 32: return pick_qc<BF16, MODE, 32>(a, qc, stream);
+    default: return pick_qc<BF16, MODE, 64>(a, qc, stream);
   }
 }
 
@@ -388,13 +405,16 @@ hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t strea
   const bool chunks_ok = aligned16 && a.D % V == 0 && a.dims % V == 0 &&
                          (a.traditional || half % V == 0) && a.L <= 0x7fffffff;
   if (chunks_ok && !force_generic_path()) {
-    const int npc = a.traditional ? a.dims / V : half / V;
+    // Interleaved rows whose half is a whole number of chunks use the two-chunk layout.
+    const int mode = !a.traditional ? M_HALF : (half % V == 0 ? M_TRAD2 : M_TRAD1);
+    const int npc = mode == M_TRAD1 ? a.dims / V : half / V;
     const int nqc = (a.D - a.dims) / V;
     for (int g = 8; g <= 64; g *= 2) {
       if (npc <= g && nqc <= 2 * g) {
         const int qc = (nqc + g - 1) / g;
-        return a.traditional ? pick_g<BF16, false>(a, g, qc, stream)
-                             : pick_g<BF16, true>(a, g, qc, stream);
+        if (mode == M_HALF) return pick_g<BF16, M_HALF>(a, g, qc, stream);
+        if (mode == M_TRAD2) return pick_g<BF16, M_TRAD2>(a, g, qc, stream);
+        return pick_g<BF16, M_TRAD1>(a, g, qc, stream);
       }
     }
   }
