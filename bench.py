@@ -353,7 +353,9 @@ def suite(args):
         k = n_sets(2 * xs.numel() * 2)
         xl = [xs.cuda() for _ in range(k)]
         ol = [torch.empty_like(xl[0]) for _ in range(k)]
-        nbytes = 2 * xs.numel() * 2
+        # Masked scores need not be read: the bytes are the kept scores (row r keeps r + 1
+        # of L columns with rows = L) plus the whole output.
+        nbytes = B * H * (L * (L + 1) // 2) * 2 + xs.numel() * 2
         per = time_graph(lambda i: nrm.causal_softmax(xl[i % k], L, out=ol[i % k]), calls(nbytes))
         emit("9b", "causal_softmax", [B * H, L, L], nbytes, B * H * L, per)
         del xl, ol

@@ -181,8 +181,16 @@ sm_rows(SmArgs a) {
   const char* xr = (const char*)a.x + row * a.n * ESZ;
   u32x4 xv[NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k)
-    xv[k] = ld16_nt(xr + (int64_t)(EXACT ? chunk(k) : min(chunk(k), nvec - 1)) * 16);
+  for (int k = 0; k < NV; ++k) {
+    if constexpr (OP == SM_CAUSAL) {
+      // A chunk wholly past the row's causal cut is never read: its scores are replaced.
+      xv[k] = u32x4{0, 0, 0, 0};
+      if (chunk(k) * V <= cut)
+        xv[k] = ld16_nt(xr + (int64_t)(EXACT ? chunk(k) : min(chunk(k), nvec - 1)) * 16);
+    } else {
+      xv[k] = ld16_nt(xr + (int64_t)(EXACT ? chunk(k) : min(chunk(k), nvec - 1)) * 16);
+    }
+  }
 
   // Score of element e of chunk k as the operation sees it (masked, or -inf when absent).
   auto score = [&](int k, int e, float f) {
@@ -299,6 +307,8 @@ sm_stream(SmArgs a) {
   const float lowest = lowest_of(BF16);
   const int64_t nch = a.n / V;
   const int64_t e0 = row * a.n;
+  const int64_t tgt_chunk = r.target < 0 ? -1 : r.target / V;
+  const int tgt_e = r.target < 0 ? -1 : (int)(r.target % V);
   auto score = [&](int64_t c, float f) {
     if constexpr (OP == SM_CAUSAL) return c <= r.cut ? f : lowest;
     return f;
@@ -338,15 +348,15 @@ sm_stream(SmArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t j = j0 + (int64_t)u * 256;
       if (j < nch) {
+        // CE: one compare per chunk says whether it holds the target (tgt_chunk), then a
+        // scalar compare per element.
+        const bool own = CE && j == tgt_chunk;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const int64_t c = j * V + e;
-          float ex = sm_exp(score(c, f[u][e]) - mm);
-          if constexpr (CE) {
-            if (c == r.target) {
-              xt_s[0] = f[u][e];  // published by the barrier of the maximum's reduction
-              ex = 0.f;
-            }
+          float ex = sm_exp(score(j * V + e, f[u][e]) - mm);
+          if (own && e == tgt_e) {
+            xt_s[0] = f[u][e];  // published by the barrier of the maximum's reduction
+            ex = 0.f;
           }
           s += ex;
         }
@@ -398,13 +408,11 @@ sm_stream(SmArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t j = j0 + (int64_t)u * 256;
       if (j < nch) {
+        const bool own = OP == SM_CE_VJP && j == tgt_chunk;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const int64_t c = j * V + e;
-          float p = sm_exp(score(c, f[u][e]) - M) * inv;
-          if constexpr (OP == SM_CE_VJP) {
-            if (c == r.target) p = gt;
-          }
+          float p = sm_exp(score(j * V + e, f[u][e]) - M) * inv;
+          if (own && e == tgt_e) p = gt;
           f[u][e] = p;
         }
         if constexpr (V == Fmt<BF16>::VEC) {
