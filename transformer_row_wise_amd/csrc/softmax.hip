@@ -295,13 +295,14 @@ sm_rows(SmArgs a) {
   }
 }
 
-template <bool BF16, int OP, int V>
-__global__ void __launch_bounds__(256)
+template <bool BF16, int OP, int V, int TPB>
+__global__ void __launch_bounds__(TPB)
 sm_stream(SmArgs a) {
   constexpr bool CE = OP == SM_CE || OP == SM_CE_VJP;
   constexpr int U = 4;  // chunks loaded together per step
   constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CAUSAL || OP == SM_CE_VJP;
-  __shared__ float red_m[4], red_s[4], xt_s[1];
+  constexpr int NW = TPB / 64;
+  __shared__ float red_m[NW], red_s[NW], xt_s[1];
   const int64_t row = blockIdx.x;
   const SmRow r = sm_row<OP>(a, row);
   const float lowest = lowest_of(BF16);
@@ -317,11 +318,11 @@ sm_stream(SmArgs a) {
   // -inf every score it has seen is -inf, and contributes 0). Each step loads U chunks
   // (clamped to the row, unconditional) before using any.
   float m = -__builtin_inff(), s = 0.f;
-  for (int64_t j0 = threadIdx.x; j0 < nch; j0 += 256 * U) {
+  for (int64_t j0 = threadIdx.x; j0 < nch; j0 += TPB * U) {
     float f[U][V];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = min(j0 + (int64_t)u * 256, nch - 1);
+      const int64_t j = min(j0 + (int64_t)u * TPB, nch - 1);
       if constexpr (V == Fmt<BF16>::VEC) {
         const void* p = (const char*)a.x + (e0 + j * V) * Fmt<BF16>::ESZ;
         // Rows with an output pass are read with cached loads, so that the second read
@@ -334,9 +335,9 @@ sm_stream(SmArgs a) {
     float cm = m;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (j0 + (int64_t)u * 256 < nch) {
+      if (j0 + (int64_t)u * TPB < nch) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) cm = fmaxf(cm, score((j0 + u * 256) * V + e, f[u][e]));
+        for (int e = 0; e < V; ++e) cm = fmaxf(cm, score((j0 + u * TPB) * V + e, f[u][e]));
       }
     }
     if (cm > m) {
@@ -346,7 +347,7 @@ sm_stream(SmArgs a) {
     const float mm = m == -__builtin_inff() ? 0.f : m;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + (int64_t)u * 256;
+      const int64_t j = j0 + (int64_t)u * TPB;
       if (j < nch) {
         // CE: one compare per chunk says whether it holds the target (tgt_chunk), then a
         // scalar compare per element.
@@ -363,11 +364,11 @@ sm_stream(SmArgs a) {
       }
     }
   }
-  const float M = team_reduce<true>(m, red_m, 0, 4);
+  const float M = team_reduce<true>(m, red_m, 0, NW);
   float xt = 0.f;
   if constexpr (CE) xt = r.bad ? 0.f : xt_s[0];
   // Rescale each thread's sum to the row maximum, then add in a fixed order.
-  const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_exp(m - M), red_s, 0, 4);
+  const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_exp(m - M), red_s, 0, NW);
 
   if constexpr (OP == SM_LSE) {
     if (threadIdx.x == 0) {
@@ -393,11 +394,11 @@ sm_stream(SmArgs a) {
   }
   // Pass 2: each thread re-reads exactly the chunks it read in pass 1 (so in-place use is
   // safe: no thread writes a chunk another thread still has to read).
-  for (int64_t j0 = threadIdx.x; j0 < nch; j0 += 256 * U) {
+  for (int64_t j0 = threadIdx.x; j0 < nch; j0 += TPB * U) {
     float f[U][V];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = min(j0 + (int64_t)u * 256, nch - 1);
+      const int64_t j = min(j0 + (int64_t)u * TPB, nch - 1);
       if constexpr (V == Fmt<BF16>::VEC) {
         unpack<BF16>(ld16_nt((const char*)a.x + (e0 + j * V) * Fmt<BF16>::ESZ), f[u]);
       } else {
@@ -406,7 +407,7 @@ sm_stream(SmArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + (int64_t)u * 256;
+      const int64_t j = j0 + (int64_t)u * TPB;
       if (j < nch) {
         const bool own = OP == SM_CE_VJP && j == tgt_chunk;
 #pragma unroll
@@ -453,10 +454,18 @@ hipError_t sm_team(const SmArgs& a, int team, bool exact, hipStream_t stream) {
                : go_sm_rows<BF16, OP, NV, false, 0>(a, team, stream);
 }
 
+// Operations with a row output read the row twice. With 1024-thread blocks (two per
+// compute unit) about 512 rows are in flight, so the second read of a 256 KB vocabulary row
+// still finds it in the 256 MB Infinity Cache; eight 256-thread blocks per CU keep the same
+// bytes in flight but four times the rows, which evicts each row before its second read.
 template <bool BF16, int OP, int V>
 hipError_t go_sm_stream(const SmArgs& a, hipStream_t stream) {
+  constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CAUSAL || OP == SM_CE_VJP;
   if (a.rows > kSmMaxGrid) return hipErrorInvalidConfiguration;
-  sm_stream<BF16, OP, V><<<(unsigned)a.rows, 256, 0, stream>>>(a);
+  if (OUT && a.n >= 16384)
+    sm_stream<BF16, OP, V, 1024><<<(unsigned)a.rows, 1024, 0, stream>>>(a);
+  else
+    sm_stream<BF16, OP, V, 256><<<(unsigned)a.rows, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
