@@ -231,14 +231,36 @@ __device__ __forceinline__ double wave_sum(double v) {
 constexpr int DPP_ROW_ROR4 = 0x124;
 constexpr int DPP_ROW_ROR8 = 0x128;
 
+// v of lane l plus v of lane l ^ 16 (ROWS = 16) or l ^ 32 (ROWS = 32), through the gfx950
+// lane swaps (VALU, no LDS round trip). A swap of a register with itself hands every lane
+// the pair's lower-lane value and its upper-lane value; both lanes of a pair add them in that
+// order, so they agree bit for bit.
+template <int ROWS>
+__device__ __forceinline__ double swap_sum(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t l0, l1, h0, h1;
+  if constexpr (ROWS == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = a[0], l1 = a[1], h0 = b[0], h1 = b[1];
+  } else {
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = a[0], l1 = a[1], h0 = b[0], h1 = b[1];
+  }
+  return __builtin_bit_cast(double, ((uint64_t)h0 << 32) | l0) +
+         __builtin_bit_cast(double, ((uint64_t)h1 << 32) | l1);
+}
+
 // Sum over the 64 lanes of a wave, every lane ending with a total (the lanes need not agree
 // bit for bit; callers read a fixed lane): rotations by 4 and 8 inside each 16-lane row keep
 // a lane's index mod 4, and so do the xor-16 / xor-32 exchanges across rows.
 __device__ __forceinline__ double lanes_sum_mod4(double v) {
   v += dpp<DPP_ROW_ROR4>(v);
   v += dpp<DPP_ROW_ROR8>(v);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
+  v = swap_sum<16>(v);
+  v = swap_sum<32>(v);
   return v;
 }
 

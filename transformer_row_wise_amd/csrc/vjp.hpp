@@ -56,9 +56,25 @@ struct VjpRow {
   double m2;   // LN: mean(d xh)
 };
 
+// 1 / sqrt(v) in fp64 for a row scalar: the hardware's fp64 estimate (good to about single
+// precision), refined by two Newton steps y += y (1 - v y^2) / 2, each of which about squares
+// the relative error, so the result is within a few fp64 units in the last place (far below
+// what fp32 and bf16 outputs resolve).
+// Zero, subnormal, huge, infinite, negative and NaN arguments take the exact expression.
+__device__ __forceinline__ double rsqrt_row(double v) {
+  if (v >= 0x1p-1000 && v <= 0x1p+1000) {
+    const double vh = 0.5 * v;
+    double y = __builtin_amdgcn_rsq(v);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) y = __builtin_fma(y, __builtin_fma(-(vh * y), y, 0.5), y);
+    return y;
+  }
+  return 1.0 / __builtin_sqrt(v);
+}
+
 __device__ __forceinline__ VjpRow vjp_rms_scalars(double ss, double dot, double inv_n, float eps) {
   VjpRow s;
-  s.r = 1.0 / __builtin_sqrt(ss * inv_n + (double)eps);
+  s.r = rsqrt_row(ss * inv_n + (double)eps);
   s.c = s.r * s.r * s.r * (dot * inv_n);
   s.mu = s.m1 = s.m2 = 0.0;
   return s;
@@ -70,7 +86,7 @@ __device__ __forceinline__ VjpRow vjp_ln_scalars(double sx, double sxx, double s
   s.mu = sx * inv_n;
   const double v0 = sxx * inv_n - s.mu * s.mu;
   const double var = v0 < 0.0 ? 0.0 : v0;  // clamps rounding, keeps a NaN (inf - inf)
-  s.r = 1.0 / __builtin_sqrt(var + (double)eps);
+  s.r = rsqrt_row(var + (double)eps);
   s.c = 0.0;
   s.m1 = sd * inv_n;
   s.m2 = s.r * ((sdx - s.mu * sd) * inv_n);
@@ -88,8 +104,11 @@ __device__ __forceinline__ void vjp_accumulate(const float (&f)[V], const float 
   for (int e = 0; e < V; ++e) {
     if constexpr (OP == VJP_RMS) {
       if constexpr (XF) {
-        ds[0] += (double)(f[e] * f[e]);
-        ds[1] += (double)((gv[e] * wv[e]) * f[e]);
+        // x^2 and (g w) x are exact products either way; the fused form spares the fp32
+        // multiplies and rounds only the sums, as before.
+        const double xd = (double)f[e];
+        ds[0] = __builtin_fma(xd, xd, ds[0]);
+        ds[1] = __builtin_fma((double)(gv[e] * wv[e]), xd, ds[1]);
       } else {
         const double xd = (double)f[e];
         ds[0] = __builtin_fma(xd, xd, ds[0]);
@@ -116,6 +135,9 @@ __device__ __forceinline__ void vjp_outputs(const float (&f)[V], const float (&g
     const double xd = (double)f[e];
     const double gd = (double)gv[e];
     const double d = XF ? (double)(gv[e] * wv[e]) : gd * (double)wv[e];
+    // Four elements at a time: converting all eight to fp64 together costs more registers
+    // than the loads kept in flight can spare.
+    if (e == 4) __builtin_amdgcn_sched_barrier(0);
     if constexpr (OP == VJP_RMS) {
       dxv[e] = f64_to_f32(__builtin_fma(s.r, d, -(xd * s.c)));
       if constexpr (DW) {
@@ -132,13 +154,60 @@ __device__ __forceinline__ void vjp_outputs(const float (&f)[V], const float (&g
   }
 }
 
+// team_sum4 (common.hpp) in three parts, with the same arithmetic in the same order, so
+// that a caller can put work between the barrier and the use of the sums: post (each wave's
+// four totals to red), then after the caller's barrier read (this lane's team slot), then
+// finish (the team totals, read from lanes 0 .. 3 into every lane).
+__device__ __forceinline__ void team_sum4_post(const double (&s)[4], double* red) {
+  const int lane = threadIdx.x & 63;
+  const bool b = lane & 1, c = lane & 2;
+  double k0 = b ? s[1] : s[0], u0 = b ? s[0] : s[1];
+  double k1 = b ? s[3] : s[2], u1 = b ? s[2] : s[3];
+  k0 += dpp<DPP_QUAD_XOR1>(u0);
+  k1 += dpp<DPP_QUAD_XOR1>(u1);
+  double k = c ? k1 : k0;
+  const double u = c ? k0 : k1;
+  k += dpp<DPP_QUAD_XOR2>(u);
+  k = lanes_sum_mod4(k);
+  if (lane < 4) red[(threadIdx.x >> 6) * 4 + lane] = k;
+}
+
+__device__ __forceinline__ double team_sum4_read(const double* red, int wave0, int nwt) {
+  const int lane = threadIdx.x & 63;
+  const int w = lane >> 2;
+  return w < nwt ? red[(wave0 + w) * 4 + (lane & 3)] : 0.0;
+}
+
+__device__ __forceinline__ void team_sum4_finish(double t, double (&s)[4]) {
+  t = lanes_sum_mod4(t);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = readlane_f64(t, i);
+}
+
+// A value every lane holds, moved to scalar registers (the compiler cannot tell that the
+// lanes agree).
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ VjpRow vjp_row_uniform(VjpRow s) {
+  s.r = uniform_f64(s.r);
+  s.c = uniform_f64(s.c);
+  s.mu = uniform_f64(s.mu);
+  s.m1 = uniform_f64(s.m1);
+  s.m2 = uniform_f64(s.m2);
+  return s;
+}
+
 // Fast kernel: a block of G teams of T = a.team threads (G * T = blockDim.x); a team owns
 // one row at a time, thread t of a team keeping chunks t, t + T, ... (NV of them) of the
 // row in registers. Block b walks rows [b * rpb, min(rows, (b + 1) * rpb)), team i taking
 // rows b * rpb + i, + G, ...; every team runs the same number of iterations (a team past
-// the end reloads the last row and discards it), so the block barriers line up. The next
-// row's x and g are loaded before the current row is reduced. EXACT: T * NV chunks cover
-// the row; otherwise chunk indexes past the end are clamped for loads and their results
+// the end reloads the last row and discards it), so the block barriers line up. EXACT: T * NV
+// chunks cover the row; otherwise chunk indexes past the end are clamped for loads and their results
 // dropped. PG: parameter gradients wanted (dw for RMS; dw and db for LN).
 template <bool BF16, int OP, int NV, int PK, bool EXACT, bool PG>
 __global__ void __launch_bounds__(1024)
@@ -150,7 +219,9 @@ vjp_rows(VjpArgs a) {
   extern __shared__ double comb[];           // (G - 1) * T * V doubles, team combine
   const int T = a.team;
   const int G = blockDim.x / T;
-  const int team = threadIdx.x / T;
+  // T is a multiple of 64, so a wave belongs to one team: the team index, its rows and their
+  // addresses are scalars.
+  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
   const int tid = threadIdx.x - team * T;
   const int nwt = T >> 6;                    // waves per team
   const int wave0 = team * nwt;
@@ -188,9 +259,8 @@ vjp_rows(VjpArgs a) {
     }
   };
 
-  auto process = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV]) {
-    const int64_t row = row_of(it);
-    const bool valid = row < row_end;
+  // Statistics of a row: its four sums, reduced within each wave and posted to red[it & 1].
+  auto stats = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV]) {
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -201,11 +271,21 @@ vjp_rows(VjpArgs a) {
         vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
       }
     }
-    team_sum4(ds, red[it & 1], wave0, nwt);
+    team_sum4_post(ds, red[it & 1]);
+  };
+  // After the barrier that follows stats(it): the row's scalars, the same in every lane.
+  auto scalars = [&](double t) {
+    double ds[4];
+    team_sum4_finish(t, ds);
     VjpRow s;
     if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
     else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
-    if (!valid) return;
+    return vjp_row_uniform(s);
+  };
+  // dx of a row, and its dw / db terms.
+  auto outputs = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV], const VjpRow& s) {
+    const int64_t row = row_of(it);
+    if (row >= row_end) return;
     char* dr = (char*)a.dx + row * a.hidden * Fmt<BF16>::ESZ;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -222,19 +302,67 @@ vjp_rows(VjpArgs a) {
     }
   };
 
-  u32x4 xa[NV], ga[NV];
-  load_row(0, xa, ga);
-  for (int it = 0; it < iters - 1; ++it) {
-    u32x4 xb[NV], gb[NV];
-    load_row(it + 1, xb, gb);
-    process(it, xa, ga);
+  if constexpr (NV > 1) {
+    // Two chunks per thread and the column accumulators leave no registers for the ring
+    // below: one buffer pair, the next row copied in after each row, and each row's
+    // statistics, barrier and outputs in turn.
+    u32x4 xa[NV], ga[NV];
+    load_row(0, xa, ga);
+    for (int it = 0; it < iters; ++it) {
+      u32x4 xb[NV], gb[NV];
+      if (it + 1 < iters) load_row(it + 1, xb, gb);
+      stats(it, xa, ga);
+      __syncthreads();
+      const VjpRow s = scalars(team_sum4_read(red[it & 1], wave0, nwt));
+      outputs(it, xa, ga, s);
+      if (it + 1 < iters) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      xa[k] = xb[k];
-      ga[k] = gb[k];
+        for (int k = 0; k < NV; ++k) {
+          xa[k] = xb[k];
+          ga[k] = gb[k];
+        }
+      }
+    }
+  } else {
+    // Software pipeline over a ring of R row buffers. Step it loads row it + R - 1 into the
+    // buffer row it - 1 has released, posts the statistics of row it + 1, passes the
+    // barrier, issues the LDS reads of those sums, writes the outputs of row it (whose
+    // scalars the previous step finished) while the reads are in flight, and only then
+    // finishes the scalars of row it + 1. The barrier's latency thus overlaps a row's
+    // output arithmetic instead of stalling every wave of the block. The loop is unrolled
+    // by R so that each buffer keeps its registers: copying a buffer that is still being
+    // loaded would wait for the load.
+    constexpr int R = 4;
+    u32x4 xs[R][NV], gs[R][NV];
+#pragma unroll
+    for (int q = 0; q < R - 1; ++q) load_row(q, xs[q], gs[q]);
+    stats(0, xs[0], gs[0]);
+    __syncthreads();
+    VjpRow s = scalars(team_sum4_read(red[0], wave0, nwt));
+    auto step = [&](int it, int q, bool load, bool next) {
+      if (load) load_row(it + R - 1, xs[(q + R - 1) % R], gs[(q + R - 1) % R]);
+      double t = 0.0;
+      if (next) {
+        stats(it + 1, xs[(q + 1) % R], gs[(q + 1) % R]);
+        __syncthreads();
+        t = team_sum4_read(red[(it + 1) & 1], wave0, nwt);
+      }
+      outputs(it, xs[q], gs[q], s);
+      if (next) s = scalars(t);
+    };
+    int it0 = 0;
+    for (; it0 + 2 * R - 1 <= iters; it0 += R) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) step(it0 + q, q, true, true);
+    }
+    // The last rows (fewer than 2R - 1): loads and statistics only for rows that exist.
+#pragma unroll
+    for (int q = 0; q < 2 * R - 2; ++q) {
+      const int it = it0 + q;
+      if (it >= iters) break;
+      step(it, q % R, it + R - 1 < iters, it + 1 < iters);
     }
   }
-  process(iters - 1, xa, ga);
 
   if constexpr (DW || DB) {
     // Team 0 adds teams 1 .. G-1 (in that order) through LDS, one chunk slot at a time,
