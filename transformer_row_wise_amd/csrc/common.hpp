@@ -290,6 +290,22 @@ __device__ __forceinline__ void team_sum4(double (&s)[4], double* red, int wave0
   for (int i = 0; i < 4; ++i) s[i] = readlane_f64(t, i);
 }
 
+// 1 / sqrt(v) in fp64 for a row scalar: the hardware's fp64 estimate (good to about single
+// precision), refined by two Newton steps y += y (1 - v y^2) / 2, each of which about squares
+// the relative error, so the result is within a few fp64 units in the last place (far below
+// what fp32 and bf16 outputs resolve).
+// Zero, subnormal, huge, infinite, negative and NaN arguments take the exact expression.
+__device__ __forceinline__ double rsqrt_row(double v) {
+  if (v >= 0x1p-1000 && v <= 0x1p+1000) {
+    const double vh = 0.5 * v;
+    double y = __builtin_amdgcn_rsq(v);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) y = __builtin_fma(y, __builtin_fma(-(vh * y), y, 0.5), y);
+    return y;
+  }
+  return 1.0 / __builtin_sqrt(v);
+}
+
 // rstd = 1 / sqrt(sum / n + eps), formed in fp64 from an fp32 or fp64 sum (one row scalar).
 __device__ __forceinline__ double rstd_f64(double sum, int64_t n, float eps) {
   return 1.0 / __builtin_sqrt(sum / (double)n + (double)eps);

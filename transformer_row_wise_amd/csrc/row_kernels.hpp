@@ -307,7 +307,7 @@ row_block(RowArgs a) {
       if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   } else {  // OP_LN, fp64 statistics and output arithmetic
-    // One pass: sum x and sum x^2 in fp64 (for bf16, x^2 is exact in fp32 and only widened),
+    // One pass: sum x and sum x^2 in fp64 (x^2 of a bf16 or fp32 value is exact in fp64),
     // reduced together with one barrier; var = sum x^2 / n - mu^2 (fp64 keeps the
     // cancellation harmless unless |mu| / sigma exceeds ~1e6). A constant row gets var = 0
     // and x - mu = 0 exactly, so its output is exactly b. b (like w) is loaded before the
@@ -331,9 +331,9 @@ row_block(RowArgs a) {
       if (ok[k]) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          ds[e & 1] += (double)f[e];
-          if constexpr (BF16) ds[2 + (e & 1)] += (double)(f[e] * f[e]);
-          else ds[2 + (e & 1)] = __builtin_fma((double)f[e], (double)f[e], ds[2 + (e & 1)]);
+          const double xd = (double)f[e];
+          ds[e & 1] += xd;
+          ds[2 + (e & 1)] = __builtin_fma(xd, xd, ds[2 + (e & 1)]);  // x^2 exact in fp64
         }
       }
     }
@@ -346,7 +346,7 @@ row_block(RowArgs a) {
     // Clamp rounding below zero, but keep a NaN (an infinite row gives inf - inf).
     const double v0 = ds[1] * inv_n - mu * mu;
     const double var = v0 < 0.0 ? 0.0 : v0;
-    const double rstd = 1.0 / __builtin_sqrt(var + (double)a.eps);
+    const double rstd = rsqrt_row(var + (double)a.eps);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       u32x4 xr = xv[k];

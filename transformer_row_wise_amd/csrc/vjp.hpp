@@ -56,22 +56,6 @@ struct VjpRow {
   double m2;   // LN: mean(d xh)
 };
 
-// 1 / sqrt(v) in fp64 for a row scalar: the hardware's fp64 estimate (good to about single
-// precision), refined by two Newton steps y += y (1 - v y^2) / 2, each of which about squares
-// the relative error, so the result is within a few fp64 units in the last place (far below
-// what fp32 and bf16 outputs resolve).
-// Zero, subnormal, huge, infinite, negative and NaN arguments take the exact expression.
-__device__ __forceinline__ double rsqrt_row(double v) {
-  if (v >= 0x1p-1000 && v <= 0x1p+1000) {
-    const double vh = 0.5 * v;
-    double y = __builtin_amdgcn_rsq(v);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) y = __builtin_fma(y, __builtin_fma(-(vh * y), y, 0.5), y);
-    return y;
-  }
-  return 1.0 / __builtin_sqrt(v);
-}
-
 __device__ __forceinline__ VjpRow vjp_rms_scalars(double ss, double dot, double inv_n, float eps) {
   VjpRow s;
   s.r = rsqrt_row(ss * inv_n + (double)eps);
