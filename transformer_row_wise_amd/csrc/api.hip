@@ -115,6 +115,7 @@ nrm::RowArgs row_args(const void* x, const void* r, const void* w, const void* b
   a.x = x; a.r = r; a.w = w; a.b = b; a.out = out; a.h = h;
   a.rows = rows; a.hidden = hidden; a.eps = eps;
   a.w_f32 = w_dtype == NRM_F32;
+  a.inv_n = hidden > 0 ? 1.0 / (double)hidden : 0.0;
   return a;
 }
 

@@ -36,6 +36,7 @@ struct RowArgs {
   int64_t hidden;  // elements per row, < 2^31
   float eps;
   int w_f32;       // w and b stored as fp32 (else bf16, only with bf16 activations)
+  double inv_n;    // 1 / hidden, rounded to fp64
 };
 
 // Cross-lane sum over the threads of one row: the wave itself (WPR == 1) or the block,
@@ -266,9 +267,16 @@ row_block(RowArgs a) {
     ok[k] = EXACT || j < nvec;
     jj[k] = EXACT ? j : min(j, nvec - 1);
   }
+  // LayerNorm with bf16 w and b keeps them packed (8 registers per chunk instead of 16) and
+  // widens them where the output uses them.
+  constexpr bool LN_PACKED = OP == OP_LN && BF16 && PK == PK_SAME;
   float wv[NV][V];
+  u32x4 wpk[NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+  for (int k = 0; k < NV; ++k) {
+    if constexpr (LN_PACKED) wpk[k] = ld16((const uint16_t*)a.w + (int64_t)jj[k] * V);
+    else load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+  }
   u32x4 xv[NV], rv[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
@@ -311,13 +319,18 @@ row_block(RowArgs a) {
     // reduced together with one barrier; var = sum x^2 / n - mu^2 (fp64 keeps the
     // cancellation harmless unless |mu| / sigma exceeds ~1e6). A constant row gets var = 0
     // and x - mu = 0 exactly, so its output is exactly b. b (like w) is loaded before the
-    // row's statistics, kept packed when it is bf16.
+    // row's statistics.
     const bool has_b = a.b != nullptr;
     float bv[NV][V];
+    u32x4 bpk[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      if (has_b) {
-        load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv[k]);
+      if constexpr (LN_PACKED) {
+        bpk[k] = has_b ? ld16((const uint16_t*)a.b + (int64_t)jj[k] * V) : u32x4{0u, 0u, 0u, 0u};
+      } else if (has_b) {
+        // b has w's dtype; without w its kind is only known at run time.
+        if constexpr (PK == PK_NONE) load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv[k]);
+        else load_pk<BF16, PK, V>(a.b, (int64_t)jj[k] * V, bv[k]);
       } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) bv[k][e] = 0.f;
@@ -341,8 +354,11 @@ row_block(RowArgs a) {
     ds[1] = ds[2] + ds[3];
     ds[2] = ds[3] = 0.0;
     team_sum4(ds, red4, 0, nw);
-    const double inv_n = 1.0 / (double)a.hidden;
-    const double mu = ds[0] * inv_n;
+    // mu = sum / n through the reciprocal and one residual step, which lands on the correctly
+    // rounded quotient (a constant row's exact sum n c gives exactly c).
+    const double n = (double)a.hidden, inv_n = a.inv_n;
+    const double q = ds[0] * inv_n;
+    const double mu = __builtin_fma(__builtin_fma(-q, n, ds[0]), inv_n, q);
     // Clamp rounding below zero, but keep a NaN (an infinite row gives inf - inf).
     const double v0 = ds[1] * inv_n - mu * mu;
     const double var = v0 < 0.0 ? 0.0 : v0;
@@ -351,12 +367,20 @@ row_block(RowArgs a) {
     for (int k = 0; k < NV; ++k) {
       u32x4 xr = xv[k];
       __asm__ volatile("" : "+v"(xr));  // widen again rather than hold fp64 copies
-      float f[V];
+      float f[V], wf[V], bf[V];
       unpack<BF16>(xr, f);
+      if constexpr (LN_PACKED) {
+        u32x4 wr = wpk[k], br = bpk[k];
+        __asm__ volatile("" : "+v"(wr), "+v"(br));  // widen here, not at the load
+        unpack<true>(wr, wf);
+        unpack<true>(br, bf);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) wf[e] = wv[k][e], bf[e] = bv[k][e];
+      }
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wv[k][e],
-                                        (double)bv[k][e]));
+        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
       if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   }

@@ -1,10 +1,11 @@
 // Kernel-shape choice and launch of the row kernels (RMSNorm, add-RMSNorm, LayerNorm).
 //
 // For a row of n = hidden / VEC 16-byte chunks (VEC = 8 bf16 or 4 fp32), automatic choice:
-//   n <= 4096 (2048 for LayerNorm)   row_block: one block of T threads per row, NV chunks per
-//                                    thread, NV = max(2, ceil(n / 1024)), T = ceil(n / NV)
-//                                    rounded up to a wave (hidden 8192 bf16: 512 threads,
-//                                    2 chunks each);
+//   n <= 4096 (2048 for LayerNorm    row_block: one block of T threads per row, NV chunks per
+//   with fp32 w beside bf16 x)       thread, NV = max(2, ceil(n / 1024)) (LayerNorm:
+//                                    clamp(ceil(n / 256), 2, 4)), T = ceil(n / NV) rounded
+//                                    up to a wave (hidden 8192 bf16: 512 threads with 2
+//                                    chunks each, LayerNorm 256 threads with 4);
 //   otherwise, or when hidden or a base address is not 16-byte granular: the looping
 //   kernel (16-byte chunks, or single elements).
 // Measured on MI355X for add-RMSNorm bf16 [16384, 8192]: row_block streams at ~6.25 TB/s,
@@ -54,7 +55,8 @@ hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t st
   if (a.w == nullptr)
     return exact ? go_rowblock<BF16, OP, NV, PK_NONE, true>(a, threads, stream)
                  : go_rowblock<BF16, OP, NV, PK_NONE, false>(a, threads, stream);
-  if constexpr (BF16) {
+  // (LayerNorm with fp32 parameters beside bf16 data never takes more than two chunks.)
+  if constexpr (BF16 && !(OP == OP_LN && NV > 2)) {
     if (a.w_f32)
       return exact ? go_rowblock<BF16, OP, NV, PK_F32, true>(a, threads, stream)
                    : go_rowblock<BF16, OP, NV, PK_F32, false>(a, threads, stream);
@@ -63,24 +65,30 @@ hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t st
                : go_rowblock<BF16, OP, NV, PK_SAME, false>(a, threads, stream);
 }
 
-// One block per row: NV = max(2, ceil(n / 1024)) chunks per thread (at most 4; 2 for
-// LayerNorm, whose fp64 temporaries need the registers), T = ceil(n / NV) rounded up to a
-// wave. Two 16-byte chunks per thread measured best: at hidden 8192 bf16, 512 threads with
-// two chunks each beat 1024 threads with one (add-RMSNorm 172 vs 182 us, RMSNorm 86 vs
-// 95 us); four per thread gain nothing.
+// One block per row: NV = max(2, ceil(n / 1024)) chunks per thread (at most 4), T = ceil(n /
+// NV) rounded up to a wave. Two 16-byte chunks per thread measured best for the RMS forms:
+// at hidden 8192 bf16, 512 threads with two chunks each beat 1024 threads with one
+// (add-RMSNorm 172 vs 182 us, RMSNorm 86 vs 95 us); four per thread gain nothing. LayerNorm
+// is bound by its fp64 arithmetic rather than by bytes in flight, and its per-row work (the
+// reduction, the row scalars) is better spread over more elements per thread: NV =
+// clamp(ceil(n / 256), 2, 4) (affine [16384, 8192] bf16 106 -> 102 us), except with fp32
+// parameters beside bf16 data, whose widened w and b leave room for only two chunks.
 template <bool BF16, int OP>
 hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* done) {
   *done = false;
-  const int64_t nv = std::max<int64_t>(2, (n + 1023) / 1024);
-  if (nv > (OP == OP_LN ? 2 : 4) || a.rows > kMaxGrid) return hipSuccess;
+  const bool ln_wide = OP == OP_LN && !(BF16 && a.w_f32);
+  const int64_t nv = ln_wide ? std::min<int64_t>(4, std::max<int64_t>(2, (n + 255) / 256))
+                             : std::max<int64_t>(2, (n + 1023) / 1024);
+  if (nv > (OP == OP_LN && !ln_wide ? 2 : 4) || n > nv * 1024 || a.rows > kMaxGrid)
+    return hipSuccess;
   const int threads = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
   const bool exact = (int64_t)threads * nv == n;
   *done = true;
   switch (nv) {
     case 1: return rowblock_pk<BF16, OP, 1>(a, threads, exact, stream);
     case 2: return rowblock_pk<BF16, OP, 2>(a, threads, exact, stream);
-    case 3: if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 3>(a, threads, exact, stream); break;
-    case 4: if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 4>(a, threads, exact, stream); break;
+    case 3: return rowblock_pk<BF16, OP, 3>(a, threads, exact, stream);
+    case 4: return rowblock_pk<BF16, OP, 4>(a, threads, exact, stream);
     default: break;
   }
   *done = false;
