@@ -9,9 +9,14 @@
 // CrossEntropyVjp ((logits, targets, loss, g): its gradient for the logits).
 //
 // Arithmetic: fp32 throughout (the pages' float32 accumulation). Per row, m = max and
-// S = sum exp(x - m) over the row; exp(t) = 2^(t log2 e) on the hardware exp2, with the
-// argument shifted up by 64 and the result scaled by 2^-64 where it would fall below the
-// normal range (so tiny probabilities keep their subnormal values). Cross-entropy keeps the
+// S = sum exp(x - m) over the row. The exponentials are formed scaled by 2^64, as
+// 2^(fma(t, log2 e, 64)) on the hardware exp2 (three instructions, no range test): the
+// hardware's results stop at the normal range, and the scale keeps every exponential that
+// fp32 or bf16 can hold away from that floor. The scale cancels in every ratio (outputs,
+// the loss's log1p and its gradient) and is taken off exactly, by a power-of-two product of
+// a sum of at least 2^64, before a logarithm. Rounding t log2 e + 64 to fp32 costs at most
+// ~1.3e-6 relative per exponential. A probability below the normal range comes out of one
+// product with the row's reciprocal sum, rounded once. Cross-entropy keeps the
 // target's term apart: with e_t = exp(x_t - m) and R = the sum over the other columns,
 //   loss = log1p(R / e_t)                      (= logsumexp - x_t, no cancellation)
 //   d loss / d x_t = -R / (R + e_t),   d loss / d x_j = exp(x_j - m) / (R + e_t)
@@ -38,12 +43,16 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// exp(t) for t <= 0 (or NaN), fp32.
-__device__ __forceinline__ float sm_exp(float t) {
-  const float y = t * kLog2e;
-  const bool tiny = y < -126.0f;
-  const float r = __builtin_amdgcn_exp2f(tiny ? y + 64.0f : y);
-  return tiny ? r * 5.421010862427522e-20f : r;  // 2^-64
+// 2^64 exp(t) for t <= 0 (or NaN), fp32.
+__device__ __forceinline__ float sm_exp64(float t) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(t, kLog2e, 64.0f));
+}
+
+// exp(t) for t <= 0, fp32, for the factors that rescale a sum to a larger maximum: a factor
+// below the normal range flushes to 0, which only drops terms at least 2^62 times smaller
+// than the sum they join (whose maximum contributes 2^64).
+__device__ __forceinline__ float sm_factor(float t) {
+  return __builtin_amdgcn_exp2f(t * kLog2e);
 }
 
 __device__ __forceinline__ float lowest_of(bool bf16) {
@@ -125,18 +134,18 @@ __device__ __forceinline__ SmRow sm_row(const SmArgs& a, int64_t row) {
   return r;
 }
 
-// log(sum exp(x)) from the row's maximum m and S = sum exp(x - m); an infinite maximum is
-// the result itself (+inf: some score is +inf; -inf: every score is -inf, the sum is 0).
+// log(sum exp(x)) from the row's maximum m and s = 2^64 sum exp(x - m); an infinite maximum
+// is the result itself (+inf: some score is +inf; -inf: every score is -inf, the sum is 0).
 __device__ __forceinline__ float lse_of(float m, float s) {
   if (__builtin_isinf(m)) return m;
-  return m + __builtin_amdgcn_logf(s) * 0.6931471805599453f;
+  return m + __builtin_amdgcn_logf(s * 0x1p-64f) * 0.6931471805599453f;
 }
 
-// The loss from the row's maximum m, the target's logit x_t, e_t = exp(x_t - m) and the sum
-// R of the other columns' exponentials.
+// The loss from the row's maximum m, the target's logit x_t, e_t = 2^64 exp(x_t - m) and the
+// sum R of the other columns' exponentials (scaled alike).
 __device__ __forceinline__ float ce_loss(float m, float x_t, float e_t, float rest) {
   if (m - x_t < 60.f) return log1pf(rest / e_t);
-  return (m - x_t) + logf(rest + e_t);
+  return (m - x_t) + logf((rest + e_t) * 0x1p-64f);
 }
 
 }  // namespace
@@ -240,7 +249,7 @@ sm_rows(SmArgs a) {
     unpack<BF16>(xv[k], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      float ex = sm_exp(score(k, e, f[e]) - m);
+      float ex = sm_exp64(score(k, e, f[e]) - m);
       if (!ok(k)) ex = 0.f;
       if constexpr (CE) {
         if (is_tgt(k, e)) ex = 0.f;  // R excludes the target
@@ -259,7 +268,7 @@ sm_rows(SmArgs a) {
   }
   if constexpr (OP == SM_CE) {
     if (live && tid == 0) {
-      const float e_t = sm_exp(xt - m);
+      const float e_t = sm_exp64(xt - m);
       a.loss[row] = r.bad ? __builtin_nanf("") : ce_loss(m, xt, e_t, s);
     }
     return;
@@ -267,7 +276,7 @@ sm_rows(SmArgs a) {
   // Softmax, CausalSoftmax, CrossEntropyVjp: the output row.
   float inv, gt = 0.f;
   if constexpr (OP == SM_CE_VJP) {
-    const float e_t = sm_exp(xt - m);
+    const float e_t = sm_exp64(xt - m);
     const float tot = s + e_t;
     inv = r.g / tot;
     gt = -r.g * (s / tot);  // d loss / d x_t, times g
@@ -285,7 +294,7 @@ sm_rows(SmArgs a) {
     unpack<BF16>(xv[k], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      float p = sm_exp(score(k, e, f[e]) - m) * inv;
+      float p = sm_exp64(score(k, e, f[e]) - m) * inv;
       if constexpr (OP == SM_CE_VJP) {
         if (is_tgt(k, e)) p = gt;
       }
@@ -341,7 +350,7 @@ sm_stream(SmArgs a) {
       }
     }
     if (cm > m) {
-      s = s * sm_exp(m - cm);
+      s = s * sm_factor(m - cm);
       m = cm;
     }
     const float mm = m == -__builtin_inff() ? 0.f : m;
@@ -354,7 +363,7 @@ sm_stream(SmArgs a) {
         const bool own = CE && j == tgt_chunk;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          float ex = sm_exp(score(j * V + e, f[u][e]) - mm);
+          float ex = sm_exp64(score(j * V + e, f[u][e]) - mm);
           if (own && e == tgt_e) {
             xt_s[0] = f[u][e];  // published by the barrier of the maximum's reduction
             ex = 0.f;
@@ -368,7 +377,7 @@ sm_stream(SmArgs a) {
   float xt = 0.f;
   if constexpr (CE) xt = r.bad ? 0.f : xt_s[0];
   // Rescale each thread's sum to the row maximum, then add in a fixed order.
-  const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_exp(m - M), red_s, 0, NW);
+  const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_factor(m - M), red_s, 0, NW);
 
   if constexpr (OP == SM_LSE) {
     if (threadIdx.x == 0) {
@@ -379,12 +388,12 @@ sm_stream(SmArgs a) {
   }
   if constexpr (OP == SM_CE) {
     if (threadIdx.x == 0)
-      a.loss[row] = r.bad ? __builtin_nanf("") : ce_loss(M, xt, sm_exp(xt - M), S);
+      a.loss[row] = r.bad ? __builtin_nanf("") : ce_loss(M, xt, sm_exp64(xt - M), S);
     return;
   }
   float inv, gt = 0.f;
   if constexpr (OP == SM_CE_VJP) {
-    const float e_t = sm_exp(xt - M);
+    const float e_t = sm_exp64(xt - M);
     const float tot = S + e_t;
     inv = r.g / tot;
     gt = -r.g * (S / tot);
@@ -412,7 +421,7 @@ sm_stream(SmArgs a) {
         const bool own = OP == SM_CE_VJP && j == tgt_chunk;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          float p = sm_exp(score(j * V + e, f[u][e]) - M) * inv;
+          float p = sm_exp64(score(j * V + e, f[u][e]) - M) * inv;
           if (own && e == tgt_e) p = gt;
           f[u][e] = p;
         }
