@@ -240,6 +240,11 @@ sm_rows(SmArgs a) {
 
   // Each pass widens the raw chunks again: the opaque redefinition keeps the compiler from
   // holding a previous pass's widened values (two floats per bf16 pair) across the barrier.
+  // Operations with a row output keep the exponentials of up to four chunks (32 registers)
+  // for the output pass instead of forming them twice.
+  constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CAUSAL || OP == SM_CE_VJP;
+  constexpr bool KEEP = OUT && NV <= 4;
+  float ek[KEEP ? NV : 1][V];
 #pragma unroll
   for (int k = 0; k < NV; ++k) __asm__ volatile("" : "+v"(xv[k]));
   float s = 0.f;
@@ -254,6 +259,7 @@ sm_rows(SmArgs a) {
       if constexpr (CE) {
         if (is_tgt(k, e)) ex = 0.f;  // R excludes the target
       }
+      if constexpr (KEEP) ek[k][e] = ex;
       s += ex;
     }
   }
@@ -286,15 +292,17 @@ sm_rows(SmArgs a) {
   }
   if (!live) return;
   char* orow = (char*)a.out + row * a.n * ESZ;
+  if constexpr (!KEEP) {
 #pragma unroll
-  for (int k = 0; k < NV; ++k) __asm__ volatile("" : "+v"(xv[k]));
+    for (int k = 0; k < NV; ++k) __asm__ volatile("" : "+v"(xv[k]));
+  }
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     float f[V];
-    unpack<BF16>(xv[k], f);
+    if constexpr (!KEEP) unpack<BF16>(xv[k], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      float p = sm_exp64(score(k, e, f[e]) - m) * inv;
+      float p = (KEEP ? ek[k][e] : sm_exp64(score(k, e, f[e]) - m)) * inv;
       if constexpr (OP == SM_CE_VJP) {
         if (is_tgt(k, e)) p = gt;
       }
