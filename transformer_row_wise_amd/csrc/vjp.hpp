@@ -168,6 +168,36 @@ __device__ __forceinline__ void team_sum4_finish(double t, double (&s)[4]) {
   for (int i = 0; i < 4; ++i) s[i] = readlane_f64(t, i);
 }
 
+// The same for two sums (RMS): lanes pair up (lane l keeps sum l & 1 of the pair), the rest
+// of the wave reduction keeps a lane's parity, and each wave posts two totals; after the
+// barrier lanes 0 .. 2 nwt - 1 hold the team's posted values (nwt <= 16) and the parity
+// classes of the lower 32 lanes are summed. Lanes 0 and 1 end with the two team totals.
+__device__ __forceinline__ void team_sum2_post(double s0, double s1, double* red) {
+  const int lane = threadIdx.x & 63;
+  const bool b = lane & 1;
+  double k = b ? s1 : s0;
+  const double u = b ? s0 : s1;
+  k += dpp<DPP_QUAD_XOR1>(u);
+  k += dpp<DPP_QUAD_XOR2>(k);
+  k = lanes_sum_mod4(k);
+  if (lane < 2) red[(threadIdx.x >> 6) * 2 + lane] = k;
+}
+
+__device__ __forceinline__ double team_sum2_read(const double* red, int wave0, int nwt) {
+  const int lane = threadIdx.x & 63;
+  const int w = lane >> 1;
+  return w < nwt ? red[(wave0 + w) * 2 + (lane & 1)] : 0.0;
+}
+
+__device__ __forceinline__ void team_sum2_finish(double t, double (&s)[2]) {
+  t += dpp<DPP_QUAD_XOR2>(t);
+  t += dpp<DPP_ROW_ROR4>(t);
+  t += dpp<DPP_ROW_ROR8>(t);
+  t = swap_sum<16>(t);
+  s[0] = readlane_f64(t, 0);
+  s[1] = readlane_f64(t, 1);
+}
+
 // A value every lane holds, moved to scalar registers (the compiler cannot tell that the
 // lanes agree).
 __device__ __forceinline__ double uniform_f64(double v) {
@@ -199,7 +229,7 @@ vjp_rows(VjpArgs a) {
   constexpr bool DW = PG, DB = PG && OP == VJP_LN;
   constexpr bool XF = BF16 && PK != PK_F32;
   constexpr int V = Fmt<BF16>::VEC;
-  __shared__ double red[2][16 * 4];          // [iteration parity][wave * 4 + sum]
+  __shared__ double red[2][16 * 4];          // [iteration parity][wave * sums + sum]
   extern __shared__ double comb[];           // (G - 1) * T * V doubles, team combine
   const int T = a.team;
   const int G = blockDim.x / T;
@@ -255,15 +285,26 @@ vjp_rows(VjpArgs a) {
         vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
       }
     }
-    team_sum4_post(ds, red[it & 1]);
+    if constexpr (OP == VJP_RMS) team_sum2_post(ds[0], ds[1], red[it & 1]);
+    else team_sum4_post(ds, red[it & 1]);
   };
-  // After the barrier that follows stats(it): the row's scalars, the same in every lane.
+  // After that barrier: this lane's slot of the posted sums.
+  auto sums_read = [&](int it) {
+    if constexpr (OP == VJP_RMS) return team_sum2_read(red[it & 1], wave0, nwt);
+    else return team_sum4_read(red[it & 1], wave0, nwt);
+  };
+  // Then the row's scalars, the same in every lane.
   auto scalars = [&](double t) {
-    double ds[4];
-    team_sum4_finish(t, ds);
     VjpRow s;
-    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
-    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
+    if constexpr (OP == VJP_RMS) {
+      double ds[2];
+      team_sum2_finish(t, ds);
+      s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
+    } else {
+      double ds[4];
+      team_sum4_finish(t, ds);
+      s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
+    }
     return vjp_row_uniform(s);
   };
   // dx of a row, and its dw / db terms.
@@ -297,7 +338,7 @@ vjp_rows(VjpArgs a) {
       if (it + 1 < iters) load_row(it + 1, xb, gb);
       stats(it, xa, ga);
       __syncthreads();
-      const VjpRow s = scalars(team_sum4_read(red[it & 1], wave0, nwt));
+      const VjpRow s = scalars(sums_read(it));
       outputs(it, xa, ga, s);
       if (it + 1 < iters) {
 #pragma unroll
@@ -322,14 +363,14 @@ vjp_rows(VjpArgs a) {
     for (int q = 0; q < R - 1; ++q) load_row(q, xs[q], gs[q]);
     stats(0, xs[0], gs[0]);
     __syncthreads();
-    VjpRow s = scalars(team_sum4_read(red[0], wave0, nwt));
+    VjpRow s = scalars(sums_read(0));
     auto step = [&](int it, int q, bool load, bool next) {
       if (load) load_row(it + R - 1, xs[(q + R - 1) % R], gs[(q + R - 1) % R]);
       double t = 0.0;
       if (next) {
         stats(it + 1, xs[(q + 1) % R], gs[(q + 1) % R]);
         __syncthreads();
-        t = team_sum4_read(red[(it + 1) & 1], wave0, nwt);
+        t = sums_read(it + 1);
       }
       outputs(it, xs[q], gs[q], s);
       if (next) s = scalars(t);
