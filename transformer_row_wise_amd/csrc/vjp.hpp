@@ -218,9 +218,11 @@ __device__ __forceinline__ VjpRow vjp_row_uniform(VjpRow s) {
 
 // Fast kernel: a block of G teams of T = a.team threads (G * T = blockDim.x); a team owns
 // one row at a time, thread t of a team keeping chunks t, t + T, ... (NV of them) of the
-// row in registers. Block b walks rows [b * rpb, min(rows, (b + 1) * rpb)), team i taking
-// rows b * rpb + i, + G, ...; every team runs the same number of iterations (a team past
-// the end reloads the last row and discards it), so the block barriers line up. EXACT: T * NV
+// row in registers. With P blocks, step it of team i of block b takes row (it G + i) P + b:
+// the blocks walk the rows strided, so that at any moment the grid streams a contiguous
+// window of the arrays (blocks that each walked a contiguous run of rows read addresses a
+// run apart, which measured slower). Every team runs the same number of iterations (a team
+// past the end reloads the last row and discards it), so the block barriers line up. EXACT: T * NV
 // chunks cover the row; otherwise chunk indexes past the end are clamped for loads and their results
 // dropped. PG: parameter gradients wanted (dw for RMS; dw and db for LN).
 template <bool BF16, int OP, int NV, int PK, bool EXACT, bool PG>
@@ -240,8 +242,6 @@ vjp_rows(VjpArgs a) {
   const int nwt = T >> 6;                    // waves per team
   const int wave0 = team * nwt;
   const int nvec = (int)(a.hidden / V);
-  const int64_t row0 = (int64_t)blockIdx.x * a.rpb;
-  const int64_t row_end = min(a.rows, row0 + a.rpb);
   const int iters = (int)((a.rpb + G - 1) / G);
 
   int jj[NV];
@@ -261,9 +261,11 @@ vjp_rows(VjpArgs a) {
 #pragma unroll
     for (int e = 0; e < V; ++e) accw[k][e] = accb[k][e] = 0.0;
 
-  auto row_of = [&](int it) { return row0 + (int64_t)it * G + team; };
+  auto row_of = [&](int it) {
+    return ((int64_t)it * G + team) * (int64_t)gridDim.x + blockIdx.x;
+  };
   auto load_row = [&](int it, u32x4 (&xv)[NV], u32x4 (&gv)[NV]) {
-    const int64_t row = min(row_of(it), row_end - 1);
+    const int64_t row = min(row_of(it), a.rows - 1);
     const char* xr = (const char*)a.x + row * a.hidden * Fmt<BF16>::ESZ;
     const char* gr = (const char*)a.g + row * a.hidden * Fmt<BF16>::ESZ;
 #pragma unroll
@@ -310,7 +312,7 @@ vjp_rows(VjpArgs a) {
   // dx of a row, and its dw / db terms.
   auto outputs = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV], const VjpRow& s) {
     const int64_t row = row_of(it);
-    if (row >= row_end) return;
+    if (row >= a.rows) return;
     char* dr = (char*)a.dx + row * a.hidden * Fmt<BF16>::ESZ;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -506,10 +508,18 @@ vjp_colsum(const double* part0, void* out0, const double* part1, void* out1, int
   const int c = threadIdx.x & 15;
   const int s = threadIdx.x >> 4;
   const int64_t col = (int64_t)blockIdx.x * 16 + c;
-  double acc = 0.0;
-  if (col < hidden) {
-    for (int64_t p = s; p < nparts; p += 16) acc += part[p * hidden + col];
+  // nparts <= 256: at most 16 rows per thread, all loaded before any is added (one memory
+  // latency instead of sixteen), then added in order.
+  static_assert(VJP_MAX_PARTIALS <= 16 * 16, "vjp_colsum covers at most 256 partial rows");
+  double v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t p = s + 16 * i;
+    v[i] = (col < hidden && p < nparts) ? part[p * hidden + col] : 0.0;
   }
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc += v[i];
   red[s][c] = acc;
   __syncthreads();
   if (s == 0 && col < hidden) {

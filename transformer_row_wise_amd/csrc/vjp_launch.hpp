@@ -5,8 +5,8 @@
 // elements, so hidden <= 8192 for bf16 and fp32):
 //   vjp_rows, a team of T = ceil(n / NV) threads (rounded up to a wave) per row, NV the
 //   smallest chunk count per thread that keeps T <= 1024; G = min(1024 / T, 8) teams per
-//   block. The grid is vjp_partials(rows) blocks of rpb consecutive rows each (with
-//   parameter gradients, one partial row per block).
+//   block. The grid is vjp_partials(rows) blocks of at most rpb rows each, taken strided
+//   (with parameter gradients, one partial row per block).
 // Otherwise vjp_generic (256 threads, 16-byte chunks or single elements, any width).
 // The partial rows are then added by vjp_colsum.
 #pragma once
