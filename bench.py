@@ -16,6 +16,10 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
 --summarize-trace TRACE_DB
                write profiles/add_rms_norm_bf16_16384x8192.md from the kernel trace of a
                --profile run and the counter summary.
+--summarize-counters PMC_DB
+               write profiles/valu_issue_suite_kernels.md (VALU issue share per kernel) from
+               a `rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE`
+               run of `bench.py --only fwd,vjp,sm`.
 --summarize-pmc FETCH_FILE WRITE_FILE
                turn two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` outputs (rocpd .db or
                counter_collection.csv) of a
@@ -604,6 +608,9 @@ def summarize_trace(trace_db):
 SUITE_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_suite -o suite -- "
                    "python3 bench.py --only vjp,rope,sm")
 SUITE_TRACE_MD = os.path.join(ROOT, "profiles", "suite_kernels_backward_rope_softmax.md")
+COUNTERS_CMD = ("rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE "
+                "-d gpurun_out/pmc_valu -o valu -- python3 bench.py --only fwd,vjp,sm")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "valu_issue_suite_kernels.md")
 
 
 def summarize_suite_trace(trace_db):
@@ -641,6 +648,51 @@ def summarize_suite_trace(trace_db):
     print("\n".join(L))
 
 
+def summarize_counters(db):
+    """VALU issue share per kernel from a `--pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU
+    GRBM_GUI_ACTIVE` run of suite groups, written to profiles/valu_issue_suite_kernels.md."""
+    import re
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    vals = {}
+    for name, cn, v in con.execute(
+            "select kernel_name, counter_name, value from counters_collection order by id"):
+        vals.setdefault(name, {}).setdefault(cn, []).append(float(v))
+    con.close()
+
+    def short(n):
+        n = re.sub(r"\(nrm::\w+\)$", "", n.replace("void ", ""))
+        n = re.sub(r"\(double const\*.*\)$", "", n)
+        return n if len(n) < 70 else n[:67] + "..."
+
+    L = ["# VALU issue of the suite kernels on one MI355X (`rocprofv3 --pmc`)", "",
+         "Counters per dispatch (median over the dispatches of each kernel) of a run of the "
+         "forward, backward and softmax suite groups. GRBM_GUI_ACTIVE reads the sum over the "
+         "8 XCDs: an eighth of it, at 2.4 GHz, matches each kernel's traced duration. "
+         "`VALU share` = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) / "
+         "(1024 SIMDs x the per-XCD active cycles): near 100% the kernel is bound by "
+         "instruction issue, not by HBM. A kernel that serves several workloads (the same "
+         "template at several shapes) shows the median over all of its dispatches; under the "
+         "counters every dispatch runs alone, so durations exceed the suite's.", "", "From the repository root, with `TMPDIR=/tmp`:",
+         "", "```", COUNTERS_CMD, "python3 bench.py --summarize-counters "
+         "gpurun_out/pmc_valu/valu_results.db", "```", "",
+         "| kernel | dispatches | us (active cycles / 8 / 2.4 GHz) | VALU instructions per wave "
+         "| VALU share |", "|---|---|---|---|---|"]
+    for name, cs in sorted(vals.items()):
+        if "nrm::" not in name or "GRBM_GUI_ACTIVE" not in cs or "SQ_INSTS_VALU" not in cs:
+            continue
+        gui = statistics.median(cs["GRBM_GUI_ACTIVE"]) / 8
+        vi = statistics.median(cs["SQ_INSTS_VALU"])
+        waves = statistics.median(cs["SQ_WAVES"])
+        share = 4 * vi / 1024 / gui if gui else 0.0
+        L.append(f"| `{short(name)}` | {len(cs['SQ_INSTS_VALU'])} | {gui / 2400:.1f} | "
+                 f"{vi / waves:.0f} | {100 * share:.0f}% |")
+    with open(COUNTERS_MD, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -655,7 +707,11 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DB")
     ap.add_argument("--summarize-suite-trace", metavar="TRACE_DB")
+    ap.add_argument("--summarize-counters", metavar="PMC_DB")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return 0
