@@ -129,9 +129,12 @@ __device__ __forceinline__ void vjp_outputs(const float (&f)[V], const float (&g
         accw[e] = __builtin_fma(gx, s.r, accw[e]);
       }
     } else {
-      // (d - m1) first: it is exactly 0 where d equals its row mean (a one-element row).
+      // d - m1 as one fma: g w is exact in fp64 (bf16 or fp32 values), so this is the
+      // exact difference rounded once, as (d - m1) from the exact d would be; it is exactly
+      // 0 where d equals its row mean (a one-element row).
       const double xh = (xd - s.mu) * s.r;
-      dxv[e] = f64_to_f32(__builtin_fma(-xh, s.m2, d - s.m1) * s.r);
+      const double dm = __builtin_fma(gd, (double)wv[e], -s.m1);
+      dxv[e] = f64_to_f32(__builtin_fma(-xh, s.m2, dm) * s.r);
       if constexpr (DW) accw[e] = __builtin_fma(gd, xh, accw[e]);
       if constexpr (DB) accb[e] += gd;
     }
