@@ -357,8 +357,12 @@ hipError_t go_fast(const RopeArgs& a0, hipStream_t stream) {
   constexpr int RPB = 4 * (64 / G);
   const int64_t steps = (a.BH + (int64_t)RPB * R - 1) / ((int64_t)RPB * R);
   // Enough blocks for about one full round on the chip (~1024 blocks of 256 threads),
-  // while each block's sin/cos table is shared by as many rows as possible.
-  int64_t chunks = (1024 + a.L - 1) / a.L;
+  // while each block's sin/cos table is shared by as many rows as possible. Rotation-only
+  // launches with four rows per lane group (157 VGPRs: 768 blocks resident) take one block
+  // per position instead, so that the grid fits one round (Rope [8,32,512,128] 16.1 ->
+  // 15.2 us; with the normalisation it measured slightly slower, so NormRope keeps the
+  // wider grid).
+  int64_t chunks = (R == 4 && !a.normalize) ? 1 : (1024 + a.L - 1) / a.L;
   if (chunks > steps) chunks = steps;
   if (chunks > 65535) chunks = 65535;
   if (chunks < 1) chunks = 1;
