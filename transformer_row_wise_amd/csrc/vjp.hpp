@@ -14,10 +14,11 @@
 // one unit in the last place of the result: an fp32 statistic would miss it on a few
 // elements per million.
 //
-// dw and db sum over rows. A block owns a contiguous run of rows and accumulates its column
-// sums in fp64 registers (each thread always holds the same columns); at the end the block
-// writes one fp64 partial row to the caller's workspace, and vjp_colsum adds the partial
-// rows in a fixed order. Results are therefore identical run to run.
+// dw and db sum over rows. A block owns a fixed set of rows (vjp_rows: rows strided across
+// the blocks; vjp_generic: a contiguous run) and accumulates its column sums in fp64
+// registers (each thread always holds the same columns); at the end the block writes one
+// fp64 partial row to the caller's workspace, and vjp_colsum adds the partial rows in a
+// fixed order. Results are therefore identical run to run.
 #pragma once
 
 #include "row_kernels.hpp"
@@ -40,14 +41,14 @@ struct VjpArgs {
   double* part_b;     // [blocks][hidden] partial sums for db (LN), or null
   int64_t rows;
   int64_t hidden;     // < 2^31
-  int64_t rpb;        // rows per block
+  int64_t rpb;        // rows per block, at most
   double inv_n;       // 1 / hidden
   float eps;
   int w_f32;          // w stored as fp32 (else bf16, only with bf16 activations)
   int team;           // threads per row (fast kernel): a multiple of 64
 };
 
-// Row scalars of one row, from its four sums.
+// Row scalars of one row, from its sums (two for RMS, four for LN).
 struct VjpRow {
   double r;    // reciprocal standard deviation
   double c;    // RMS: r^3 sum(g w x) / D
