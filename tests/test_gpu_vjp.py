@@ -45,6 +45,18 @@ def test_vjp_row_counts(nrm_lib, ln, rows, hidden):
     check_vjp(nrm_lib, _inp(rows, hidden, "bf16", "bf16", rows, ln), ln)
 
 
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("rows", [512, 768, 1277, 1536, 1792, 2048, 2301, 2816])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_vjp_rows_per_block(nrm_lib, ln, rows, dt):
+    """One 1024-thread team per row (hidden 8192) with 2, 3, 5, 6, 7, 8, 9 and 11 rows per
+    block (256 blocks, rows strided): every mix of the row ring's start, its unrolled loop
+    and its last rows, and of the two-chunk loop for fp32."""
+    say(f"vjp {'ln' if ln else 'rms'} rows={rows} hidden=8192 {dt}")
+    sel = np.r_[0:4, rows // 2 - 2:rows // 2 + 2, rows - 4:rows]
+    check_vjp(nrm_lib, _inp(rows, 8192, dt, dt, rows + 3, ln), ln, rows_sel=sel, chunk=1024)
+
+
 @pytest.mark.parametrize("path", ["chunked", "scalar"])
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
 @pytest.mark.parametrize("hidden", [512, 4096, 8192])
