@@ -16,7 +16,9 @@ from gpu_util import DEV, dev, f64, forced_path, say
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = [1, 2, 7, 8, 64, 100, 512, 520, 4096, 8192, 16384, 65536, 128256, 131072, 140000]
+# 20000 and 40000: streaming rows of one and two steps (their first step parked in LDS)
+WIDTHS = [1, 2, 7, 8, 64, 100, 512, 520, 4096, 8192, 16384, 20000, 40000, 65536, 128256, 131072,
+          140000]
 PATHS = [None, "chunked", "scalar"]
 
 
@@ -77,7 +79,7 @@ def _ce_check(nrm, inp, dt, path=None, i32=False, sel=None):
     return loss, want
 
 
-@pytest.mark.parametrize("V", [2, 100, 1000, 32000, 128256, 151936])
+@pytest.mark.parametrize("V", [2, 100, 1000, 20000, 32000, 128256, 151936])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_cross_entropy_vocab(nrm_lib, V, dt):
     say(f"cross_entropy V={V} {dt}")
