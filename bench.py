@@ -27,7 +27,8 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
                by what the same counters read for the 16-byte copy kernel of known size.
 
 Fields beyond the contract: roofline (algorithmic bytes per launch over the average launch
-time measured with HIP events on the launch stream, against 8 TB/s), copy_ceiling_GBps (a
+time measured with HIP events on the launch stream, against 8 TB/s), copy2_ceiling_GBps (two
+arrays copied into two, the headline's byte pattern without arithmetic), copy_ceiling_GBps (a
 plain 16-byte copy of the same byte count), and cpu_baseline (the fp64 oracle on a bounded
 sample of the same workload, in a process pool over the host's cores).
 """
@@ -50,6 +51,7 @@ ROWS, HIDDEN = 16384, 8192
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_add_rms_norm_bf16_16384x8192.json")
 HEADLINE_KERNEL = "row_block<true, 1, 2, 1, true>"  # bf16, add-RMSNorm, 2 chunks/thread, w bf16, exact
 COPY_KERNEL = "copy16_kernel"
+COPY2_KERNEL = "copy16x2_kernel"
 
 
 # Files the headline kernel and the copy kernel that scales the counters are built from.
@@ -150,6 +152,22 @@ def copy_ceiling(nbytes, steps):
     return 2 * half / (gpu_ms * 1e-3) / 1e9
 
 
+def copy2_ceiling(nbytes, steps):
+    """GB/s of the library's two-into-two 16-byte copy moving nbytes in all: two arrays of
+    nbytes/4 in, two out (the headline's byte pattern without arithmetic)."""
+    import torch
+    import transformer_row_wise_amd as nrm
+
+    q = (nbytes // 4) // 16 * 16
+    s1 = torch.empty(q, dtype=torch.uint8, device="cuda")
+    s2, d1, d2 = torch.empty_like(s1), torch.empty_like(s1), torch.empty_like(s1)
+    s1.fill_(1)
+    s2.fill_(2)
+    gpu_ms, _ = time_calls(lambda i: nrm.bench_copy2(s1, s2, d1, d2), steps, steps)
+    del s1, s2, d1, d2
+    return 4 * q / (gpu_ms * 1e-3) / 1e9
+
+
 def stored_traffic(nbytes):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel sources; else None."""
@@ -242,9 +260,11 @@ def headline(args):
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = nbytes / (wall_ms * 1e-3) / 1e9
     ceiling = copy_ceiling(nbytes, max(100, args.steps // 2))
+    ceiling2 = copy2_ceiling(nbytes, max(100, args.steps // 2))
     if args.profile:
         print(json.dumps({"profile_run": True, "avg_launch_us": gpu_ms * 1e3,
-                          "achieved_GBps": achieved, "copy_GBps": ceiling}), flush=True)
+                          "achieved_GBps": achieved, "copy_GBps": ceiling,
+                          "copy2_GBps": ceiling2}), flush=True)
         return
     traffic = stored_traffic(nbytes)
     res = {
@@ -270,6 +290,7 @@ def headline(args):
         "bytes_per_step": nbytes,
         "kernel_us_mean": round(gpu_ms * 1e3, 2),
         "copy_ceiling_GBps": round(ceiling, 1),
+        "copy2_ceiling_GBps": round(ceiling2, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -577,12 +598,17 @@ def summarize_trace(trace_db):
         L.append(f"| `{name}` | {calls} | {avg:.2f} | {sum(tail) / len(tail):.2f} | "
                  f"{min(d):.2f} | {max(d):.2f} |")
     kavg = [r[3] for r in rows if HEADLINE_KERNEL in r[0]][0]
-    cavg = [r[3] for r in rows if COPY_KERNEL in r[0]][0]
+    cavg = [r[3] for r in rows if COPY_KERNEL in r[0] and COPY2_KERNEL not in r[0]][0]
+    c2 = [r[3] for r in rows if COPY2_KERNEL in r[0]]
     cb = 2 * ((alg // 2) // 16 * 16)
+    cb2 = 4 * ((alg // 4) // 16 * 16)
+    two = (f" Two arrays into two (the headline's pattern without arithmetic): "
+           f"{cb2 / (c2[0] * 1e-6) / 1e9:.0f} GB/s ({100 * cb2 / (c2[0] * 1e-6) / 8e12:.1f}%)."
+           if c2 else "")
     L += ["", f"Headline kernel: {alg:,} algorithmic bytes / {kavg:.2f} us = "
           f"{alg / (kavg * 1e-6) / 1e9:.0f} GB/s ({100 * alg / (kavg * 1e-6) / 8e12:.1f}% of 8 TB/s). "
           f"Copy of the same byte count: {cb / (cavg * 1e-6) / 1e9:.0f} GB/s "
-          f"({100 * cb / (cavg * 1e-6) / 8e12:.1f}%).", "",
+          f"({100 * cb / (cavg * 1e-6) / 8e12:.1f}%).{two}", "",
           "## HBM bytes (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, one counter per run)",
           "", "```", *PMC_CMDS, "```", "",
           "| quantity | FETCH_SIZE | WRITE_SIZE |", "|---|---|---|",

@@ -380,6 +380,18 @@ int nrm_version(void);
  */
 nrm_status nrm_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
+/*
+ * Measurement helper, not one of the operations above: dst1 = src1 and dst2 = src2, `bytes`
+ * bytes each, with one 16-byte load of each source and one 16-byte store of each destination
+ * per thread: the residual add-RMSNorm's byte pattern (two arrays in, two out) without
+ * arithmetic, reported as that pattern's achievable-bandwidth ceiling. All four arrays are
+ * device memory, 16-byte aligned; no destination may overlap a source or the other
+ * destination (the two sources may overlap). Errors: NULL -> NRM_ERR_NULL; bytes < 0 or not
+ * a multiple of 16 -> NRM_ERR_SHAPE; misaligned or overlapping -> NRM_ERR_ALIAS.
+ */
+nrm_status nrm_bench_copy2(const void* src1, const void* src2, void* dst1, void* dst2,
+                           int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

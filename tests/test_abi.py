@@ -84,6 +84,7 @@ def test_null_pointers(L):
     assert ln(L, x=None) == NULL
     assert rope(L, out=None) == NULL and "out_or_cache" in err(L)
     assert L.nrm_bench_copy(None, P, 16, None) == NULL
+    assert L.nrm_bench_copy2(P, P + MB, None, P + 3 * MB, 16, None) == NULL
 
 
 def test_shapes(L):
@@ -103,6 +104,7 @@ def test_shapes(L):
     assert rope(L, cache=1, cache_len=10, offset=7, L_=4) == SHAPE
     assert "offset + L must be <= cache_len (10), got 7 + 4" in err(L)
     assert L.nrm_bench_copy(P, P + MB, 17, None) == SHAPE
+    assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB, P + 3 * MB, 17, None) == SHAPE
 
 
 def test_dtypes(L):
@@ -129,6 +131,9 @@ def test_aliasing(L):
     assert rope(L, out=P, B=0) == OK  # out == x: allowed
     assert rope(L, out=P, cache=1, cache_len=8) == ALIAS and "cache must not overlap x" in err(L)
     assert L.nrm_bench_copy(P, P + 8, 64, None) == ALIAS
+    assert L.nrm_bench_copy2(P, P + MB, P + 32, P + 3 * MB, 64, None) == ALIAS   # dst1 on src1
+    assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB, P + 2 * MB, 64, None) == ALIAS  # dst1 = dst2
+    assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB + 8, P + 3 * MB, 64, None) == ALIAS  # unaligned
 
 
 def test_zero_rows_is_a_noop(L):
@@ -138,6 +143,7 @@ def test_zero_rows_is_a_noop(L):
     assert rope(L, B=0) == OK and rope(L, L_=0) == OK and rope(L, H=0) == OK
     assert rope(L, L_=0, cache=1, cache_len=0) == OK
     assert L.nrm_bench_copy(P, P + MB, 0, None) == OK
+    assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB, P + 3 * MB, 0, None) == OK
 
 
 def test_error_message_cleared_by_next_call(L):

@@ -602,4 +602,26 @@ nrm_status nrm_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t
   return launched(fn, nrm::launch_copy16(src, dst, bytes / 16, stream));
 }
 
+nrm_status nrm_bench_copy2(const void* src1, const void* src2, void* dst1, void* dst2,
+                           int64_t bytes, hipStream_t stream) {
+  static const char* fn = "nrm_bench_copy2";
+  g_err.clear();
+  if (bytes < 0 || bytes % 16)
+    return fail(NRM_ERR_SHAPE, "%s: bytes must be a non-negative multiple of 16, got %lld", fn,
+                (long long)bytes);
+  if (bytes == 0) return NRM_OK;
+  if (!src1 || !src2 || !dst1 || !dst2)
+    return fail(NRM_ERR_NULL, "%s: src1, src2, dst1 and dst2 must not be NULL, got %p %p %p %p",
+                fn, src1, src2, dst1, dst2);
+  if (!aligned16(src1) || !aligned16(src2) || !aligned16(dst1) || !aligned16(dst2))
+    return fail(NRM_ERR_ALIAS, "%s: every array must be 16-byte aligned, got %p %p %p %p", fn,
+                src1, src2, dst1, dst2);
+  const auto s1 = span(src1, bytes), s2 = span(src2, bytes), o1 = span(dst1, bytes),
+             o2 = span(dst2, bytes);
+  if (overlap(o1, s1) || overlap(o1, s2) || overlap(o2, s1) || overlap(o2, s2) || overlap(o1, o2))
+    return fail(NRM_ERR_ALIAS, "%s: a destination overlaps a source or the other destination",
+                fn);
+  return launched(fn, nrm::launch_copy16x2(src1, src2, dst1, dst2, bytes / 16, stream));
+}
+
 }  // extern "C"

@@ -1,5 +1,5 @@
-// The 16-byte copy used as the bandwidth ceiling and to calibrate the byte counters, and
-// the NRM_FORCE_PATH test override.
+// The 16-byte copies used as bandwidth ceilings (one stream into one, and two into two) and
+// to calibrate the byte counters, and the NRM_FORCE_PATH test override.
 #include <cstdlib>
 #include <cstring>
 
@@ -34,6 +34,29 @@ hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t st
   const int64_t blocks = (n16 + 255) / 256;
   if (blocks > kMaxCopyGrid) return hipErrorInvalidValue;
   copy16_kernel<<<(unsigned)blocks, 256, 0, stream>>>((const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError();
+}
+
+// Two streams copied into two, one 16-byte chunk of each per thread, 512 threads per block,
+// non-temporal: the residual add-RMSNorm's byte pattern (two inputs in, two outputs out)
+// without arithmetic. The fastest shape measured for that pattern on MI355X (~77% of 8 TB/s;
+// one or two chunks per thread at 256 or 1024 threads reach 74-76%).
+__global__ void __launch_bounds__(512)
+copy16x2_kernel(const u32x4* s1, const u32x4* s2, u32x4* d1, u32x4* d2, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x;
+  if (i < n) {
+    const u32x4 a = ld16_nt(s1 + i), b = ld16_nt(s2 + i);
+    st16_nt(d1 + i, a);
+    st16_nt(d2 + i, b);
+  }
+}
+
+hipError_t launch_copy16x2(const void* s1, const void* s2, void* d1, void* d2, int64_t n16,
+                           hipStream_t stream) {
+  const int64_t blocks = (n16 + 511) / 512;
+  if (blocks > kMaxCopyGrid) return hipErrorInvalidValue;
+  copy16x2_kernel<<<(unsigned)blocks, 512, 0, stream>>>((const u32x4*)s1, (const u32x4*)s2,
+                                                        (u32x4*)d1, (u32x4*)d2, n16);
   return hipGetLastError();
 }
 

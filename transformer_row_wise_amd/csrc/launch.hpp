@@ -19,5 +19,7 @@ template <bool BF16, int OP>
 hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream);
 
 hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t stream);
+hipError_t launch_copy16x2(const void* s1, const void* s2, void* d1, void* d2, int64_t n16,
+                           hipStream_t stream);
 
 }  // namespace nrm
