@@ -160,6 +160,53 @@ def test_rope_positions_matches_offset_form(nrm_lib):
     compare.check_exact_bits(qo, r.transpose(0, 1).contiguous(), "positions vs offset form")
 
 
+@pytest.mark.parametrize("Hq,Hk", [(8, 2), (1, 1), (3, 0), (40, 40)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("trad", [False, True])
+@pytest.mark.parametrize("fkind", [None, "loguniform"])
+def test_rope_positions_many_tokens(nrm_lib, Hq, Hk, dt, trad, fkind):
+    """4099 tokens (not a multiple of the positions a block takes) of 128 rotated features:
+    the several-positions-per-block kernel, with 1 to 80 rows per position, bf16 and fp32,
+    both pair layouts and both frequency forms; the oracle checks sampled tokens, the first
+    and last ones among them."""
+    T, D = 4099, 128
+    say(f"rope_positions T={T} Hq={Hq} Hk={Hk} {dt} trad={trad} freqs={fkind}")
+    inp = workloads.rope_qk_inputs(T, Hq, Hk, D, dt, seed=Hq + 3 * Hk, positions="random",
+                                   max_position=1 << 20)
+    freqs, ms = _freqs(fkind, D, np.random.default_rng(Hq))
+    qo, ko = nrm_lib.rope_positions(dev(inp.positions), dev(inp.q),
+                                    dev(inp.k) if Hk else None, dims=D, traditional=trad,
+                                    base=10000.0, freqs=dev(freqs), mscale=ms)
+    torch.cuda.synchronize()
+    sel = np.unique(np.r_[0:5, T - 5:T, np.random.default_rng(T).choice(T, 40, replace=False)])
+    kw = dict(dims=D, traditional=trad, base=10000.0, scale=1.0, forward=True, dtype=dt,
+              freqs=f64(freqs), mscale=ms)
+    p = inp.positions.numpy()[sel]
+    compare.check_output(qo[sel], oracle.rope_positions(f64(inp.q[sel]), p, **kw), dt, "q")
+    if Hk:
+        compare.check_output(ko[sel], oracle.rope_positions(f64(inp.k[sel]), p, **kw), dt, "k")
+
+
+@pytest.mark.parametrize("i32", [False, True])
+def test_rope_positions_many_tokens_inverse(nrm_lib, i32):
+    """The inverse rotation, int64 or int32 positions and a position scale on the
+    several-positions kernel, against the oracle on sampled tokens."""
+    T, Hq, Hk, D = 4103, 8, 2, 128
+    say(f"rope_positions inverse T={T} int32={i32}")
+    inp = workloads.rope_qk_inputs(T, Hq, Hk, D, "bf16", seed=21, positions="random",
+                                   max_position=1 << 20)
+    pos = inp.positions.to(torch.int32) if i32 else inp.positions
+    qo, ko = nrm_lib.rope_positions(dev(pos), dev(inp.q), dev(inp.k), base=10000.0, scale=0.5,
+                                    forward=False)
+    torch.cuda.synchronize()
+    sel = np.unique(np.r_[0:3, T - 3:T, np.random.default_rng(22).choice(T, 30, replace=False)])
+    kw = dict(dims=D, traditional=False, base=10000.0, scale=0.5, forward=False, dtype="bf16",
+              freqs=None, mscale=1.0)
+    p = inp.positions.numpy()[sel]
+    compare.check_output(qo[sel], oracle.rope_positions(f64(inp.q[sel]), p, **kw), "bf16", "q")
+    compare.check_output(ko[sel], oracle.rope_positions(f64(inp.k[sel]), p, **kw), "bf16", "k")
+
+
 @pytest.mark.slow
 def test_rope_positions_full_size(nrm_lib):
     """The benchmark's prefill shape ([16384, 32 + 8, 128] bf16, base 500000, divisors

@@ -294,6 +294,108 @@ rope_fast(RopeArgs a) {
   }
 }
 
+// Rotation-only rows over many positions, few rows per position (the query/key form: one
+// token's heads): a block of 256 threads takes PB consecutive positions, builds their
+// (cos, sin) tables in one pass of its threads (LDS), and walks its PB * BH row slots
+// (position-major) in steps of 256 / G rows, one row per lane group, through a ring of three
+// steps' loads (two steps in flight ahead of the one rotated). Each row reads its position's
+// (cos, sin) from LDS. One position per block measured slower: every block paid the table's
+// latency (and the frequency load) for only BH rows, and its rows took two steps whose second
+// waited for the first. The arithmetic is rope_fast's, term for term (no normalisation: the
+// features enter unscaled, the rotation is scaled by mscale).
+template <bool BF16, int MODE, int G, int PB>
+__global__ void __launch_bounds__(256)
+rope_multi(RopeArgs a) {
+  constexpr bool HALF = MODE == M_HALF;
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr int SPS = 256 / G;  // row slots per step
+  constexpr int NR = 3;         // ring of steps
+  extern __shared__ double2 cs_t[];  // [PB][half] (cos, sin)
+  const int half = a.dims / 2;
+  const int lane = threadIdx.x & 63;
+  const int g = threadIdx.x / G;  // lane group of the block
+  const int lj = lane % G;
+  const int64_t l0 = (int64_t)blockIdx.x * PB;
+  const int npos = (int)min((int64_t)PB, a.L - l0);
+  const int nslots = npos * (int)a.BH;
+  const int nsteps = (nslots + SPS - 1) / SPS;
+  const int off_u = lj * V;
+  const int off_v = half + off_u;
+  const double ms = (double)a.mscale;
+
+  u32x4 xu[NR], xv[NR];
+  auto slot_of = [&](int k) { return k * SPS + g; };
+  auto load = [&](int k, u32x4& u, u32x4& v) {
+    const int sl = min(slot_of(k), nslots - 1);
+    const int p = sl / (int)a.BH, bh = sl - p * (int)a.BH;
+    const char* xrow = rope_in_row(a, bh, l0 + p, ESZ);
+    u = ld16_nt(xrow + off_u * ESZ);
+    v = ld16_nt(xrow + off_v * ESZ);
+  };
+#pragma unroll
+  for (int q = 0; q < NR - 1; ++q) load(q, xu[q], xv[q]);
+  for (int t = threadIdx.x; t < npos * half; t += 256) {
+    const int p = t / half, i = t - p * half;
+    const double theta = rope_theta(a, i);
+    const double ang = ((double)a.scale * (double)rope_position(a, l0 + p)) * theta;
+    double sn, cs;
+    rope_sincos(ang, &sn, &cs);
+    cs_t[t] = double2{cs, a.forward ? sn : -sn};
+  }
+  __syncthreads();
+
+  auto rotate = [&](int k, const u32x4& ru, const u32x4& rv) {
+    const int sl = slot_of(k);
+    if (sl >= nslots) return;
+    const int p = sl / (int)a.BH, bh = sl - p * (int)a.BH;
+    const double2* tab = cs_t + p * half;
+    float fu[V], fv[V];
+    unpack<BF16>(ru, fu);
+    unpack<BF16>(rv, fv);
+    if constexpr (HALF) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const double2 t = tab[lj * V + e];
+        const double u = (double)fu[e], v = (double)fv[e];
+        fu[e] = f64_to_f32((u * t.x - v * t.y) * ms);
+        fv[e] = f64_to_f32((u * t.y + v * t.x) * ms);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < V / 2; ++e) {
+        const double2 t1 = tab[lj * (V / 2) + e];
+        const double2 t2 = tab[half / 2 + lj * (V / 2) + e];
+        const double u = (double)fu[2 * e], v = (double)fu[2 * e + 1];
+        fu[2 * e] = f64_to_f32((u * t1.x - v * t1.y) * ms);
+        fu[2 * e + 1] = f64_to_f32((u * t1.y + v * t1.x) * ms);
+        const double u2 = (double)fv[2 * e], v2 = (double)fv[2 * e + 1];
+        fv[2 * e] = f64_to_f32((u2 * t2.x - v2 * t2.y) * ms);
+        fv[2 * e + 1] = f64_to_f32((u2 * t2.y + v2 * t2.x) * ms);
+      }
+    }
+    char* orow = rope_out_row(a, bh, l0 + p, ESZ);
+    st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
+    st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
+  };
+  // Unrolled by NR so that every ring buffer keeps its registers (as in the backward).
+  int k0 = 0;
+  for (; k0 + 2 * NR - 1 <= nsteps; k0 += NR) {
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      load(k0 + q + NR - 1, xu[(q + NR - 1) % NR], xv[(q + NR - 1) % NR]);
+      rotate(k0 + q, xu[q], xv[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2 * NR - 2; ++q) {
+    const int k = k0 + q;
+    if (k >= nsteps) break;
+    if (k + NR - 1 < nsteps) load(k + NR - 1, xu[(q + NR - 1) % NR], xv[(q + NR - 1) % NR]);
+    rotate(k, xu[q % NR], xv[q % NR]);
+  }
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(256)
 rope_generic(RopeArgs a) {
@@ -413,6 +515,24 @@ hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t strea
     const int mode = !a.traditional ? M_HALF : (half % V == 0 ? M_TRAD2 : M_TRAD1);
     const int npc = mode == M_TRAD1 ? a.dims / V : half / V;
     const int nqc = (a.D - a.dims) / V;
+    // Rotation only, every feature rotated, few rows per position and many positions:
+    // several positions per block (rope_multi).
+    if (!a.normalize && nqc == 0 && mode != M_TRAD1 && a.BH < 256 && a.L >= 4096 &&
+        (npc == 8 || npc == 16)) {
+      constexpr int PB = 4;
+      const size_t lds = (size_t)PB * half * sizeof(double2);
+      const int64_t blocks = (a.L + PB - 1) / PB;
+      if (blocks <= 0x7fffffff) {
+        if (mode == M_HALF) {
+          if (npc == 8) rope_multi<BF16, M_HALF, 8, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
+          else rope_multi<BF16, M_HALF, 16, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
+        } else {
+          if (npc == 8) rope_multi<BF16, M_TRAD2, 8, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
+          else rope_multi<BF16, M_TRAD2, 16, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
+        }
+        return hipGetLastError();
+      }
+    }
     for (int g = 8; g <= 64; g *= 2) {
       if (npc <= g && nqc <= 2 * g) {
         const int qc = (nqc + g - 1) / g;
