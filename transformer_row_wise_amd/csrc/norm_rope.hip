@@ -297,11 +297,12 @@ rope_fast(RopeArgs a) {
 // Rotation-only rows over many positions, few rows per position (the query/key form: one
 // token's heads): a block of 256 threads takes PB consecutive positions, builds their
 // (cos, sin) tables in one pass of its threads (LDS), and walks its PB * BH row slots
-// (position-major) in steps of 256 / G rows, one row per lane group, through a ring of three
-// steps' loads (two steps in flight ahead of the one rotated). Each row reads its position's
-// (cos, sin) from LDS. One position per block measured slower: every block paid the table's
-// latency (and the frequency load) for only BH rows, and its rows took two steps whose second
-// waited for the first. The arithmetic is rope_fast's, term for term (no normalisation: the
+// (position-major) in steps of 256 / G rows, one row per lane group, through a ring of two
+// steps' loads (the next step in flight while one is rotated; 123 VGPRs, four waves per SIMD:
+// a ring of three at 131 VGPRs and eight positions per block both measured slower). Each row
+// reads its position's (cos, sin) from LDS. One position per block measured slower still:
+// every block paid the table's latency (and the frequency load) for only BH rows, and its
+// rows took two steps whose second waited for the first. The arithmetic is rope_fast's, term for term (no normalisation: the
 // features enter unscaled, the rotation is scaled by mscale).
 template <bool BF16, int MODE, int G, int PB>
 __global__ void __launch_bounds__(256)
@@ -310,7 +311,7 @@ rope_multi(RopeArgs a) {
   constexpr int V = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr int SPS = 256 / G;  // row slots per step
-  constexpr int NR = 3;         // ring of steps
+  constexpr int NR = 2;         // ring of steps
   extern __shared__ double2 cs_t[];  // [PB][half] (cos, sin)
   const int half = a.dims / 2;
   const int lane = threadIdx.x & 63;
