@@ -304,7 +304,7 @@ rope_fast(RopeArgs a) {
 // every block paid the table's latency (and the frequency load) for only BH rows, and its
 // rows took two steps whose second waited for the first. The arithmetic is rope_fast's, term for term (no normalisation: the
 // features enter unscaled, the rotation is scaled by mscale).
-template <bool BF16, int MODE, int G, int PB>
+template <bool BF16, int MODE, int G, int PB, bool MS>
 __global__ void __launch_bounds__(256)
 rope_multi(RopeArgs a) {
   constexpr bool HALF = MODE == M_HALF;
@@ -323,7 +323,7 @@ rope_multi(RopeArgs a) {
   const int nsteps = (nslots + SPS - 1) / SPS;
   const int off_u = lj * V;
   const int off_v = half + off_u;
-  const double ms = (double)a.mscale;
+  const double ms = (double)a.mscale;  // MS: mscale != 1 (else the product is skipped: exact)
 
   u32x4 xu[NR], xv[NR];
   auto slot_of = [&](int k) { return k * SPS + g; };
@@ -359,8 +359,8 @@ rope_multi(RopeArgs a) {
       for (int e = 0; e < V; ++e) {
         const double2 t = tab[lj * V + e];
         const double u = (double)fu[e], v = (double)fv[e];
-        fu[e] = f64_to_f32((u * t.x - v * t.y) * ms);
-        fv[e] = f64_to_f32((u * t.y + v * t.x) * ms);
+        fu[e] = f64_to_f32(MS ? (u * t.x - v * t.y) * ms : u * t.x - v * t.y);
+        fv[e] = f64_to_f32(MS ? (u * t.y + v * t.x) * ms : u * t.y + v * t.x);
       }
     } else {
 #pragma unroll
@@ -368,11 +368,11 @@ rope_multi(RopeArgs a) {
         const double2 t1 = tab[lj * (V / 2) + e];
         const double2 t2 = tab[half / 2 + lj * (V / 2) + e];
         const double u = (double)fu[2 * e], v = (double)fu[2 * e + 1];
-        fu[2 * e] = f64_to_f32((u * t1.x - v * t1.y) * ms);
-        fu[2 * e + 1] = f64_to_f32((u * t1.y + v * t1.x) * ms);
+        fu[2 * e] = f64_to_f32(MS ? (u * t1.x - v * t1.y) * ms : u * t1.x - v * t1.y);
+        fu[2 * e + 1] = f64_to_f32(MS ? (u * t1.y + v * t1.x) * ms : u * t1.y + v * t1.x);
         const double u2 = (double)fv[2 * e], v2 = (double)fv[2 * e + 1];
-        fv[2 * e] = f64_to_f32((u2 * t2.x - v2 * t2.y) * ms);
-        fv[2 * e + 1] = f64_to_f32((u2 * t2.y + v2 * t2.x) * ms);
+        fv[2 * e] = f64_to_f32(MS ? (u2 * t2.x - v2 * t2.y) * ms : u2 * t2.x - v2 * t2.y);
+        fv[2 * e + 1] = f64_to_f32(MS ? (u2 * t2.y + v2 * t2.x) * ms : u2 * t2.y + v2 * t2.x);
       }
     }
     char* orow = rope_out_row(a, bh, l0 + p, ESZ);
@@ -524,12 +524,24 @@ hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t strea
       const size_t lds = (size_t)PB * half * sizeof(double2);
       const int64_t blocks = (a.L + PB - 1) / PB;
       if (blocks <= 0x7fffffff) {
+        const unsigned nb = (unsigned)blocks;
+        const bool ms = a.mscale != 1.f;  // a unit mscale skips its product (exact either way)
         if (mode == M_HALF) {
-          if (npc == 8) rope_multi<BF16, M_HALF, 8, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
-          else rope_multi<BF16, M_HALF, 16, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
+          if (npc == 8) {
+            if (ms) rope_multi<BF16, M_HALF, 8, PB, true><<<nb, 256, lds, stream>>>(a);
+            else rope_multi<BF16, M_HALF, 8, PB, false><<<nb, 256, lds, stream>>>(a);
+          } else {
+            if (ms) rope_multi<BF16, M_HALF, 16, PB, true><<<nb, 256, lds, stream>>>(a);
+            else rope_multi<BF16, M_HALF, 16, PB, false><<<nb, 256, lds, stream>>>(a);
+          }
         } else {
-          if (npc == 8) rope_multi<BF16, M_TRAD2, 8, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
-          else rope_multi<BF16, M_TRAD2, 16, PB><<<(unsigned)blocks, 256, lds, stream>>>(a);
+          if (npc == 8) {
+            if (ms) rope_multi<BF16, M_TRAD2, 8, PB, true><<<nb, 256, lds, stream>>>(a);
+            else rope_multi<BF16, M_TRAD2, 8, PB, false><<<nb, 256, lds, stream>>>(a);
+          } else {
+            if (ms) rope_multi<BF16, M_TRAD2, 16, PB, true><<<nb, 256, lds, stream>>>(a);
+            else rope_multi<BF16, M_TRAD2, 16, PB, false><<<nb, 256, lds, stream>>>(a);
+          }
         }
         return hipGetLastError();
       }
