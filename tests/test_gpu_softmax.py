@@ -50,10 +50,13 @@ def test_softmax_paths_and_rows(nrm_lib, path, n, rows):
 
 @pytest.mark.parametrize("N,R,L,rows", [(2, 8, 8, 8), (2, 64, 512, 64), (1, 512, 512, 512),
                                         (3, 6, 4, 3), (2, 16, 1000, 8), (1, 12, 2, 12),
-                                        (4, 128, 4096, 128)])
+                                        (4, 128, 4096, 128), (1, 2048, 16400, 2048),
+                                        (1, 64, 70000, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("path", [None, "scalar"])
 def test_causal_softmax(nrm_lib, N, R, L, rows, dt, path):
+    # L = 16400 and 70000 (bf16): rows kept in registers, 8 and 16 chunks per thread, the
+    # cut inside the last chunks of each thread, whole chunks past it never read
     say(f"causal N={N} R={R} L={L} rows={rows} {dt} path={path}")
     x = workloads.scores((N, R, L), dt, seed=R + L)
     with forced_path(path):
@@ -136,14 +139,15 @@ def test_softmax_special_values(nrm_lib):
             compare.check_output(lse, oracle.softmax.logsumexp(f64(xs), dt), dt, what="lse")
 
 
-def test_softmax_in_place(nrm_lib):
-    say("softmax and gradient in place")
+@pytest.mark.parametrize("n", [3000, 128256])
+def test_softmax_in_place(nrm_lib, n):
+    say(f"softmax and gradient in place n={n}")
     for path in (None, "scalar"):
         with forced_path(path):
-            x = dev(workloads.scores((40, 3000), "bf16", seed=8))
+            x = dev(workloads.scores((40, n), "bf16", seed=8))
             ref = nrm_lib.softmax(x)
             nrm_lib.softmax(x, out=x)
-            inp = workloads.ce_inputs(40, 3000, "bf16", seed=9, g="normal")
+            inp = workloads.ce_inputs(40, n, "bf16", seed=9, g="normal")
             lg = dev(inp.logits)
             dref = nrm_lib.cross_entropy_vjp(lg, dev(inp.targets), dev(inp.g))
             nrm_lib.cross_entropy_vjp(lg, dev(inp.targets), dev(inp.g), dlogits=lg)
