@@ -338,9 +338,12 @@ sm_stream(SmArgs a) {
   // so that the second pass reads them from LDS: the oldest data of pass 1 is the likeliest
   // to have left the caches by then (cross-entropy gradient [4096, 128256] 428 -> 419 us;
   // parking the last step instead measured slower, 453 us).
+  // The second step's U chunks stay in registers for the second pass (16 VGPRs, within the
+  // 64 that keep two 1024-thread blocks per CU; the gradient 394 -> 380 us).
   constexpr bool HOLD = OUT && V == Fmt<BF16>::VEC;
   constexpr int HU = 3;
   extern __shared__ u32x4 held[];  // HOLD: HU * TPB chunks
+  u32x4 kept[HOLD ? U : 1];
   const int64_t stepc = (int64_t)TPB * U;
   const int64_t nsteps = (nch + stepc - 1) / stepc;
   float m = -__builtin_inff(), s = 0.f;
@@ -358,6 +361,7 @@ sm_stream(SmArgs a) {
         const u32x4 raw = OUT ? ld16(p) : ld16_nt(p);
         if constexpr (HOLD) {
           if (u < HU && si == 0) held[u * TPB + threadIdx.x] = raw;
+          if (si == 1) kept[u] = raw;
         }
         unpack<BF16>(raw, f[u]);
       } else {
@@ -437,6 +441,8 @@ sm_stream(SmArgs a) {
       if constexpr (V == Fmt<BF16>::VEC) {
         if (HOLD && u < HU && si == 0)
           unpack<BF16>(held[u * TPB + threadIdx.x], f[u]);
+        else if (HOLD && si == 1)
+          unpack<BF16>(kept[u], f[u]);
         else
           unpack<BF16>(ld16_nt((const char*)a.x + (e0 + j * V) * Fmt<BF16>::ESZ), f[u]);
       } else {
