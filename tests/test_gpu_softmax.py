@@ -16,9 +16,10 @@ from gpu_util import DEV, dev, f64, forced_path, say
 
 pytestmark = pytest.mark.gpu
 
-# 20000 and 40000: streaming rows of one and two steps (their first step parked in LDS)
-WIDTHS = [1, 2, 7, 8, 64, 100, 512, 520, 4096, 8192, 16384, 20000, 40000, 65536, 128256, 131072,
-          140000]
+# 5000 and 10000 (bf16): register rows whose team is 192 threads (three waves, one team per
+# block); 20000 and 40000: streaming rows of one and two steps (their first step parked in LDS)
+WIDTHS = [1, 2, 7, 8, 64, 100, 512, 520, 4096, 5000, 8192, 10000, 16384, 20000, 40000, 65536,
+          128256, 131072, 140000]
 PATHS = [None, "chunked", "scalar"]
 
 
@@ -50,13 +51,15 @@ def test_softmax_paths_and_rows(nrm_lib, path, n, rows):
 
 @pytest.mark.parametrize("N,R,L,rows", [(2, 8, 8, 8), (2, 64, 512, 64), (1, 512, 512, 512),
                                         (3, 6, 4, 3), (2, 16, 1000, 8), (1, 12, 2, 12),
-                                        (4, 128, 4096, 128), (1, 2048, 16400, 2048),
-                                        (1, 64, 70000, 64)])
+                                        (4, 128, 4096, 128), (1, 2048, 12000, 2048),
+                                        (1, 1024, 5000, 1024), (1, 256, 16384, 256),
+                                        (1, 2048, 16400, 2048), (1, 64, 70000, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("path", [None, "scalar"])
 def test_causal_softmax(nrm_lib, N, R, L, rows, dt, path):
-    # L = 16400 and 70000 (bf16): rows kept in registers, 8 and 16 chunks per thread, the
-    # cut inside the last chunks of each thread, whole chunks past it never read
+    # L = 12000 and 16384 (bf16), 5000 (fp32): rows of 8 chunks per thread in registers,
+    # the cut inside the last chunks of each thread and whole chunks past it never read;
+    # 16400 and 70000: the streaming kernel
     say(f"causal N={N} R={R} L={L} rows={rows} {dt} path={path}")
     x = workloads.scores((N, R, L), dt, seed=R + L)
     with forced_path(path):
@@ -82,7 +85,7 @@ def _ce_check(nrm, inp, dt, path=None, i32=False, sel=None):
     return loss, want
 
 
-@pytest.mark.parametrize("V", [2, 100, 1000, 20000, 32000, 128256, 151936])
+@pytest.mark.parametrize("V", [2, 100, 1000, 5000, 10000, 20000, 32000, 128256, 151936])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_cross_entropy_vocab(nrm_lib, V, dt):
     say(f"cross_entropy V={V} {dt}")

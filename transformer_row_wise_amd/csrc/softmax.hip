@@ -59,6 +59,32 @@ __device__ __forceinline__ float lowest_of(bool bf16) {
   return bf16 ? -3.3895313892515355e38f : -3.4028234663852886e38f;
 }
 
+// The dtype's lowest finite value in every element of a 16-byte chunk.
+template <bool BF16>
+__device__ __forceinline__ u32x4 lowest_chunk() {
+  const unsigned b = BF16 ? 0xff7fff7fu : 0xff7fffffu;
+  return u32x4{b, b, b, b};
+}
+
+// Chunk v, whose first element is column `first`, with each column past `cut` replaced by
+// the dtype's lowest finite value (the causal mask, applied once to the packed scores).
+template <bool BF16>
+__device__ __forceinline__ u32x4 mask_past(u32x4 v, int first, int cut) {
+  const int keep = cut - first + 1;  // leading elements kept
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (BF16) {
+      // Element 2d in the low half of dword d, 2d + 1 in the high half.
+      const unsigned lo = 2 * d < keep ? (v[d] & 0xffffu) : 0xff7fu;
+      const unsigned hi = 2 * d + 1 < keep ? (v[d] & 0xffff0000u) : 0xff7f0000u;
+      v[d] = lo | hi;
+    } else {
+      v[d] = d < keep ? v[d] : 0xff7fffffu;
+    }
+  }
+  return v;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) { return dpp<CTRL>(v); }
 
@@ -182,6 +208,11 @@ sm_rows(SmArgs a) {
   auto chunk = [&](int k) { return tid + k * T; };
   auto ok = [&](int k) { return EXACT || chunk(k) < nvec; };
   const int cut = (int)r.cut;
+  // CausalSoftmax with eight chunks per thread masks the packed scores once, as they are
+  // loaded: a compare per element in each pass took the kernel into scratch (~1700 spilled
+  // registers; [2048, 12000] bf16 1119 -> 22 us). With fewer chunks the per-element compare
+  // measured faster ([256, 512, 512] bf16 42 against 47 us).
+  constexpr bool MASK_LOAD = OP == SM_CAUSAL && NV >= 8;
   // The target's chunk and its element within the chunk (team-uniform): per chunk one
   // vector compare says whether this thread owns it, per element a scalar compare.
   const int tgt_chunk = r.target < 0 ? -1 : (int)(r.target / V);
@@ -191,7 +222,15 @@ sm_rows(SmArgs a) {
   u32x4 xv[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    if constexpr (OP == SM_CAUSAL) {
+    if constexpr (MASK_LOAD) {
+      // A chunk wholly past the row's causal cut is never read; masked scores become the
+      // lowest value here, once, so that the passes below read plain scores.
+      xv[k] = lowest_chunk<BF16>();
+      if (chunk(k) * V <= cut)
+        xv[k] = mask_past<BF16>(
+            ld16_nt(xr + (int64_t)(EXACT ? chunk(k) : min(chunk(k), nvec - 1)) * 16),
+            chunk(k) * V, cut);
+    } else if constexpr (OP == SM_CAUSAL) {
       // A chunk wholly past the row's causal cut is never read: its scores are replaced.
       xv[k] = u32x4{0, 0, 0, 0};
       if (chunk(k) * V <= cut)
@@ -204,7 +243,7 @@ sm_rows(SmArgs a) {
   // Score of element e of chunk k as the operation sees it (masked, or -inf when absent).
   auto score = [&](int k, int e, float f) {
     if (!ok(k)) return -__builtin_inff();
-    if constexpr (OP == SM_CAUSAL) return chunk(k) * V + e <= cut ? f : lowest;
+    if constexpr (OP == SM_CAUSAL && !MASK_LOAD) return chunk(k) * V + e <= cut ? f : lowest;
     return f;
   };
 
@@ -478,7 +517,9 @@ template <bool BF16, int OP, int NV, bool EXACT, int SUB>
 hipError_t go_sm_rows(const SmArgs& a0, int team, hipStream_t stream) {
   SmArgs a = a0;
   a.team = team;
-  const int threads = team >= 256 ? team : 256;
+  // Several teams per 256-thread block when the team divides 256 (16 .. 128 threads), else
+  // one team per block (192 threads, or 256 and more): a block holds whole teams only.
+  const int threads = team < 256 && 256 % team == 0 ? 256 : team;
   const int G = threads / team;
   const int64_t blocks = (a.rows + G - 1) / G;
   if (blocks > kSmMaxGrid) return hipErrorInvalidConfiguration;
