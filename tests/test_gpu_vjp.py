@@ -88,6 +88,18 @@ def test_vjp_optional_gradients(nrm_lib, ln):
 
 
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("hidden,dt,wdt", [(8000, "bf16", "bf16"), (8000, "bf16", "f32"),
+                                           (8000, "bf16", None), (4000, "f32", "f32"),
+                                           (4000, "f32", None)])
+def test_vjp_ragged_rows_many(nrm_lib, ln, hidden, dt, wdt):
+    """Rows of 1000 chunks (a 1024-thread team, the last 24 lanes past the row's end) with
+    2301 rows: 256 blocks of up to 9 rows each, so every team runs the register ring's steady
+    state and its tail with clamped chunks."""
+    say(f"vjp ragged many rows {'ln' if ln else 'rms'} hidden={hidden} {dt} w={wdt}")
+    check_vjp(nrm_lib, _inp(2301, hidden, dt, wdt, 23, ln), ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
 def test_vjp_zero_rows_zero_parameter_gradients(nrm_lib, ln):
     say(f"vjp zero rows {'ln' if ln else 'rms'}")
     x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)

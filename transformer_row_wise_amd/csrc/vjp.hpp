@@ -264,6 +264,17 @@ vjp_rows(VjpArgs a) {
   for (int k = 0; k < NV; ++k)
 #pragma unroll
     for (int e = 0; e < V; ++e) accw[k][e] = accb[k][e] = 0.0;
+  // fp32 parameters beside bf16 data take fp64 products with g: at ragged widths an opaque
+  // copy of w at each use keeps the compiler from holding their fp64 conversions (16
+  // registers) across the loop, which spilled the ring to scratch; converting again costs 8
+  // instructions a row (at whole-wave widths holding them measured faster).
+  auto wuse = [&](int k, float (&wl)[V]) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      wl[e] = wv[k][e];
+      if constexpr (PK == PK_F32 && !EXACT) __asm__ volatile("" : "+v"(wl[e]));
+    }
+  };
 
   auto row_of = [&](int it) {
     return ((int64_t)it * G + team) * (int64_t)gridDim.x + blockIdx.x;
@@ -284,11 +295,23 @@ vjp_rows(VjpArgs a) {
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      if (ok[k]) {
-        float f[V], gf[V];
-        unpack<BF16>(xv[k], f);
-        unpack<BF16>(gv[k], gf);
-        vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
+      if constexpr (EXACT) {
+        if (ok[k]) {
+          float f[V], gf[V];
+          unpack<BF16>(xv[k], f);
+          unpack<BF16>(gv[k], gf);
+          vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
+        }
+      } else {
+        // A chunk past the row's end (a clamped duplicate) enters as zeros, which add
+        // exactly nothing to any sum: a select rather than a branch, which kept the ring's
+        // registers live around it and spilled them to scratch.
+        const u32x4 z = u32x4{0, 0, 0, 0};
+        float f[V], gf[V], wl[V];
+        unpack<BF16>(ok[k] ? xv[k] : z, f);
+        unpack<BF16>(ok[k] ? gv[k] : z, gf);
+        wuse(k, wl);
+        vjp_accumulate<OP, V, XF>(f, gf, wl, ds);
       }
     }
     if constexpr (OP == VJP_RMS) team_sum2_post(ds[0], ds[1], red[it & 1]);
@@ -325,10 +348,11 @@ vjp_rows(VjpArgs a) {
       // costs more registers than converting again.
       u32x4 xr = xv[k], gr = gv[k];
       __asm__ volatile("" : "+v"(xr), "+v"(gr));
-      float f[V], gf[V], dxv[V];
+      float f[V], gf[V], dxv[V], wl[V];
       unpack<BF16>(xr, f);
       unpack<BF16>(gr, gf);
-      vjp_outputs<OP, V, DW, DB, XF>(f, gf, wv[k], s, dxv, accw[k], accb[k]);
+      wuse(k, wl);
+      vjp_outputs<OP, V, DW, DB, XF>(f, gf, wl, s, dxv, accw[k], accb[k]);
       if (ok[k]) st16_nt(dr + (int64_t)jj[k] * 16, pack<BF16>(dxv));
     }
   };
@@ -363,7 +387,7 @@ vjp_rows(VjpArgs a) {
     // output arithmetic instead of stalling every wave of the block. The loop is unrolled
     // by R so that each buffer keeps its registers: copying a buffer that is still being
     // loaded would wait for the load.
-    constexpr int R = 4;
+    constexpr int R = OP == VJP_LN && (PK == PK_F32 || !EXACT) ? 3 : 4;
     u32x4 xs[R][NV], gs[R][NV];
 #pragma unroll
     for (int q = 0; q < R - 1; ++q) load_row(q, xs[q], gs[q]);
