@@ -100,6 +100,19 @@ def test_vjp_ragged_rows_many(nrm_lib, ln, hidden, dt, wdt):
 
 
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("hidden,dt,wdt", [(12000, "bf16", "bf16"), (12288, "bf16", "bf16"),
+                                           (16384, "bf16", "bf16"), (16384, "bf16", "f32"),
+                                           (12000, "bf16", None), (10000, "f32", "f32"),
+                                           (16384, "f32", "f32")])
+def test_vjp_wide_rows(nrm_lib, ln, hidden, dt, wdt):
+    """Rows of 8193 to 16384 elements: 16 per thread, one team of up to 1024 threads per row,
+    the dw column sums accumulated in LDS; 700 rows (256 blocks of up to 3 rows), exact and
+    ragged widths."""
+    say(f"vjp wide rows {'ln' if ln else 'rms'} hidden={hidden} {dt} w={wdt}")
+    check_vjp(nrm_lib, _inp(700, hidden, dt, wdt, 29, ln), ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
 def test_vjp_zero_rows_zero_parameter_gradients(nrm_lib, ln):
     say(f"vjp zero rows {'ln' if ln else 'rms'}")
     x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)

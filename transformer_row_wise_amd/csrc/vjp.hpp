@@ -110,11 +110,19 @@ __device__ __forceinline__ void vjp_accumulate(const float (&f)[V], const float 
   }
 }
 
-// dx of V elements, and the dw / db column accumulators, in fp64.
-template <int OP, int V, bool DW, bool DB, bool XF>
+// A thread's V column accumulators in LDS, element e at p[e * stride] (element-major, so
+// that the lanes of a wave touch consecutive doubles).
+struct LdsCols {
+  double* p;
+  int stride;
+  __device__ __forceinline__ double& operator[](int e) const { return p[e * stride]; }
+};
+
+// dx of V elements, and the dw / db column accumulators (registers, or LdsCols), in fp64.
+template <int OP, int V, bool DW, bool DB, bool XF, typename AW, typename AB>
 __device__ __forceinline__ void vjp_outputs(const float (&f)[V], const float (&gv)[V],
                                             const float (&wv)[V], const VjpRow& s,
-                                            float (&dxv)[V], double* accw, double* accb) {
+                                            float (&dxv)[V], AW accw, AB accb) {
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     const double xd = (double)f[e];
@@ -235,8 +243,13 @@ vjp_rows(VjpArgs a) {
   constexpr bool DW = PG, DB = PG && OP == VJP_LN;
   constexpr bool XF = BF16 && PK != PK_F32;
   constexpr int V = Fmt<BF16>::VEC;
+  // LW: 16 elements per thread (rows of up to 16384 with one 1024-thread team, G = 1): the
+  // dw accumulators live in LDS, NV * V * T doubles (128 KB at T = 1024), since in
+  // registers beside LN's db they would spill.
+  constexpr bool LW = DW && NV * V >= 16;
   __shared__ double red[2][16 * 4];          // [iteration parity][wave * sums + sum]
-  extern __shared__ double comb[];           // (G - 1) * T * V doubles, team combine
+  extern __shared__ double comb[];           // (G - 1) * T * V doubles (team combine), or
+                                             // LW: the dw accumulators
   const int T = a.team;
   const int G = blockDim.x / T;
   // T is a multiple of 64, so a wave belongs to one team: the team index, its rows and their
@@ -264,6 +277,15 @@ vjp_rows(VjpArgs a) {
   for (int k = 0; k < NV; ++k)
 #pragma unroll
     for (int e = 0; e < V; ++e) accw[k][e] = accb[k][e] = 0.0;
+  // LW: element e of chunk k of this thread's columns at comb[(k V + e) T + tid]; each
+  // thread reads and writes only its own slots, so no barrier orders them.
+  auto lw_cols = [&](int k) { return LdsCols{comb + (k * V) * T + tid, T}; };
+  if constexpr (LW) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < V; ++e) lw_cols(k)[e] = 0.0;
+  }
   // fp32 parameters beside bf16 data take fp64 products with g: at ragged widths an opaque
   // copy of w at each use keeps the compiler from holding their fp64 conversions (16
   // registers) across the loop, which spilled the ring to scratch; converting again costs 8
@@ -352,7 +374,8 @@ vjp_rows(VjpArgs a) {
       unpack<BF16>(xr, f);
       unpack<BF16>(gr, gf);
       wuse(k, wl);
-      vjp_outputs<OP, V, DW, DB, XF>(f, gf, wl, s, dxv, accw[k], accb[k]);
+      if constexpr (LW) vjp_outputs<OP, V, DW, DB, XF>(f, gf, wl, s, dxv, lw_cols(k), accb[k]);
+      else vjp_outputs<OP, V, DW, DB, XF>(f, gf, wl, s, dxv, accw[k], accb[k]);
       if (ok[k]) st16_nt(dr + (int64_t)jj[k] * 16, pack<BF16>(dxv));
     }
   };
@@ -427,6 +450,17 @@ vjp_rows(VjpArgs a) {
       if ((pass == 0 && !DW) || (pass == 1 && !DB)) continue;
       double (&acc)[NV][V] = pass == 0 ? accw : accb;
       double* part = (pass == 0 ? a.part_w : a.part_b) + (int64_t)blockIdx.x * a.hidden;
+      if (LW && pass == 0) {  // one team per block: its LDS columns are the partial row
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          if (ok[k]) {
+            double* p = part + (int64_t)jj[k] * V;
+#pragma unroll
+            for (int e = 0; e < V; ++e) p[e] = lw_cols(k)[e];
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         if (G > 1) {

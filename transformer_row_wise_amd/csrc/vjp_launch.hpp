@@ -1,12 +1,13 @@
 // Kernel-shape choice and launch of the RMSNorm / LayerNorm backward kernels.
 //
 // For rows of n = hidden / VEC 16-byte chunks (VEC = 8 bf16, 4 fp32), when hidden and the
-// base addresses are 16-byte granular and a thread's share fits in registers (NV * VEC <= 8
-// elements, so hidden <= 8192 for bf16 and fp32):
+// base addresses are 16-byte granular and hidden <= 16384:
 //   vjp_rows, a team of T = ceil(n / NV) threads (rounded up to a wave) per row, NV the
-//   smallest chunk count per thread that keeps T <= 1024; G = min(1024 / T, 8) teams per
-//   block. The grid is vjp_partials(rows) blocks of at most rpb rows each, taken strided
-//   (with parameter gradients, one partial row per block).
+//   smallest chunk count per thread that keeps T <= 1024 among NV * VEC = 8 elements or
+//   fewer (column sums in registers; hidden <= 8192) and NV * VEC = 16 (one team per block,
+//   the dw column sums in LDS); G = min(1024 / T, 8) teams per block. The grid is
+//   vjp_partials(rows) blocks of at most rpb rows each, taken strided (with parameter
+//   gradients, one partial row per block).
 // Otherwise vjp_generic (256 threads, 16-byte chunks or single elements, any width).
 // The partial rows are then added by vjp_colsum.
 #pragma once
@@ -39,7 +40,9 @@ template <bool BF16, int OP, int NV, int PK, bool EXACT, bool PG>
 hipError_t go_vjp_rows(const VjpArgs& a, int64_t blocks, int threads, hipStream_t stream) {
   constexpr int V = Fmt<BF16>::VEC;
   const int G = threads / a.team;
-  const size_t lds = PG && G > 1 ? (size_t)(G - 1) * a.team * V * sizeof(double) : 0;
+  const size_t lds = PG && NV * V >= 16 ? (size_t)NV * V * a.team * sizeof(double)
+                     : PG && G > 1    ? (size_t)(G - 1) * a.team * V * sizeof(double)
+                                      : 0;
   vjp_rows<BF16, OP, NV, PK, EXACT, PG><<<(unsigned)blocks, threads, lds, stream>>>(a);
   return hipGetLastError();
 }
@@ -70,13 +73,19 @@ hipError_t vjp_rows_pg(const VjpArgs& a, bool pg, int64_t blocks, int threads, b
 template <bool BF16, int OP>
 hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool* done) {
   constexpr int V = Fmt<BF16>::VEC;
-  // At most 8 elements per thread: the fp64 column accumulators of 16 (LN: dw and db, 64
-  // registers) push the kernel past 128 registers, into scratch.
-  constexpr int MAX_NV = 8 / V;  // 1 for bf16, 2 for fp32
+  // Up to 8 elements per thread with the fp64 column accumulators in registers; rows of up
+  // to 16384 elements take 16 per thread (one 1024-thread team per row) with the dw
+  // accumulators in LDS (128 KB): in registers, 16 of them beside LN's db (64 registers)
+  // push the kernel past 128 registers, into scratch.
+  constexpr int MAX_NV = 8 / V;   // 1 for bf16, 2 for fp32
+  constexpr int WIDE_NV = 16 / V;  // 2 for bf16, 4 for fp32
   *done = false;
   int nv = 1;
   while (nv <= MAX_NV && (n + nv - 1) / nv > 1024) nv *= 2;
-  if (nv > MAX_NV) return hipSuccess;
+  if (nv > MAX_NV) {
+    if ((n + WIDE_NV - 1) / WIDE_NV > 1024) return hipSuccess;
+    nv = WIDE_NV;
+  }
   const int team = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
   const bool exact = (int64_t)team * nv == n;
   const int gmax = std::max(1, std::min(8, 1024 / team));
@@ -91,7 +100,8 @@ hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool*
   const int threads = G * team;
   switch (nv) {
     case 1: return vjp_rows_pg<BF16, OP, 1>(a, pg, blocks, threads, exact, stream);
-    case 2: if constexpr (!BF16) return vjp_rows_pg<BF16, OP, 2>(a, pg, blocks, threads, exact, stream); break;
+    case 2: return vjp_rows_pg<BF16, OP, 2>(a, pg, blocks, threads, exact, stream);
+    case 4: if constexpr (!BF16) return vjp_rows_pg<BF16, OP, 4>(a, pg, blocks, threads, exact, stream); break;
     default: break;
   }
   *done = false;
