@@ -291,6 +291,10 @@ vjp_rows(VjpArgs a) {
   // registers) across the loop, which spilled the ring to scratch; converting again costs 8
   // instructions a row (at whole-wave widths holding them measured faster).
   auto wuse = [&](int k, float (&wl)[V]) {
+    if constexpr (PK == PK_F32 && NV * V >= 16) {
+      load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wl);
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       wl[e] = wv[k][e];
