@@ -59,6 +59,30 @@ def test_layer_norm_shapes(nrm_lib, hidden, dt, wdt, affine):
     check_ln(nrm_lib, inp)
 
 
+# Narrow rows take teams of 4 .. 64 lanes with several rows per block: 1001 rows leave the last
+# block partly empty; chunk counts 1, 2, 3, 8, 15, 16, 32, 64, 125, 128 (bf16) and 2, 16, 25,
+# 32, 64, 128 (fp32) cover every team size, exact and ragged.
+NARROW = [("bf16", 8), ("bf16", 16), ("bf16", 24), ("bf16", 64), ("bf16", 120), ("bf16", 128),
+          ("bf16", 256), ("bf16", 512), ("bf16", 1000), ("bf16", 1024), ("f32", 8), ("f32", 64),
+          ("f32", 100), ("f32", 128), ("f32", 256), ("f32", 512)]
+
+
+@pytest.mark.parametrize("dt,hidden", NARROW)
+@pytest.mark.parametrize("wkind", ["same", "f32", None])
+def test_narrow_rows_many(nrm_lib, dt, hidden, wkind):
+    wdt = None if wkind is None else ("f32" if wkind == "f32" else dt)
+    say(f"narrow rows=1001 hidden={hidden} {dt} w={wdt}")
+    check_add(nrm_lib, _row(1001, hidden, dt, wdt, seed=hidden + 7, r=("normal", 0.0, 1.0),
+                            eps=1e-6))
+    check_rms(nrm_lib, _row(1001, hidden, dt, wdt, seed=hidden + 8, x=("t3",), eps=1e-5))
+    inp = workloads.row_inputs(1001, hidden, dt, seed=hidden + 9, x=("normal", 0.5, 2.0),
+                               w=("normal", 1.0, 0.1), b=("normal", 0.0, 0.1),
+                               w_dtype=wdt or dt, eps=1e-5)
+    if wkind is None:
+        inp.w = inp.b = None
+    check_ln(nrm_lib, inp)
+
+
 @pytest.mark.parametrize("path", ["wave", "block", "rowblock", "chunked", "scalar"])
 @pytest.mark.parametrize("hidden", [512, 4096, 5120, 8192, 16384, 24576])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -7,7 +7,9 @@
 //
 // Shapes of the same arithmetic:
 //   row_block               one block of up to 1024 threads per row, NV 16-byte chunks per
-//                           thread in registers (the default for rows of up to 4096 chunks);
+//                           thread in registers (the default for rows of 129 to 4096 chunks);
+//   row_team                the same with a team of 4 .. 64 lanes per row and 256 / team
+//                           rows per block (rows of up to 128 chunks);
 //   row_regs<..., WPR = 1>  one wave64 per row, the whole row in registers (hidden <= 64*NV*VEC);
 //                           a block holds four independent waves (four rows);
 //   row_regs<..., WPR = 8>  one 512-thread block per row, row in registers, cross-wave sums
@@ -245,18 +247,26 @@ __device__ __forceinline__ void load_pk(const void* p, int64_t i, float (&f)[V])
 // no tail guards. Otherwise a chunk index past the row end is clamped to the last chunk
 // for loads (so every load is unconditional and the compiler's waits stay exact) and the
 // stores of such chunks are skipped.
-template <bool BF16, int OP, int NV, int PK, bool EXACT>
-__global__ void __launch_bounds__(1024)
-row_block(RowArgs a) {
+// SUB > 0 (4 .. 64, narrow rows): a team of SUB lanes per row instead, 256 / SUB rows per
+// block, the row's sums by lane exchanges inside the team (no LDS, no barrier); a team past
+// the last row loads that row and stores nothing.
+template <bool BF16, int OP, int NV, int PK, bool EXACT, int SUB>
+__device__ __forceinline__ void row_block_body(RowArgs a) {
   constexpr int V = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   __shared__ float red_f[16];
   __shared__ double red4[16 * 4];
-  const int T = blockDim.x;
+  const int T = SUB ? SUB : blockDim.x;
   const int nw = T >> 6;
-  const int tid = threadIdx.x;
+  const int tid = SUB ? (int)(threadIdx.x & (SUB - 1)) : (int)threadIdx.x;
   const int nvec = (int)(a.hidden / V);
-  const int64_t row = blockIdx.x;
+  bool live = true;
+  int64_t row = blockIdx.x;
+  if constexpr (SUB > 0) {
+    row = (int64_t)blockIdx.x * (blockDim.x / SUB) + threadIdx.x / SUB;
+    live = row < a.rows;
+    if (!live) row = a.rows - 1;
+  }
   const int64_t base = row * a.hidden * ESZ;
 
   int jj[NV];
@@ -296,7 +306,7 @@ row_block(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < V; ++e) f[e] = f[e] + fr[e];
         xv[k] = pack<BF16>(f);  // h, rounded to the storage type
-        if (ok[k]) st16_nt((char*)a.h + base + (int64_t)jj[k] * 16, xv[k]);
+        if (live && ok[k]) st16_nt((char*)a.h + base + (int64_t)jj[k] * 16, xv[k]);
         unpack<BF16>(xv[k], f);
       }
       if (ok[k]) {
@@ -304,7 +314,9 @@ row_block(RowArgs a) {
         for (int e = 0; e < V; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
       }
     }
-    const float ss = block_row_sum(acc, red_f, nw);
+    float ss;
+    if constexpr (SUB > 0) ss = group_sum<SUB>(acc);
+    else ss = block_row_sum(acc, red_f, nw);
     const float rstd = (float)rstd_f64((double)ss, a.hidden, a.eps);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -312,7 +324,7 @@ row_block(RowArgs a) {
       unpack<BF16>(xv[k], f);
 #pragma unroll
       for (int e = 0; e < V; ++e) f[e] = (f[e] * rstd) * wv[k][e];
-      if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
+      if (live && ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   } else {  // OP_LN, fp64 statistics and output arithmetic
     // One pass: sum x and sum x^2 in fp64 (x^2 of a bf16 or fp32 value is exact in fp64),
@@ -353,7 +365,12 @@ row_block(RowArgs a) {
     ds[0] += ds[1];
     ds[1] = ds[2] + ds[3];
     ds[2] = ds[3] = 0.0;
-    team_sum4(ds, red4, 0, nw);
+    if constexpr (SUB > 0) {
+      ds[0] = group_sum<SUB>(ds[0]);
+      ds[1] = group_sum<SUB>(ds[1]);
+    } else {
+      team_sum4(ds, red4, 0, nw);
+    }
     // mu = sum / n through the reciprocal and one residual step, which lands on the correctly
     // rounded quotient (a constant row's exact sum n c gives exactly c).
     const double n = (double)a.hidden, inv_n = a.inv_n;
@@ -381,9 +398,23 @@ row_block(RowArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e)
         f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
-      if (ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
+      if (live && ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   }
+}
+
+template <bool BF16, int OP, int NV, int PK, bool EXACT>
+__global__ void __launch_bounds__(1024)
+row_block(RowArgs a) {
+  row_block_body<BF16, OP, NV, PK, EXACT, 0>(a);
+}
+
+// Narrow rows: teams of SUB lanes (4 .. 64) with two chunks per lane, 256 / SUB rows per
+// 256-thread block.
+template <bool BF16, int OP, int PK, bool EXACT, int SUB>
+__global__ void __launch_bounds__(256)
+row_team(RowArgs a) {
+  row_block_body<BF16, OP, 2, PK, EXACT, SUB>(a);
 }
 
 // One block of 256 threads per row, looping over the row in chunks of V elements

@@ -1,6 +1,9 @@
 // Kernel-shape choice and launch of the row kernels (RMSNorm, add-RMSNorm, LayerNorm).
 //
 // For a row of n = hidden / VEC 16-byte chunks (VEC = 8 bf16 or 4 fp32), automatic choice:
+//   n <= 128                         row_team: teams of SUB = 4 .. 64 lanes (two chunks each,
+//                                    the smallest power of two that covers the row), 256 / SUB
+//                                    rows per block;
 //   n <= 4096 (2048 for LayerNorm    row_block: one block of T threads per row, NV chunks per
 //   with fp32 w beside bf16 x)       thread, NV = max(2, ceil(n / 1024)) (LayerNorm:
 //                                    clamp(ceil(n / 256), 2, 4)), T = ceil(n / NV) rounded
@@ -48,6 +51,49 @@ template <bool BF16, int OP, int NV, int PK, bool EXACT>
 hipError_t go_rowblock(const RowArgs& a, int threads, hipStream_t stream) {
   row_block<BF16, OP, NV, PK, EXACT><<<(unsigned)a.rows, threads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+// Narrow rows: teams of SUB lanes, two chunks each, 256 / SUB rows per 256-thread block.
+template <bool BF16, int OP, int PK, bool EXACT, int SUB>
+hipError_t go_rowsub(const RowArgs& a, hipStream_t stream) {
+  const int64_t blocks = (a.rows + 256 / SUB - 1) / (256 / SUB);
+  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  row_team<BF16, OP, PK, EXACT, SUB><<<(unsigned)blocks, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int OP, int SUB>
+hipError_t rowsub_pk(const RowArgs& a, bool exact, hipStream_t stream) {
+  if (a.w == nullptr)
+    return exact ? go_rowsub<BF16, OP, PK_NONE, true, SUB>(a, stream)
+                 : go_rowsub<BF16, OP, PK_NONE, false, SUB>(a, stream);
+  if constexpr (BF16) {
+    if (a.w_f32)
+      return exact ? go_rowsub<BF16, OP, PK_F32, true, SUB>(a, stream)
+                   : go_rowsub<BF16, OP, PK_F32, false, SUB>(a, stream);
+  }
+  return exact ? go_rowsub<BF16, OP, PK_SAME, true, SUB>(a, stream)
+               : go_rowsub<BF16, OP, PK_SAME, false, SUB>(a, stream);
+}
+
+// Rows of at most 128 chunks (1024 bf16 or 512 fp32 values): two chunks per lane and the
+// smallest team of 4 .. 64 lanes that covers the row. A block of one row's team would be
+// mostly idle lanes (a 128-wide bf16 row is 16 chunks, so 8 of a wave's 64 lanes).
+template <bool BF16, int OP>
+hipError_t try_rowsub(const RowArgs& a, int64_t n, hipStream_t stream, bool* done) {
+  *done = false;
+  if (n > 128) return hipSuccess;
+  const int64_t half = (n + 1) / 2;
+  const int sub = half <= 4 ? 4 : half <= 8 ? 8 : half <= 16 ? 16 : half <= 32 ? 32 : 64;
+  const bool exact = 2 * (int64_t)sub == n;
+  *done = true;
+  switch (sub) {
+    case 4: return rowsub_pk<BF16, OP, 4>(a, exact, stream);
+    case 8: return rowsub_pk<BF16, OP, 8>(a, exact, stream);
+    case 16: return rowsub_pk<BF16, OP, 16>(a, exact, stream);
+    case 32: return rowsub_pk<BF16, OP, 32>(a, exact, stream);
+    default: return rowsub_pk<BF16, OP, 64>(a, exact, stream);
+  }
 }
 
 template <bool BF16, int OP, int NV>
@@ -163,6 +209,10 @@ hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream) {
   }
   if (path == PATH_BLOCK && a.rows <= kMaxGrid) {
     err = try_block<BF16, OP>(a, (int)((n + 511) / 512), stream, &done);
+    if (done) return err;
+  }
+  if (path == PATH_AUTO) {
+    err = try_rowsub<BF16, OP>(a, n, stream, &done);
     if (done) return err;
   }
   if (path == PATH_AUTO || path == PATH_ROWBLOCK || path == PATH_WAVE || path == PATH_BLOCK) {
