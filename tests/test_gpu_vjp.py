@@ -113,6 +113,20 @@ def test_vjp_wide_rows(nrm_lib, ln, hidden, dt, wdt):
 
 
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("hidden,dt,wdt", [(8, "bf16", "bf16"), (64, "bf16", "bf16"),
+                                           (120, "bf16", "bf16"), (128, "bf16", "f32"),
+                                           (128, "bf16", None), (256, "bf16", "bf16"),
+                                           (16, "f32", "f32"), (100, "f32", None),
+                                           (128, "f32", "f32")])
+def test_vjp_narrow_rows_many(nrm_lib, ln, hidden, dt, wdt):
+    """Rows of at most 32 chunks: teams of 8, 16 or 32 lanes, 256 / team rows in flight per
+    block. 30001 rows give every team several rows (the two-buffer loop and a ragged last
+    step) and leave some teams with none in the last step."""
+    say(f"vjp narrow rows {'ln' if ln else 'rms'} rows=30001 hidden={hidden} {dt} w={wdt}")
+    check_vjp(nrm_lib, _inp(30001, hidden, dt, wdt, 31, ln), ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
 def test_vjp_zero_rows_zero_parameter_gradients(nrm_lib, ln):
     say(f"vjp zero rows {'ln' if ln else 'rms'}")
     x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)

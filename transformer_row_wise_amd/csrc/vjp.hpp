@@ -493,6 +493,105 @@ vjp_rows(VjpArgs a) {
   }
 }
 
+// Narrow rows (at most 32 chunks): a team of SUB = 8, 16 or 32 lanes per row, one chunk per
+// lane, 1024 / SUB teams per 1024-thread block (the grid is one block per partial row, at
+// most 256, so the block has to fill the compute unit). With P blocks, step it of team i of block b
+// takes row (it (1024 / SUB) + i) P + b, as in vjp_rows. A row's sums are lane exchanges inside
+// the team (no LDS, no barrier); the next row's chunks are loaded while the current one is
+// computed (two buffers, the loop unrolled by two so that no buffer is copied). A team past
+// the last row computes on a clamped row and neither stores nor accumulates it. At the end
+// the teams' column sums meet in LDS and are added in team order into the block's partial
+// row.
+template <bool BF16, int OP, int PK, bool EXACT, int SUB, bool PG>
+__global__ void __launch_bounds__(1024)
+vjp_team(VjpArgs a) {
+  constexpr bool DW = PG, DB = PG && OP == VJP_LN;
+  constexpr bool XF = BF16 && PK != PK_F32;
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int TB = 1024 / SUB;             // teams per block
+  __shared__ double comb[1024 * V];          // [thread][element], the column sums' meeting
+  const int team = threadIdx.x / SUB;
+  const int tid = threadIdx.x & (SUB - 1);
+  const int nvec = (int)(a.hidden / V);
+  const int iters = (int)((a.rpb + TB - 1) / TB);
+  const bool ok = EXACT || tid < nvec;
+  const int jj = EXACT ? tid : min(tid, nvec - 1);
+  float wv[V];
+  load_pk<BF16, PK, V>(a.w, (int64_t)jj * V, wv);
+  double accw[V], accb[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) accw[e] = accb[e] = 0.0;
+
+  auto row_of = [&](int it) {
+    return ((int64_t)it * TB + team) * (int64_t)gridDim.x + blockIdx.x;
+  };
+  auto load = [&](int it, u32x4& xv, u32x4& gv) {
+    const int64_t row = min(row_of(it), a.rows - 1);
+    xv = ld16_nt((const char*)a.x + (row * a.hidden + (int64_t)jj * V) * Fmt<BF16>::ESZ);
+    gv = ld16_nt((const char*)a.g + (row * a.hidden + (int64_t)jj * V) * Fmt<BF16>::ESZ);
+  };
+  auto process = [&](int it, const u32x4& xv, const u32x4& gv) {
+    const int64_t row = row_of(it);
+    const u32x4 z = u32x4{0, 0, 0, 0};
+    float f[V], gf[V];
+    unpack<BF16>(ok ? xv : z, f);  // a lane past the row's end adds zeros to the sums
+    unpack<BF16>(ok ? gv : z, gf);
+    double ds[4] = {0.0, 0.0, 0.0, 0.0};
+    vjp_accumulate<OP, V, XF>(f, gf, wv, ds);
+    VjpRow s;
+    if constexpr (OP == VJP_RMS) {
+      s = vjp_rms_scalars(group_sum<SUB>(ds[0]), group_sum<SUB>(ds[1]), a.inv_n, a.eps);
+    } else {
+      s = vjp_ln_scalars(group_sum<SUB>(ds[0]), group_sum<SUB>(ds[1]), group_sum<SUB>(ds[2]),
+                         group_sum<SUB>(ds[3]), a.inv_n, a.eps);
+    }
+    if (row >= a.rows) return;
+    u32x4 xr = xv, gr = gv;
+    __asm__ volatile("" : "+v"(xr), "+v"(gr));  // widen again rather than hold the fp64 copies
+    float dxv[V];
+    unpack<BF16>(xr, f);
+    unpack<BF16>(gr, gf);
+    vjp_outputs<OP, V, DW, DB, XF>(f, gf, wv, s, dxv, accw, accb);
+    if (ok) st16_nt((char*)a.dx + (row * a.hidden + (int64_t)jj * V) * Fmt<BF16>::ESZ,
+                    pack<BF16>(dxv));
+  };
+
+  u32x4 xa, ga, xb, gb;
+  if (iters > 0) load(0, xa, ga);
+  for (int it = 0; it < iters; it += 2) {
+    if (it + 1 < iters) load(it + 1, xb, gb);
+    process(it, xa, ga);
+    if (it + 1 >= iters) break;
+    if (it + 2 < iters) load(it + 2, xa, ga);
+    process(it + 1, xb, gb);
+  }
+
+  if constexpr (DW || DB) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((pass == 0 && !DW) || (pass == 1 && !DB)) continue;
+      const double* acc = pass == 0 ? accw : accb;
+      if (pass == 1) __syncthreads();  // the dw pass has read its slots
+#pragma unroll
+      for (int e = 0; e < V; ++e) comb[threadIdx.x * V + e] = acc[e];
+      __syncthreads();
+      if (team == 0 && ok) {
+        double t[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) t[e] = comb[tid * V + e];
+        for (int q = 1; q < TB; ++q) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) t[e] += comb[(q * SUB + tid) * V + e];
+        }
+        double* p = (pass == 0 ? a.part_w : a.part_b) + (int64_t)blockIdx.x * a.hidden +
+                    (int64_t)jj * V;
+#pragma unroll
+        for (int e = 0; e < V; ++e) p[e] = t[e];
+      }
+    }
+  }
+}
+
 // Generic kernel: any row width, V elements per access (VEC for 16-byte aligned rows, else
 // 1). One 256-thread block per run of rows; each row is read twice (the second pass mostly
 // from L2), and the block's partial row in the workspace is updated in place by the thread

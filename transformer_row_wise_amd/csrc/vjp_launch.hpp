@@ -8,6 +8,8 @@
 //   the dw column sums in LDS); G = min(1024 / T, 8) teams per block. The grid is
 //   vjp_partials(rows) blocks of at most rpb rows each, taken strided (with parameter
 //   gradients, one partial row per block).
+// Rows of at most 32 chunks take vjp_team instead: teams of 8, 16 or 32 lanes, one chunk per
+// lane, 1024 / team rows in flight per block.
 // Otherwise vjp_generic (256 threads, 16-byte chunks or single elements, any width).
 // The partial rows are then added by vjp_colsum.
 #pragma once
@@ -84,6 +86,47 @@ hipError_t vjp_rows_pg(const VjpArgs& a, bool pg, int64_t blocks, int threads, b
             : vjp_rows_pk<BF16, OP, NV, false>(a, blocks, threads, exact, stream);
 }
 
+template <bool BF16, int OP, int PK, bool EXACT, int SUB>
+hipError_t go_vjp_team(const VjpArgs& a, bool pg, int64_t blocks, hipStream_t stream) {
+  if (pg) vjp_team<BF16, OP, PK, EXACT, SUB, true><<<(unsigned)blocks, 1024, 0, stream>>>(a);
+  else vjp_team<BF16, OP, PK, EXACT, SUB, false><<<(unsigned)blocks, 1024, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int OP, int SUB>
+hipError_t vjp_team_pk(const VjpArgs& a, bool pg, bool exact, int64_t blocks,
+                       hipStream_t stream) {
+  if (a.w == nullptr)
+    return exact ? go_vjp_team<BF16, OP, PK_NONE, true, SUB>(a, pg, blocks, stream)
+                 : go_vjp_team<BF16, OP, PK_NONE, false, SUB>(a, pg, blocks, stream);
+  if constexpr (BF16) {
+    if (a.w_f32)
+      return exact ? go_vjp_team<BF16, OP, PK_F32, true, SUB>(a, pg, blocks, stream)
+                   : go_vjp_team<BF16, OP, PK_F32, false, SUB>(a, pg, blocks, stream);
+  }
+  return exact ? go_vjp_team<BF16, OP, PK_SAME, true, SUB>(a, pg, blocks, stream)
+               : go_vjp_team<BF16, OP, PK_SAME, false, SUB>(a, pg, blocks, stream);
+}
+
+// Rows of at most 32 chunks (256 bf16 or 128 fp32 values): vjp_team with one chunk per lane
+// and the smallest team of 8, 16 or 32 lanes that covers the row. vjp_rows' teams are whole
+// waves, which at these widths leave most lanes idle (a 128-wide bf16 row is 16 chunks).
+template <bool BF16, int OP>
+hipError_t try_vjp_team(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool* done) {
+  *done = false;
+  if (n > 32) return hipSuccess;
+  const int sub = n <= 8 ? 8 : n <= 16 ? 16 : 32;
+  const bool exact = n == sub;
+  const int64_t blocks = vjp_partials(a.rows);
+  a.rpb = (a.rows + blocks - 1) / blocks;
+  *done = true;
+  switch (sub) {
+    case 8: return vjp_team_pk<BF16, OP, 8>(a, pg, exact, blocks, stream);
+    case 16: return vjp_team_pk<BF16, OP, 16>(a, pg, exact, blocks, stream);
+    default: return vjp_team_pk<BF16, OP, 32>(a, pg, exact, blocks, stream);
+  }
+}
+
 // Fast path; *done = false when the row does not fit it.
 template <bool BF16, int OP>
 hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool* done) {
@@ -155,7 +198,9 @@ hipError_t launch_vjp(const VjpArgs& a, void* dw, void* db, bool aligned16, hipS
   const bool vec = aligned16 && a.hidden % V == 0 && path != PATH_SCALAR;
   hipError_t err = hipSuccess;
   bool done = false;
-  if (vec && path != PATH_CHUNKED) err = try_vjp_rows<BF16, OP>(a, pg, a.hidden / V, stream, &done);
+  if (vec && path == PATH_AUTO) err = try_vjp_team<BF16, OP>(a, pg, a.hidden / V, stream, &done);
+  if (vec && !done && path != PATH_CHUNKED)
+    err = try_vjp_rows<BF16, OP>(a, pg, a.hidden / V, stream, &done);
   if (!done) err = vec ? go_vjp_generic<BF16, OP, V>(a, pg, stream)
                        : go_vjp_generic<BF16, OP, 1>(a, pg, stream);
   if (err != hipSuccess || !pg) return err;
