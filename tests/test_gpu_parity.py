@@ -121,6 +121,8 @@ ROPE_SHAPES = [
     (1, 1, 2, 7, 6),
     (1, 2, 3, 128, 0),
     (3, 5, 33, 128, 128),
+    (2, 16, 33, 64, 64),     # 4-lane groups (bf16), 32 rows per position
+    (1, 4, 9, 64, 32),       # 4-lane groups with pass-through chunks
 ]
 
 
@@ -159,6 +161,24 @@ def test_norm_rope_positions(nrm_lib, offset, scale):
         with forced_path(path):
             check_rope(nrm_lib, rp)
             check_rope(nrm_lib, rp, traditional=True)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 4099, 128), (2, 3, 4100, 64), (1, 16, 4097, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("traditional", [False, True])
+@pytest.mark.parametrize("wkind", ["bf16", "f32", None])
+@pytest.mark.parametrize("cache", [False, True])
+def test_norm_rope_many_positions(nrm_lib, shape, traditional, wkind, cache):
+    """Few heads at thousands of positions with every feature rotated: several positions
+    per block (lane groups of 4 or 8), normalised, with bf16, fp32 or no weight, into an
+    output or rows offset .. offset + L of a cache."""
+    B, H, L, D = shape
+    say(f"norm_rope many positions {shape} trad={traditional} w={wkind} cache={cache}")
+    rp = workloads.rope_inputs(B, H, L, D, "bf16", seed=L + D, w_dtype=wkind,
+                               w=None if wkind is None else ("uniform", 0.5, 1.5),
+                               offset=37 if cache else 0)
+    c = torch.zeros(B, H, L + 50, D, dtype=torch.bfloat16) if cache else None
+    check_rope(nrm_lib, rp, traditional=traditional, cache=c)
 
 
 @pytest.mark.parametrize("traditional", [False, True])

@@ -164,13 +164,14 @@ def test_rope_positions_matches_offset_form(nrm_lib):
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("trad", [False, True])
 @pytest.mark.parametrize("fkind", [None, "loguniform"])
-def test_rope_positions_many_tokens(nrm_lib, Hq, Hk, dt, trad, fkind):
-    """4099 tokens (not a multiple of the positions a block takes) of 128 rotated features:
-    the several-positions-per-block kernel, with 1 to 80 rows per position, bf16 and fp32,
-    both pair layouts and both frequency forms; the oracle checks sampled tokens, the first
-    and last ones among them."""
-    T, D = 4099, 128
-    say(f"rope_positions T={T} Hq={Hq} Hk={Hk} {dt} trad={trad} freqs={fkind}")
+@pytest.mark.parametrize("D", [128, 64])
+def test_rope_positions_many_tokens(nrm_lib, Hq, Hk, dt, trad, fkind, D):
+    """4099 tokens (not a multiple of the positions a block takes) of 128 or 64 rotated
+    features: the several-positions-per-block kernel (lane groups of 4, 8 or 16), with 1 to 80
+    rows per position, bf16 and fp32, both pair layouts and both frequency forms; the oracle
+    checks sampled tokens, the first and last ones among them."""
+    T = 4099
+    say(f"rope_positions T={T} D={D} Hq={Hq} Hk={Hk} {dt} trad={trad} freqs={fkind}")
     inp = workloads.rope_qk_inputs(T, Hq, Hk, D, dt, seed=Hq + 3 * Hk, positions="random",
                                    max_position=1 << 20)
     freqs, ms = _freqs(fkind, D, np.random.default_rng(Hq))

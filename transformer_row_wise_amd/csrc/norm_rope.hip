@@ -29,6 +29,8 @@
 // issues the loads of R rows before computing any of them (memory-level parallelism: a
 // 128-wide bf16 row is only 256 bytes), with clamped, unconditional addresses; the table
 // is built while the first rows are in flight.
+// rope_multi: rows of few heads at many positions (fewer than 256 rows per position, at least
+// 4096 positions, every feature rotated): a block takes several consecutive positions.
 // rope_generic: any D / dims / alignment, one wave per row, element at a time.
 #include "rope.hpp"
 
@@ -302,9 +304,11 @@ rope_fast(RopeArgs a) {
 // a ring of three at 131 VGPRs and eight positions per block both measured slower). Each row
 // reads its position's (cos, sin) from LDS. One position per block measured slower still:
 // every block paid the table's latency (and the frequency load) for only BH rows, and its
-// rows took two steps whose second waited for the first. The arithmetic is rope_fast's, term for term (no normalisation: the
-// features enter unscaled, the rotation is scaled by mscale).
-template <bool BF16, int MODE, int G, int PB, bool MS>
+// rows took two steps whose second waited for the first. The arithmetic is rope_fast's, term
+// for term: without normalisation the features enter unscaled and the rotation is scaled by
+// mscale; with it (NORM, every feature rotated) the row's sum of squares is a lane exchange
+// inside the group, x w is rotated and the result scaled by rstd mscale.
+template <bool BF16, int MODE, int G, int PB, bool MS, bool NORM>
 __global__ void __launch_bounds__(256)
 rope_multi(RopeArgs a) {
   constexpr bool HALF = MODE == M_HALF;
@@ -324,6 +328,13 @@ rope_multi(RopeArgs a) {
   const int off_u = lj * V;
   const int off_v = half + off_u;
   const double ms = (double)a.mscale;  // MS: mscale != 1 (else the product is skipped: exact)
+  float wu[V], wv[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) wu[e] = wv[e] = 1.f;
+  if (NORM && a.w != nullptr) {
+    load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
+    load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
+  }
 
   u32x4 xu[NR], xv[NR];
   auto slot_of = [&](int k) { return k * SPS + g; };
@@ -354,25 +365,41 @@ rope_multi(RopeArgs a) {
     float fu[V], fv[V];
     unpack<BF16>(ru, fu);
     unpack<BF16>(rv, fv);
+    // The rotation's scale: mscale, times the row's rstd with NORM (then x w is rotated).
+    double rs = ms;
+    if constexpr (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fu[e], fu[e], ss);
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fv[e], fv[e], ss);
+      rs = rstd_f64((double)group_sum<G>(ss), a.D, a.eps) * ms;
+    }
+    constexpr bool SCALE = MS || NORM;
     if constexpr (HALF) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const double2 t = tab[lj * V + e];
-        const double u = (double)fu[e], v = (double)fv[e];
-        fu[e] = f64_to_f32(MS ? (u * t.x - v * t.y) * ms : u * t.x - v * t.y);
-        fv[e] = f64_to_f32(MS ? (u * t.y + v * t.x) * ms : u * t.y + v * t.x);
+        const double u = NORM ? (double)fu[e] * (double)wu[e] : (double)fu[e];
+        const double v = NORM ? (double)fv[e] * (double)wv[e] : (double)fv[e];
+        fu[e] = f64_to_f32(SCALE ? (u * t.x - v * t.y) * rs : u * t.x - v * t.y);
+        fv[e] = f64_to_f32(SCALE ? (u * t.y + v * t.x) * rs : u * t.y + v * t.x);
       }
     } else {
 #pragma unroll
       for (int e = 0; e < V / 2; ++e) {
         const double2 t1 = tab[lj * (V / 2) + e];
         const double2 t2 = tab[half / 2 + lj * (V / 2) + e];
-        const double u = (double)fu[2 * e], v = (double)fu[2 * e + 1];
-        fu[2 * e] = f64_to_f32(MS ? (u * t1.x - v * t1.y) * ms : u * t1.x - v * t1.y);
-        fu[2 * e + 1] = f64_to_f32(MS ? (u * t1.y + v * t1.x) * ms : u * t1.y + v * t1.x);
-        const double u2 = (double)fv[2 * e], v2 = (double)fv[2 * e + 1];
-        fv[2 * e] = f64_to_f32(MS ? (u2 * t2.x - v2 * t2.y) * ms : u2 * t2.x - v2 * t2.y);
-        fv[2 * e + 1] = f64_to_f32(MS ? (u2 * t2.y + v2 * t2.x) * ms : u2 * t2.y + v2 * t2.x);
+        const double u = NORM ? (double)fu[2 * e] * (double)wu[2 * e] : (double)fu[2 * e];
+        const double v =
+            NORM ? (double)fu[2 * e + 1] * (double)wu[2 * e + 1] : (double)fu[2 * e + 1];
+        fu[2 * e] = f64_to_f32(SCALE ? (u * t1.x - v * t1.y) * rs : u * t1.x - v * t1.y);
+        fu[2 * e + 1] = f64_to_f32(SCALE ? (u * t1.y + v * t1.x) * rs : u * t1.y + v * t1.x);
+        const double u2 = NORM ? (double)fv[2 * e] * (double)wv[2 * e] : (double)fv[2 * e];
+        const double v2 =
+            NORM ? (double)fv[2 * e + 1] * (double)wv[2 * e + 1] : (double)fv[2 * e + 1];
+        fv[2 * e] = f64_to_f32(SCALE ? (u2 * t2.x - v2 * t2.y) * rs : u2 * t2.x - v2 * t2.y);
+        fv[2 * e + 1] = f64_to_f32(SCALE ? (u2 * t2.y + v2 * t2.x) * rs : u2 * t2.y + v2 * t2.x);
       }
     }
     char* orow = rope_out_row(a, bh, l0 + p, ESZ);
@@ -494,11 +521,24 @@ hipError_t pick_qc(const RopeArgs& a, int qc, hipStream_t stream) {
 template <bool BF16, int MODE>
 hipError_t pick_g(const RopeArgs& a, int g, int qc, hipStream_t stream) {
   switch (g) {
+    case 4: return pick_qc<BF16, MODE, 4>(a, qc, stream);
     case 8: return pick_qc<BF16, MODE, 8>(a, qc, stream);
     case 16: return pick_qc<BF16, MODE, 16>(a, qc, stream);
     case 32: return pick_qc<BF16, MODE, 32>(a, qc, stream);
     default: return pick_qc<BF16, MODE, 64>(a, qc, stream);
   }
+}
+
+// rope_multi: normalised rows always scale the rotation (by rstd mscale); rotation-only rows
+// skip a unit mscale's product (exact either way).
+template <bool BF16, int MODE, int G, int PB>
+hipError_t go_multi(const RopeArgs& a, int64_t blocks, hipStream_t stream) {
+  const size_t lds = (size_t)PB * (a.dims / 2) * sizeof(double2);
+  const unsigned nb = (unsigned)blocks;
+  if (a.normalize) rope_multi<BF16, MODE, G, PB, false, true><<<nb, 256, lds, stream>>>(a);
+  else if (a.mscale != 1.f) rope_multi<BF16, MODE, G, PB, true, false><<<nb, 256, lds, stream>>>(a);
+  else rope_multi<BF16, MODE, G, PB, false, false><<<nb, 256, lds, stream>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -516,37 +556,30 @@ hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t strea
     const int mode = !a.traditional ? M_HALF : (half % V == 0 ? M_TRAD2 : M_TRAD1);
     const int npc = mode == M_TRAD1 ? a.dims / V : half / V;
     const int nqc = (a.D - a.dims) / V;
-    // Rotation only, every feature rotated, few rows per position and many positions:
-    // several positions per block (rope_multi).
-    if (!a.normalize && nqc == 0 && mode != M_TRAD1 && a.BH < 256 && a.L >= 4096 &&
-        (npc == 8 || npc == 16)) {
-      constexpr int PB = 4;
-      const size_t lds = (size_t)PB * half * sizeof(double2);
-      const int64_t blocks = (a.L + PB - 1) / PB;
+    // Every feature rotated, few rows per position and many positions: several positions
+    // per block (rope_multi). With the normalisation only for 64-feature rows: its variant
+    // holds 139 registers (three waves per SIMD), which at 128 features measured no faster
+    // than one position per block (NormRope [1, 32, 4096, 128] bf16: 20.2 us either way;
+    // [4, 8, 8192, 64]: 31.1 -> 20.9 us).
+    if (nqc == 0 && mode != M_TRAD1 && a.BH < 256 && a.L >= 4096 &&
+        (npc == 4 || ((npc == 8 || npc == 16) && !a.normalize))) {
+      // Eight positions per block for 4-lane rows (64 features), so that a block still
+      // holds 256 rows at 32 rows per position and its table one entry per thread.
+      const int64_t pb = npc == 4 ? 8 : 4;
+      const int64_t blocks = (a.L + pb - 1) / pb;
       if (blocks <= 0x7fffffff) {
-        const unsigned nb = (unsigned)blocks;
-        const bool ms = a.mscale != 1.f;  // a unit mscale skips its product (exact either way)
-        if (mode == M_HALF) {
-          if (npc == 8) {
-            if (ms) rope_multi<BF16, M_HALF, 8, PB, true><<<nb, 256, lds, stream>>>(a);
-            else rope_multi<BF16, M_HALF, 8, PB, false><<<nb, 256, lds, stream>>>(a);
-          } else {
-            if (ms) rope_multi<BF16, M_HALF, 16, PB, true><<<nb, 256, lds, stream>>>(a);
-            else rope_multi<BF16, M_HALF, 16, PB, false><<<nb, 256, lds, stream>>>(a);
-          }
-        } else {
-          if (npc == 8) {
-            if (ms) rope_multi<BF16, M_TRAD2, 8, PB, true><<<nb, 256, lds, stream>>>(a);
-            else rope_multi<BF16, M_TRAD2, 8, PB, false><<<nb, 256, lds, stream>>>(a);
-          } else {
-            if (ms) rope_multi<BF16, M_TRAD2, 16, PB, true><<<nb, 256, lds, stream>>>(a);
-            else rope_multi<BF16, M_TRAD2, 16, PB, false><<<nb, 256, lds, stream>>>(a);
-          }
-        }
-        return hipGetLastError();
+        const bool half_mode = mode == M_HALF;
+        if (npc == 4)
+          return half_mode ? go_multi<BF16, M_HALF, 4, 8>(a, blocks, stream)
+                           : go_multi<BF16, M_TRAD2, 4, 8>(a, blocks, stream);
+        if (npc == 8)
+          return half_mode ? go_multi<BF16, M_HALF, 8, 4>(a, blocks, stream)
+                           : go_multi<BF16, M_TRAD2, 8, 4>(a, blocks, stream);
+        return half_mode ? go_multi<BF16, M_HALF, 16, 4>(a, blocks, stream)
+                         : go_multi<BF16, M_TRAD2, 16, 4>(a, blocks, stream);
       }
     }
-    for (int g = 8; g <= 64; g *= 2) {
+    for (int g = 4; g <= 64; g *= 2) {
       if (npc <= g && nqc <= 2 * g) {
         const int qc = (nqc + g - 1) / g;
         if (mode == M_HALF) return pick_g<BF16, M_HALF>(a, g, qc, stream);
