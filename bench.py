@@ -11,6 +11,8 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
 --suite        also prints one JSON line per synthetic workload (all four ops) to stderr,
                rotating buffer sets when a call's working set would fit in the 256 MB
                Infinity Cache.
+--sweep        bandwidth of every operation across row widths (about 256 MB per call), one
+               JSON line per case to stderr; no headline line.
 --profile      only warm-up and timed calls of the headline kernel plus the copy kernel
                (for rocprofv3 runs); no CPU baseline.
 --summarize-trace TRACE_DB
@@ -488,6 +490,78 @@ def suite(args):
         torch.cuda.empty_cache()
 
 
+def sweep(args):
+    """Bandwidth across row widths: one line per (operation, dtype, width) to stderr, each call
+    moving about 256 MB (rows = 256 MB / the row's bytes), timed like the suite lines. It shows
+    how each kernel shape holds up away from the benchmark's widths."""
+    import torch
+
+    import transformer_row_wise_amd as nrm
+
+    nrm.load()
+    target = 256 * 2**20
+    dts = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+    def run(op, dt, shape, fn, nbytes):
+        avg = statistics.median(time_graph(lambda i: fn(), 24))
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        print(json.dumps({"sweep": op, "dtype": dt, "shape": shape, "bytes": nbytes,
+                          "gpu_us_median": round(avg * 1e3, 2), "gpu_GBps": round(gbps, 1),
+                          "pct_peak": round(100 * gbps / PEAK_GBPS, 1)}), file=sys.stderr,
+              flush=True)
+
+    for dt in ("bf16", "f32"):
+        es = 2 if dt == "bf16" else 4
+        for H in (64, 128, 256, 512, 1024, 2048, 4096, 5120, 8192, 12288, 16384, 32768):
+            R = max(64, target // (H * es * 4))
+            x = torch.randn(R, H, device="cuda").to(dts[dt])
+            r = torch.randn(R, H, device="cuda").to(dts[dt])
+            w = torch.ones(H, device="cuda").to(dts[dt])
+            b = torch.zeros(H, device="cuda").to(dts[dt])
+            out, h = torch.empty_like(x), torch.empty_like(x)
+            n = x.numel() * es
+            run("add_rms_norm", dt, [R, H], lambda: nrm.add_rms_norm(x, r, w, 1e-6, out=out, h=h), 4 * n)
+            run("rms_norm", dt, [R, H], lambda: nrm.rms_norm(x, w, 1e-6, out=out), 2 * n)
+            run("layer_norm", dt, [R, H], lambda: nrm.layer_norm(x, w, b, 1e-5, out=out), 2 * n)
+            del x, r, out, h
+        for H in (64, 128, 256, 512, 1024, 2048, 4096, 8192, 12288, 16384):
+            R = max(64, target // (H * es * 3))
+            x = torch.randn(R, H, device="cuda").to(dts[dt])
+            g = torch.randn(R, H, device="cuda").to(dts[dt])
+            w = torch.ones(H, device="cuda").to(dts[dt])
+            dx, dw, db = torch.empty_like(x), torch.empty_like(w), torch.empty_like(w)
+            ws = torch.empty(nrm.vjp_workspace_bytes(R, H, True), dtype=torch.uint8, device="cuda")
+            n = x.numel() * es
+            run("rms_norm_vjp", dt, [R, H],
+                lambda: nrm.rms_norm_vjp(x, w, g, 1e-6, dx=dx, dw=dw, workspace=ws), 3 * n)
+            run("layer_norm_vjp", dt, [R, H],
+                lambda: nrm.layer_norm_vjp(x, w, g, 1e-5, dx=dx, dw=dw, db=db, workspace=ws), 3 * n)
+            del x, g, dx
+        for V in (128, 512, 2048, 8192, 16384, 32000, 65536, 128256, 151936):
+            R = max(64, target // (V * es * 2))
+            x = torch.randn(R, V, device="cuda").to(dts[dt])
+            out = torch.empty_like(x)
+            lse = torch.empty(R, 1, device="cuda").to(dts[dt])
+            tg = torch.randint(0, V, (R,), device="cuda")
+            gl = torch.ones(R, device="cuda")
+            loss = torch.empty(R, device="cuda")
+            n = x.numel() * es
+            run("softmax", dt, [R, V], lambda: nrm.softmax(x, out=out), 2 * n)
+            run("logsumexp", dt, [R, V], lambda: nrm.logsumexp(x, out=lse), n)
+            run("cross_entropy", dt, [R, V], lambda: nrm.cross_entropy(x, tg, loss=loss), n)
+            run("cross_entropy_vjp", dt, [R, V],
+                lambda: nrm.cross_entropy_vjp(x, tg, gl, dlogits=out), 2 * n)
+            del x, out
+    for B, H, L, D in ((1, 32, 4096, 128), (8, 32, 512, 128), (4, 8, 8192, 64),
+                       (2, 16, 2048, 256), (1, 64, 8192, 128)):
+        x = torch.randn(B, H, L, D, device="cuda").to(torch.bfloat16)
+        out = torch.empty_like(x)
+        w = torch.ones(D, device="cuda").to(torch.bfloat16)
+        n = x.numel() * 2
+        run("rope", "bf16", [B, H, L, D], lambda: nrm.rope(x, out=out), 2 * n)
+        run("norm_rope", "bf16", [B, H, L, D], lambda: nrm.norm_rope(x, w, out=out), 2 * n)
+
+
 # --------------------------------------------------------------------------- counters
 
 def _pmc_per_dispatch(path, counter):
@@ -728,6 +802,8 @@ def main():
     ap.add_argument("--only", metavar="GROUPS",
                     help="with --suite: comma-separated groups among fwd, vjp, rope, sm "
                          "(skips the headline line)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="bandwidth across row widths, one line per case (stderr)")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_FILE", "WRITE_FILE"))
@@ -753,6 +829,9 @@ def main():
               f"independent, so N GPUs would each run this same kernel on their own rows); "
               f"got --gpus {args.gpus}", file=sys.stderr)
         return 2
+    if args.sweep:
+        sweep(args)
+        return 0
     if not args.only:
         headline(args)
     if args.suite or args.only:
