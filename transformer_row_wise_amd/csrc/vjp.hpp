@@ -14,11 +14,12 @@
 // one unit in the last place of the result: an fp32 statistic would miss it on a few
 // elements per million.
 //
-// dw and db sum over rows. A block owns a fixed set of rows (vjp_rows: rows strided across
-// the blocks; vjp_generic: a contiguous run) and accumulates its column sums in fp64
-// registers (each thread always holds the same columns); at the end the block writes one
-// fp64 partial row to the caller's workspace, and vjp_colsum adds the partial rows in a
-// fixed order. Results are therefore identical run to run.
+// dw and db sum over rows. A block owns a fixed set of rows (vjp_rows and vjp_team: rows
+// strided across the blocks; vjp_generic: a contiguous run) and accumulates its column sums
+// in fp64 (registers, or LDS for vjp_rows' dw at 16 elements per thread; each thread always
+// holds the same columns); at the end the block writes one fp64 partial row to the caller's
+// workspace, and vjp_colsum adds the partial rows in a fixed order. Results are therefore
+// identical run to run.
 #pragma once
 
 #include "row_kernels.hpp"
@@ -286,10 +287,11 @@ vjp_rows(VjpArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) lw_cols(k)[e] = 0.0;
   }
-  // fp32 parameters beside bf16 data take fp64 products with g: at ragged widths an opaque
-  // copy of w at each use keeps the compiler from holding their fp64 conversions (16
-  // registers) across the loop, which spilled the ring to scratch; converting again costs 8
-  // instructions a row (at whole-wave widths holding them measured faster).
+  // fp32 parameters beside bf16 data take fp64 products with g, and the compiler would hold
+  // their fp64 conversions (16 registers) across the loop, which spilled it to scratch.
+  // With 16 elements per thread w is read again (an L2 hit) at each use; at ragged widths
+  // with fewer, an opaque copy at each use makes it convert them again (8 instructions a
+  // row; at whole-wave widths holding them measured faster).
   auto wuse = [&](int k, float (&wl)[V]) {
     if constexpr (PK == PK_F32 && NV * V >= 16) {
       load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wl);
@@ -495,13 +497,13 @@ vjp_rows(VjpArgs a) {
 
 // Narrow rows (at most 32 chunks): a team of SUB = 8, 16 or 32 lanes per row, one chunk per
 // lane, 1024 / SUB teams per 1024-thread block (the grid is one block per partial row, at
-// most 256, so the block has to fill the compute unit). With P blocks, step it of team i of block b
-// takes row (it (1024 / SUB) + i) P + b, as in vjp_rows. A row's sums are lane exchanges inside
-// the team (no LDS, no barrier); the next row's chunks are loaded while the current one is
-// computed (two buffers, the loop unrolled by two so that no buffer is copied). A team past
-// the last row computes on a clamped row and neither stores nor accumulates it. At the end
-// the teams' column sums meet in LDS and are added in team order into the block's partial
-// row.
+// most 256, so the block has to fill the compute unit). With P blocks, step it of team i of
+// block b takes row (it (1024 / SUB) + i) P + b, as in vjp_rows. A row's sums are lane
+// exchanges inside the team (no LDS, no barrier); the next row's chunks are loaded while the
+// current one is computed (two buffers, the loop unrolled by two so that no buffer is
+// copied). A team past the last row computes on a clamped row and neither stores nor
+// accumulates it. At the end the teams' column sums meet in LDS and are added in team order
+// into the block's partial row.
 template <bool BF16, int OP, int PK, bool EXACT, int SUB, bool PG>
 __global__ void __launch_bounds__(1024)
 vjp_team(VjpArgs a) {

@@ -60,9 +60,11 @@ hipError_t vjp_rows_pk(const VjpArgs& a, int64_t blocks, int threads, bool exact
   // faster in the whole-width form.
   if constexpr (NV * Fmt<BF16>::VEC >= 16 && (OP == VJP_LN) == BF16) {
     (void)exact;
-    if (a.w == nullptr) return go_vjp_rows<BF16, OP, NV, PK_NONE, false, PG>(a, blocks, threads, stream);
+    if (a.w == nullptr)
+      return go_vjp_rows<BF16, OP, NV, PK_NONE, false, PG>(a, blocks, threads, stream);
     if constexpr (BF16) {
-      if (a.w_f32) return go_vjp_rows<BF16, OP, NV, PK_F32, false, PG>(a, blocks, threads, stream);
+      if (a.w_f32)
+        return go_vjp_rows<BF16, OP, NV, PK_F32, false, PG>(a, blocks, threads, stream);
     }
     return go_vjp_rows<BF16, OP, NV, PK_SAME, false, PG>(a, blocks, threads, stream);
   } else {
@@ -159,7 +161,9 @@ hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool*
   switch (nv) {
     case 1: return vjp_rows_pg<BF16, OP, 1>(a, pg, blocks, threads, exact, stream);
     case 2: return vjp_rows_pg<BF16, OP, 2>(a, pg, blocks, threads, exact, stream);
-    case 4: if constexpr (!BF16) return vjp_rows_pg<BF16, OP, 4>(a, pg, blocks, threads, exact, stream); break;
+    case 4:
+      if constexpr (!BF16) return vjp_rows_pg<BF16, OP, 4>(a, pg, blocks, threads, exact, stream);
+      break;
     default: break;
   }
   *done = false;
