@@ -18,8 +18,8 @@ pytestmark = pytest.mark.gpu
 
 # 5000 and 10000 (bf16): register rows whose team is 192 threads (three waves, one team per
 # block); 20000 and 40000: streaming rows of one and two steps (their first step parked in LDS)
-WIDTHS = [1, 2, 7, 8, 64, 100, 512, 520, 4096, 5000, 8192, 10000, 16384, 20000, 40000, 65536,
-          128256, 131072, 140000]
+WIDTHS = [1, 2, 7, 8, 33, 64, 100, 512, 520, 4096, 5000, 8192, 10000, 16384, 20000, 40000,
+          50257, 65536, 100277, 128256, 131072, 140000]
 PATHS = [None, "chunked", "scalar"]
 
 
@@ -85,7 +85,8 @@ def _ce_check(nrm, inp, dt, path=None, i32=False, sel=None):
     return loss, want
 
 
-@pytest.mark.parametrize("V", [2, 100, 1000, 5000, 10000, 20000, 32000, 128256, 151936])
+@pytest.mark.parametrize("V", [2, 100, 1000, 5000, 10000, 20000, 32000, 50257, 100277, 128256,
+                               151936])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_cross_entropy_vocab(nrm_lib, V, dt):
     say(f"cross_entropy V={V} {dt}")
@@ -142,7 +143,53 @@ def test_softmax_special_values(nrm_lib):
             compare.check_output(lse, oracle.softmax.logsumexp(f64(xs), dt), dt, what="lse")
 
 
-@pytest.mark.parametrize("n", [3000, 128256])
+def test_softmax_misaligned_bases(nrm_lib):
+    """Rows starting 2 bytes past a 16-byte boundary (a view one element into a buffer):
+    head, chunk body and tail per row, with an output of the same phase; an output of another
+    phase takes the one-element-at-a-time kernel; the loss and its gradient alike."""
+    say("softmax misaligned bases")
+    rows, n = 6, 4096
+    flat = dev(workloads.scores((1, rows * n + 8), "bf16", seed=77)).reshape(-1)
+    x = flat[1:1 + rows * n].view(rows, n)
+    oflat = torch.empty_like(flat)
+    out_same = oflat[1:1 + rows * n].view(rows, n)
+    got_same = nrm_lib.softmax(x, out=out_same)
+    got_other = nrm_lib.softmax(x)
+    lse = nrm_lib.logsumexp(x)
+    torch.cuda.synchronize()
+    want = oracle.softmax.softmax(f64(x.cpu()), "bf16")
+    compare.check_output(got_same, want, "bf16", what="softmax, same phase")
+    compare.check_output(got_other, want, "bf16", what="softmax, other phase")
+    compare.check_output(lse, oracle.softmax.logsumexp(f64(x.cpu()), "bf16"), "bf16", what="lse")
+    tg = torch.from_numpy(np.random.default_rng(78).integers(0, n, rows))
+    tg[0], tg[1] = 0, n - 1  # first and last column: in a row's head and tail
+    g = torch.from_numpy(np.random.default_rng(79).normal(size=rows).astype(np.float32))
+    loss = nrm_lib.cross_entropy(x, dev(tg))
+    dl = nrm_lib.cross_entropy_vjp(x, dev(tg), dev(g), dlogits=out_same)
+    torch.cuda.synchronize()
+    compare.check_f32(f64(loss), oracle.softmax.cross_entropy(f64(x.cpu()), tg.numpy()), what="loss")
+    compare.check_output(dl, oracle.softmax.cross_entropy_vjp(f64(x.cpu()), tg.numpy(), g.numpy(),
+                                                              "bf16"), "bf16", what="dlogits")
+
+
+def test_softmax_special_values_odd_width(nrm_lib):
+    say("softmax special values, odd width")
+    x = workloads.scores((5, 1001), "f32", seed=17)
+    x[0, 3] = float("nan")       # in the first row's body
+    x[1, :500] = -float("inf")
+    x[2, :] = -float("inf")
+    x[3, 1000] = float("inf")    # in a tail
+    x[4, :] = 1e30
+    for dt in ("f32", "bf16"):
+        xs = x.to(torch.bfloat16) if dt == "bf16" else x
+        got = nrm_lib.softmax(dev(xs))
+        lse = nrm_lib.logsumexp(dev(xs))
+        torch.cuda.synchronize()
+        compare.check_output(got, oracle.softmax.softmax(f64(xs), dt), dt, what="softmax")
+        compare.check_output(lse, oracle.softmax.logsumexp(f64(xs), dt), dt, what="lse")
+
+
+@pytest.mark.parametrize("n", [3000, 50257, 128256])
 def test_softmax_in_place(nrm_lib, n):
     say(f"softmax and gradient in place n={n}")
     for path in (None, "scalar"):

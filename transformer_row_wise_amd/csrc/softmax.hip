@@ -509,6 +509,161 @@ sm_stream(SmArgs a) {
   }
 }
 
+// sm_mis: rows whose width or start is not a whole number of 16-byte chunks (an odd
+// vocabulary such as 50257 columns), for every operation but CausalSoftmax. Each row splits
+// into a head of hd < VEC elements up to its first 16-byte boundary, a body of whole chunks
+// and a tail of fewer than VEC elements; thread t < hd + tail holds one head or tail element
+// as a scalar, and the body streams as in sm_stream (U chunks per step, an online maximum and
+// rescaled sum per thread, then for row outputs a second, cached pass). The output row has
+// the input row's phase (the host checks that the two bases agree modulo 16), so its body
+// chunks are 16-byte aligned too.
+template <bool BF16, int OP, int TPB>
+__global__ void __launch_bounds__(TPB)
+sm_mis(SmArgs a) {
+  constexpr bool CE = OP == SM_CE || OP == SM_CE_VJP;
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr int U = 4;
+  constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CE_VJP;
+  constexpr int NW = TPB / 64;
+  __shared__ float red_m[NW], red_s[NW], xt_s[1];
+  const int64_t row = blockIdx.x;
+  const SmRow r = sm_row<OP>(a, row);
+  const int64_t n = a.n;
+  const int64_t e0 = row * n;
+  const char* xrow = (const char*)a.x + e0 * ESZ;
+  const int hd = (int)min((int64_t)((16 - ((uintptr_t)xrow & 15)) & 15) / ESZ, n);
+  const int64_t nch = (n - hd) / V;
+  const int tl = (int)(n - hd - nch * V);
+  const char* xbody = xrow + (int64_t)hd * ESZ;  // 16-byte aligned
+  // This thread's scalar element (column sc), if any.
+  const bool has_s = (int)threadIdx.x < hd + tl;
+  const int64_t sc = (int)threadIdx.x < hd ? (int64_t)threadIdx.x
+                                            : hd + nch * V + ((int64_t)threadIdx.x - hd);
+  float sv = -__builtin_inff();
+  if (has_s) {
+    float t[1];
+    load_act<BF16, 1>(a.x, e0 + sc, t);
+    sv = t[0];
+  }
+  const int64_t tb = r.target < 0 ? -1 : r.target - hd;  // CE: target's index in the body
+  const int64_t tgt_chunk = tb < 0 || tb >= nch * V ? -1 : tb / V;
+  const int tgt_e = tgt_chunk < 0 ? -1 : (int)(tb % V);
+  const bool s_tgt = CE && has_s && sc == r.target;
+
+  // Pass 1: the scalar element first, then the body, online (max, rescaled sum) per thread.
+  float m = -__builtin_inff(), s = 0.f;
+  if (has_s) {
+    m = fmaxf(m, sv);
+    const float mm = m == -__builtin_inff() ? 0.f : m;
+    float ex = sm_exp64(sv - mm);
+    if (s_tgt) {
+      xt_s[0] = sv;  // published by the barrier of the maximum's reduction
+      ex = 0.f;
+    }
+    s = ex;
+  }
+  const int64_t stepc = (int64_t)TPB * U;
+  const int64_t nsteps = (nch + stepc - 1) / stepc;
+  for (int64_t si = 0; si < nsteps; ++si) {
+    const int64_t j0 = threadIdx.x + si * stepc;
+    if (j0 >= nch) break;
+    float f[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = min(j0 + (int64_t)u * TPB, nch - 1);
+      const u32x4 raw = OUT ? ld16(xbody + j * 16) : ld16_nt(xbody + j * 16);
+      unpack<BF16>(raw, f[u]);
+    }
+    float cm = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + (int64_t)u * TPB < nch) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) cm = fmaxf(cm, f[u][e]);
+      }
+    }
+    if (cm > m) {
+      s = s * sm_factor(m - cm);
+      m = cm;
+    }
+    const float mm = m == -__builtin_inff() ? 0.f : m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + (int64_t)u * TPB;
+      if (j < nch) {
+        const bool own = CE && j == tgt_chunk;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          float ex = sm_exp64(f[u][e] - mm);
+          if (own && e == tgt_e) {
+            xt_s[0] = f[u][e];
+            ex = 0.f;
+          }
+          s += ex;
+        }
+      }
+    }
+  }
+  const float M = team_reduce<true>(m, red_m, 0, NW);
+  float xt = 0.f;
+  if constexpr (CE) xt = r.bad ? 0.f : xt_s[0];
+  const float S = team_reduce<false>(m == -__builtin_inff() ? 0.f : s * sm_factor(m - M), red_s, 0, NW);
+
+  if constexpr (OP == SM_LSE) {
+    if (threadIdx.x == 0) {
+      float o[1] = {lse_of(M, S)};
+      store_act<BF16, 1>(a.out, row, o);
+    }
+    return;
+  }
+  if constexpr (OP == SM_CE) {
+    if (threadIdx.x == 0)
+      a.loss[row] = r.bad ? __builtin_nanf("") : ce_loss(M, xt, sm_exp64(xt - M), S);
+    return;
+  }
+  float inv, gt = 0.f;
+  if constexpr (OP == SM_CE_VJP) {
+    const float e_t = sm_exp64(xt - M);
+    const float tot = S + e_t;
+    inv = r.g / tot;
+    gt = -r.g * (S / tot);
+    if (r.bad) inv = gt = __builtin_nanf("");
+  } else {
+    inv = 1.f / S;
+  }
+  // Pass 2: each thread writes exactly what it read (in-place use is safe).
+  char* obody = (char*)a.out + (e0 + hd) * ESZ;
+  if (has_s) {
+    float o[1] = {s_tgt ? gt : sm_exp64(sv - M) * inv};
+    store_act<BF16, 1>(a.out, e0 + sc, o);
+  }
+  for (int64_t si = 0; si < nsteps; ++si) {
+    const int64_t j0 = threadIdx.x + si * stepc;
+    if (j0 >= nch) break;
+    float f[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = min(j0 + (int64_t)u * TPB, nch - 1);
+      unpack<BF16>(ld16_nt(xbody + j * 16), f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + (int64_t)u * TPB;
+      if (j < nch) {
+        const bool own = OP == SM_CE_VJP && j == tgt_chunk;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          float p = sm_exp64(f[u][e] - M) * inv;
+          if (own && e == tgt_e) p = gt;
+          f[u][e] = p;
+        }
+        st16_nt(obody + j * 16, pack<BF16>(f[u]));
+      }
+    }
+  }
+}
+
 namespace {
 
 constexpr int64_t kSmMaxGrid = 0x7fffffff;
@@ -560,13 +715,31 @@ hipError_t go_sm_stream(const SmArgs& a, hipStream_t stream) {
 
 // Register kernel for rows of up to 2048 chunks: NV = ceil(chunks / 256) (at most 8), raised
 // towards 4 as far as the team keeps 16 lanes; T = ceil(chunks / NV), rounded up to 16, 32
-// or a multiple of 64. Longer rows and unaligned rows: the streaming kernel.
+// or a multiple of 64. Longer rows: the streaming kernel. Rows that are not whole chunks:
+// sm_mis (CausalSoftmax, or an output of another phase: the streaming kernel one element at a
+// time).
 template <bool BF16, int OP>
 hipError_t launch_softmax(const SmArgs& a, bool aligned16, hipStream_t stream) {
   constexpr int V = Fmt<BF16>::VEC;
   const int path = forced_path();
   const bool vec = aligned16 && a.n % V == 0 && path != PATH_SCALAR;
-  if (!vec) return go_sm_stream<BF16, OP, 1>(a, stream);
+  if (!vec) {
+    // Rows not made of whole 16-byte chunks: head, chunk body and tail per row (sm_mis),
+    // when an output row shares its input row's phase; otherwise one element at a time.
+    if constexpr (OP != SM_CAUSAL) {
+      constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CE_VJP;
+      const bool same_phase = !OUT || (((uintptr_t)a.x ^ (uintptr_t)a.out) & 15u) == 0;
+      if (path != PATH_SCALAR && same_phase && ((uintptr_t)a.x & (Fmt<BF16>::ESZ - 1)) == 0) {
+        if (a.rows > kSmMaxGrid) return hipErrorInvalidConfiguration;
+        if (OUT && a.n >= 16384)
+          sm_mis<BF16, OP, 1024><<<(unsigned)a.rows, 1024, 0, stream>>>(a);
+        else
+          sm_mis<BF16, OP, 256><<<(unsigned)a.rows, 256, 0, stream>>>(a);
+        return hipGetLastError();
+      }
+    }
+    return go_sm_stream<BF16, OP, 1>(a, stream);
+  }
   const int64_t n = a.n / V;
   if (path != PATH_CHUNKED && n <= 2048) {
     int nv = (int)std::min<int64_t>(8, (n + 255) / 256);
