@@ -111,7 +111,15 @@ def _raise(status):
     raise NrmError(status, L.nrm_status_name(status).decode(), L.nrm_last_error().decode())
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream():
+    """The current device's current stream, as a raw handle (torch's direct accessor where it
+    exists: a fraction of a microsecond against ~3 for torch.cuda.current_stream())."""
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
     return torch.cuda.current_stream().cuda_stream
 
 
@@ -129,9 +137,9 @@ def _dtype_code(t, what):
 def _check_act(t, what, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what} must be a torch.Tensor, got {type(t).__name__}")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{what} must be on a HIP device, got {t.device}")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{what} must be on {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
