@@ -127,6 +127,52 @@ def test_vjp_narrow_rows_many(nrm_lib, ln, hidden, dt, wdt):
 
 
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("hidden,dt,wdt", [(1001, "bf16", "bf16"), (2047, "bf16", "f32"),
+                                           (3001, "bf16", None), (4100, "bf16", "bf16"),
+                                           (6150, "bf16", "bf16"), (8191, "bf16", "bf16"),
+                                           (7000, "bf16", "f32"), (1001, "f32", "f32"),
+                                           (4097, "f32", None), (6145, "f32", "f32"),
+                                           (100, "bf16", "bf16"), (33, "f32", "f32")])
+def test_vjp_element_rows(nrm_lib, ln, hidden, dt, wdt):
+    """Widths that are not whole 16-byte chunks: 1 (33), 2 (100), 4 (up to 4096), 6 or 8
+    elements per thread in one block per run of rows (8 only with bf16 weights; wider rows,
+    and 7000 with fp32 weights, take the generic kernel). 2301 rows: runs of 9 rows (whole
+    and partial trips of the 2-, 3- and 4-deep register rings) and a last run of 6."""
+    say(f"vjp element rows {'ln' if ln else 'rms'} rows=2301 hidden={hidden} {dt} w={wdt}")
+    check_vjp(nrm_lib, _inp(2301, hidden, dt, wdt, 37, ln), ln)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_vjp_misaligned_bases(nrm_lib, ln, dt):
+    """x, g and dx one element past a 16-byte boundary (views into larger buffers), with a
+    width of whole chunks: the single-element kernel."""
+    say(f"vjp misaligned bases {'ln' if ln else 'rms'} {dt}")
+    rows, n = 300, 4096
+    inp = _inp(rows, n, dt, dt, 41, ln)
+
+    def shifted(t):
+        buf = torch.zeros(rows * n + 8, dtype=t.dtype, device=DEV)
+        v = buf[1:1 + rows * n].view(rows, n)
+        v.copy_(dev(t))
+        return v
+
+    x, g = shifted(inp.x), shifted(inp.g)
+    dxo = torch.empty(rows * n + 8, dtype=x.dtype, device=DEV)[1:1 + rows * n].view(rows, n)
+    w = dev(inp.w)
+    if ln:
+        got = nrm_lib.layer_norm_vjp(x, w, g, inp.eps, dx=dxo)
+    else:
+        got = nrm_lib.rms_norm_vjp(x, w, g, inp.eps, dx=dxo)
+    torch.cuda.synchronize()
+    assert got[0].data_ptr() == dxo.data_ptr()
+    want_dx, want_params = vjp_oracle(inp, ln)
+    compare.check_output(got[0], want_dx, dt, what="dx")
+    for name, gv, wv in zip(("dw", "db"), got[1:], want_params):
+        compare.check_output(gv, wv, dt, what=name)
+
+
+@pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
 def test_vjp_zero_rows_zero_parameter_gradients(nrm_lib, ln):
     say(f"vjp zero rows {'ln' if ln else 'rms'}")
     x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)

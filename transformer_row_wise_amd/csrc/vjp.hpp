@@ -15,7 +15,7 @@
 // elements per million.
 //
 // dw and db sum over rows. A block owns a fixed set of rows (vjp_rows and vjp_team: rows
-// strided across the blocks; vjp_generic: a contiguous run) and accumulates its column sums
+// strided across the blocks; vjp_generic and vjp_elems: a contiguous run) and accumulates its column sums
 // in fp64 (registers, or LDS for vjp_rows' dw at 16 elements per thread; each thread always
 // holds the same columns); at the end the block writes one fp64 partial row to the caller's
 // workspace, and vjp_colsum adds the partial rows in a fixed order. Results are therefore
@@ -657,6 +657,107 @@ vjp_generic(VjpArgs a) {
         if constexpr (DW) pw[j * V + e] = aw[e];
         if constexpr (DB) pb[j * V + e] = ab[e];
       }
+    }
+  }
+}
+
+// Rows of up to 8192 elements, in single elements (for widths that are not whole 16-byte
+// chunks, or rows that do not start on a 16-byte boundary). One block of T threads per run
+// of rows; thread t holds the K elements at columns t + T e of a row (so a wave's loads are
+// consecutive elements), and its dw / db column sums in registers for the whole run. Each
+// row is read once, and the loads of the next rows (one to three, as the registers allow)
+// are in flight during the current row's reduction. XF: bf16 x, g and w (exact fp32
+// products, see vjp_accumulate). At 8 elements per thread the dw and db sums live in LDS
+// (LW, K * T doubles each, element-major): in registers, LN's 32 accumulator registers push
+// the kernel into scratch.
+template <bool BF16, int OP, int K, bool PG, bool XF>
+__global__ void __launch_bounds__(1024)
+vjp_elems(VjpArgs a) {
+  constexpr bool DW = PG, DB = PG && OP == VJP_LN;
+  constexpr bool LW = DW && K >= 8, LB = DB && K >= 8;
+  __shared__ double red[2][16 * 4];
+  extern __shared__ double colw[];
+  const int T = blockDim.x;
+  const int tid = threadIdx.x;
+  const int64_t H = a.hidden;
+  const int64_t row0 = (int64_t)blockIdx.x * a.rpb;
+  const int64_t row_end = min(a.rows, row0 + a.rpb);
+  bool ok[K];
+  float wv[K];
+  double aw[K], ab[K];
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    const int64_t c = tid + (int64_t)T * e;
+    ok[e] = e < K - 1 || c < H;  // the launch keeps T (K - 1) <= H
+    float t[1] = {1.f};
+    if (ok[e] && a.w != nullptr) load_param<BF16, 1>(a.w, a.w_f32, c, t);
+    wv[e] = ok[e] ? t[0] : 0.f;
+    aw[e] = ab[e] = 0.0;
+  }
+  // This thread's columns, touched by no other thread: no barrier needed.
+  const LdsCols lw{colw + tid, T}, lb{colw + K * T + tid, T};
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    if constexpr (LW) lw[e] = 0.0;
+    if constexpr (LB) lb[e] = 0.0;
+  }
+  // Ring of R register sets: the loads for row i + R - 1 are issued before row i's sums.
+  constexpr int R = K <= 2 ? 4 : K <= 4 ? 3 : 2;
+  float xs[R][K], gs[R][K];
+  auto load = [&](int64_t row, float (&xv)[K], float (&gv)[K]) {
+    const int64_t e0 = row * H + tid;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      float t[1] = {0.f}, u[1] = {0.f};
+      if (ok[e]) {
+        load_act<BF16, 1>(a.x, e0 + (int64_t)T * e, t);
+        load_act<BF16, 1>(a.g, e0 + (int64_t)T * e, u);
+      }
+      xv[e] = t[0];
+      gv[e] = u[0];
+    }
+  };
+  auto step = [&](int64_t row, const float (&xv)[K], const float (&gv)[K], double* rb) {
+    double ds[4] = {0.0, 0.0, 0.0, 0.0};
+    vjp_accumulate<OP, K, XF>(xv, gv, wv, ds);
+    team_sum4(ds, rb, 0, T >> 6);
+    VjpRow s;
+    if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
+    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
+    float dxv[K];
+    if constexpr (LB) vjp_outputs<OP, K, DW, DB, XF>(xv, gv, wv, s, dxv, lw, lb);
+    else if constexpr (LW) vjp_outputs<OP, K, DW, DB, XF>(xv, gv, wv, s, dxv, lw, ab);
+    else vjp_outputs<OP, K, DW, DB, XF>(xv, gv, wv, s, dxv, aw, ab);
+    const int64_t e0 = row * H + tid;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const float t[1] = {dxv[e]};
+      if (ok[e]) store_act<BF16, 1>(a.dx, e0 + (int64_t)T * e, t);
+    }
+  };
+  // R rows per trip, so that the register sets are picked at compile time; consecutive rows
+  // alternate reduction slots (a slot is rewritten only after the next row's barrier, which
+  // every thread reaches after reading it). Loads past the last row repeat the last row, so
+  // every load is unconditional.
+  if (row0 < row_end) {
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) load(min(row0 + i, row_end - 1), xs[i], gs[i]);
+  }
+  for (int64_t row = row0; row < row_end; row += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (row + i >= row_end) break;
+      load(min(row + i + R - 1, row_end - 1), xs[(i + R - 1) % R], gs[(i + R - 1) % R]);
+      step(row + i, xs[i], gs[i], red[R % 2 == 0 ? i & 1 : (row + i - row0) & 1]);
+    }
+  }
+  if constexpr (PG) {
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const int64_t c = tid + (int64_t)T * e;
+      if (!ok[e]) continue;
+      if constexpr (DW) a.part_w[(int64_t)blockIdx.x * H + c] = LW ? lw[e] : aw[e];
+      if constexpr (DB) a.part_b[(int64_t)blockIdx.x * H + c] = LB ? lb[e] : ab[e];
     }
   }
 }

@@ -10,6 +10,9 @@
 //   gradients, one partial row per block).
 // Rows of at most 32 chunks take vjp_team instead: teams of 8, 16 or 32 lanes, one chunk per
 // lane, 1024 / team rows in flight per block.
+// Rows that are not whole 16-byte chunks (or not 16-byte aligned), up to 8192 elements
+// (6144 with fp32 data or weights): vjp_elems, single elements, 1 to 8 per thread (4 for most
+// rows up to 2048), one block per run of rows.
 // Otherwise vjp_generic (256 threads, 16-byte chunks or single elements, any width).
 // The partial rows are then added by vjp_colsum.
 #pragma once
@@ -170,6 +173,59 @@ hipError_t try_vjp_rows(VjpArgs a, bool pg, int64_t n, hipStream_t stream, bool*
   return hipSuccess;
 }
 
+template <bool BF16, int OP, int K, bool PG, bool XF>
+void go_elems(const VjpArgs& a, int64_t blocks, unsigned threads, size_t lds,
+              hipStream_t stream) {
+  vjp_elems<BF16, OP, K, PG, XF><<<(unsigned)blocks, threads, lds, stream>>>(a);
+}
+
+template <bool BF16, int OP, int K>
+hipError_t go_vjp_elems(VjpArgs a, bool pg, hipStream_t stream) {
+  const int64_t blocks = vjp_partials(a.rows);
+  a.rpb = (a.rows + blocks - 1) / blocks;
+  const int64_t per = (a.hidden + K - 1) / K;
+  const unsigned threads = (unsigned)((per + 63) / 64 * 64);
+  // Only a thread's last element can fall past the row's end (vjp_elems relies on it).
+  if ((int64_t)threads * (K - 1) > a.hidden || threads > 1024) return hipErrorInvalidConfiguration;
+  // vjp_elems' LDS column sums: dw, and db for LN.
+  const size_t lds = pg && K >= 8 ? (size_t)(OP == VJP_LN ? 2 : 1) * K * threads * 8 : 0;
+  if constexpr (BF16) {
+    if (!a.w_f32) {
+      if (pg) go_elems<BF16, OP, K, true, true>(a, blocks, threads, lds, stream);
+      else go_elems<BF16, OP, K, false, true>(a, blocks, threads, 0, stream);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (K < 8) {  // try_vjp_elems takes 8 only with bf16 weights
+    if (pg) go_elems<BF16, OP, K, true, false>(a, blocks, threads, lds, stream);
+    else go_elems<BF16, OP, K, false, false>(a, blocks, threads, 0, stream);
+  }
+  return hipGetLastError();
+}
+
+// Rows of single elements: vjp_elems with K elements per thread. Rows of up to 2048 take 4
+// where the thread count allows it (only a thread's last element past the row's end), else
+// 2, else 1: at one element per thread the row's reduction costs more than its elements
+// (1001-wide fp32 rows 77 -> 53 us, bf16 163 -> 137 us). Wider rows take the fewest of 6 or
+// 8 that fit a 1024-thread block; 8 only with bf16 x, g and w: with fp64 products (fp32
+// data or weights) that variant runs out of registers. *done = false for wider rows.
+template <bool BF16, int OP>
+hipError_t try_vjp_elems(const VjpArgs& a, bool pg, hipStream_t stream, bool* done) {
+  const int64_t n = a.hidden;
+  *done = n <= (BF16 && !a.w_f32 ? 8 : 6) * 1024;
+  if (!*done) return hipSuccess;
+  auto fits = [n](int64_t k) {
+    const int64_t t = ((n + k - 1) / k + 63) / 64 * 64;
+    return t * (k - 1) <= n && t <= 1024;
+  };
+  if (n <= 2048 && fits(4)) return go_vjp_elems<BF16, OP, 4>(a, pg, stream);
+  if (n <= 2048 && fits(2)) return go_vjp_elems<BF16, OP, 2>(a, pg, stream);
+  if (n <= 1024) return go_vjp_elems<BF16, OP, 1>(a, pg, stream);
+  if (n <= 4096) return go_vjp_elems<BF16, OP, 4>(a, pg, stream);
+  if (n <= 6144) return go_vjp_elems<BF16, OP, 6>(a, pg, stream);
+  return go_vjp_elems<BF16, OP, 8>(a, pg, stream);
+}
+
 template <bool BF16, int OP, int V>
 hipError_t go_vjp_generic(VjpArgs a, bool pg, hipStream_t stream) {
   int64_t blocks;
@@ -205,6 +261,7 @@ hipError_t launch_vjp(const VjpArgs& a, void* dw, void* db, bool aligned16, hipS
   if (vec && path == PATH_AUTO) err = try_vjp_team<BF16, OP>(a, pg, a.hidden / V, stream, &done);
   if (vec && !done && path != PATH_CHUNKED)
     err = try_vjp_rows<BF16, OP>(a, pg, a.hidden / V, stream, &done);
+  if (!vec && path == PATH_AUTO) err = try_vjp_elems<BF16, OP>(a, pg, stream, &done);
   if (!done) err = vec ? go_vjp_generic<BF16, OP, V>(a, pg, stream)
                        : go_vjp_generic<BF16, OP, 1>(a, pg, stream);
   if (err != hipSuccess || !pg) return err;
