@@ -11,8 +11,9 @@ import torch
 
 import compare
 import workloads
-from gpu_util import (DEV, check_add, check_ln, check_rms, check_rope, dev, f64, forced_path,
-                      run_rope, say)
+import oracle
+from gpu_util import (DEV, assert_h_exact, check_add, check_ln, check_rms, check_rope, dev, f64,
+                      forced_path, run_rope, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +82,69 @@ def test_narrow_rows_many(nrm_lib, dt, hidden, wkind):
     if wkind is None:
         inp.w = inp.b = None
     check_ln(nrm_lib, inp)
+
+
+# Widths that are not whole 16-byte chunks: one block per row with 1 (33), 2 (100), 4 (up to
+# 4096), 8 (up to 8192) or 12 (up to 12288) elements per thread; 12289 takes the looping kernel.
+ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 1001), ("bf16", 4100), ("bf16", 8191),
+         ("bf16", 10001), ("bf16", 12287), ("bf16", 12289), ("f32", 1001), ("f32", 4097),
+         ("f32", 12285)]
+
+
+@pytest.mark.parametrize("dt,hidden", ELEMS)
+@pytest.mark.parametrize("wkind", ["same", "f32", None])
+def test_element_rows(nrm_lib, dt, hidden, wkind):
+    if wkind == "f32" and dt == "f32":
+        pytest.skip("same as 'same' for fp32 data")
+    wdt = None if wkind is None else ("f32" if wkind == "f32" else dt)
+    say(f"element rows=300 hidden={hidden} {dt} w={wdt}")
+    check_add(nrm_lib, _row(300, hidden, dt, wdt, seed=hidden + 11, r=("normal", 0.0, 1.0),
+                            eps=1e-6))
+    check_rms(nrm_lib, _row(300, hidden, dt, wdt, seed=hidden + 12, x=("t3",), eps=1e-5))
+    for affine in ("wb", "w", "b", "none"):
+        inp = workloads.row_inputs(300, hidden, dt, seed=hidden + 13, x=("normal", 0.5, 2.0),
+                                   w=("normal", 1.0, 0.1), b=("normal", 0.0, 0.1),
+                                   w_dtype=wdt or dt, eps=1e-5)
+        if wkind is None or "w" not in affine:
+            inp.w = None
+        if wkind is None or "b" not in affine:
+            inp.b = None
+        check_ln(nrm_lib, inp)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_misaligned_bases(nrm_lib, dt):
+    """x, r, h and out one element past a 16-byte boundary (views into larger buffers) with a
+    width of whole chunks: the single-element kernel, for all three forward operations."""
+    say(f"forward misaligned bases {dt}")
+    rows, n = 300, 4096
+
+    def shifted(t=None, like=None):
+        src = t if t is not None else like
+        buf = torch.zeros(rows * n + 8, dtype=src.dtype, device=DEV)
+        v = buf[1:1 + rows * n].view(rows, n)
+        if t is not None:
+            v.copy_(dev(t))
+        return v
+
+    inp = _row(rows, n, dt, dt, seed=51, r=("normal", 0.0, 1.0), eps=1e-6)
+    x, r = shifted(inp.x), shifted(inp.r)
+    out, h = shifted(like=x), shifted(like=x)
+    got, gh = nrm_lib.add_rms_norm(x, r, dev(inp.w), inp.eps, out=out, h=h)
+    got2 = nrm_lib.rms_norm(x, dev(inp.w), inp.eps, out=shifted(like=x))
+    lin = workloads.row_inputs(rows, n, dt, seed=52, x=("normal", 0.5, 2.0),
+                               w=("normal", 1.0, 0.1), b=("normal", 0.0, 0.1), eps=1e-5)
+    got3 = nrm_lib.layer_norm(shifted(lin.x), dev(lin.w), dev(lin.b), lin.eps,
+                              out=shifted(like=x))
+    torch.cuda.synchronize()
+    assert got.data_ptr() == out.data_ptr() and gh.data_ptr() == h.data_ptr()
+    want_out, want_h = oracle.add_rms_norm(f64(inp.x), f64(inp.r), f64(inp.w), inp.eps, dt)
+    assert_h_exact(gh, want_h)
+    compare.check_output(got, want_out, dt, what="add_rms_norm out")
+    compare.check_output(got2, oracle.rms_norm(f64(inp.x), f64(inp.w), inp.eps, dt), dt,
+                         what="rms_norm out")
+    compare.check_output(got3, oracle.layer_norm(f64(lin.x), f64(lin.w), f64(lin.b), lin.eps,
+                                                 dt), dt, what="layer_norm out")
 
 
 @pytest.mark.parametrize("path", ["wave", "block", "rowblock", "chunked", "scalar"])

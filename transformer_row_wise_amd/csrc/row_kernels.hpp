@@ -14,9 +14,12 @@
 //                           a block holds four independent waves (four rows);
 //   row_regs<..., WPR = 8>  one 512-thread block per row, row in registers, cross-wave sums
 //                           through LDS (hidden <= 512*NV*VEC);
+//   row_elems               one block per row, K single elements per thread in registers:
+//                           RMSNorm and LayerNorm rows whose width or base addresses are not
+//                           16-byte multiples, up to 12288 elements;
 //   row_chunked             one 256-thread block per row looping over the row: any width, and
-//                           V = 1 for rows whose width or base addresses are not 16-byte
-//                           multiples. The row is re-read (L2) for the second pass.
+//                           V = 1 for the other rows of that kind. The row is re-read (L2)
+//                           for the second pass.
 // Every element of x (and r) is read from HBM once and every output element written once;
 // w and b are small and come from L2.
 #pragma once
@@ -493,6 +496,99 @@ row_chunked(RowArgs a) {
       }
     }
     __syncthreads();  // the LDS slots are reused by the next row of this block
+  }
+}
+
+// One element of x / r / h / out at element index i, non-temporal (touched once).
+template <bool BF16>
+__device__ __forceinline__ float ld1_nt(const void* p, int64_t i) {
+  if constexpr (BF16) return bf16_to_f32(__builtin_nontemporal_load((const uint16_t*)p + i));
+  else return __builtin_nontemporal_load((const float*)p + i);
+}
+template <bool BF16>
+__device__ __forceinline__ void st1_nt(void* p, int64_t i, float v) {
+  if constexpr (BF16) __builtin_nontemporal_store(f32_to_bf16(v), (uint16_t*)p + i);
+  else __builtin_nontemporal_store(v, (float*)p + i);
+}
+
+// Rows that are not whole 16-byte chunks (an odd width, or a base off a 16-byte boundary),
+// up to 12288 elements: one row per block of T threads, thread t holding the K elements at
+// columns t + T e in registers (a wave's accesses are consecutive elements), so the row is
+// read once; the arithmetic is row_chunked's. The launch keeps T (K - 1) <= hidden, so only
+// a thread's last element can fall past the row's end; such an element loads as 0 (adding
+// nothing to the sums; LayerNorm's second sum skips it) and is not stored. HB: LayerNorm
+// with a shift vector.
+template <bool BF16, int OP, int K, int PK, bool HB>
+__global__ void __launch_bounds__(1024)
+row_elems(RowArgs a) {
+  __shared__ float red_f[16];
+  __shared__ double red_d[2][16];
+  const int T = blockDim.x, nw = T >> 6;
+  const int64_t H = a.hidden;
+  const int64_t e0 = (int64_t)blockIdx.x * H + threadIdx.x;
+  bool ok[K];
+  float f[K];
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    ok[e] = e < K - 1 || threadIdx.x + (int64_t)T * e < H;
+    f[e] = ok[e] ? ld1_nt<BF16>(a.x, e0 + (int64_t)T * e) : 0.f;
+  }
+  if constexpr (OP == OP_ADD_RMS) {
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const float fr = ok[e] ? ld1_nt<BF16>(a.r, e0 + (int64_t)T * e) : 0.f;
+      float t[1] = {f[e] + fr};
+      round_to_storage<BF16, 1>(t);
+      f[e] = t[0];
+      if (ok[e]) st1_nt<BF16>(a.h, e0 + (int64_t)T * e, f[e]);
+    }
+  }
+  // Scale (and shift) at this thread's columns; a column past the end reads the last one.
+  float wv[K], bv[K];
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    const int64_t c = min((int64_t)threadIdx.x + (int64_t)T * e, H - 1);
+    float t[1];
+    load_pk<BF16, PK, 1>(a.w, c, t);
+    wv[e] = t[0];
+    if constexpr (HB) {
+      if constexpr (PK == PK_NONE) load_param<BF16, 1>(a.b, a.w_f32, c, t);  // b without w
+      else load_pk<BF16, PK, 1>(a.b, c, t);
+      bv[e] = t[0];
+    }
+  }
+  float y[K];
+  if constexpr (OP == OP_RMS || OP == OP_ADD_RMS) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < K; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
+    const float rstd = (float)rstd_f64((double)block_row_sum(acc, red_f, nw), a.hidden, a.eps);
+#pragma unroll
+    for (int e = 0; e < K; ++e) y[e] = (f[e] * rstd) * wv[e];
+  } else {
+    double s1 = 0.0;
+#pragma unroll
+    for (int e = 0; e < K; ++e) s1 += (double)f[e];
+    const double mu = block_row_sum(s1, red_d[0], nw) / (double)a.hidden;
+    double s2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const double d = ok[e] ? (double)f[e] - mu : 0.0;
+      s2 = __builtin_fma(d, d, s2);
+    }
+    const double rstd = rstd_f64(block_row_sum(s2, red_d[1], nw), a.hidden, a.eps);
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      double t = ((double)f[e] - mu) * rstd;
+      if constexpr (PK != PK_NONE && HB) t = __builtin_fma(t, (double)wv[e], (double)bv[e]);
+      else if constexpr (PK != PK_NONE) t = t * (double)wv[e];
+      else if constexpr (HB) t = t + (double)bv[e];
+      y[e] = f64_to_f32(t);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    if (ok[e]) st1_nt<BF16>(a.out, e0 + (int64_t)T * e, y[e]);
   }
 }
 

@@ -9,8 +9,9 @@
 //                                    clamp(ceil(n / 256), 2, 4)), T = ceil(n / NV) rounded
 //                                    up to a wave (hidden 8192 bf16: 512 threads with 2
 //                                    chunks each, LayerNorm 256 threads with 4);
-//   otherwise, or when hidden or a base address is not 16-byte granular: the looping
-//   kernel (16-byte chunks, or single elements).
+//   hidden or a base address not 16-byte granular, hidden <= 12288: row_elems, one block per
+//   row, K single elements per thread in registers (RMSNorm and LayerNorm);
+//   otherwise the looping kernel (16-byte chunks, or single elements).
 // Measured on MI355X for add-RMSNorm bf16 [16384, 8192]: row_block streams at ~6.25 TB/s,
 // one wave per row (the whole row in one wave's registers) at ~5.2 TB/s, the 512-thread
 // register kernel without streaming hints at ~5.9 TB/s. Those two stay available through
@@ -45,6 +46,46 @@ hipError_t go_chunked(const RowArgs& a, hipStream_t stream) {
   const int64_t blocks = a.rows < 1048576 ? a.rows : 1048576;
   row_chunked<BF16, OP, V><<<(unsigned)blocks, 256, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool BF16, int OP, int K, int PK>
+void go_elems_hb(const RowArgs& a, unsigned threads, hipStream_t stream) {
+  if (OP == OP_LN && a.b != nullptr)
+    row_elems<BF16, OP, K, PK, OP == OP_LN><<<(unsigned)a.rows, threads, 0, stream>>>(a);
+  else
+    row_elems<BF16, OP, K, PK, false><<<(unsigned)a.rows, threads, 0, stream>>>(a);
+}
+
+template <bool BF16, int OP, int K>
+hipError_t go_rowelems(const RowArgs& a, hipStream_t stream) {
+  const int64_t t = ((a.hidden + K - 1) / K + 63) / 64 * 64;
+  // Only a thread's last element can fall past the row's end (row_elems relies on it).
+  if (t * (K - 1) > a.hidden || t > 1024 || a.rows > kMaxGrid) return hipErrorInvalidConfiguration;
+  const unsigned threads = (unsigned)t;
+  if (a.w == nullptr) go_elems_hb<BF16, OP, K, PK_NONE>(a, threads, stream);
+  else if (BF16 && a.w_f32) go_elems_hb<BF16, OP, K, BF16 ? PK_F32 : PK_SAME>(a, threads, stream);
+  else go_elems_hb<BF16, OP, K, PK_SAME>(a, threads, stream);
+  return hipGetLastError();
+}
+
+// Rows of single elements (a width or base that is not 16-byte granular), up to 12288:
+// row_elems with K = 4 where the thread count allows it (only a thread's last element past
+// the row's end), else 2 or 1, and 8 or 12 for rows over 4096 and 8192. *done = false for
+// wider rows.
+template <bool BF16, int OP>
+hipError_t try_rowelems(const RowArgs& a, hipStream_t stream, bool* done) {
+  const int64_t n = a.hidden;
+  *done = n <= 12288;
+  if (!*done) return hipSuccess;
+  auto fits = [n](int64_t k) {
+    const int64_t t = ((n + k - 1) / k + 63) / 64 * 64;
+    return t * (k - 1) <= n && t <= 1024;
+  };
+  if (n > 8192) return go_rowelems<BF16, OP, 12>(a, stream);
+  if (n > 4096) return go_rowelems<BF16, OP, 8>(a, stream);
+  if (fits(4)) return go_rowelems<BF16, OP, 4>(a, stream);
+  if (fits(2)) return go_rowelems<BF16, OP, 2>(a, stream);
+  return go_rowelems<BF16, OP, 1>(a, stream);
 }
 
 template <bool BF16, int OP, int NV, int PK, bool EXACT>
@@ -199,7 +240,18 @@ hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream) {
   constexpr int V = Fmt<BF16>::VEC;
   const int path = forced_path();
   const bool vec = aligned16 && a.hidden % V == 0 && path != PATH_SCALAR;
-  if (!vec) return go_chunked<BF16, OP, 1>(a, stream);
+  if (!vec) {
+    // add-RMSNorm (two loads and two stores of single elements) keeps the looping kernel:
+    // at [8184, 4100] bf16 it streams at 44% of peak there against 40% in row_elems.
+    if constexpr (OP != OP_ADD_RMS) {
+      if (path == PATH_AUTO) {
+        bool done = false;
+        const hipError_t e = try_rowelems<BF16, OP>(a, stream, &done);
+        if (done) return e;
+      }
+    }
+    return go_chunked<BF16, OP, 1>(a, stream);
+  }
   const int64_t n = a.hidden / V;
   bool done = false;
   hipError_t err = hipSuccess;
