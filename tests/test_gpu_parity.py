@@ -452,6 +452,25 @@ def test_in_place_many_rows(nrm_lib, path):
         compare.check_bf16(x, want_ln, what="layer_norm in x")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_in_place_element_rows(nrm_lib, dt):
+    """out == x for RMSNorm and LayerNorm on rows of single elements (width 4100)."""
+    say(f"in-place element rows {dt}")
+    import oracle
+
+    inp = _row(300, 4100, dt, dt, seed=13, x=("t3",), b=("normal", 0, 0.1), eps=1e-6)
+    x, w, b = dev(inp.x), dev(inp.w), dev(inp.b)
+    nrm_lib.rms_norm(x, w, inp.eps, out=x)
+    torch.cuda.synchronize()
+    compare.check_output(x, oracle.rms_norm(f64(inp.x), f64(inp.w), inp.eps, dt), dt,
+                         what="rms_norm in x")
+    x = dev(inp.x)
+    nrm_lib.layer_norm(x, w, b, 1e-5, out=x)
+    torch.cuda.synchronize()
+    compare.check_output(x, oracle.layer_norm(f64(inp.x), f64(inp.w), f64(inp.b), 1e-5, dt), dt,
+                         what="layer_norm in x")
+
+
 def test_hip_graph_replays(nrm_lib):
     """The library's launches capture into a HIP graph (torch.cuda.CUDAGraph) and every
     replay matches the eager call on the inputs present at that replay; the inputs change

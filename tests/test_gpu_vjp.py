@@ -192,8 +192,10 @@ def test_vjp_zero_rows_zero_parameter_gradients(nrm_lib, ln):
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
 @pytest.mark.parametrize("into", ["x", "g"])
 def test_vjp_in_place(nrm_lib, ln, into):
-    """dx written over x or over g gives the out-of-place bits (fast and generic kernels)."""
-    for path, hidden in ((None, 4096), ("chunked", 4096), ("scalar", 1000)):
+    """dx written over x or over g gives the out-of-place bits (fast, single-element and
+    generic kernels)."""
+    for path, hidden in ((None, 4096), (None, 1000), (None, 4100), ("chunked", 4096),
+                         ("scalar", 1000)):
         say(f"vjp in place into {into} {'ln' if ln else 'rms'} path={path}")
         inp = _inp(300, hidden, "bf16", "bf16", 12, ln)
         with forced_path(path):
@@ -232,16 +234,19 @@ def test_vjp_special_rows(nrm_lib):
 
 
 @pytest.mark.parametrize("ln", [False, True], ids=["rms", "ln"])
-def test_vjp_graph_replays(nrm_lib, ln):
-    """Captured in a HIP graph (row kernel + column sum), every replay matches eager."""
-    say(f"vjp graph {'ln' if ln else 'rms'}")
-    inp = _inp(1024, 4096, "bf16", "bf16", 15, ln)
+@pytest.mark.parametrize("hidden", [4096, 8191])
+def test_vjp_graph_replays(nrm_lib, ln, hidden):
+    """Captured in a HIP graph (row kernel + column sum), every replay matches eager; 8191
+    takes the single-element kernel with its column sums in LDS."""
+    say(f"vjp graph {'ln' if ln else 'rms'} hidden={hidden}")
+    inp = _inp(1024, hidden, "bf16", "bf16", 15, ln)
     x, w, g = dev(inp.x), dev(inp.w), dev(inp.g)
     eager = run_vjp(nrm_lib, inp, ln)
     dx = torch.empty_like(x)
     dw = torch.empty_like(w)
     db = torch.empty_like(w) if ln else None
-    ws = torch.empty(nrm_lib.vjp_workspace_bytes(1024, 4096, ln), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(nrm_lib.vjp_workspace_bytes(1024, hidden, ln), dtype=torch.uint8,
+                     device=DEV)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
