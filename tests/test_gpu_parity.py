@@ -84,6 +84,26 @@ def test_narrow_rows_many(nrm_lib, dt, hidden, wkind):
     check_ln(nrm_lib, inp)
 
 
+@pytest.mark.parametrize("dt,wdt,hidden", [("bf16", "bf16", 8192), ("bf16", "bf16", 4000),
+                                           ("bf16", "bf16", 6000), ("bf16", "f32", 2048),
+                                           ("bf16", "f32", 1000), ("f32", "f32", 8192),
+                                           ("f32", "f32", 1000)])
+@pytest.mark.parametrize("affine", ["wb", "w", "b"])
+def test_layer_norm_row_pairs(nrm_lib, dt, wdt, hidden, affine):
+    """LayerNorm with w and / or b over 4096 rows or more: two rows per block (2, 3 or 4 chunks
+    per thread, exact and ragged widths). 4097 rows: the last block's second row is past the
+    end. Compared on the first, middle and last rows."""
+    say(f"layer_norm row pairs rows=4097 hidden={hidden} {dt} w={wdt} {affine}")
+    inp = workloads.row_inputs(4097, hidden, dt, seed=hidden + 17, x=("normal", 0.5, 2.0),
+                               w=("normal", 1.0, 0.1), b=("normal", 0.0, 0.1), w_dtype=wdt,
+                               eps=1e-5)
+    if "w" not in affine:
+        inp.w = None
+    if "b" not in affine:
+        inp.b = None
+    check_ln(nrm_lib, inp, rows_sel=np.r_[0:3, 2047:2050, 4093:4097])
+
+
 # Widths that are not whole 16-byte chunks: one block per row with 1 (33), 2 (100), 4 (up to
 # 4096), 8 (up to 8192) or 12 (up to 12288) elements per thread; 12289 takes the looping kernel.
 ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 1001), ("bf16", 4100), ("bf16", 8191),

@@ -10,6 +10,8 @@
 //                           thread in registers (the default for rows of 129 to 4096 chunks);
 //   row_team                the same with a team of 4 .. 64 lanes per row and 256 / team
 //                           rows per block (rows of up to 128 chunks);
+//   row_ln_pair             LayerNorm as row_block with two rows per block (w and b loaded
+//                           once per pair);
 //   row_regs<..., WPR = 1>  one wave64 per row, the whole row in registers (hidden <= 64*NV*VEC);
 //                           a block holds four independent waves (four rows);
 //   row_regs<..., WPR = 8>  one 512-thread block per row, row in registers, cross-wave sums
@@ -418,6 +420,110 @@ template <bool BF16, int OP, int PK, bool EXACT, int SUB>
 __global__ void __launch_bounds__(256)
 row_team(RowArgs a) {
   row_block_body<BF16, OP, 2, PK, EXACT, SUB>(a);
+}
+
+// LayerNorm, two rows per block: thread t keeps chunks t, t + T, ... (NV of them) of both
+// rows in registers, loads w and b once for the pair, and the four row sums (sum x and
+// sum x^2 of each row) take one team_sum4, so a row costs half a barrier and half the
+// parameter loads of row_block. The statistics and output arithmetic are row_block's. The
+// second row of the last block may be past the end: it then repeats the first row's loads
+// and stores nothing.
+template <bool BF16, int NV, int PK, bool EXACT>
+__global__ void __launch_bounds__(1024)
+row_ln_pair(RowArgs a) {
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr bool LN_PACKED = BF16 && PK == PK_SAME;
+  __shared__ double red4[16 * 4];
+  const int T = blockDim.x, nw = T >> 6, tid = threadIdx.x;
+  const int nvec = (int)(a.hidden / V);
+  const int64_t r0 = 2 * (int64_t)blockIdx.x;
+  const bool live1 = r0 + 1 < a.rows;
+  const int64_t base[2] = {r0 * a.hidden * ESZ, (live1 ? r0 + 1 : r0) * a.hidden * ESZ};
+  int jj[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int j = tid + k * T;
+    ok[k] = EXACT || j < nvec;
+    jj[k] = EXACT ? j : min(j, nvec - 1);
+  }
+  const bool has_b = a.b != nullptr;
+  float wv[NV][V], bv[NV][V];
+  u32x4 wpk[NV], bpk[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if constexpr (LN_PACKED) {
+      wpk[k] = ld16((const uint16_t*)a.w + (int64_t)jj[k] * V);
+      bpk[k] = has_b ? ld16((const uint16_t*)a.b + (int64_t)jj[k] * V) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+      if (has_b) {
+        if constexpr (PK == PK_NONE) load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv[k]);
+        else load_pk<BF16, PK, V>(a.b, (int64_t)jj[k] * V, bv[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) bv[k][e] = 0.f;
+      }
+    }
+  }
+  u32x4 xv[2][NV];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) xv[r][k] = ld16_nt((const char*)a.x + base[r] + (int64_t)jj[k] * 16);
+  }
+  double ds[4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    double p[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float f[V];
+      unpack<BF16>(xv[r][k], f);
+      if (ok[k]) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const double xd = (double)f[e];
+          p[e & 1] += xd;
+          p[2 + (e & 1)] = __builtin_fma(xd, xd, p[2 + (e & 1)]);  // x^2 exact in fp64
+        }
+      }
+    }
+    ds[2 * r] = p[0] + p[1];
+    ds[2 * r + 1] = p[2] + p[3];
+  }
+  team_sum4(ds, red4, 0, nw);
+  const double n = (double)a.hidden, inv_n = a.inv_n;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r == 1 && !live1) break;
+    const double q = ds[2 * r] * inv_n;
+    const double mu = __builtin_fma(__builtin_fma(-q, n, ds[2 * r]), inv_n, q);
+    const double v0 = ds[2 * r + 1] * inv_n - mu * mu;
+    const double var = v0 < 0.0 ? 0.0 : v0;
+    const double rstd = rsqrt_row(var + (double)a.eps);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      u32x4 xr = xv[r][k];
+      __asm__ volatile("" : "+v"(xr));  // widen again rather than hold fp64 copies
+      float f[V], wf[V], bf[V];
+      unpack<BF16>(xr, f);
+      if constexpr (LN_PACKED) {
+        u32x4 wr = wpk[k], br = bpk[k];
+        __asm__ volatile("" : "+v"(wr), "+v"(br));  // widen here, not at the load
+        unpack<true>(wr, wf);
+        unpack<true>(br, bf);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) wf[e] = wv[k][e], bf[e] = bv[k][e];
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
+      if (ok[k]) st16_nt((char*)a.out + base[r] + (int64_t)jj[k] * 16, pack<BF16>(f));
+    }
+  }
 }
 
 // One block of 256 threads per row, looping over the row in chunks of V elements

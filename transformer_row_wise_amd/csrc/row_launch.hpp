@@ -8,7 +8,9 @@
 //   with fp32 w beside bf16 x)       thread, NV = max(2, ceil(n / 1024)) (LayerNorm:
 //                                    clamp(ceil(n / 256), 2, 4)), T = ceil(n / NV) rounded
 //                                    up to a wave (hidden 8192 bf16: 512 threads with 2
-//                                    chunks each, LayerNorm 256 threads with 4);
+//                                    chunks each, LayerNorm 256 threads with 4); LayerNorm
+//                                    with w or b over 4096 rows or more: row_ln_pair, the
+//                                    same per thread for two rows per block;
 //   hidden or a base address not 16-byte granular, hidden <= 12288: row_elems, one block per
 //   row, K single elements per thread in registers (RMSNorm and LayerNorm);
 //   otherwise the looping kernel (16-byte chunks, or single elements).
@@ -160,6 +162,26 @@ hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t st
 // reduction, the row scalars) is better spread over more elements per thread: NV =
 // clamp(ceil(n / 256), 2, 4) (affine [16384, 8192] bf16 106 -> 102 us), except with fp32
 // parameters beside bf16 data, whose widened w and b leave room for only two chunks.
+template <bool BF16, int NV, int PK, bool EXACT>
+hipError_t go_lnpair(const RowArgs& a, int threads, hipStream_t stream) {
+  row_ln_pair<BF16, NV, PK, EXACT><<<(unsigned)((a.rows + 1) / 2), threads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int NV>
+hipError_t lnpair_pk(const RowArgs& a, int threads, bool exact, hipStream_t stream) {
+  if (a.w == nullptr)
+    return exact ? go_lnpair<BF16, NV, PK_NONE, true>(a, threads, stream)
+                 : go_lnpair<BF16, NV, PK_NONE, false>(a, threads, stream);
+  if constexpr (BF16 && NV <= 2) {
+    if (a.w_f32)
+      return exact ? go_lnpair<BF16, NV, PK_F32, true>(a, threads, stream)
+                   : go_lnpair<BF16, NV, PK_F32, false>(a, threads, stream);
+  }
+  return exact ? go_lnpair<BF16, NV, PK_SAME, true>(a, threads, stream)
+               : go_lnpair<BF16, NV, PK_SAME, false>(a, threads, stream);
+}
+
 template <bool BF16, int OP>
 hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* done) {
   *done = false;
@@ -171,6 +193,20 @@ hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* d
   const int threads = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
   const bool exact = (int64_t)threads * nv == n;
   *done = true;
+  // LayerNorm with a scale or shift over 4096 rows or more: two rows per block (w and b
+  // loaded once per pair). bf16 [16384, 8192] 99 -> 92 us, fp32 207 -> 173 us, bf16 beside
+  // fp32 w and b [16384, 4096] 62 -> 52 us. Without parameters the pair's extra registers cost
+  // more than it saves (84 -> 88 us), so that case keeps one row per block.
+  if constexpr (OP == OP_LN) {
+    if (a.rows >= 4096 && (a.w != nullptr || a.b != nullptr)) {
+      switch (nv) {
+        case 2: return lnpair_pk<BF16, 2>(a, threads, exact, stream);
+        case 3: return lnpair_pk<BF16, 3>(a, threads, exact, stream);
+        case 4: return lnpair_pk<BF16, 4>(a, threads, exact, stream);
+        default: break;
+      }
+    }
+  }
   switch (nv) {
     case 1: return rowblock_pk<BF16, OP, 1>(a, threads, exact, stream);
     case 2: return rowblock_pk<BF16, OP, 2>(a, threads, exact, stream);
