@@ -104,6 +104,17 @@ def test_layer_norm_row_pairs(nrm_lib, dt, wdt, hidden, affine):
     check_ln(nrm_lib, inp, rows_sel=np.r_[0:3, 2047:2050, 4093:4097])
 
 
+@pytest.mark.parametrize("dt,wdt,hidden", [("f32", "f32", 8192), ("f32", "f32", 12000),
+                                           ("f32", "f32", 16384), ("bf16", "f32", 4096),
+                                           ("bf16", "f32", 5000), ("bf16", "f32", 24000)])
+def test_rms_norm_row_pairs(nrm_lib, dt, wdt, hidden):
+    """RMSNorm with fp32 weights over 4096 rows or more: two rows per block (2, 3 or 4 chunks
+    per thread, exact and ragged). 4097 rows: the last block's second row is past the end."""
+    say(f"rms_norm row pairs rows=4097 hidden={hidden} {dt} w={wdt}")
+    inp = _row(4097, hidden, dt, wdt, seed=hidden + 19, x=("t3",), eps=1e-5)
+    check_rms(nrm_lib, inp, rows_sel=np.r_[0:3, 2047:2050, 4093:4097])
+
+
 # Widths that are not whole 16-byte chunks: one block per row with 1 (33), 2 (100), 4 (up to
 # 4096), 8 (up to 8192) or 12 (up to 12288) elements per thread; 12289 takes the looping kernel.
 ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 1001), ("bf16", 4100), ("bf16", 8191),

@@ -10,8 +10,8 @@
 //                           thread in registers (the default for rows of 129 to 4096 chunks);
 //   row_team                the same with a team of 4 .. 64 lanes per row and 256 / team
 //                           rows per block (rows of up to 128 chunks);
-//   row_ln_pair             LayerNorm as row_block with two rows per block (w and b loaded
-//                           once per pair);
+//   row_ln_pair,            LayerNorm (with w or b) and RMSNorm (with fp32 w) as row_block
+//   row_rms_pair            with two rows per block (the parameters loaded once per pair);
 //   row_regs<..., WPR = 1>  one wave64 per row, the whole row in registers (hidden <= 64*NV*VEC);
 //                           a block holds four independent waves (four rows);
 //   row_regs<..., WPR = 8>  one 512-thread block per row, row in registers, cross-wave sums
@@ -521,6 +521,76 @@ row_ln_pair(RowArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e)
         f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
+      if (ok[k]) st16_nt((char*)a.out + base[r] + (int64_t)jj[k] * 16, pack<BF16>(f));
+    }
+  }
+}
+
+// RMSNorm with an fp32 scale, two rows per block, as row_ln_pair: each thread holds its NV chunks
+// of both rows and loads w once for the pair; the two rows' fp32 sums of squares are reduced
+// together (one barrier), in row_block's order. The arithmetic is row_block's.
+template <bool BF16, int NV, int PK, bool EXACT>
+__global__ void __launch_bounds__(1024)
+row_rms_pair(RowArgs a) {
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  __shared__ float red[16 * 2];
+  const int T = blockDim.x, nw = T >> 6, tid = threadIdx.x;
+  const int nvec = (int)(a.hidden / V);
+  const int64_t r0 = 2 * (int64_t)blockIdx.x;
+  const bool live1 = r0 + 1 < a.rows;
+  const int64_t base[2] = {r0 * a.hidden * ESZ, (live1 ? r0 + 1 : r0) * a.hidden * ESZ};
+  int jj[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int j = tid + k * T;
+    ok[k] = EXACT || j < nvec;
+    jj[k] = EXACT ? j : min(j, nvec - 1);
+  }
+  float wv[NV][V];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+  u32x4 xv[2][NV];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) xv[r][k] = ld16_nt((const char*)a.x + base[r] + (int64_t)jj[k] * 16);
+  }
+  float acc[2] = {0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float f[V];
+      unpack<BF16>(xv[r][k], f);
+      if (ok[k]) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[r] = __builtin_fmaf(f[e], f[e], acc[r]);
+      }
+    }
+    acc[r] = wave_sum(acc[r]);
+  }
+  if ((tid & 63) == 0) {
+    red[(tid >> 6) * 2] = acc[0];
+    red[(tid >> 6) * 2 + 1] = acc[1];
+  }
+  __syncthreads();
+  float ss[2] = {red[0], red[1]};
+  for (int i = 1; i < nw; ++i) {
+    ss[0] += red[2 * i];
+    ss[1] += red[2 * i + 1];
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r == 1 && !live1) break;
+    const float rstd = (float)rstd_f64((double)ss[r], a.hidden, a.eps);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float f[V];
+      unpack<BF16>(xv[r][k], f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) f[e] = (f[e] * rstd) * wv[k][e];
       if (ok[k]) st16_nt((char*)a.out + base[r] + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   }
