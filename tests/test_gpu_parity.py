@@ -18,8 +18,8 @@ from gpu_util import (DEV, assert_h_exact, check_add, check_ln, check_rms, check
 pytestmark = pytest.mark.gpu
 
 # widths: tiny, not a 16-byte multiple, one wave per row, one block per row, looping kernel
-HIDDEN = [1, 2, 7, 8, 64, 100, 512, 520, 1000, 4096, 5120, 8192, 8200, 12288, 16384, 32768,
-          40000, 70000]
+HIDDEN = [1, 2, 7, 8, 64, 100, 512, 520, 1000, 4096, 5120, 8192, 8200, 12288, 16384, 24576,
+          32768, 40000, 49152, 65536, 70000]
 WEIGHTS = [("bf16", "bf16"), ("bf16", "f32"), ("bf16", None), ("f32", "f32"), ("f32", None)]
 
 

@@ -285,12 +285,17 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
   // LayerNorm with bf16 w and b keeps them packed (8 registers per chunk instead of 16) and
   // widens them where the output uses them.
   constexpr bool LN_PACKED = OP == OP_LN && BF16 && PK == PK_SAME;
+  // Rows of more than 4 chunks per thread (RMS forms only) load w after the row's sum: x, r
+  // and a widened w of 8 chunks would not fit the 128 registers of a 1024-thread block.
+  constexpr bool W_LATE = OP != OP_LN && NV > 4;
   float wv[NV][V];
   u32x4 wpk[NV];
+  if constexpr (!W_LATE) {
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    if constexpr (LN_PACKED) wpk[k] = ld16((const uint16_t*)a.w + (int64_t)jj[k] * V);
-    else load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+    for (int k = 0; k < NV; ++k) {
+      if constexpr (LN_PACKED) wpk[k] = ld16((const uint16_t*)a.w + (int64_t)jj[k] * V);
+      else load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+    }
   }
   u32x4 xv[NV], rv[NV];
 #pragma unroll
@@ -323,6 +328,10 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     if constexpr (SUB > 0) ss = group_sum<SUB>(acc);
     else ss = block_row_sum(acc, red_f, nw);
     const float rstd = (float)rstd_f64((double)ss, a.hidden, a.eps);
+    if constexpr (W_LATE) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       float f[V];

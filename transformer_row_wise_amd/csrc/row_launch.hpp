@@ -4,8 +4,9 @@
 //   n <= 128                         row_team: teams of SUB = 4 .. 64 lanes (two chunks each,
 //                                    the smallest power of two that covers the row), 256 / SUB
 //                                    rows per block;
-//   n <= 4096 (2048 for LayerNorm    row_block: one block of T threads per row, NV chunks per
-//   with fp32 w beside bf16 x)       thread, NV = max(2, ceil(n / 1024)) (LayerNorm:
+//   n <= 8192 (LayerNorm: 4096,      row_block: one block of T threads per row, NV chunks per
+//   2048 with fp32 w beside bf16 x)  thread, NV = max(2, ceil(n / 1024)), 5 and 7 taken as
+//                                    6 and 8 (w loaded after the row's sum past 4) (LayerNorm:
 //                                    clamp(ceil(n / 256), 2, 4)), T = ceil(n / NV) rounded
 //                                    up to a wave (hidden 8192 bf16: 512 threads with 2
 //                                    chunks each, LayerNorm 256 threads with 4); LayerNorm
@@ -155,7 +156,7 @@ hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t st
                : go_rowblock<BF16, OP, NV, PK_SAME, false>(a, threads, stream);
 }
 
-// One block per row: NV = max(2, ceil(n / 1024)) chunks per thread (at most 4), T = ceil(n /
+// One block per row: NV = max(2, ceil(n / 1024)) chunks per thread (at most 8), T = ceil(n /
 // NV) rounded up to a wave. Two 16-byte chunks per thread measured best for the RMS forms:
 // at hidden 8192 bf16, 512 threads with two chunks each beat 1024 threads with one
 // (add-RMSNorm 172 vs 182 us, RMSNorm 86 vs 95 us); four per thread gain nothing. LayerNorm
@@ -201,9 +202,14 @@ template <bool BF16, int OP>
 hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* done) {
   *done = false;
   const bool ln_wide = OP == OP_LN && !(BF16 && a.w_f32);
-  const int64_t nv = ln_wide ? std::min<int64_t>(4, std::max<int64_t>(2, (n + 255) / 256))
-                             : std::max<int64_t>(2, (n + 1023) / 1024);
-  if (nv > (OP == OP_LN && !ln_wide ? 2 : 4) || n > nv * 1024 || a.rows > kMaxGrid)
+  int64_t nv = ln_wide ? std::min<int64_t>(4, std::max<int64_t>(2, (n + 255) / 256))
+                       : std::max<int64_t>(2, (n + 1023) / 1024);
+  // RMS forms past 4096 chunks (16384 fp32 / 32768 bf16 values): 6 or 8 chunks per thread
+  // (the only counts instantiated above 4), up to 8192 chunks.
+  // bf16 rows with fp32 w stop at 6: eight widened fp32 w chunks spill at 8.
+  if (OP != OP_LN && nv > 4) nv = nv <= 6 ? 6 : 8;
+  if (nv == 8 && BF16 && a.w != nullptr && a.w_f32) return hipSuccess;
+  if (nv > (OP == OP_LN ? (ln_wide ? 4 : 2) : 8) || n > nv * 1024 || a.rows > kMaxGrid)
     return hipSuccess;
   const int threads = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
   const bool exact = (int64_t)threads * nv == n;
@@ -240,6 +246,12 @@ hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* d
     case 2: return rowblock_pk<BF16, OP, 2>(a, threads, exact, stream);
     case 3: return rowblock_pk<BF16, OP, 3>(a, threads, exact, stream);
     case 4: return rowblock_pk<BF16, OP, 4>(a, threads, exact, stream);
+    case 6:
+      if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 6>(a, threads, exact, stream);
+      break;
+    case 8:
+      if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 8>(a, threads, exact, stream);
+      break;
     default: break;
   }
   *done = false;
