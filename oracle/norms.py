@@ -51,13 +51,16 @@ def layer_norm(x, w, b, eps, dtype):
     nuvec-core ``fast::FastOp``, variant ``LayerNorm``: ``w`` and ``b`` 1-D or the scalars
     1 and 0. nuvec-nn ``layers.rs``, ``LayerNorm``: affine by default, ``without_bias`` drops
     b, ``affine(false)`` drops both. Reading: var is the biased (divide by D) variance,
-    taken in a second pass around the mean.
+    taken in a second pass around the mean. The mean takes one correction step (mean +
+    mean(x - mean), the corrected two-pass mean), so that its float64 rounding error stays
+    negligible against the spread even when |mean| / std is as large as 1e6.
     """
     x = _f64(x)
     w = _f64(w)
     b = _f64(b)
     d = x.shape[-1]
     mean = np.sum(x, axis=-1, keepdims=True) / d
+    mean = mean + np.sum(x - mean, axis=-1, keepdims=True) / d
     centred = x - mean
     var = np.sum(centred * centred, axis=-1, keepdims=True) / d
     y = centred / np.sqrt(var + f32_param(eps))

@@ -40,18 +40,25 @@ def rms_norm_vjp(x, w, g, eps, dtype, w_dtype=None):
 
 
 def layer_norm_vjp(x, w, b, g, eps, dtype, w_dtype=None):
-    """Returns (dx, dw, db) for LayerNorm (b does not enter the gradients)."""
+    """Returns (dx, dw, db) for LayerNorm (b does not enter the gradients).
+
+    Two sums are written in a form that is equal by definition and stays accurate in
+    float64 when a mean is large against the spread: the mean of x takes one correction
+    step (mean + mean(x - mean), the corrected two-pass mean), and mean(d xh) is taken as
+    mean((d - mean(d)) xh), which is the same number because mean(xh) = 0. Formed
+    directly, mean(d xh) multiplies the rounding error of sum(xh) by mean(d)."""
     x2 = _rows(x)
     g2 = _rows(g)
     d = x2.shape[-1]
     wv = np.ones(d) if w is None else np.asarray(w, dtype=np.float64)
     mu = np.sum(x2, axis=-1, keepdims=True) / d
+    mu = mu + np.sum(x2 - mu, axis=-1, keepdims=True) / d
     c = x2 - mu
     r = 1.0 / np.sqrt(np.sum(c * c, axis=-1, keepdims=True) / d + f32_param(eps))
     xh = c * r
     dxh = g2 * wv
     m1 = np.sum(dxh, axis=-1, keepdims=True) / d
-    m2 = np.sum(dxh * xh, axis=-1, keepdims=True) / d
+    m2 = np.sum((dxh - m1) * xh, axis=-1, keepdims=True) / d
     dx = r * (dxh - m1 - xh * m2)
     dw = np.sum(g2 * xh, axis=0)
     db = np.sum(g2, axis=0)

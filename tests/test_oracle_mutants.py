@@ -86,6 +86,12 @@ MUTANTS = [
     ("rope_scaling.py", "out[mid] = f[mid] / ((1.0 - s) / factor + s)",
      "out[mid] = f[mid] / (s / factor + (1.0 - s))", "Llama 3 blend weights swapped"),
     ("rope_scaling.py", "keep = 1.0 - ramp", "keep = ramp", "YaRN ramp reversed"),
+    ("rope_scaling.py", "inv = keep / f + (1.0 - keep) / (factor * f)",
+     "inv = 1.0 / (keep * f + (1.0 - keep) * factor * f)",
+     "YaRN blends the divisors instead of the inverse frequencies"),
+    ("rope_scaling.py", "inv = keep / f + (1.0 - keep) / (factor * f)",
+     "inv = 1.0 / (f * factor ** (1.0 - keep))",
+     "YaRN blends geometrically"),
     ("rope_scaling.py", "low = max(math.floor(corr_dim(beta_fast)), 0)",
      "low = max(math.floor(corr_dim(beta_slow)), 0)", "YaRN ramp start from beta_slow"),
     ("rope_scaling.py", "return 1.0 if s <= 1 else 0.1 * m * math.log(s) + 1.0",
@@ -132,7 +138,7 @@ MUTANTS = [
      "LayerNormVjp db scaled by w"),
     ("vjp.py", "np.sum(c * c, axis=-1, keepdims=True) / d", "np.sum(c * c, axis=-1, keepdims=True) / (d - 1)",
      "LayerNormVjp unbiased variance"),
-    ("vjp.py", "m2 = np.sum(dxh * xh, axis=-1, keepdims=True) / d",
+    ("vjp.py", "m2 = np.sum((dxh - m1) * xh, axis=-1, keepdims=True) / d",
      "m2 = np.sum(dxh * c, axis=-1, keepdims=True) / d", "LayerNormVjp m2 not normalised"),
 ]
 
