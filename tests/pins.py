@@ -614,6 +614,22 @@ def pin_yarn_ramp(o):
     assert ms2 == 1.0, "equal mscale and mscale_all_dim cancel"
 
 
+def pin_yarn_ramp_interior(o):
+    """A hand-worked pair on the ramp (YaRN, section 3.2: the ramp blends the two inverse
+    frequencies linearly). dims 8 and base 16 give divisors f_i = 16^(i/4) = 2^i, and
+    d(r) = 8 ln(64 / (2 pi r)) / (2 ln 16) = log2(64 / (2 pi r)); with original context 64,
+    beta_fast 8 and beta_slow 4: d(8) = log2(4 / pi) = 0.35, so the ramp starts at pair
+    floor(0.35) = 0, and d(4) = log2(8 / pi) = 1.35, so it ends at ceil(1.35) = 2. Pair 1
+    sits at ramp 1/2: 1/f' = (1/2) (1/f + 1/(factor f)) = (1/2)(1/2 + 1/6) = 1/3 with
+    factor 3, so f' = 3 (a linear blend of the divisors would give 4, a geometric one
+    sqrt(12)). Pair 0 keeps f = 1; pairs 2 and 3 get 3 f = 12 and 24. The attention factor is
+    0.1 ln 3 + 1."""
+    S = o.rope_scaling
+    got, ms = S.yarn_freqs(8, 16.0, factor=3.0, original_max=64, beta_fast=8.0, beta_slow=4.0)
+    _same_values(got, [1.0, 3.0, 12.0, 24.0], "YaRN ramp at 0, 1/2, 1, 1")
+    _close(ms, 0.1 * np.log(3.0) + 1.0, 1e-15, 0, "attention factor of factor 3")
+
+
 def pin_su_scaling(o):
     S = o.rope_scaling
     dims, base = 16, 10000.0

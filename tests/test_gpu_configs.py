@@ -1,7 +1,7 @@
-"""The five synthetic workloads at full size, through the same calls the bench times.
-Small ones are compared with the oracle in full; the [16384, 8192] and [65536, 5120] ones on
-a fixed sample of rows (first, last, and 510 drawn with a fixed seed, which with 1% outlier
-rows includes several of them), computed one by one by the oracle."""
+"""The five synthetic workloads at full size, through the same calls the bench times, every
+output element compared with the oracle: the small ones in this process, the [16384, 8192]
+and [65536, 5120] ones in chunks of rows over a process pool (oracle_pool), h bit for bit on
+every row."""
 
 import numpy as np
 import pytest
@@ -9,14 +9,10 @@ import torch
 
 import compare
 import workloads
+import oracle_pool
 from gpu_util import DEV, check_add, check_ln, check_rope, dev, f64, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
-
-
-def sample_rows(rows, n=510, seed=123):
-    pick = np.random.default_rng(seed).choice(rows, size=min(n, rows), replace=False)
-    return torch.from_numpy(np.unique(np.concatenate([[0, rows - 1], pick])))
 
 
 def test_cfg1_add_rms_fp32_small(nrm_lib):
@@ -33,7 +29,9 @@ def test_cfg2_add_rms_bf16_4k(nrm_lib):
 def test_cfg3_layer_norm_bf16(nrm_lib, affine):
     say(f"cfg3 LayerNorm bf16 [16384,8192] affine={affine}")
     inp = workloads.cfg_layer_norm_bf16(affine=affine)
-    check_ln(nrm_lib, inp, rows_sel=sample_rows(16384))
+    out = nrm_lib.layer_norm(dev(inp.x), dev(inp.w), dev(inp.b), inp.eps)
+    torch.cuda.synchronize()
+    oracle_pool.check_layer_norm_all_rows(inp.x, inp.w, inp.b, inp.eps, out)
 
 
 @pytest.mark.parametrize("traditional", [False, True])
@@ -63,4 +61,6 @@ def test_cfg5_add_rms_at_scale(nrm_lib, scale_inputs, shape, dt):
     if dt == "bf16":
         inp = workloads.RowInputs(x=inp.x.to(torch.bfloat16), r=inp.r.to(torch.bfloat16),
                                   w=inp.w.to(torch.bfloat16), b=None, eps=inp.eps)
-    check_add(nrm_lib, inp, rows_sel=sample_rows(shape[0]))
+    out, h = nrm_lib.add_rms_norm(dev(inp.x), dev(inp.r), dev(inp.w), inp.eps)
+    torch.cuda.synchronize()
+    oracle_pool.check_add_rms_all_rows(inp.x, inp.r, inp.w, inp.eps, out, h)
