@@ -290,6 +290,54 @@ __device__ __forceinline__ void team_sum4(double (&s)[4], double* red, int wave0
   for (int i = 0; i < 4; ++i) s[i] = readlane_f64(t, i);
 }
 
+// ------------------------------------------------------------------ row pivots
+//
+// LayerNorm's statistics are sums about a pivot taken from the row, not raw moments. The
+// variance from sum(x^2)/n - mean^2 cancels catastrophically when |mean| is far above the
+// standard deviation sigma (an fp32 row such as 1e4 + N(0, 0.01) loses every bit of fp64).
+// About a pivot p that is one of the row's values, |p - mean| <= sigma sqrt(n - 1)
+// (Samuelson's inequality), so sum((x - p)^2) / n <= n sigma^2 and the variance
+// sum((x - p)^2) / n - (mean - p)^2 loses at most log2(n) bits. x - p is exact in fp64
+// for bf16 and fp32 values whose exponents are within 29 of each other, and off by one
+// rounding otherwise. Every thread of a row uses the same pivot (the row's first element),
+// so the sums combine as they are.
+
+// A 32-bit word at a wave-uniform, 4-byte aligned address, through the scalar data cache
+// (into scalar registers, no vector registers held while it is in flight). Only for data
+// the kernel has not written before this read.
+__device__ __forceinline__ uint32_t sload_u32(const void* p) {
+  return *(const __attribute__((address_space(4))) uint32_t*)p;
+}
+
+// Element i of a bf16 or fp32 array, at a wave-uniform address, by a scalar load of the
+// aligned word that holds it (a bf16 element is either half of its word).
+template <bool BF16>
+__device__ __forceinline__ float sload_elem(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    const uintptr_t a = (uintptr_t)((const uint16_t*)p + i);
+    const uint32_t w = sload_u32((const void*)(a & ~(uintptr_t)3));
+    return __builtin_bit_cast(float, (a & 2) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __builtin_bit_cast(float, sload_u32((const float*)p + i));
+  }
+}
+
+// The first lane's 32-bit value of each aligned group of G lanes (G = 1 .. 64) in every lane
+// of the group: the pivot of a team of G lanes that owns one row.
+template <int G>
+__device__ __forceinline__ uint32_t group_first(uint32_t v) {
+  if constexpr (G == 64) return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+  else return (uint32_t)__shfl((int)v, (int)(threadIdx.x & 63 & ~(G - 1)), 64);
+}
+
+// Decode one element from the first 32 bits of a chunk (element 0: the low half of a bf16
+// pair, or the fp32 value).
+template <bool BF16>
+__device__ __forceinline__ float first_elem(uint32_t raw) {
+  if constexpr (BF16) return bf16lo(raw);
+  else return __builtin_bit_cast(float, raw);
+}
+
 // 1 / sqrt(v) in fp64 for a row scalar: the hardware's fp64 estimate (good to about single
 // precision), refined by two Newton steps y += y (1 - v y^2) / 2, each of which about squares
 // the relative error, so the result is within a few fp64 units in the last place (far below

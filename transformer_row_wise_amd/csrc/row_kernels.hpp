@@ -341,11 +341,11 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
       if (live && ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   } else {  // OP_LN, fp64 statistics and output arithmetic
-    // One pass: sum x and sum x^2 in fp64 (x^2 of a bf16 or fp32 value is exact in fp64),
-    // reduced together with one barrier; var = sum x^2 / n - mu^2 (fp64 keeps the
-    // cancellation harmless unless |mu| / sigma exceeds ~1e6). A constant row gets var = 0
-    // and x - mu = 0 exactly, so its output is exactly b. b (like w) is loaded before the
-    // row's statistics.
+    // One pass: the sum and the sum of squares of x - p in fp64 about the row's first
+    // element p (the row pivots of common.hpp), reduced together with one barrier; var =
+    // sum((x-p)^2)/n - (mean - p)^2 loses at most log2(n) bits however large |mean| / sigma
+    // is. A constant row gets x - p = 0 everywhere, so mean = p, var = 0 and x - mean = 0
+    // exactly: its output is exactly b. b (like w) is loaded before the row's statistics.
     const bool has_b = a.b != nullptr;
     float bv[NV][V];
     u32x4 bpk[NV];
@@ -362,6 +362,11 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
         for (int e = 0; e < V; ++e) bv[k][e] = 0.f;
       }
     }
+    // A team's first lane holds the row's chunk 0; a block reads the row's first element
+    // through the scalar cache.
+    double piv;
+    if constexpr (SUB > 0) piv = (double)first_elem<BF16>(group_first<SUB>(xv[0][0]));
+    else piv = (double)sload_elem<BF16>((const char*)a.x + base, 0);
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -370,9 +375,9 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
       if (ok[k]) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const double xd = (double)f[e];
-          ds[e & 1] += xd;
-          ds[2 + (e & 1)] = __builtin_fma(xd, xd, ds[2 + (e & 1)]);  // x^2 exact in fp64
+          const double xs = (double)f[e] - piv;
+          ds[e & 1] += xs;
+          ds[2 + (e & 1)] = __builtin_fma(xs, xs, ds[2 + (e & 1)]);
         }
       }
     }
@@ -385,13 +390,14 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     } else {
       team_sum4(ds, red4, 0, nw);
     }
-    // mu = sum / n through the reciprocal and one residual step, which lands on the correctly
-    // rounded quotient (a constant row's exact sum n c gives exactly c).
+    // mean - p = sum / n through the reciprocal and one residual step, which lands on the
+    // correctly rounded quotient.
     const double n = (double)a.hidden, inv_n = a.inv_n;
-    const double q = ds[0] * inv_n;
-    const double mu = __builtin_fma(__builtin_fma(-q, n, ds[0]), inv_n, q);
+    double q = ds[0] * inv_n;
+    q = __builtin_fma(__builtin_fma(-q, n, ds[0]), inv_n, q);
+    const double mu = piv + q;
     // Clamp rounding below zero, but keep a NaN (an infinite row gives inf - inf).
-    const double v0 = ds[1] * inv_n - mu * mu;
+    const double v0 = ds[1] * inv_n - q * q;
     const double var = v0 < 0.0 ? 0.0 : v0;
     const double rstd = rsqrt_row(var + (double)a.eps);
 #pragma unroll
@@ -482,6 +488,11 @@ row_ln_pair(RowArgs a) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) xv[r][k] = ld16_nt((const char*)a.x + base[r] + (int64_t)jj[k] * 16);
   }
+  // Each row's sums about its first element (the row pivots of common.hpp); the two rows'
+  // four sums take one reduction.
+  double piv[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) piv[r] = (double)sload_elem<BF16>((const char*)a.x + base[r], 0);
   double ds[4];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -493,9 +504,9 @@ row_ln_pair(RowArgs a) {
       if (ok[k]) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const double xd = (double)f[e];
-          p[e & 1] += xd;
-          p[2 + (e & 1)] = __builtin_fma(xd, xd, p[2 + (e & 1)]);  // x^2 exact in fp64
+          const double xs = (double)f[e] - piv[r];
+          p[e & 1] += xs;
+          p[2 + (e & 1)] = __builtin_fma(xs, xs, p[2 + (e & 1)]);
         }
       }
     }
@@ -507,9 +518,10 @@ row_ln_pair(RowArgs a) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     if (r == 1 && !live1) break;
-    const double q = ds[2 * r] * inv_n;
-    const double mu = __builtin_fma(__builtin_fma(-q, n, ds[2 * r]), inv_n, q);
-    const double v0 = ds[2 * r + 1] * inv_n - mu * mu;
+    double q = ds[2 * r] * inv_n;
+    q = __builtin_fma(__builtin_fma(-q, n, ds[2 * r]), inv_n, q);
+    const double mu = piv[r] + q;
+    const double v0 = ds[2 * r + 1] * inv_n - q * q;
     const double var = v0 < 0.0 ? 0.0 : v0;
     const double rstd = rsqrt_row(var + (double)a.eps);
 #pragma unroll

@@ -5,11 +5,13 @@
 // Per row of D features, with r the row's reciprocal standard deviation:
 //   RMS  r = 1/sqrt(sum(x^2)/D + eps), c = r^3 * sum(g w x) / D
 //        dx = r (g w) - x c,                 dw += g x r
-//   LN   mu = sum(x)/D, var = sum(x^2)/D - mu^2, r = 1/sqrt(var + eps), xh = (x - mu) r,
-//        d = g w, m1 = sum(d)/D, m2 = sum(d xh)/D = r (sum(d x) - mu sum(d)) / D
+//   LN   mu = sum(x)/D, var = sum((x - mu)^2)/D, r = 1/sqrt(var + eps), xh = (x - mu) r,
+//        d = g w, m1 = sum(d)/D, m2 = sum(d xh)/D = r sum((d - m1)(x - mu)) / D
 //        dx = r (d - m1 - xh m2),            dw += g xh,   db += g
-// All row statistics come from one pass (LN's variance from the raw moments), accumulated in
-// fp64, so a row needs a single cross-thread reduction. The statistics and the per-element
+// All row statistics come from one pass, accumulated in fp64, so a row needs a single
+// cross-thread reduction. LN's four sums are taken about pivots from the row (x and d of an
+// element of the row: the row pivots of common.hpp), so neither the variance nor m2
+// cancels catastrophically when a mean is large against the spread. The statistics and the per-element
 // outputs are fp64 because dx is a difference of two terms that can cancel, and the bar is
 // one unit in the last place of the result: an fp32 statistic would miss it on a few
 // elements per million.
@@ -66,26 +68,33 @@ __device__ __forceinline__ VjpRow vjp_rms_scalars(double ss, double dot, double 
   return s;
 }
 
+// LN from its sums about the pivots px (of x) and pd (of d = g w): sx = sum(x - px),
+// sxx = sum((x - px)^2), sd = sum(d - pd), sdx = sum((d - pd)(x - px)). With qx = mean(x) -
+// px and qd = mean(d) - pd: var = sxx/D - qx^2 and sum((d - m1)(x - mu))/D = sdx/D - qx qd.
 __device__ __forceinline__ VjpRow vjp_ln_scalars(double sx, double sxx, double sd, double sdx,
-                                                 double inv_n, float eps) {
+                                                 double px, double pd, double inv_n, float eps) {
   VjpRow s;
-  s.mu = sx * inv_n;
-  const double v0 = sxx * inv_n - s.mu * s.mu;
+  const double qx = sx * inv_n, qd = sd * inv_n;
+  s.mu = px + qx;
+  const double v0 = sxx * inv_n - qx * qx;
   const double var = v0 < 0.0 ? 0.0 : v0;  // clamps rounding, keeps a NaN (inf - inf)
   s.r = rsqrt_row(var + (double)eps);
   s.c = 0.0;
-  s.m1 = sd * inv_n;
-  s.m2 = s.r * ((sdx - s.mu * sd) * inv_n);
+  s.m1 = pd + qd;
+  s.m2 = s.r * __builtin_fma(-qx, qd, sdx * inv_n);
   return s;
 }
 
-// Statistic sums of V elements, all accumulated in fp64: RMS (sum x^2, sum g w x), LN (sum x,
-// sum x^2, sum d, sum d x) with d = g w. XF: x, g and w are bf16 values (8 significant
-// bits), so x^2, g w and g w x are exact in fp32 and only need widening; otherwise the
-// products are formed in fp64 (exact up to one rounding of g w x).
-template <int OP, int V, bool XF>
+// Statistic sums of V elements, all accumulated in fp64: RMS (sum x^2, sum g w x), LN (sum
+// x - px, sum (x - px)^2, sum d - pd, sum (d - pd)(x - px)) with d = g w about the pivots
+// px, pd. XF: x, g and w are bf16 values (8 significant bits), so x^2, g w and g w x are
+// exact in fp32 and only need widening; otherwise the products are formed in fp64 (exact up
+// to one rounding of g w x). on(e): element e belongs to the row. RMS takes masked elements
+// as zeros, which add nothing; LN's shifted terms of a masked element are set to zero.
+template <int OP, int V, bool XF, typename ON>
 __device__ __forceinline__ void vjp_accumulate(const float (&f)[V], const float (&gv)[V],
-                                               const float (&wv)[V], double (&ds)[4]) {
+                                               const float (&wv)[V], double (&ds)[4],
+                                               double px, double pd, ON on) {
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     if constexpr (OP == VJP_RMS) {
@@ -101,14 +110,41 @@ __device__ __forceinline__ void vjp_accumulate(const float (&f)[V], const float 
         ds[1] = __builtin_fma((double)gv[e] * (double)wv[e], xd, ds[1]);
       }
     } else {
-      const double xd = (double)f[e];
       const double d = XF ? (double)(gv[e] * wv[e]) : (double)gv[e] * (double)wv[e];
-      ds[0] += xd;
-      ds[1] = __builtin_fma(xd, xd, ds[1]);
-      ds[2] += d;
-      ds[3] = __builtin_fma(d, xd, ds[3]);
+      const bool in = on(e);
+      const double xs = in ? (double)f[e] - px : 0.0;
+      const double dd = in ? d - pd : 0.0;
+      ds[0] += xs;
+      ds[1] = __builtin_fma(xs, xs, ds[1]);
+      ds[2] += dd;
+      ds[3] = __builtin_fma(dd, xs, ds[3]);
     }
   }
+}
+
+// Every element of the row counts (chunks wholly inside the row).
+struct AllOn {
+  __device__ __forceinline__ bool operator()(int) const { return true; }
+};
+// Every element of a chunk counts or none does.
+struct ChunkOn {
+  bool on;
+  __device__ __forceinline__ bool operator()(int) const { return on; }
+};
+
+// LN's pivots of a row: px = x and pd = d = g w (formed as vjp_accumulate forms d) of one
+// element of the row (x0, g0, w0), the same in every thread of the row.
+template <bool XF>
+__device__ __forceinline__ void vjp_pivots(float x0, float g0, float w0, double& px, double& pd) {
+  px = (double)x0;
+  pd = XF ? (double)(g0 * w0) : (double)g0 * (double)w0;
+}
+
+// w at column 0 (1 when absent), read once per kernel through the scalar cache.
+template <bool BF16>
+__device__ __forceinline__ float vjp_w0(const VjpArgs& a) {
+  if (a.w == nullptr) return 1.f;
+  return (!BF16 || a.w_f32) ? sload_elem<false>(a.w, 0) : sload_elem<true>(a.w, 0);
 }
 
 // A thread's V column accumulators in LDS, element e at p[e * stride] (element-major, so
@@ -307,7 +343,12 @@ vjp_rows(VjpArgs a) {
   auto row_of = [&](int it) {
     return ((int64_t)it * G + team) * (int64_t)gridDim.x + blockIdx.x;
   };
-  auto load_row = [&](int it, u32x4 (&xv)[NV], u32x4 (&gv)[NV]) {
+  // LN: w at column 0, for the rows' d pivots.
+  const float w0 = OP == VJP_LN ? vjp_w0<BF16>(a) : 1.f;
+  // A row's chunks, and (LN) its pivots x and g at column 0 through the scalar cache (scalar
+  // registers: nothing held in vector registers while the row is in flight).
+  struct Piv { float x, g; };
+  auto load_row = [&](int it, u32x4 (&xv)[NV], u32x4 (&gv)[NV], Piv& pv) {
     const int64_t row = min(row_of(it), a.rows - 1);
     const char* xr = (const char*)a.x + row * a.hidden * Fmt<BF16>::ESZ;
     const char* gr = (const char*)a.g + row * a.hidden * Fmt<BF16>::ESZ;
@@ -316,11 +357,19 @@ vjp_rows(VjpArgs a) {
       xv[k] = ld16_nt(xr + (int64_t)jj[k] * 16);
       gv[k] = ld16_nt(gr + (int64_t)jj[k] * 16);
     }
+    if constexpr (OP == VJP_LN) {
+      pv.x = sload_elem<BF16>(xr, 0);
+      pv.g = sload_elem<BF16>(gr, 0);
+    }
   };
 
-  // Statistics of a row: its four sums, reduced within each wave and posted to red[it & 1].
-  auto stats = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV]) {
+  // Statistics of a row: its sums (LN: about the row's pivots, which are returned), reduced
+  // within each wave and posted to red[it & 1].
+  struct RowPiv { double x, d; };
+  auto stats = [&](int it, const u32x4 (&xv)[NV], const u32x4 (&gv)[NV], const Piv& pv) {
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
+    double px = 0.0, pd = 0.0;
+    if constexpr (OP == VJP_LN) vjp_pivots<XF>(pv.x, pv.g, w0, px, pd);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       if constexpr (EXACT) {
@@ -328,7 +377,7 @@ vjp_rows(VjpArgs a) {
           float f[V], gf[V];
           unpack<BF16>(xv[k], f);
           unpack<BF16>(gv[k], gf);
-          vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds);
+          vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds, px, pd, AllOn{});
         }
       } else {
         // A chunk past the row's end (a clamped duplicate) enters as zeros, which add
@@ -339,28 +388,32 @@ vjp_rows(VjpArgs a) {
         unpack<BF16>(ok[k] ? xv[k] : z, f);
         unpack<BF16>(ok[k] ? gv[k] : z, gf);
         wuse(k, wl);
-        vjp_accumulate<OP, V, XF>(f, gf, wl, ds);
+        vjp_accumulate<OP, V, XF>(f, gf, wl, ds, px, pd, ChunkOn{ok[k]});
       }
     }
     if constexpr (OP == VJP_RMS) team_sum2_post(ds[0], ds[1], red[it & 1]);
     else team_sum4_post(ds, red[it & 1]);
+    return RowPiv{px, pd};
   };
-  // After that barrier: this lane's slot of the posted sums.
-  auto sums_read = [&](int it) {
-    if constexpr (OP == VJP_RMS) return team_sum2_read(red[it & 1], wave0, nwt);
-    else return team_sum4_read(red[it & 1], wave0, nwt);
+  // After that barrier: this lane's slot of the posted sums (with the row's pivots).
+  struct Posted { double t, px, pd; };
+  auto sums_read = [&](int it, const RowPiv& rp) {
+    Posted p{0.0, rp.x, rp.d};
+    if constexpr (OP == VJP_RMS) p.t = team_sum2_read(red[it & 1], wave0, nwt);
+    else p.t = team_sum4_read(red[it & 1], wave0, nwt);
+    return p;
   };
   // Then the row's scalars, the same in every lane.
-  auto scalars = [&](double t) {
+  auto scalars = [&](const Posted& p) {
     VjpRow s;
     if constexpr (OP == VJP_RMS) {
       double ds[2];
-      team_sum2_finish(t, ds);
+      team_sum2_finish(p.t, ds);
       s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
     } else {
       double ds[4];
-      team_sum4_finish(t, ds);
-      s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
+      team_sum4_finish(p.t, ds);
+      s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], p.px, p.pd, a.inv_n, a.eps);
     }
     return vjp_row_uniform(s);
   };
@@ -391,13 +444,15 @@ vjp_rows(VjpArgs a) {
     // below: one buffer pair, the next row copied in after each row, and each row's
     // statistics, barrier and outputs in turn.
     u32x4 xa[NV], ga[NV];
-    load_row(0, xa, ga);
+    Piv pa{0.f, 0.f};
+    load_row(0, xa, ga, pa);
     for (int it = 0; it < iters; ++it) {
       u32x4 xb[NV], gb[NV];
-      if (it + 1 < iters) load_row(it + 1, xb, gb);
-      stats(it, xa, ga);
+      Piv pb{0.f, 0.f};
+      if (it + 1 < iters) load_row(it + 1, xb, gb, pb);
+      const RowPiv rp = stats(it, xa, ga, pa);
       __syncthreads();
-      const VjpRow s = scalars(sums_read(it));
+      const VjpRow s = scalars(sums_read(it, rp));
       outputs(it, xa, ga, s);
       if (it + 1 < iters) {
 #pragma unroll
@@ -405,6 +460,7 @@ vjp_rows(VjpArgs a) {
           xa[k] = xb[k];
           ga[k] = gb[k];
         }
+        pa = pb;
       }
     }
   } else {
@@ -418,18 +474,19 @@ vjp_rows(VjpArgs a) {
     // loaded would wait for the load.
     constexpr int R = OP == VJP_LN && (PK == PK_F32 || !EXACT) ? 3 : 4;
     u32x4 xs[R][NV], gs[R][NV];
+    Piv ps[R];
 #pragma unroll
-    for (int q = 0; q < R - 1; ++q) load_row(q, xs[q], gs[q]);
-    stats(0, xs[0], gs[0]);
+    for (int q = 0; q < R - 1; ++q) load_row(q, xs[q], gs[q], ps[q]);
+    RowPiv rp = stats(0, xs[0], gs[0], ps[0]);
     __syncthreads();
-    VjpRow s = scalars(sums_read(0));
+    VjpRow s = scalars(sums_read(0, rp));
     auto step = [&](int it, int q, bool load, bool next) {
-      if (load) load_row(it + R - 1, xs[(q + R - 1) % R], gs[(q + R - 1) % R]);
-      double t = 0.0;
+      if (load) load_row(it + R - 1, xs[(q + R - 1) % R], gs[(q + R - 1) % R], ps[(q + R - 1) % R]);
+      Posted t{0.0, 0.0, 0.0};
       if (next) {
-        stats(it + 1, xs[(q + 1) % R], gs[(q + 1) % R]);
+        const RowPiv np = stats(it + 1, xs[(q + 1) % R], gs[(q + 1) % R], ps[(q + 1) % R]);
         __syncthreads();
-        t = sums_read(it + 1);
+        t = sums_read(it + 1, np);
       }
       outputs(it, xs[q], gs[q], s);
       if (next) s = scalars(t);
@@ -535,17 +592,26 @@ vjp_team(VjpArgs a) {
   auto process = [&](int it, const u32x4& xv, const u32x4& gv) {
     const int64_t row = row_of(it);
     const u32x4 z = u32x4{0, 0, 0, 0};
+    // LN: the row's pivots, x, g and w at column 0, which the team's first lane holds.
+    double px = 0.0, pd = 0.0;
+    if constexpr (OP == VJP_LN) {
+      auto first = [](float v) {
+        return __builtin_bit_cast(float, group_first<SUB>(__builtin_bit_cast(uint32_t, v)));
+      };
+      vjp_pivots<XF>(first(first_elem<BF16>(xv[0])), first(first_elem<BF16>(gv[0])), first(wv[0]),
+                     px, pd);
+    }
     float f[V], gf[V];
-    unpack<BF16>(ok ? xv : z, f);  // a lane past the row's end adds zeros to the sums
+    unpack<BF16>(ok ? xv : z, f);  // a lane past the row's end adds nothing to the sums
     unpack<BF16>(ok ? gv : z, gf);
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
-    vjp_accumulate<OP, V, XF>(f, gf, wv, ds);
+    vjp_accumulate<OP, V, XF>(f, gf, wv, ds, px, pd, ChunkOn{ok});
     VjpRow s;
     if constexpr (OP == VJP_RMS) {
       s = vjp_rms_scalars(group_sum<SUB>(ds[0]), group_sum<SUB>(ds[1]), a.inv_n, a.eps);
     } else {
       s = vjp_ln_scalars(group_sum<SUB>(ds[0]), group_sum<SUB>(ds[1]), group_sum<SUB>(ds[2]),
-                         group_sum<SUB>(ds[3]), a.inv_n, a.eps);
+                         group_sum<SUB>(ds[3]), px, pd, a.inv_n, a.eps);
     }
     if (row >= a.rows) return;
     u32x4 xr = xv, gr = gv;
@@ -611,9 +677,17 @@ vjp_generic(VjpArgs a) {
   double* pw = DW ? a.part_w + (int64_t)blockIdx.x * a.hidden : nullptr;
   double* pb = DB ? a.part_b + (int64_t)blockIdx.x * a.hidden : nullptr;
 
+  const float w0 = OP == VJP_LN ? vjp_w0<BF16>(a) : 1.f;
   for (int64_t row = row0; row < row_end; ++row) {
     const int64_t e0 = row * a.hidden;
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
+    // LN: the row's pivots (x and d = g w at column 0).
+    double px = 0.0, pd = 0.0;
+    if constexpr (OP == VJP_LN) {
+      const float x0 = sload_elem<BF16>(a.x, e0), g0 = sload_elem<BF16>(a.g, e0);
+      if (xf) vjp_pivots<BF16>(x0, g0, w0, px, pd);
+      else vjp_pivots<false>(x0, g0, w0, px, pd);
+    }
     for (int64_t j = threadIdx.x; j < nch; j += 256) {
       float f[V], gf[V], wv[V];
       load_act<BF16, V>(a.x, e0 + j * V, f);
@@ -624,14 +698,14 @@ vjp_generic(VjpArgs a) {
 #pragma unroll
         for (int e = 0; e < V; ++e) wv[e] = 1.f;
       }
-      if (xf) vjp_accumulate<OP, V, BF16>(f, gf, wv, ds);
-      else vjp_accumulate<OP, V, false>(f, gf, wv, ds);
+      if (xf) vjp_accumulate<OP, V, BF16>(f, gf, wv, ds, px, pd, AllOn{});
+      else vjp_accumulate<OP, V, false>(f, gf, wv, ds, px, pd, AllOn{});
     }
     team_sum4(ds, red, 0, 4);
     __syncthreads();  // red is rewritten by the next row
     VjpRow s;
     if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
-    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
+    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], px, pd, a.inv_n, a.eps);
     const bool first = row == row0;
     for (int64_t j = threadIdx.x; j < nch; j += 256) {
       float f[V], gf[V], wv[V], dxv[V];
@@ -702,9 +776,15 @@ vjp_elems(VjpArgs a) {
     if constexpr (LB) lb[e] = 0.0;
   }
   // Ring of R register sets: the loads for row i + R - 1 are issued before row i's sums.
+  // LN: with each row's pivots, x and g at column 0, read through the scalar cache.
   constexpr int R = K <= 2 ? 4 : K <= 4 ? 3 : 2;
-  float xs[R][K], gs[R][K];
-  auto load = [&](int64_t row, float (&xv)[K], float (&gv)[K]) {
+  float xs[R][K], gs[R][K], pxs[R], pgs[R];
+  const float w0 = OP == VJP_LN ? vjp_w0<BF16>(a) : 1.f;
+  auto load = [&](int64_t row, float (&xv)[K], float (&gv)[K], float& px0, float& pg0) {
+    if constexpr (OP == VJP_LN) {
+      px0 = sload_elem<BF16>(a.x, row * H);
+      pg0 = sload_elem<BF16>(a.g, row * H);
+    }
     const int64_t e0 = row * H + tid;
 #pragma unroll
     for (int e = 0; e < K; ++e) {
@@ -717,13 +797,17 @@ vjp_elems(VjpArgs a) {
       gv[e] = u[0];
     }
   };
-  auto step = [&](int64_t row, const float (&xv)[K], const float (&gv)[K], double* rb) {
+  auto on = [&](int e) { return ok[e]; };
+  auto step = [&](int64_t row, const float (&xv)[K], const float (&gv)[K], float px0, float pg0,
+                  double* rb) {
     double ds[4] = {0.0, 0.0, 0.0, 0.0};
-    vjp_accumulate<OP, K, XF>(xv, gv, wv, ds);
+    double px = 0.0, pd = 0.0;
+    if constexpr (OP == VJP_LN) vjp_pivots<XF>(px0, pg0, w0, px, pd);
+    vjp_accumulate<OP, K, XF>(xv, gv, wv, ds, px, pd, on);
     team_sum4(ds, rb, 0, T >> 6);
     VjpRow s;
     if constexpr (OP == VJP_RMS) s = vjp_rms_scalars(ds[0], ds[1], a.inv_n, a.eps);
-    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], a.inv_n, a.eps);
+    else s = vjp_ln_scalars(ds[0], ds[1], ds[2], ds[3], px, pd, a.inv_n, a.eps);
     float dxv[K];
     if constexpr (LB) vjp_outputs<OP, K, DW, DB, XF>(xv, gv, wv, s, dxv, lw, lb);
     else if constexpr (LW) vjp_outputs<OP, K, DW, DB, XF>(xv, gv, wv, s, dxv, lw, ab);
@@ -741,14 +825,15 @@ vjp_elems(VjpArgs a) {
   // every load is unconditional.
   if (row0 < row_end) {
 #pragma unroll
-    for (int i = 0; i < R - 1; ++i) load(min(row0 + i, row_end - 1), xs[i], gs[i]);
+    for (int i = 0; i < R - 1; ++i) load(min(row0 + i, row_end - 1), xs[i], gs[i], pxs[i], pgs[i]);
   }
   for (int64_t row = row0; row < row_end; row += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       if (row + i >= row_end) break;
-      load(min(row + i + R - 1, row_end - 1), xs[(i + R - 1) % R], gs[(i + R - 1) % R]);
-      step(row + i, xs[i], gs[i], red[R % 2 == 0 ? i & 1 : (row + i - row0) & 1]);
+      load(min(row + i + R - 1, row_end - 1), xs[(i + R - 1) % R], gs[(i + R - 1) % R],
+           pxs[(i + R - 1) % R], pgs[(i + R - 1) % R]);
+      step(row + i, xs[i], gs[i], pxs[i], pgs[i], red[R % 2 == 0 ? i & 1 : (row + i - row0) & 1]);
     }
   }
   if constexpr (PG) {
