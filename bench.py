@@ -257,12 +257,18 @@ def headline(args):
     def step(_):
         nrm.add_rms_norm(x, r, w, inp.eps, out=out, h=h)
 
+    # The copy ceilings run first: about 1.3 s of streaming at the same byte count, which
+    # brings the GPU to the clocks it holds under sustained load (it needs about a second), so
+    # that the headline's few timed steps are not taken on the way up. Under a profiler they
+    # stay short.
+    copy_steps = max(100, args.steps // 2) if args.profile else 2000
+    print(f"# copy ceilings, {copy_steps} steps each", file=sys.stderr, flush=True)
+    ceiling = copy_ceiling(nbytes, copy_steps)
+    ceiling2 = copy2_ceiling(nbytes, copy_steps)
     print(f"# timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     gpu_ms, wall_ms = time_calls(step, args.steps, args.warmup)
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
     value = nbytes / (wall_ms * 1e-3) / 1e9
-    ceiling = copy_ceiling(nbytes, max(100, args.steps // 2))
-    ceiling2 = copy2_ceiling(nbytes, max(100, args.steps // 2))
     if args.profile:
         print(json.dumps({"profile_run": True, "avg_launch_us": gpu_ms * 1e3,
                           "achieved_GBps": achieved, "copy_GBps": ceiling,

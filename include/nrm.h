@@ -383,7 +383,8 @@ nrm_status nrm_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t
 /*
  * Measurement helper, not one of the operations above: dst1 = src1 and dst2 = src2, `bytes`
  * bytes each, with one 16-byte load of each source and one 16-byte store of each destination
- * per thread: the residual add-RMSNorm's byte pattern (two arrays in, two out) without
+ * per thread, 512-thread blocks at two per compute unit (the fastest shape measured for this
+ * pattern): the residual add-RMSNorm's byte pattern (two arrays in, two out) without
  * arithmetic, reported as that pattern's achievable-bandwidth ceiling. All four arrays are
  * device memory, 16-byte aligned; no destination may overlap a source or the other
  * destination (the two sources may overlap). Errors: NULL -> NRM_ERR_NULL; bytes < 0 or not

@@ -39,8 +39,12 @@ hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t st
 
 // Two streams copied into two, one 16-byte chunk of each per thread, 512 threads per block,
 // non-temporal: the residual add-RMSNorm's byte pattern (two inputs in, two outputs out)
-// without arithmetic. The fastest shape measured for that pattern on MI355X (~77% of 8 TB/s;
-// one or two chunks per thread at 256 or 1024 threads reach 74-76%).
+// without arithmetic, in the fastest shape measured for that pattern on MI355X. The launch
+// reserves 58 KB of LDS per block (unused), which caps residency at two blocks (16 waves)
+// per compute unit: 82% of 8 TB/s over four rotating buffer sets, against 76-78% at three or
+// four blocks per CU and 78% at one. Two chunks of each array per thread, 256- or 1024-thread
+// blocks, or a barrier between the loads and the stores at four blocks per CU stay at 74-79%.
+constexpr size_t kCopy2Lds = 58000;
 __global__ void __launch_bounds__(512)
 copy16x2_kernel(const u32x4* s1, const u32x4* s2, u32x4* d1, u32x4* d2, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x;
@@ -55,8 +59,8 @@ hipError_t launch_copy16x2(const void* s1, const void* s2, void* d1, void* d2, i
                            hipStream_t stream) {
   const int64_t blocks = (n16 + 511) / 512;
   if (blocks > kMaxCopyGrid) return hipErrorInvalidValue;
-  copy16x2_kernel<<<(unsigned)blocks, 512, 0, stream>>>((const u32x4*)s1, (const u32x4*)s2,
-                                                        (u32x4*)d1, (u32x4*)d2, n16);
+  copy16x2_kernel<<<(unsigned)blocks, 512, kCopy2Lds, stream>>>((const u32x4*)s1, (const u32x4*)s2,
+                                                                (u32x4*)d1, (u32x4*)d2, n16);
   return hipGetLastError();
 }
 
