@@ -296,6 +296,27 @@ nrm_status nrm_layer_norm_vjp(const void* x, const void* w, const void* g, void*
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nrm_layer_norm_vjp without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid it). The
+ * fp64 partial column sums of dw and db go to a scratch array that the library holds in
+ * device memory (32 MiB per GPU it runs on, kept until the process ends), not to a caller's
+ * workspace; the call allocates nothing. Arguments, layout, results and errors are those of
+ * nrm_layer_norm_vjp (the same kernels, the same bits), except:
+ *   - rows x hidden may need at most 32 MiB of partial sums, i.e. hidden <= 8192 at any row
+ *     count (with dw or db requested); beyond that -> NRM_ERR_SHAPE, nothing launched;
+ *   - every call on one GPU shares that GPU's scratch: calls that may overlap on one GPU
+ *     (different streams, different host threads) race and must be ordered by the caller;
+ *     calls on one stream are ordered already. The scratch holds the last call's partial
+ *     sums; each call writes every partial sum it reads, so nothing needs clearing.
+ *   - the scratch's device address is looked up (hipGetSymbolAddress) on the first call on
+ *     each device; failure there -> NRM_ERR_DEVICE.
+ */
+nrm_status nrm_layer_norm_vjp_noalloc(const void* x, const void* w, const void* g, void* dx,
+                                      void* dw, void* db, int64_t rows, int64_t hidden,
+                                      float eps, nrm_dtype dtype, nrm_dtype w_dtype,
+                                      hipStream_t stream);
+
+/*
  * Softmax over the last axis of x [rows, n]: out = exp(x - max) / sum(exp(x - max)).
  * Source: nuvec-core 0.5.0 fast::FastOp, variant Softmax ((x): softmax over the last axis,
  * accumulated in float32). Arithmetic fp32; the result is rounded once to dtype; every

@@ -194,6 +194,19 @@ def test_vjp_workspace_bytes(L):
     assert L.nrm_norm_vjp_workspace_bytes(4, 0, 1) == 0
 
 
+def test_vjp_noalloc_host_errors(L):
+    """The allocation-free backward checks dtypes, sizes and its scratch limit (32 MiB of
+    partial sums: hidden <= 8192 at any row count) on the host, before any HIP call."""
+    f = L.nrm_layer_norm_vjp_noalloc
+    assert f(P, None, P + 64 * MB, P + 128 * MB, P + 192 * MB, P + 256 * MB, 4, 8, 1e-5, 7, BF16,
+             None) == DTYPE and "nrm_layer_norm_vjp_noalloc: dtype" in err(L)
+    assert f(P, None, P + 64 * MB, P + 128 * MB, P + 192 * MB, P + 256 * MB, -1, 8, 1e-5, BF16,
+             BF16, None) == SHAPE
+    assert f(P, None, P + 64 * MB, P + 128 * MB, P + 192 * MB, P + 256 * MB, 4096, 8200, 1e-5,
+             BF16, BF16, None) == SHAPE and "at most 33554432 scratch bytes" in err(L)
+    assert L.nrm_norm_vjp_workspace_bytes(4096, 8192, 1) == 32 << 20  # the largest that fits
+
+
 def test_vjp_argument_errors(L):
     assert rvjp(L, x=None) == NULL and "nrm_rms_norm_vjp: x must not be NULL" in err(L)
     assert rvjp(L, g=None) == NULL and "g must not be NULL" in err(L)

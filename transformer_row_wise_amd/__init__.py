@@ -33,7 +33,8 @@ __all__ = [
     "NrmError", "load", "lib", "rms_norm", "add_rms_norm", "layer_norm", "norm_rope",
     "rms_norm_vjp", "layer_norm_vjp", "vjp_workspace_bytes", "rope", "rope_positions",
     "rope_freqs_llama3", "rope_freqs_yarn", "rope_freqs_su", "softmax", "causal_softmax",
-    "logsumexp", "cross_entropy", "cross_entropy_vjp", "bench_copy", "bench_copy2", "NRM_F32",
+    "logsumexp", "cross_entropy", "cross_entropy_vjp", "bench_copy", "bench_copy2",
+    "layer_norm_vjp_noalloc", "NRM_F32",
     "NRM_BF16", "LIB_PATH",
 ]
 
@@ -61,6 +62,8 @@ _SIGNATURES = {
     "nrm_rms_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz, _vp],
     "nrm_layer_norm_vjp": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int, _vp, _sz,
                            _vp],
+    "nrm_layer_norm_vjp_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _int,
+                                   _vp],
     "nrm_softmax": [_vp, _vp, _i64, _i64, _int, _vp],
     "nrm_causal_softmax": [_vp, _vp, _i64, _i64, _i64, _i64, _int, _vp],
     "nrm_logsumexp": [_vp, _vp, _i64, _i64, _int, _vp],
@@ -331,6 +334,22 @@ def layer_norm_vjp(x, w, g, eps=1e-5, want_dw=True, want_db=True, dx=None, dw=No
     ws, ws_bytes = _workspace(workspace, need, x)
     st = load().nrm_layer_norm_vjp(_ptr(x), _ptr(w), _ptr(g), _ptr(dx), _ptr(dw), _ptr(db), rows,
                                    hidden, eps, dt, wdt, _ptr(ws), ws_bytes, _stream())
+    if st:
+        _raise(st)
+    return dx, dw, db
+
+
+def layer_norm_vjp_noalloc(x, w, g, eps=1e-5, want_dw=True, want_db=True, dx=None, dw=None,
+                           db=None):
+    """layer_norm_vjp through nrm_layer_norm_vjp_noalloc: the partial column sums go to the
+    library's static device scratch, so the call allocates no workspace (pass dx, dw and db
+    to allocate nothing at all). Calls that may overlap on one GPU must be ordered."""
+    dt, rows, hidden, w, wdt, pdtype = _vjp_common(x, w, g)
+    dx = _out_like(dx, x, "dx")
+    dw = _param_grad(want_dw, dw, hidden, x, pdtype, "dw")
+    db = _param_grad(want_db, db, hidden, x, pdtype, "db")
+    st = load().nrm_layer_norm_vjp_noalloc(_ptr(x), _ptr(w), _ptr(g), _ptr(dx), _ptr(dw),
+                                           _ptr(db), rows, hidden, eps, dt, wdt, _stream())
     if st:
         _raise(st)
     return dx, dw, db

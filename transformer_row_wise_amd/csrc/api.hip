@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -345,6 +346,80 @@ nrm_status nrm_layer_norm_vjp(const void* x, const void* w, const void* g, void*
                               size_t workspace_bytes, hipStream_t stream) {
   return norm_vjp("nrm_layer_norm_vjp", true, x, w, g, dx, dw, db, rows, hidden, eps, dtype,
                   w_dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of nrm_layer_norm_vjp_noalloc: the fp64 partial column sums of dw and db, in a
+// file-scope device array (each GPU the library runs on holds its own copy until the process
+// ends) instead of a caller workspace. 32 MiB covers LayerNorm rows of up to 8192 values at any
+// row count (at most 256 partial rows of dw and of db). In host code the array's name is only
+// a stand-in: its device address, which differs per GPU, comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device of `stream` (the current device for the null stream),
+// looked up on the first call on each device, with that device current.
+nrm_status scratch_on(const char* fn, hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess)
+    return fail(NRM_ERR_DEVICE, "%s: no current device: %s, got HIP error %d", fn,
+                hipGetErrorString(e), (int)e);
+  int dev = cur;
+  if (stream != nullptr && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess)
+    return fail(NRM_ERR_DEVICE, "%s: stream's device unknown: %s, got HIP error %d", fn,
+                hipGetErrorString(e), (int)e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(NRM_ERR_DEVICE, "%s: device index must be below %d, got %d", fn, kMaxDevices, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(NRM_ERR_DEVICE, "%s: cannot select device %d: %s, got HIP error %d", fn, dev,
+                  hipGetErrorString(e), (int)e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(NRM_ERR_DEVICE, "%s: scratch address on device %d: %s, got HIP error %d", fn,
+                  dev, hipGetErrorString(e), (int)e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NRM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nrm_status nrm_layer_norm_vjp_noalloc(const void* x, const void* w, const void* g, void* dx,
+                                      void* dw, void* db, int64_t rows, int64_t hidden,
+                                      float eps, nrm_dtype dtype, nrm_dtype w_dtype,
+                                      hipStream_t stream) {
+  static const char* fn = "nrm_layer_norm_vjp_noalloc";
+  g_err.clear();
+  nrm_status st = check_dtypes(fn, dtype, w_dtype);
+  if (st) return st;
+  if ((st = check_rows(fn, rows, hidden, dtype))) return st;
+  void* ws = nullptr;
+  if ((dw || db) && rows > 0) {
+    const size_t need = nrm_norm_vjp_workspace_bytes(rows, hidden, 1);
+    if (need > kScratchBytes)
+      return fail(NRM_ERR_SHAPE,
+                  "%s: rows x hidden must need at most %zu scratch bytes (hidden <= 8192 at any "
+                  "row count), got %lld x %lld needing %zu", fn, kScratchBytes,
+                  (long long)rows, (long long)hidden, need);
+    if ((st = scratch_on(fn, stream, &ws))) return st;
+  }
+  return norm_vjp(fn, true, x, w, g, dx, dw, db, rows, hidden, eps, dtype, w_dtype, ws,
+                  ws ? kScratchBytes : 0, stream);
 }
 
 nrm_status nrm_rope(const void* x, void* out, int64_t N, int64_t L, int64_t D, int64_t dims,
