@@ -8,9 +8,17 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite] [--no-cpu-baseline]
 
---suite        also prints one JSON line per synthetic workload (all four ops) to stderr,
-               rotating buffer sets when a call's working set would fit in the 256 MB
-               Infinity Cache.
+--suite        also prints one JSON line per workload to stderr, rotating buffer sets when a
+               call's working set would fit in the 256 MB Infinity Cache. The synthetic
+               configurations (1-5d) carry every measurement field: GPU time, GB/s, % of
+               peak, rows/s, copy ceilings of the same bytes, HBM fetch / write MB (stored
+               counter summary), and the fp64 oracle over the whole workload in the same run
+               (its seconds, cores, GB/s, and the parity of this run's output).
+--counters     eager calls of every configuration and of one workload per other operation,
+               for rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE runs).
+--summarize-configs TRACE_DB FETCH_DB WRITE_DB
+               write profiles/suite_configs.md and profiles/traffic_suite_configs.json from
+               those three runs of --counters.
 --sweep        bandwidth of every operation across row widths (about 256 MB per call), one
                JSON line per case to stderr; no headline line.
 --profile      only warm-up and timed calls of the headline kernel plus the copy kernel
@@ -341,20 +349,10 @@ def suite(args):
                           "gpu_us_min": round(min(per) * 1e3, 3),
                           "timing": "HIP graph of back-to-back calls, median of 10 replays",
                           "gpu_GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 2),
-                          "rows_per_s": round(rows / (avg * 1e-3), 1)}), file=sys.stderr,
-              flush=True)
-
-    def run_add(cfg, inp):
-        rows, hidden = inp.x.shape
-        es = inp.x.element_size()
-        nbytes = add_rms_bytes(rows, hidden, es, inp.w.element_size())
-        sets = [(inp.x.cuda(), inp.r.cuda()) for _ in range(n_sets(nbytes))]
-        w = inp.w.cuda()
-        outs = [(torch.empty_like(s[0]), torch.empty_like(s[0])) for s in sets]
-        per = time_graph(lambda i: nrm.add_rms_norm(*sets[i % len(sets)], w, inp.eps,
-                                                    out=outs[i % len(sets)][0],
-                                                    h=outs[i % len(sets)][1]), calls(nbytes))
-        emit(cfg, "add_rms_norm", [rows, hidden, str(inp.x.dtype)], nbytes, rows, per)
+                          "rows_per_s": round(rows / (avg * 1e-3), 1),
+                          "fetch_MB": (traffic_entry(cfg) or {}).get("fetch_MB"),
+                          "write_MB": (traffic_entry(cfg) or {}).get("write_MB")}),
+              file=sys.stderr, flush=True)
 
     def run_vjp(cfg, inp, ln):
         rows, hidden = inp.x.shape
@@ -442,58 +440,572 @@ def suite(args):
             del f32, bf
     if "fwd" not in groups:
         return
-    run_add("1", workloads.cfg_add_rms_small_f32())
-    run_add("2", workloads.cfg_add_rms_4k_bf16())
-    for affine in (True, False):
+    run_configs(args, nrm, torch, workloads, n_sets, calls, traffic_entry)
+
+
+# --------------------------------------------------------------------------- synthetic configs
+
+# The synthetic configurations of the benchmark (one line each), and one workload per
+# operation of the backward, Rope and softmax groups, in the order the counter runs take them.
+CONFIG_IDS = ["1", "2", "3a", "3b", "4a", "4b", "4c", "4d", "5a", "5b", "5c", "5d"]
+NEXT_IDS = ["6a", "7a", "8a", "8b", "9a", "9b", "9c", "9d", "9e"]
+# Kernel dispatches of one call, where more than one (the backward adds its column sums).
+DISPATCHES_PER_CALL = {"6a": 2, "7a": 2}
+SUITE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_suite_configs.json")
+SUITE_MD = os.path.join(ROOT, "profiles", "suite_configs.md")
+CAL_BYTES = 512 * 2**20  # the calibration copy, bytes each way
+ORACLE_CHUNK_ROWS = 256
+
+
+def library_source_hash():
+    """Hash of every library source and the compiler flags: a stored per-config counter
+    reading is used only for this exact code."""
+    import glob
+
+    from transformer_row_wise_amd import build as nrm_build
+    h = hashlib.sha256()
+    flags = [f.replace(nrm_build.ROOT, ".") for f in nrm_build.FLAGS]
+    h.update(" ".join(flags).encode() + b"\0")
+    for path in sorted(glob.glob(os.path.join(ROOT, "transformer_row_wise_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _np_bits(t):
+    """A CPU numpy copy of a tensor's bits: bf16 -> uint16, fp32 -> float32."""
+    import numpy as np
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def build_case(cid, nrm, torch, workloads, n_sets):
+    """One workload as a dict: op, dtype, shape, algorithmic bytes, rows, the kernel
+    dispatches one call issues, `call(i)` (buffer set i % k), and `jobs()` (runs set 0 once
+    and returns the oracle's chunks of rows, each with the GPU's output for it; configs only)."""
+    import numpy as np
+
+    dev = "cuda"
+    if cid in ("1", "2", "5a", "5b", "5c", "5d"):
+        if cid == "1":
+            inp = workloads.cfg_add_rms_small_f32()
+        elif cid == "2":
+            inp = workloads.cfg_add_rms_4k_bf16()
+        else:
+            shape = (16384, 8192) if cid in ("5a", "5b") else (65536, 5120)
+            inp = workloads.cfg_add_rms_scale(*shape, dtype="f32")
+            if cid in ("5a", "5c"):
+                inp = workloads.RowInputs(x=inp.x.to(torch.bfloat16), r=inp.r.to(torch.bfloat16),
+                                          w=inp.w.to(torch.bfloat16), b=None, eps=inp.eps)
+        rows, hidden = inp.x.shape
+        nbytes = add_rms_bytes(rows, hidden, inp.x.element_size(), inp.w.element_size())
+        k = n_sets(nbytes)
+        sets = [(inp.x.to(dev), inp.r.to(dev)) for _ in range(k)]
+        w = inp.w.to(dev)
+        outs = [(torch.empty_like(sets[0][0]), torch.empty_like(sets[0][0])) for _ in range(k)]
+
+        def call(i):
+            nrm.add_rms_norm(*sets[i % k], w, inp.eps, out=outs[i % k][0], h=outs[i % k][1])
+
+        def jobs():
+            call(0)
+            torch.cuda.synchronize()
+            xb, rb, wb, ob, hb = (_np_bits(t) for t in (inp.x, inp.r, inp.w, outs[0][0], outs[0][1]))
+            c = ORACLE_CHUNK_ROWS
+            return [("add", xb[i:i + c], rb[i:i + c], wb, inp.eps, ob[i:i + c], hb[i:i + c])
+                    for i in range(0, rows, c)]
+
+        return dict(cfg=cid, op="add_rms_norm", dtype=str(inp.x.dtype).replace("torch.", ""),
+                    shape=[rows, hidden], bytes=nbytes, rows=rows, dispatches=1, call=call,
+                    jobs=jobs, copy2=True)
+    if cid in ("3a", "3b"):
+        affine = cid == "3a"
         inp = workloads.cfg_layer_norm_bf16(affine=affine)
         rows, hidden = inp.x.shape
         nbytes = 2 * rows * hidden * 2 + (2 * hidden * 2 if affine else 0)
-        x = inp.x.cuda()
-        w = inp.w.cuda() if affine else None
-        b = inp.b.cuda() if affine else None
+        x = inp.x.to(dev)
+        w = inp.w.to(dev) if affine else None
+        b = inp.b.to(dev) if affine else None
         out = torch.empty_like(x)
-        per = time_graph(lambda i: nrm.layer_norm(x, w, b, inp.eps, out=out), calls(nbytes))
-        emit("3a" if affine else "3b", "layer_norm", [rows, hidden], nbytes, rows, per)
-        del x, out
-    def run_copy(cfg, nbytes):
-        """The 16-byte copy moving the same bytes (half in, half out): the small-call ceiling."""
-        half = (nbytes // 2) // 16 * 16
-        k = n_sets(nbytes)
-        srcs = [torch.ones(half, dtype=torch.uint8, device="cuda") for _ in range(k)]
-        dsts = [torch.empty_like(srcs[0]) for _ in range(k)]
-        per = time_graph(lambda i: nrm.bench_copy(srcs[i % k], dsts[i % k]), calls(nbytes))
-        emit(cfg, "copy (ceiling)", [half], 2 * half, 0, per)
 
-    run_copy("4-copy", 2 * 8 * 32 * 512 * 128 * 2)
-    for cache in (False, True):
-        for trad in (False, True):
-            rp = workloads.cfg_norm_rope_bf16(offset=workloads.NORM_ROPE_CACHE_OFFSET if cache else 0)
-            B, H, L, D = rp.x.shape
-            nbytes = 2 * B * H * L * D * 2 + D * 2
-            k = n_sets(nbytes)
-            xs = [rp.x.cuda() for _ in range(k)]
-            w = rp.w.cuda()
-            if cache:
-                dsts = [torch.zeros(B, H, workloads.NORM_ROPE_CACHE_LEN, D, dtype=torch.bfloat16,
-                                    device="cuda") for _ in range(k)]
+        def call(i):
+            nrm.layer_norm(x, w, b, inp.eps, out=out)
+
+        def jobs():
+            call(0)
+            torch.cuda.synchronize()
+            xb, ob = _np_bits(inp.x), _np_bits(out)
+            wb = _np_bits(inp.w) if affine else None
+            bb = _np_bits(inp.b) if affine else None
+            c = ORACLE_CHUNK_ROWS
+            return [("ln", xb[i:i + c], wb, bb, inp.eps, ob[i:i + c]) for i in range(0, rows, c)]
+
+        return dict(cfg=cid, op="layer_norm" + ("" if affine else "_no_affine"), dtype="bfloat16",
+                    shape=[rows, hidden], bytes=nbytes, rows=rows, dispatches=1, call=call,
+                    jobs=jobs, copy2=False)
+    if cid in ("4a", "4b", "4c", "4d"):
+        cache, trad = cid in ("4c", "4d"), cid in ("4b", "4d")
+        rp = workloads.cfg_norm_rope_bf16(offset=workloads.NORM_ROPE_CACHE_OFFSET if cache else 0)
+        B, H, L, D = rp.x.shape
+        nbytes = 2 * B * H * L * D * 2 + D * 2
+        k = n_sets(nbytes)
+        xs = [rp.x.to(dev) for _ in range(k)]
+        w = rp.w.to(dev)
+        if cache:
+            dsts = [torch.zeros(B, H, workloads.NORM_ROPE_CACHE_LEN, D, dtype=torch.bfloat16,
+                                device=dev) for _ in range(k)]
+        else:
+            dsts = [torch.empty_like(xs[0]) for _ in range(k)]
+
+        def call(i):
+            nrm.norm_rope(xs[i % k], w, eps=rp.eps, dims=rp.dims, traditional=trad,
+                          base=rp.base, scale=rp.scale, offset=rp.offset,
+                          cache=dsts[i % k] if cache else None, out=None if cache else dsts[i % k])
+
+        def jobs():
+            call(0)
+            torch.cuda.synchronize()
+            xb, wb, ob = _np_bits(rp.x), _np_bits(rp.w), _np_bits(dsts[0])
+            p = (rp.eps, rp.dims, trad, rp.base, rp.scale, rp.offset, cache)
+            return [("rope", xb[i:i + 1], wb, p, ob[i:i + 1]) for i in range(B)]
+
+        return dict(cfg=cid, op="norm_rope" + ("_cache" if cache else "") +
+                    ("_interleaved" if trad else "_half"), dtype="bfloat16", shape=[B, H, L, D],
+                    bytes=nbytes, rows=B * H * L, dispatches=1, call=call, jobs=jobs, copy2=False)
+    # One workload per operation of the other groups (counter evidence only).
+    if cid in ("6a", "7a"):
+        ln = cid == "7a"
+        f32 = workloads.cfg_ln_vjp(dtype="f32") if ln else workloads.cfg_rms_vjp(dtype="f32")
+        x, g = f32.x.to(torch.bfloat16).to(dev), f32.g.to(torch.bfloat16).to(dev)
+        w = f32.w.to(torch.bfloat16).to(dev)
+        rows, hidden = x.shape
+        dx, dw, db = torch.empty_like(x), torch.empty_like(w), torch.empty_like(w)
+        ws = torch.empty(nrm.vjp_workspace_bytes(rows, hidden, ln), dtype=torch.uint8, device=dev)
+        nbytes = 3 * rows * hidden * 2 + hidden * 2 * (3 if ln else 2)
+
+        def call(i):
+            if ln:
+                nrm.layer_norm_vjp(x, w, g, f32.eps, dx=dx, dw=dw, db=db, workspace=ws)
             else:
-                dsts = [torch.empty_like(xs[0]) for _ in range(k)]
-            per = time_graph(
-                lambda i: nrm.norm_rope(xs[i % k], w, eps=rp.eps, traditional=trad,
-                                        offset=rp.offset, cache=dsts[i % k] if cache else None,
-                                        out=None if cache else dsts[i % k]),
-                calls(nbytes))
-            emit("4" + "abcd"[2 * cache + trad], "norm_rope" + ("_cache" if cache else "") +
-                 ("_interleaved" if trad else "_half"), [B, H, L, D], nbytes, B * H * L, per)
-            del xs, dsts
-    for shape, tag in (((16384, 8192), "5"), ((65536, 5120), "5")):
-        f32 = workloads.cfg_add_rms_scale(*shape, dtype="f32")
-        bf = workloads.RowInputs(x=f32.x.to(torch.bfloat16), r=f32.r.to(torch.bfloat16),
-                                 w=f32.w.to(torch.bfloat16), b=None, eps=f32.eps)
-        run_add(tag + ("a" if shape[1] == 8192 else "c"), bf)
-        run_add(tag + ("b" if shape[1] == 8192 else "d"), f32)
-        del f32, bf
+                nrm.rms_norm_vjp(x, w, g, f32.eps, dx=dx, dw=dw, workspace=ws)
+
+        return dict(cfg=cid, op="layer_norm_vjp" if ln else "rms_norm_vjp", dtype="bfloat16",
+                    shape=[rows, hidden], bytes=nbytes, rows=rows, dispatches=2, call=call)
+    if cid == "8a":
+        inp = workloads.cfg_rope_qk_bf16()
+        T, Hq, Hk, D = workloads.ROPE_QK_SHAPE
+        freqs, ms = nrm.rope_freqs_llama3(D, workloads.ROPE_QK_BASE)
+        q, kk, pos, fr = inp.q.to(dev), inp.k.to(dev), inp.positions.to(dev), freqs.to(dev)
+        qo, ko = torch.empty_like(q), torch.empty_like(kk)
+        nbytes = 2 * T * (Hq + Hk) * D * 2 + T * 8 + D // 2 * 4
+
+        def call(i):
+            nrm.rope_positions(pos, q, kk, base=workloads.ROPE_QK_BASE, freqs=fr, mscale=ms,
+                               q_out=qo, k_out=ko)
+
+        return dict(cfg=cid, op="rope_positions_llama3", dtype="bfloat16", shape=[T, Hq, Hk, D],
+                    bytes=nbytes, rows=T * (Hq + Hk), dispatches=1, call=call)
+    if cid == "8b":
+        rp = workloads.cfg_norm_rope_bf16()
+        x = rp.x.to(dev)
+        out = torch.empty_like(x)
+        B, H, L, D = x.shape
+
+        def call(i):
+            nrm.rope(x, out=out)
+
+        return dict(cfg=cid, op="rope", dtype="bfloat16", shape=[B, H, L, D],
+                    bytes=2 * x.numel() * 2, rows=B * H * L, dispatches=1, call=call)
+    if cid in ("9a", "9b"):
+        causal = cid == "9b"
+        shape = (8 * 32, 512, 512) if causal else (16384, 8192)
+        x = workloads.scores(shape, "bf16", seed=1 if causal else 0).to(dev)
+        out = torch.empty_like(x)
+        if causal:
+            N, R, L = shape
+            nbytes = N * (L * (L + 1) // 2) * 2 + x.numel() * 2
+        else:
+            nbytes = 2 * x.numel() * 2
+
+        def call(i):
+            if causal:
+                nrm.causal_softmax(x, shape[1], out=out)
+            else:
+                nrm.softmax(x, out=out)
+
+        return dict(cfg=cid, op="causal_softmax" if causal else "softmax", dtype="bfloat16",
+                    shape=list(shape), bytes=nbytes, rows=x.numel() // shape[-1], dispatches=1,
+                    call=call)
+    if cid in ("9c", "9d", "9e"):
+        inp = workloads.cfg_ce_bf16()
+        rows, V = workloads.CE_SHAPE
+        lg, tg, g = inp.logits.to(dev), inp.targets.to(dev), inp.g.to(dev)
+        nb_in = rows * V * 2
+        if cid == "9c":
+            lse = torch.empty(rows, 1, dtype=torch.bfloat16, device=dev)
+            call, op, nbytes = (lambda i: nrm.logsumexp(lg, out=lse)), "logsumexp", nb_in + rows * 2
+        elif cid == "9d":
+            loss = torch.empty(rows, dtype=torch.float32, device=dev)
+            call = lambda i: nrm.cross_entropy(lg, tg, loss=loss)
+            op, nbytes = "cross_entropy", nb_in + rows * 12
+        else:
+            dl = torch.empty_like(lg)
+            call = lambda i: nrm.cross_entropy_vjp(lg, tg, g, dlogits=dl)
+            op, nbytes = "cross_entropy_vjp", 2 * nb_in + rows * 12
+        return dict(cfg=cid, op=op, dtype="bfloat16", shape=[rows, V], bytes=nbytes, rows=rows,
+                    dispatches=1, call=call)
+    raise ValueError(cid)
+
+
+def _bf16_ordered(bits):
+    import numpy as np
+
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _f32_ordered(v):
+    import numpy as np
+
+    b = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.int64)
+    return np.where(b & 0x80000000, -(b & 0x7FFFFFFF), b & 0x7FFFFFFF)
+
+
+def _compare(got, want):
+    """(largest distance in units in the last place, elements over the bar) of one output
+    chunk: bf16 within 1 ulp, fp32 within 1e-5 relative + 1e-6 absolute; NaN only with NaN."""
+    import numpy as np
+
+    if got.dtype == np.uint16:
+        wb = (np.asarray(want, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        gn = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+        wn = ((wb & 0x7F80) == 0x7F80) & ((wb & 0x7F) != 0)
+        d = np.abs(_bf16_ordered(got) - _bf16_ordered(wb))
+        d = np.where(gn & wn, 0, np.where(gn ^ wn, 1 << 40, d))
+        return int(d.max()) if d.size else 0, int(np.count_nonzero(d > 1))
+    g = got.astype(np.float64)
+    w = np.asarray(want, np.float64)
+    gn, wn = np.isnan(g), np.isnan(w)
+    d = np.abs(_f32_ordered(got) - _f32_ordered(w.astype(np.float32)))
+    d = np.where(gn & wn, 0, np.where(gn ^ wn, 1 << 40, d))
+    with np.errstate(invalid="ignore"):
+        bad = ~(np.abs(g - w) <= 1e-6 + 1e-5 * np.abs(w))
+    bad &= ~(np.isinf(g) & np.isinf(w) & (g == w))
+    bad = np.where(gn & wn, False, bad) | (gn ^ wn)
+    return int(d.max()) if d.size else 0, int(np.count_nonzero(bad))
+
+
+def _config_oracle_job(job):
+    """One worker: the fp64 oracle on one chunk, timed, then compared with the GPU's output.
+    Returns (oracle seconds, max ulp, over the bar, h bits that differ)."""
+    import numpy as np
+
+    import oracle
+
+    def dec(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+
+    kind = job[0]
+    t0 = time.perf_counter()
+    if kind == "add":
+        _, x, r, w, eps, out, h = job
+        dt = "bf16" if x.dtype == np.uint16 else "f32"
+        want_out, want_h = oracle.add_rms_norm(dec(x), dec(r), dec(w), eps, dt)
+        t = time.perf_counter() - t0
+        mu, over = _compare(out, want_out)
+        if dt == "bf16":
+            hb = (np.asarray(want_h, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            hbad = int(np.count_nonzero(hb != h))
+        else:
+            hbad = int(np.count_nonzero(np.asarray(want_h, np.float64).astype(np.float32).view(np.uint32)
+                                        != h.view(np.uint32)))
+        return t, mu, over, hbad
+    if kind == "ln":
+        _, x, w, b, eps, out = job
+        want = oracle.layer_norm(dec(x), dec(w), dec(b), eps, "bf16" if x.dtype == np.uint16 else "f32")
+        t = time.perf_counter() - t0
+        return (t, *_compare(out, want), 0)
+    if kind == "rope":
+        _, x, w, (eps, dims, trad, base, scale, offset, cache), out = job
+        cache_in = np.zeros(out.shape) if cache else None
+        want = oracle.norm_rope(dec(x), dec(w), normalize=True, eps=eps, dims=dims,
+                                traditional=trad, base=base, scale=scale, offset=offset,
+                                forward=True, dtype="bf16", cache=cache_in)
+        t = time.perf_counter() - t0
+        return (t, *_compare(out, want), 0)
+    raise ValueError(kind)
+
+
+def oracle_parity(jobs):
+    """The oracle over every chunk in a spawn process pool over the host's cores (at most
+    16), each chunk compared with the GPU's output. Returns the suite fields."""
+    import multiprocessing as mp
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_config_oracle_job, jobs[:1])  # start-up and imports, untimed
+        t0 = time.perf_counter()
+        res = pool.map(_config_oracle_job, jobs, chunksize=1)
+        wall = time.perf_counter() - t0
+    return {"parity_max_ulp": max(r[1] for r in res), "parity_over_tol": sum(r[2] for r in res),
+            "h_bits_differ": sum(r[3] for r in res), "oracle_s": round(wall, 3),
+            "oracle_cpu_s": round(sum(r[0] for r in res), 2), "oracle_cores": cores}
+
+
+def traffic_entry(cid):
+    """Stored per-config counter figures for the current library sources, else None."""
+    try:
+        with open(SUITE_TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("library_source_hash") != library_source_hash():
+        return None
+    return t.get("cases", {}).get(cid)
+
+
+def run_configs(args, nrm, torch, workloads, n_sets, calls, traffic):
+    """One JSON line per synthetic configuration (stderr) with the measurement fields: GPU
+    time from a captured HIP graph (median of 10 replays, rotating buffer sets under 512 MB),
+    GB/s, % of peak, rows/s, the 16-byte copy of the same bytes (and, for add-RMSNorm, the
+    two-into-two copy), HBM fetch / write MB from the stored counter summary, and the oracle
+    over the whole workload in the same run: its time, cores, GB/s, and the parity of this
+    run's own output (largest ulp distance, elements over the bar, h bits that differ)."""
+
+    def copy_gbps(nbytes, two):
+        q = (nbytes // (4 if two else 2)) // 16 * 16
+        k = n_sets(nbytes)
+        if two:
+            bufs = [[torch.ones(q, dtype=torch.uint8, device="cuda") for _ in range(4)] for _ in range(k)]
+            fn = lambda i: nrm.bench_copy2(*bufs[i % k])
+            moved = 4 * q
+        else:
+            bufs = [[torch.ones(q, dtype=torch.uint8, device="cuda") for _ in range(2)] for _ in range(k)]
+            fn = lambda i: nrm.bench_copy(*bufs[i % k])
+            moved = 2 * q
+        avg = statistics.median(time_graph(fn, calls(nbytes)))
+        del bufs
+        return moved / (avg * 1e-3) / 1e9
+
+    for cid in CONFIG_IDS:
+        case = build_case(cid, nrm, torch, workloads, n_sets)
+        nbytes = case["bytes"]
+        per = time_graph(case["call"], calls(nbytes))
+        avg = statistics.median(per)
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        line = {"cfg": cid, "op": case["op"], "dtype": case["dtype"], "shape": case["shape"],
+                "bytes": nbytes, "gpu_us_median": round(avg * 1e3, 3),
+                "gpu_us_min": round(min(per) * 1e3, 3),
+                "timing": "HIP graph of back-to-back calls, median of 10 replays",
+                "gpu_GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 2),
+                "rows_per_s": round(case["rows"] / (avg * 1e-3), 1),
+                "copy_ceiling_GBps": round(copy_gbps(nbytes, False), 1)}
+        if case["copy2"]:
+            line["copy2_ceiling_GBps"] = round(copy_gbps(nbytes, True), 1)
+        t = traffic(cid)
+        line["fetch_MB"] = t["fetch_MB"] if t else None
+        line["write_MB"] = t["write_MB"] if t else None
+        if not args.no_cpu_baseline:
+            par = oracle_parity(case["jobs"]())
+            par["oracle_GBps"] = round(nbytes / par["oracle_s"] / 1e9, 4)
+            line.update(par)
+        print(json.dumps(line), file=sys.stderr, flush=True)
+        del case
         torch.cuda.empty_cache()
+
+
+def counter_run(args):
+    """For rocprofv3 (kernel trace, or one --pmc counter per run): the calibration copy, then
+    every configuration and one workload per other operation, each called --counter-calls
+    times back to back (one synchronisation per workload), in CONFIG_IDS + NEXT_IDS order.
+    --summarize-configs attributes the dispatches by that order."""
+    import torch
+
+    import transformer_row_wise_amd as nrm
+    import workloads
+
+    nrm.load()
+    n = args.counter_calls
+    src = torch.ones(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        nrm.bench_copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+    for cid in CONFIG_IDS + NEXT_IDS:
+        print(f"# counters: {cid}", file=sys.stderr, flush=True)
+        case = build_case(cid, nrm, torch, workloads, lambda nb: 1)
+        for i in range(n):
+            case["call"](i)
+        torch.cuda.synchronize()
+        del case
+        torch.cuda.empty_cache()
+
+
+CONFIG_CMDS = [
+    "rocprofv3 --kernel-trace -d gpurun_out/cfg_trace -o trace -- python3 bench.py --counters "
+    "--counter-calls 20",
+    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/cfg_fetch -o fetch -- python3 bench.py --counters",
+    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/cfg_write -o write -- python3 bench.py --counters",
+    "python3 bench.py --summarize-configs gpurun_out/cfg_trace/trace_results.db "
+    "gpurun_out/cfg_fetch/fetch_results.db gpurun_out/cfg_write/write_results.db",
+]
+
+
+def _dispatches(db, counter=None):
+    """The library's kernel dispatches of a rocpd database in dispatch order: (name, duration
+    us, vgprs, accum vgprs, lds bytes, scratch bytes, workgroup size) from a kernel trace, or
+    (name, counter value) from a counter run."""
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    if counter is None:
+        q = ("select name, duration, vgpr_count, accum_vgpr_count, lds_size, scratch_size, "
+             "workgroup_x * workgroup_y * workgroup_z from kernels order by dispatch_id")
+        rows = [(r[0], r[1] / 1000.0, *r[2:]) for r in con.execute(q)]
+    else:
+        q = ("select kernel_name, sum(value) from counters_collection where counter_name = ? "
+             "group by dispatch_id order by dispatch_id")
+        rows = list(con.execute(q, (counter,)))
+    con.close()
+    return [r for r in rows if "nrm::" in r[0]]
+
+
+def summarize_configs(trace_db, fetch_db, write_db):
+    """Per-configuration kernel time, registers, occupancy and HBM bytes (FETCH_SIZE and
+    WRITE_SIZE in KiB per dispatch, scaled by what they read for the calibration copy), to
+    profiles/traffic_suite_configs.json and profiles/suite_configs.md."""
+    import re
+
+    tr = _dispatches(trace_db)
+    fe = _dispatches(fetch_db, "FETCH_SIZE")
+    wr = _dispatches(write_db, "WRITE_SIZE")
+
+    per_call = 1 + sum(DISPATCHES_PER_CALL.get(c, 1) for c in CONFIG_IDS + NEXT_IDS)
+
+    def split(rows):
+        """Dispatches in run order -> {case: [per-call lists of dispatches]}."""
+        calls = len(rows) // per_call
+        if calls * per_call != len(rows):
+            raise SystemExit(f"{len(rows)} dispatches is not a multiple of {per_call}: the run "
+                             "and CONFIG_IDS + NEXT_IDS differ")
+        out, i = {"cal": rows[:calls]}, calls
+        for cid in CONFIG_IDS + NEXT_IDS:
+            nd = DISPATCHES_PER_CALL.get(cid, 1)
+            out[cid] = [rows[i + c * nd:i + (c + 1) * nd] for c in range(calls)]
+            i += nd * calls
+        return out
+
+    T, F, W = split(tr), split(fe), split(wr)
+    for name, *_ in T["cal"] + F["cal"] + W["cal"]:
+        assert "copy16_kernel" in name, name
+    cal_f = statistics.median(v for _, v in F["cal"])
+    cal_w = statistics.median(v for _, v in W["cal"])
+    scale_f, scale_w = CAL_BYTES / (cal_f * 1024), CAL_BYTES / (cal_w * 1024)
+
+    def short(n):
+        n = re.sub(r"\(nrm::\w+\)$", "", n.replace("void ", "").replace("nrm::", ""))
+        n = re.sub(r"\(.*\)$", "", n)
+        return n if len(n) < 60 else n[:57] + "..."
+
+    cases = {}
+    for cid in CONFIG_IDS + NEXT_IDS:
+        calls_t = T[cid]
+        main = [c[0] for c in calls_t]
+        us = statistics.median(sum(d[1] for d in c) for c in calls_t)
+        f_kib = statistics.median(sum(d[1] for d in c) for c in F[cid])
+        w_kib = statistics.median(sum(d[1] for d in c) for c in W[cid])
+        name, _, vg, avg, lds, scr, wg = main[0]
+        # rocprofv3 reports half the compiler's VGPR count on gfx950 (the compiler's 46, 54,
+        # 128 and 157 read as 24, 28, 64 and 80): the compiler's count is twice the field.
+        vgprs = 2 * (vg + avg)
+        waves_per_simd = min(8, 512 // max(8, (vgprs + 7) // 8 * 8))
+        cases[cid] = {"kernel": short(name), "dispatches_per_call": len(calls_t[0]),
+                      "us_median": round(us, 2), "vgprs": vgprs, "trace_vgpr_count": vg,
+                      "accum_vgprs": avg, "lds_bytes": lds, "scratch_bytes_per_lane": scr,
+                      "workgroup": wg, "waves_per_simd_by_vgprs": waves_per_simd,
+                      "fetch_MB": round(f_kib * 1024 * scale_f / 1e6, 2),
+                      "write_MB": round(w_kib * 1024 * scale_w / 1e6, 2)}
+    meta = _case_meta()
+    for cid, c in cases.items():
+        alg = meta[cid]["bytes"]
+        c["algorithmic_MB"] = round(alg / 1e6, 2)
+        c["traffic_over_algorithmic"] = round((c["fetch_MB"] + c["write_MB"]) * 1e6 / alg, 4)
+        c["GBps_trace"] = round(alg / (c["us_median"] * 1e-6) / 1e9, 1)
+        c["pct_peak_trace"] = round(100 * alg / (c["us_median"] * 1e-6) / 8e12, 1)
+        c["op"] = meta[cid]["op"]
+        c["shape"] = meta[cid]["shape"]
+    summary = {"library_source_hash": library_source_hash(), "fetch_scale": scale_f,
+               "write_scale": scale_w, "calibration_bytes_each_way": CAL_BYTES,
+               "commands": CONFIG_CMDS, "cases": cases}
+    with open(SUITE_TRAFFIC_FILE, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    L = ["# Every configuration on one MI355X: kernel time, registers and HBM traffic", "",
+         "`bench.py --counters` calls each synthetic configuration (1-5d) and one workload of "
+         "each other operation (6a-9e) eagerly, one call at a time; a kernel trace (20 calls "
+         "each) gives the time and the registers, and two counter runs (3 calls each) give "
+         "FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what it reads for a copy of "
+         f"{CAL_BYTES // 2**20} MiB each way (x{scale_f:.3f} fetch, x{scale_w:.3f} write). "
+         "The calls of a workload run back to back; workloads under 512 MB run here without "
+         "buffer rotation, so their repeat calls may hit the Infinity Cache (the counters "
+         "count L2 misses either way), and the suite's graph-timed lines remain the reference "
+         "for time.", "",
+         f"Library sources hash: `{summary['library_source_hash']}`.", "",
+         "From the repository root, with `TMPDIR=/tmp`:", "", "```", *CONFIG_CMDS, "```", "",
+         "VGPRs are the compiler's count (rocprofv3's vgpr_count field reads half of it on "
+         "gfx950); waves/SIMD is what that count allows (8 at most); scratch is bytes per lane "
+         "(register spills). Traffic above 1.0 is the backward's fp64 partial column sums "
+         "(16.8 MB per parameter at [16384, 8192], written and read once), register spills, or a second read "
+         "that missed the Infinity Cache (the cross-entropy gradient).", "",
+         "| cfg | op | kernel | us | % of 8 TB/s | VGPRs | waves/SIMD | scratch B/lane | fetch MB | "
+         "write MB | algorithmic MB | traffic / algorithmic |",
+         "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for cid, c in cases.items():
+        L.append(f"| {cid} | {c['op']} | `{c['kernel']}` | {c['us_median']:.2f} | "
+                 f"{c['pct_peak_trace']:.1f} | {c['vgprs']} | {c['waves_per_simd_by_vgprs']} | "
+                 f"{c['scratch_bytes_per_lane']} | {c['fetch_MB']:.1f} | {c['write_MB']:.1f} | "
+                 f"{c['algorithmic_MB']:.1f} | {c['traffic_over_algorithmic']:.3f} |")
+    with open(SUITE_MD, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
+def _case_meta():
+    """op, shape and algorithmic bytes of each case, without a GPU (the same formulas as
+    build_case)."""
+    m = {}
+    for cid, shape, es in (("1", (64, 512), 4), ("2", (4096, 4096), 2), ("5a", (16384, 8192), 2),
+                           ("5b", (16384, 8192), 4), ("5c", (65536, 5120), 2),
+                           ("5d", (65536, 5120), 4)):
+        m[cid] = {"op": "add_rms_norm", "shape": list(shape),
+                  "bytes": add_rms_bytes(shape[0], shape[1], es, es)}
+    m["3a"] = {"op": "layer_norm", "shape": [16384, 8192], "bytes": 2 * 16384 * 8192 * 2 + 2 * 8192 * 2}
+    m["3b"] = {"op": "layer_norm_no_affine", "shape": [16384, 8192], "bytes": 2 * 16384 * 8192 * 2}
+    for cid, op in (("4a", "norm_rope_half"), ("4b", "norm_rope_interleaved"),
+                    ("4c", "norm_rope_cache_half"), ("4d", "norm_rope_cache_interleaved")):
+        m[cid] = {"op": op, "shape": [8, 32, 512, 128], "bytes": 2 * 8 * 32 * 512 * 128 * 2 + 128 * 2}
+    m["6a"] = {"op": "rms_norm_vjp", "shape": [16384, 8192], "bytes": 3 * 16384 * 8192 * 2 + 8192 * 2 * 2}
+    m["7a"] = {"op": "layer_norm_vjp", "shape": [16384, 8192], "bytes": 3 * 16384 * 8192 * 2 + 8192 * 2 * 3}
+    m["8a"] = {"op": "rope_positions_llama3", "shape": [16384, 32, 8, 128],
+               "bytes": 2 * 16384 * 40 * 128 * 2 + 16384 * 8 + 64 * 4}
+    m["8b"] = {"op": "rope", "shape": [8, 32, 512, 128], "bytes": 2 * 8 * 32 * 512 * 128 * 2}
+    m["9a"] = {"op": "softmax", "shape": [16384, 8192], "bytes": 2 * 16384 * 8192 * 2}
+    m["9b"] = {"op": "causal_softmax", "shape": [256, 512, 512],
+               "bytes": 256 * (512 * 513 // 2) * 2 + 256 * 512 * 512 * 2}
+    rows, V = 4096, 128256
+    m["9c"] = {"op": "logsumexp", "shape": [rows, V], "bytes": rows * V * 2 + rows * 2}
+    m["9d"] = {"op": "cross_entropy", "shape": [rows, V], "bytes": rows * V * 2 + rows * 12}
+    m["9e"] = {"op": "cross_entropy_vjp", "shape": [rows, V], "bytes": 2 * rows * V * 2 + rows * 12}
+    return m
 
 
 def sweep(args):
@@ -816,7 +1328,14 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_DB")
     ap.add_argument("--summarize-suite-trace", metavar="TRACE_DB")
     ap.add_argument("--summarize-counters", metavar="PMC_DB")
+    ap.add_argument("--counters", action="store_true",
+                    help="eager calls of every configuration, for rocprofv3 runs")
+    ap.add_argument("--counter-calls", type=int, default=3)
+    ap.add_argument("--summarize-configs", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
+    if args.summarize_configs:
+        summarize_configs(*args.summarize_configs)
+        return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
         return 0
@@ -837,6 +1356,9 @@ def main():
         return 2
     if args.sweep:
         sweep(args)
+        return 0
+    if args.counters:
+        counter_run(args)
         return 0
     if not args.only:
         headline(args)
