@@ -16,19 +16,23 @@
 // attention factor of the scaled variants; 1 otherwise).
 //
 // Precision: the angle, theta and sin/cos are fp64 (an fp32 angle at positions in the
-// thousands is off by ~1e-4 rad). The rotation u*c - v*s runs in fp64 on u = x*w (exact in
-// fp64), so cancellation between the two products costs nothing; the fp32 row statistic only
-// scales the result. Features at index >= dims get x * rstd * w in fp32.
+// thousands is off by ~1e-4 rad). The rotation of a pair (x_i, x_j) with scales (w_i, w_j)
+// runs in fp64, every product exact or rounded once in fp64 (relative ~1e-16), so cancellation
+// between its two terms costs nothing at fp32 or bf16 output precision; the row statistic
+// (fp32 sum of squares, fp64 rstd) only scales the result. Features at index >= dims get
+// x * rstd * w in fp32.
 //
-// rope_fast: one block per (position l, chunk of rows at that position). The block first computes
-// (cos, sin) of every pair at its position into LDS, once, then each group of G lanes takes
-// rows: in half mode a lane loads the 16-byte chunk at feature j*VEC and its partner chunk
-// at dims/2 + j*VEC, so each rotated pair sits in one lane and no lane exchange is needed;
-// in traditional mode a chunk holds VEC/2 neighbouring pairs. The row's sum of squares is a
-// DPP reduction over the G lanes. Rows with the same l share the LDS table. A lane group
+// rope_fast: one block per (position l, chunk of rows at that position). The block first
+// computes, for every pair at its position, the rotation's coefficients with the scales
+// folded in (w_i cos, w_j sin, w_i sin, w_j cos) into LDS, once; then each group of G lanes
+// takes rows: in half mode a lane loads the 16-byte chunk at feature j*VEC and its partner
+// chunk at dims/2 + j*VEC, so each rotated pair sits in one lane and no lane exchange is
+// needed; in traditional mode a chunk holds VEC/2 neighbouring pairs. The row's sum of squares
+// is a DPP reduction over the G lanes. Rows with the same l share the LDS table. A lane group
 // issues the loads of R rows before computing any of them (memory-level parallelism: a
-// 128-wide bf16 row is only 256 bytes), with clamped, unconditional addresses; the table
-// is built while the first rows are in flight.
+// 128-wide bf16 row is only 256 bytes); the table is built while the first rows are in
+// flight, and every row's stores follow the whole step's arithmetic (storing each row as
+// soon as it is done measured 10% slower on NormRope [8, 32, 512, 128]).
 // rope_multi: rows of few heads at many positions (fewer than 256 rows per position, at least
 // 4096 positions, every feature rotated): a block takes several consecutive positions.
 // rope_generic: any D / dims / alignment, one wave per row, element at a time.
@@ -44,10 +48,13 @@ __device__ __forceinline__ int64_t rope_position(const RopeArgs& a, int64_t l) {
   return a.pos_i64 ? ((const int64_t*)a.positions)[l] : (int64_t)((const int32_t*)a.positions)[l];
 }
 
-// Frequency of pair t: 1 / freqs[t], or base^(-2t/dims).
+// Frequency of pair t: 1 / freqs[t], or base^(-2t/dims) as 2^(-2t/dims * log2(base)) with
+// log2(base) from the host. The exponent's rounding (|exponent| <= log2(base)) leaves theta a
+// relative error of a few 1e-15: an angle error of ~1e-10 radians at position 1e5. The
+// general fp64 pow would hold ~35 more registers beside the rows in flight.
 __device__ __forceinline__ double rope_theta(const RopeArgs& a, int t) {
   if (a.freqs != nullptr) return 1.0 / (double)a.freqs[t];
-  return pow((double)a.base, (double)(-2 * t) / (double)a.dims);
+  return exp2((double)(-2 * t) / (double)a.dims * a.log2_base);
 }
 
 // Element offset of row (bh, l) in the input, and in the output.
@@ -59,6 +66,12 @@ __device__ __forceinline__ const char* rope_in_row(const RopeArgs& a, int64_t bh
 __device__ __forceinline__ char* rope_out_row(const RopeArgs& a, int64_t bh, int64_t l, int esz) {
   if (bh < a.BH1) return (char*)a.out + (bh * a.o_sbh + (a.o_row0 + l) * a.o_sl) * a.D * esz;
   return (char*)a.out2 + ((bh - a.BH1) * a.o2_sbh + l * a.o2_sl) * a.D * esz;
+}
+
+// A global-memory address held as an integer, as a pointer that the compiler still knows to
+// be global (so that accesses through it are global, not flat, instructions).
+__device__ __forceinline__ const char* global_ptr(int64_t v) {
+  return (const char*)(const __attribute__((address_space(1))) char*)v;
 }
 
 }  // namespace
@@ -115,8 +128,12 @@ __device__ __forceinline__ void rope_sincos(double a, double* sn, double* cs) {
 // chunk per lane (interleaved rows whose half is not a whole number of chunks).
 enum RopeMode : int { M_HALF = 0, M_TRAD1 = 1, M_TRAD2 = 2 };
 
+// (cos, sin) table slot of pair p: one padding slot after every eight, so that the lanes of
+// a group (eight pairs apart in half mode) read different LDS banks.
+__device__ __forceinline__ int cs_slot(int p) { return p + (p >> 3); }
+
 template <bool BF16, int MODE, int G, int QC, int R>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QC == 0 ? 4 : 1)))
 rope_fast(RopeArgs a) {
   constexpr bool HALF = MODE == M_HALF;
   constexpr bool TWO = MODE != M_TRAD1;       // two chunks per lane
@@ -127,8 +144,10 @@ rope_fast(RopeArgs a) {
   constexpr int PAIRS = TWO ? V : V / 2;      // rotated pairs per lane
   constexpr int MAXP = G * PAIRS;             // pairs one group can hold
   constexpr int QN = QC > 0 ? QC : 1;
-  __shared__ double cs_c[MAXP];
-  __shared__ double cs_s[MAXP];
+  // Per pair p with features (i, j) (i < j) and scales (w_i, w_j): the rotation's products
+  // with the scales folded in, ab = (w_i cos, w_j sin) and cd = (w_i sin, w_j cos), sin signed
+  // for the direction, by cs_slot(p).
+  __shared__ double2 tab_ab[MAXP + MAXP / 8], tab_cd[MAXP + MAXP / 8];
 
   const int64_t l = blockIdx.x;
   const int64_t pos = rope_position(a, l);
@@ -140,16 +159,11 @@ rope_fast(RopeArgs a) {
   const bool has_pc = lj < npc;
   const bool norm = a.normalize != 0;
   const bool has_w = norm && a.w != nullptr;
+  const double inv_d = 1.0 / (double)a.D;
 
-  double c[PAIRS], s[PAIRS];
-  float wu[V], wv[V], wq[QN][V];
-#pragma unroll
-  for (int e = 0; e < PAIRS; ++e) { c[e] = 1.0; s[e] = 0.0; }
-#pragma unroll
-  for (int e = 0; e < V; ++e) { wu[e] = 1.f; wv[e] = 1.f; }
   // Chunk offsets (in elements) within a row. A lane without a rotated chunk (lj >= npc)
   // or without a pass-through chunk still loads a valid chunk of the row (clamped), so that
-  // every load is unconditional; it never stores it.
+  // a row's loads take no per-lane condition; it never stores it.
   const int off_u = min(lj, max(npc - 1, 0)) * V;
   const int off_v = TWO ? half + off_u : 0;
   int off_q[QN];
@@ -159,37 +173,45 @@ rope_fast(RopeArgs a) {
     has_q[q] = QC > 0 && lj + G * q < nqc;
     off_q[q] = a.dims + min(lj + G * q, max(nqc - 1, 0)) * V;
   }
-#pragma unroll
-  for (int q = 0; q < QN; ++q) {
-#pragma unroll
-    for (int e = 0; e < V; ++e) wq[q][e] = 1.f;
-  }
   const bool any_pc = npc > 0;
   const bool any_q = QC > 0 && nqc > 0;
 
+  // Row addresses at this position: row bh of tensor A at inA + bh sA, of tensor B at
+  // inB + bh sB (the offset of B's first row folded into inB), outputs likewise. A lane's rows
+  // in a step are RPB apart, so their addresses advance by uniform steps from the first one:
+  // one set of 64-bit multiplies (quarter rate) per step instead of one per row.
+  const int64_t rowb = (int64_t)a.D * ESZ;
+  const int64_t inA = (int64_t)a.x + l * a.x_sl * rowb, sA = a.x_sbh * rowb;
+  const int64_t inB = (int64_t)a.x2 + (l * a.x2_sl - a.BH1 * a.x2_sbh) * rowb, sB = a.x2_sbh * rowb;
+  const int64_t outA = (int64_t)a.out + (a.o_row0 + l) * a.o_sl * rowb, oA = a.o_sbh * rowb;
+  const int64_t outB = (int64_t)a.out2 + (l * a.o2_sl - a.BH1 * a.o2_sbh) * rowb, oB = a.o2_sbh * rowb;
+
   // Each step handles R rows per lane group: all their loads are issued first. The loads
-  // of the first step are issued before the (cos, sin) table of this position is built,
-  // outside the step loop, so that the table's latency overlaps them and its constants
-  // are not kept live across the loop.
+  // of the first step are issued before the (cos, sin) table of this position is built, so
+  // that the table's latency overlaps them. Rows past BH (uniform over a lane group) are
+  // neither loaded nor stored.
   const int64_t bh_blk = (int64_t)blockIdx.y * a.iters * RPB * R;
   u32x4 xu[R], xv[R], xq[R][QN];
-  int64_t bhr[R];
+  int64_t bh0 = 0;
   auto load_step = [&](int it) {
+    bh0 = bh_blk + (int64_t)it * R * RPB + wave * RPW + g;
+    int64_t pa = inA + bh0 * sA, pb = inB + bh0 * sB;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      bhr[r] = bh_blk + ((int64_t)it * R + r) * RPB + wave * RPW + g;
-      const int64_t bhc = bhr[r] < a.BH ? bhr[r] : a.BH - 1;
-      const char* xrow = rope_in_row(a, bhc, l, ESZ);
+    for (int r = 0; r < R; ++r, pa += RPB * sA, pb += RPB * sB) {
+      const int64_t bh = bh0 + r * RPB;
+      const char* xrow = global_ptr(bh < a.BH1 ? pa : pb);
       xu[r] = u32x4{0, 0, 0, 0};
       xv[r] = u32x4{0, 0, 0, 0};
-      if (any_pc) {
-        xu[r] = ld16_nt(xrow + off_u * ESZ);
-        if (TWO) xv[r] = ld16_nt(xrow + off_v * ESZ);
-      }
 #pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        xq[r][q] = u32x4{0, 0, 0, 0};
-        if (any_q) xq[r][q] = ld16_nt(xrow + (int64_t)off_q[q] * ESZ);
+      for (int q = 0; q < QN; ++q) xq[r][q] = u32x4{0, 0, 0, 0};
+      if (bh < a.BH) {
+        if (any_pc) {
+          xu[r] = ld16_nt(xrow + off_u * ESZ);
+          if (TWO) xv[r] = ld16_nt(xrow + off_v * ESZ);
+        }
+#pragma unroll
+        for (int q = 0; q < QN; ++q)
+          if (any_q) xq[r][q] = ld16_nt(xrow + (int64_t)off_q[q] * ESZ);
       }
     }
   };
@@ -199,45 +221,55 @@ rope_fast(RopeArgs a) {
     const double ang = ((double)a.scale * (double)pos) * theta;
     double sn, cs;
     rope_sincos(ang, &sn, &cs);
-    cs_c[t] = cs;
-    cs_s[t] = a.forward ? sn : -sn;
+    if (!a.forward) sn = -sn;
+    float wi[1] = {1.f}, wj[1] = {1.f};
+    if (has_w) {
+      load_param<BF16, 1>(a.w, a.w_f32, HALF ? t : 2 * t, wi);
+      load_param<BF16, 1>(a.w, a.w_f32, HALF ? t + half : 2 * t + 1, wj);
+    }
+    tab_ab[cs_slot(t)] = double2{(double)wi[0] * cs, (double)wj[0] * sn};
+    tab_cd[cs_slot(t)] = double2{(double)wi[0] * sn, (double)wj[0] * cs};
+  }
+  float wq[QN][V];
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) wq[q][e] = 1.f;
+    if (has_w && has_q[q]) load_param<BF16, V>(a.w, a.w_f32, off_q[q], wq[q]);
   }
   __syncthreads();
-  if (has_pc) {
-#pragma unroll
-    for (int e = 0; e < PAIRS; ++e) {
-      const int p = HALF ? lj * V + e
-                  : (e < V / 2 ? lj * (V / 2) + e : half / 2 + lj * (V / 2) + (e - V / 2));
-      c[e] = cs_c[p];
-      s[e] = cs_s[p];
-    }
-    if (has_w) {
-      load_param<BF16, V>(a.w, a.w_f32, off_u, wu);
-      if (TWO) load_param<BF16, V>(a.w, a.w_f32, off_v, wv);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < QN; ++q)
-    if (has_w && has_q[q]) load_param<BF16, V>(a.w, a.w_f32, off_q[q], wq[q]);
+
+  // Pair p of this lane's e-th rotated pair.
+  auto pair_of = [&](int e) {
+    return HALF ? lj * V + e
+                : (e < V / 2 ? lj * (V / 2) + e : half / 2 + lj * (V / 2) + (e - V / 2));
+  };
+  // Element e of a packed chunk as fp32.
+  auto elem = [](const u32x4& v, int e) {
+    if constexpr (BF16) return (e & 1) ? bf16hi(v[e >> 1]) : bf16lo(v[e >> 1]);
+    else return __builtin_bit_cast(float, (uint32_t)v[e]);
+  };
 
   for (int it = 0; it < a.iters; ++it) {
     if (it > 0) load_step(it);
+    // The rows' scales: rstd * mscale for the rotated features (rstd = 1 without the
+    // normalisation), from each row's fp32 sum of squares over all D features.
+    double rs[R];
+    float rstd_f[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const bool live = bhr[r] < a.BH;  // uniform over the group of G lanes that owns the row
-      char* orow = rope_out_row(a, live ? bhr[r] : 0, l, ESZ);
-      float fu[V], fv[V];
-      unpack<BF16>(xu[r], fu);
-      unpack<BF16>(xv[r], fv);
       double rstd = 1.0;
       if (norm) {
         float ss = 0.f;
         if (has_pc) {
+          float f[V];
+          unpack<BF16>(xu[r], f);
 #pragma unroll
-          for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fu[e], fu[e], ss);
+          for (int e = 0; e < V; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
           if (TWO) {
+            unpack<BF16>(xv[r], f);
 #pragma unroll
-            for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fv[e], fv[e], ss);
+            for (int e = 0; e < V; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
           }
         }
 #pragma unroll
@@ -249,46 +281,84 @@ rope_fast(RopeArgs a) {
             for (int e = 0; e < V; ++e) ss = __builtin_fmaf(fq[e], fq[e], ss);
           }
         }
-        rstd = rstd_f64((double)group_sum<G>(ss), a.D, a.eps);
+        rstd = rstd_f64_newton((double)group_sum<G>(ss), inv_d, a.eps);
       }
-      const double rs = rstd * (double)a.mscale;  // scale of the rotated features
-      if (live && has_pc) {
-        if constexpr (HALF) {
+      rs[r] = rstd * (double)a.mscale;
+      rstd_f[r] = (float)rstd;
+    }
+    // Rotation, pair by pair (two pairs at a time, whose results pack into one 32-bit
+    // word): each pair's folded products are read from LDS once and applied to the step's R
+    // rows, and the results replace the inputs in their registers. A pair (u, v) of scaled
+    // features becomes ((u ab.x - v ab.y) rs, (u cd.x + v cd.y) rs).
+    if (has_pc) {
+      if constexpr (HALF) {
 #pragma unroll
-          for (int e = 0; e < V; ++e) {
-            const double u = (double)fu[e] * (double)wu[e];
-            const double v = (double)fv[e] * (double)wv[e];
-            fu[e] = f64_to_f32((u * c[e] - v * s[e]) * rs);
-            fv[e] = f64_to_f32((u * s[e] + v * c[e]) * rs);
-          }
-          st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
-          st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
-        } else {
+        for (int e = 0; e < V; e += 2) {
+          const double2 ab0 = tab_ab[cs_slot(pair_of(e))], cd0 = tab_cd[cs_slot(pair_of(e))];
+          const double2 ab1 = tab_ab[cs_slot(pair_of(e + 1))], cd1 = tab_cd[cs_slot(pair_of(e + 1))];
 #pragma unroll
-          for (int e = 0; e < V / 2; ++e) {
-            const double u = (double)fu[2 * e] * (double)wu[2 * e];
-            const double v = (double)fu[2 * e + 1] * (double)wu[2 * e + 1];
-            fu[2 * e] = f64_to_f32((u * c[e] - v * s[e]) * rs);
-            fu[2 * e + 1] = f64_to_f32((u * s[e] + v * c[e]) * rs);
-            if constexpr (TWO) {
-              const double u2 = (double)fv[2 * e] * (double)wv[2 * e];
-              const double v2 = (double)fv[2 * e + 1] * (double)wv[2 * e + 1];
-              fv[2 * e] = f64_to_f32((u2 * c[V / 2 + e] - v2 * s[V / 2 + e]) * rs);
-              fv[2 * e + 1] = f64_to_f32((u2 * s[V / 2 + e] + v2 * c[V / 2 + e]) * rs);
+          for (int r = 0; r < R; ++r) {
+            const double u0 = elem(xu[r], e), v0 = elem(xv[r], e);
+            const double u1 = elem(xu[r], e + 1), v1 = elem(xv[r], e + 1);
+            float ou[2], ov[2];
+            ou[0] = f64_to_f32((u0 * ab0.x - v0 * ab0.y) * rs[r]);
+            ov[0] = f64_to_f32((u0 * cd0.x + v0 * cd0.y) * rs[r]);
+            ou[1] = f64_to_f32((u1 * ab1.x - v1 * ab1.y) * rs[r]);
+            ov[1] = f64_to_f32((u1 * cd1.x + v1 * cd1.y) * rs[r]);
+            if constexpr (BF16) {
+              xu[r][e >> 1] = pack_bf16x2(ou[0], ou[1]);
+              xv[r][e >> 1] = pack_bf16x2(ov[0], ov[1]);
+            } else {
+              xu[r][e] = __builtin_bit_cast(unsigned, ou[0]);
+              xu[r][e + 1] = __builtin_bit_cast(unsigned, ou[1]);
+              xv[r][e] = __builtin_bit_cast(unsigned, ov[0]);
+              xv[r][e + 1] = __builtin_bit_cast(unsigned, ov[1]);
             }
           }
-          st16_nt(orow + off_u * ESZ, pack<BF16>(fu));
-          if constexpr (TWO) st16_nt(orow + off_v * ESZ, pack<BF16>(fv));
+        }
+      } else {
+        // Neighbouring pairs (2e, 2e + 1) of chunk u (pairs 0 .. V/2 - 1 of the lane) and of
+        // chunk v (pairs V/2 .. V - 1).
+#pragma unroll
+        for (int c2 = 0; c2 < (TWO ? 2 : 1); ++c2) {
+#pragma unroll
+          for (int e = 0; e < V / 2; ++e) {
+            const int slot = cs_slot(pair_of(c2 * (V / 2) + e));
+            const double2 ab = tab_ab[slot], cd = tab_cd[slot];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              u32x4& xc = c2 ? xv[r] : xu[r];
+              const double u = elem(xc, 2 * e), v = elem(xc, 2 * e + 1);
+              const float o0 = f64_to_f32((u * ab.x - v * ab.y) * rs[r]);
+              const float o1 = f64_to_f32((u * cd.x + v * cd.y) * rs[r]);
+              if constexpr (BF16) {
+                xc[e] = pack_bf16x2(o0, o1);
+              } else {
+                xc[2 * e] = __builtin_bit_cast(unsigned, o0);
+                xc[2 * e + 1] = __builtin_bit_cast(unsigned, o1);
+              }
+            }
+          }
         }
       }
-      const float rstd_f = (float)rstd;
+    }
+    int64_t pa = outA + bh0 * oA, pb = outB + bh0 * oB;
+#pragma unroll
+    for (int r = 0; r < R; ++r, pa += RPB * oA, pb += RPB * oB) {
+      const int64_t bh = bh0 + r * RPB;
+      const bool live = bh < a.BH;
+      char* orow = (char*)global_ptr(bh < a.BH1 ? pa : pb);
+      if (live && has_pc) {
+        st16_nt(orow + off_u * ESZ, xu[r]);
+        if constexpr (TWO) st16_nt(orow + off_v * ESZ, xv[r]);
+      }
 #pragma unroll
       for (int q = 0; q < QN; ++q) {
         if (live && has_q[q]) {
           float fq[V];
           unpack<BF16>(xq[r][q], fq);
 #pragma unroll
-          for (int e = 0; e < V; ++e) fq[e] = norm ? (fq[e] * rstd_f) * wq[q][e] : fq[e];
+          for (int e = 0; e < V; ++e) fq[e] = norm ? (fq[e] * rstd_f[r]) * wq[q][e] : fq[e];
           st16_nt(orow + (int64_t)off_q[q] * ESZ, pack<BF16>(fq));
         }
       }
@@ -486,13 +556,10 @@ hipError_t go_fast(const RopeArgs& a0, hipStream_t stream) {
   RopeArgs a = a0;
   constexpr int RPB = 4 * (64 / G);
   const int64_t steps = (a.BH + (int64_t)RPB * R - 1) / ((int64_t)RPB * R);
-  // Enough blocks for about one full round on the chip (~1024 blocks of 256 threads),
-  // while each block's sin/cos table is shared by as many rows as possible. Rotation-only
-  // launches with four rows per lane group (157 VGPRs: 768 blocks resident) take one block
-  // per position instead, so that the grid fits one round (Rope [8,32,512,128] 16.1 ->
-  // 15.2 us; with the normalisation it measured slightly slower, so NormRope keeps the
-  // wider grid).
-  int64_t chunks = (R == 4 && !a.normalize) ? 1 : (1024 + a.L - 1) / a.L;
+  // Enough blocks for about one full round on the chip (~1024 blocks of 256 threads, four
+  // per compute unit at <= 128 VGPRs), while each block's sin/cos table is shared by as many
+  // rows as possible.
+  int64_t chunks = (1024 + a.L - 1) / a.L;
   if (chunks > steps) chunks = steps;
   if (chunks > 65535) chunks = 65535;
   if (chunks < 1) chunks = 1;
@@ -546,7 +613,9 @@ hipError_t go_multi(const RopeArgs& a, int64_t blocks, hipStream_t stream) {
 // The fast kernel applies when every chunk is a whole 16-byte vector: D, the rotated
 // chunks and the pass-through chunks are VEC-multiples and the arrays are 16-byte aligned.
 template <bool BF16>
-hipError_t launch_norm_rope(const RopeArgs& a, bool aligned16, hipStream_t stream) {
+hipError_t launch_norm_rope(const RopeArgs& a0, bool aligned16, hipStream_t stream) {
+  RopeArgs a = a0;
+  a.log2_base = std::log2((double)a0.base);
   constexpr int V = Fmt<BF16>::VEC;
   const int half = a.dims / 2;
   const bool chunks_ok = aligned16 && a.D % V == 0 && a.dims % V == 0 &&
