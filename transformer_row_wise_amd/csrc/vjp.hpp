@@ -327,7 +327,12 @@ vjp_rows(VjpArgs a) {
   // their fp64 conversions (16 registers) across the loop, which spilled it to scratch.
   // With 16 elements per thread w is read again (an L2 hit) at each use; at ragged widths
   // with fewer, an opaque copy at each use makes it convert them again (8 instructions a
-  // row; at whole-wave widths holding them measured faster).
+  // row; at whole-wave widths holding them measured faster). LayerNorm's outputs convert w
+  // as well, and it takes the opaque copy for bf16 rows at up to 8 elements per thread (spills
+  // 47 registers -> 7; [16384, 4096] 110 -> 104 us) and fp32 rows at 16 ([8192, 16384]
+  // 690 -> 546 us); bf16 rows at 16 and fp32 rows at up to 8 measured slower with it.
+  constexpr bool OPAQUE_W = (PK == PK_F32 && !EXACT) ||
+                            (OP == VJP_LN && PK != PK_NONE && (BF16 == (NV * V < 16)));
   auto wuse = [&](int k, float (&wl)[V]) {
     if constexpr (PK == PK_F32 && NV * V >= 16) {
       load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wl);
@@ -336,7 +341,7 @@ vjp_rows(VjpArgs a) {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       wl[e] = wv[k][e];
-      if constexpr (PK == PK_F32 && !EXACT) __asm__ volatile("" : "+v"(wl[e]));
+      if constexpr (OPAQUE_W) __asm__ volatile("" : "+v"(wl[e]));
     }
   };
 
@@ -472,7 +477,10 @@ vjp_rows(VjpArgs a) {
     // output arithmetic instead of stalling every wave of the block. The loop is unrolled
     // by R so that each buffer keeps its registers: copying a buffer that is still being
     // loaded would wait for the load.
-    constexpr int R = OP == VJP_LN && (PK == PK_F32 || !EXACT) ? 3 : 4;
+    // LayerNorm keeps three rows in flight where a fourth buffer spilled: bf16 rows
+    // ([65536, 1024] 115 -> 107 us at three), fp32 parameters beside bf16 data, ragged widths.
+    // fp32 rows at whole widths keep four ([16384, 4096] 144 us, 149 at three).
+    constexpr int R = OP == VJP_LN && (BF16 || PK == PK_F32 || !EXACT) ? 3 : 4;
     u32x4 xs[R][NV], gs[R][NV];
     Piv ps[R];
 #pragma unroll
