@@ -520,33 +520,42 @@ row_ln_pair(RowArgs a) {
   }
   team_sum4(ds, red4, 0, nw);
   const double n = (double)a.hidden, inv_n = a.inv_n;
+  double mu[2], rstd[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    if (r == 1 && !live1) break;
     double q = ds[2 * r] * inv_n;
     q = __builtin_fma(__builtin_fma(-q, n, ds[2 * r]), inv_n, q);
-    const double mu = piv[r] + q;
+    mu[r] = piv[r] + q;
     const double v0 = ds[2 * r + 1] * inv_n - q * q;
     const double var = v0 < 0.0 ? 0.0 : v0;
-    const double rstd = rsqrt_row(var + (double)a.eps);
+    rstd[r] = rsqrt_row(var + (double)a.eps);
+  }
+  // Chunk by chunk, both rows: a chunk's w and b are widened to fp64 once for the pair.
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
+  for (int k = 0; k < NV; ++k) {
+    float wf[V], bf[V];
+    if constexpr (LN_PACKED) {
+      u32x4 wr = wpk[k], br = bpk[k];
+      __asm__ volatile("" : "+v"(wr), "+v"(br));  // widen here, not at the load
+      unpack<true>(wr, wf);
+      unpack<true>(br, bf);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) wf[e] = wv[k][e], bf[e] = bv[k][e];
+    }
+    double wd[V], bd[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) wd[e] = (double)wf[e], bd[e] = (double)bf[e];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r == 1 && !live1) break;
       u32x4 xr = xv[r][k];
       __asm__ volatile("" : "+v"(xr));  // widen again rather than hold fp64 copies
-      float f[V], wf[V], bf[V];
+      float f[V];
       unpack<BF16>(xr, f);
-      if constexpr (LN_PACKED) {
-        u32x4 wr = wpk[k], br = bpk[k];
-        __asm__ volatile("" : "+v"(wr), "+v"(br));  // widen here, not at the load
-        unpack<true>(wr, wf);
-        unpack<true>(br, bf);
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) wf[e] = wv[k][e], bf[e] = bv[k][e];
-      }
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
+        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu[r]) * rstd[r], wd[e], bd[e]));
       if (ok[k]) st16_nt((char*)a.out + base[r] + (int64_t)jj[k] * 16, pack<BF16>(f));
     }
   }
