@@ -249,9 +249,9 @@ size_t nrm_norm_vjp_workspace_bytes(int64_t rows, int64_t hidden, int layer_norm
  * Source: nuvec-core 0.5.0 fast::FastOp, variant RmsNormVjp, inputs (x, w, g), the gradients
  * of RmsNorm for x and w; eps an f32. Per row, with r = 1 / sqrt(sum(x^2) / D + eps):
  *   dx = r * g * w - x * r^3 * sum(g * w * x) / D,      dw = sum over rows of g * x * r.
- * Row sums accumulate in fp32; r, the per-element dx and the dw column sums are evaluated in
- * fp64 (dx is a difference that can cancel), so each result is within one unit of the last
- * place of the exact value. dw is the same bits on every run (fixed summation order).
+ * Row sums accumulate in fp64, as do r, the per-element dx and the dw column sums (dx is a
+ * difference that can cancel), so each result is within one unit of the last place of the
+ * exact value. dw is the same bits on every run (fixed summation order).
  *
  *   x, g       [rows, hidden] dtype, inputs
  *   w          [hidden] w_dtype, or NULL (= 1)

@@ -7,7 +7,8 @@
 //
 // Shapes of the same arithmetic:
 //   row_block               one block of up to 1024 threads per row, NV 16-byte chunks per
-//                           thread in registers (the default for rows of 129 to 4096 chunks);
+//                           thread in registers (the default for rows of 129 to 8192 chunks;
+//                           LayerNorm up to 4096, 2048 with fp32 w beside bf16 x);
 //   row_team                the same with a team of 4 .. 64 lanes per row and 256 / team
 //                           rows per block (rows of up to 128 chunks);
 //   row_ln_pair,            LayerNorm (with w or b) and RMSNorm (with fp32 w) as row_block

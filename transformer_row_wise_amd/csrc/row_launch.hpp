@@ -146,8 +146,12 @@ hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t st
   if (a.w == nullptr)
     return exact ? go_rowblock<BF16, OP, NV, PK_NONE, true>(a, threads, stream)
                  : go_rowblock<BF16, OP, NV, PK_NONE, false>(a, threads, stream);
-  // (LayerNorm with fp32 parameters beside bf16 data never takes more than two chunks.)
-  if constexpr (BF16 && !(OP == OP_LN && NV > 2)) {
+  // (LayerNorm with fp32 parameters beside bf16 data never takes more than two chunks, and
+  // bf16 rows with fp32 w stop at six: try_rowblock does not come here with them, and those
+  // kernels are not instantiated.)
+  if constexpr (BF16 && ((OP == OP_LN && NV > 2) || NV == 8)) {
+    if (a.w_f32) return hipErrorInvalidValue;
+  } else if constexpr (BF16) {
     if (a.w_f32)
       return exact ? go_rowblock<BF16, OP, NV, PK_F32, true>(a, threads, stream)
                    : go_rowblock<BF16, OP, NV, PK_F32, false>(a, threads, stream);
