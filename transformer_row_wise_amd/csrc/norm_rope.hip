@@ -173,8 +173,6 @@ rope_fast(RopeArgs a) {
     has_q[q] = QC > 0 && lj + G * q < nqc;
     off_q[q] = a.dims + min(lj + G * q, max(nqc - 1, 0)) * V;
   }
-  const bool any_pc = npc > 0;
-  const bool any_q = QC > 0 && nqc > 0;
 
   // Row addresses at this position: row bh of tensor A at inA + bh sA, of tensor B at
   // inB + bh sB (the offset of B's first row folded into inB), outputs likewise. A lane's rows
@@ -188,47 +186,70 @@ rope_fast(RopeArgs a) {
 
   // Each step handles R rows per lane group: all their loads are issued first. The loads
   // of the first step are issued before the (cos, sin) table of this position is built, so
-  // that the table's latency overlaps them. Rows past BH (uniform over a lane group) are
-  // neither loaded nor stored.
+  // that the table's latency overlaps them.
   const int64_t bh_blk = (int64_t)blockIdx.y * a.iters * RPB * R;
   u32x4 xu[R], xv[R], xq[R][QN];
   int64_t bh0 = 0;
+  // Rows past BH (uniform over a lane group) load the last row instead, so that every load
+  // is unconditional and the compiler's waits for them stay exact; they store nothing.
+  const int64_t last = a.BH - 1;
+  const int64_t p_last = last < a.BH1 ? inA + last * sA : inB + last * sB;
   auto load_step = [&](int it) {
     bh0 = bh_blk + (int64_t)it * R * RPB + wave * RPW + g;
     int64_t pa = inA + bh0 * sA, pb = inB + bh0 * sB;
 #pragma unroll
     for (int r = 0; r < R; ++r, pa += RPB * sA, pb += RPB * sB) {
       const int64_t bh = bh0 + r * RPB;
-      const char* xrow = global_ptr(bh < a.BH1 ? pa : pb);
-      xu[r] = u32x4{0, 0, 0, 0};
-      xv[r] = u32x4{0, 0, 0, 0};
+      const char* xrow = global_ptr(bh >= a.BH ? p_last : bh < a.BH1 ? pa : pb);
+      xu[r] = ld16_nt(xrow + off_u * ESZ);
+      xv[r] = TWO ? ld16_nt(xrow + off_v * ESZ) : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int q = 0; q < QN; ++q) xq[r][q] = u32x4{0, 0, 0, 0};
-      if (bh < a.BH) {
-        if (any_pc) {
-          xu[r] = ld16_nt(xrow + off_u * ESZ);
-          if (TWO) xv[r] = ld16_nt(xrow + off_v * ESZ);
-        }
-#pragma unroll
-        for (int q = 0; q < QN; ++q)
-          if (any_q) xq[r][q] = ld16_nt(xrow + (int64_t)off_q[q] * ESZ);
-      }
+      for (int q = 0; q < QN; ++q)
+        xq[r][q] = QC > 0 ? ld16_nt(xrow + (int64_t)off_q[q] * ESZ) : u32x4{0, 0, 0, 0};
     }
   };
+  // The scales and freqs entry of this thread's first table pair are loaded (the scales as
+  // raw 32-bit words, widened only when used) before the rows: loads return in issue order,
+  // so the table waits for them alone, not for the rows issued behind them. Only the waves
+  // that hold table pairs load them (a lane past the table reads entry 0), and only what
+  // the launch has (w, freqs).
+  const bool w32 = !BF16 || a.w_f32;
+  auto scale_word = [&](int i) {  // the word holding w[i]
+    return *(const uint32_t*)((const char*)a.w + (w32 ? 4 * (int64_t)i : (2 * (int64_t)i & ~3)));
+  };
+  auto scale_of = [&](uint32_t word, int i) {
+    if (!has_w) return 1.f;
+    if (w32) return __builtin_bit_cast(float, word);
+    return (i & 1) ? bf16hi(word) : bf16lo(word);
+  };
+  const int t0 = threadIdx.x;
+  const bool tab_wave = __builtin_amdgcn_readfirstlane(wave) * 64 < half;
+  const int tc = t0 < half ? t0 : 0;
+  uint32_t wi0 = 0u, wj0 = 0u;
+  float fr0 = 0.f;
+  if (tab_wave && has_w) {
+    wi0 = scale_word(HALF ? tc : 2 * tc);
+    wj0 = scale_word(HALF ? tc + half : 2 * tc + 1);
+  }
+  if (tab_wave && a.freqs != nullptr) fr0 = a.freqs[tc];
   load_step(0);
-  for (int t = threadIdx.x; t < half; t += 256) {
-    const double theta = rope_theta(a, t);
+  // Pair t's coefficients from its scale words and freqs entry. The first pair of each thread
+  // takes the words loaded above, outside any loop, so that its waits cover those loads only.
+  auto build = [&](int t, uint32_t wiw, uint32_t wjw, float fr) {
+    const double theta = a.freqs != nullptr ? 1.0 / (double)fr : rope_theta(a, t);
     const double ang = ((double)a.scale * (double)pos) * theta;
     double sn, cs;
     rope_sincos(ang, &sn, &cs);
     if (!a.forward) sn = -sn;
-    float wi[1] = {1.f}, wj[1] = {1.f};
-    if (has_w) {
-      load_param<BF16, 1>(a.w, a.w_f32, HALF ? t : 2 * t, wi);
-      load_param<BF16, 1>(a.w, a.w_f32, HALF ? t + half : 2 * t + 1, wj);
-    }
-    tab_ab[cs_slot(t)] = double2{(double)wi[0] * cs, (double)wj[0] * sn};
-    tab_cd[cs_slot(t)] = double2{(double)wi[0] * sn, (double)wj[0] * cs};
+    const double wi = scale_of(wiw, HALF ? t : 2 * t), wj = scale_of(wjw, HALF ? t + half : 2 * t + 1);
+    tab_ab[cs_slot(t)] = double2{wi * cs, wj * sn};
+    tab_cd[cs_slot(t)] = double2{wi * sn, wj * cs};
+  };
+  if (t0 < half) build(t0, wi0, wj0, fr0);
+  for (int t = t0 + 256; t < half; t += 256) {
+    const uint32_t wiw = has_w ? scale_word(HALF ? t : 2 * t) : 0u;
+    const uint32_t wjw = has_w ? scale_word(HALF ? t + half : 2 * t + 1) : 0u;
+    build(t, wiw, wjw, a.freqs != nullptr ? a.freqs[t] : 0.f);
   }
   float wq[QN][V];
 #pragma unroll
