@@ -245,6 +245,10 @@ rope_fast(RopeArgs a) {
     tab_ab[cs_slot(t)] = double2{wi * cs, wj * sn};
     tab_cd[cs_slot(t)] = double2{wi * sn, wj * cs};
   };
+  // A table that loads nothing (rotation only, base frequencies) is built after the rows have
+  // arrived: measured faster for that case (Rope [8, 32, 512, 128] bf16 14.7 -> 13.2 us),
+  // while with scales building it under the rows' loads is (NormRope 15.1 -> 14.3 us).
+  if (!has_w && a.freqs == nullptr) __builtin_amdgcn_s_waitcnt(0);
   if (t0 < half) build(t0, wi0, wj0, fr0);
   for (int t = t0 + 256; t < half; t += 256) {
     const uint32_t wiw = has_w ? scale_word(HALF ? t : 2 * t) : 0u;
