@@ -1175,8 +1175,9 @@ def summarize_trace(trace_db):
     alg = add_rms_bytes(ROWS, HIDDEN, 2, 2)
     L = ["# add-RMSNorm bf16 [16384, 8192] on one MI355X: kernel trace and HBM traffic", "",
          "Workload: x, r Student-t(3) with 1% of rows x1e3, w ~ N(1, 0.1) bf16, eps 1e-6. "
-         "`bench.py --profile` runs the headline kernel (1000 warm-up + 100 timed calls) and "
-         "then the 16-byte copy of the same byte count.", "",
+         "`bench.py --profile` first runs the two copy ceilings over the same byte count (the "
+         "16-byte copy, then the two-into-two copy; they also bring the clocks up), then the "
+         "headline kernel (1000 warm-up + 100 timed calls).", "",
          f"Kernel sources hash (`bench.py` `kernel_source_hash`) of the counter runs: "
          f"`{t['kernel_source_hash']}`.", "",
          "## Kernel trace (`rocprofv3 --kernel-trace --stats`)", "",

@@ -220,6 +220,8 @@ ROPE_SHAPES = [
     (3, 5, 33, 128, 128),
     (2, 16, 33, 64, 64),     # 4-lane groups (bf16), 32 rows per position
     (1, 4, 9, 64, 32),       # 4-lane groups with pass-through chunks
+    (8, 32, 3, 128, 128),    # four rows per lane group, two positions per block, odd L
+    (4, 33, 5, 128, 96),     # the same with a partial last step and pass-through chunks
 ]
 
 
