@@ -1228,7 +1228,8 @@ SUITE_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_suite -o
                    "python3 bench.py --only vjp,rope,sm")
 SUITE_TRACE_MD = os.path.join(ROOT, "profiles", "suite_kernels_backward_rope_softmax.md")
 COUNTERS_CMD = ("rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE "
-                "-d gpurun_out/pmc_valu -o valu -- python3 bench.py --only fwd,vjp,sm")
+                "-d gpurun_out/pmc_valu -o valu -- python3 bench.py --only fwd,vjp,sm "
+                "--no-cpu-baseline")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "valu_issue_suite_kernels.md")
 
 
