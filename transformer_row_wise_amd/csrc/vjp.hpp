@@ -306,9 +306,16 @@ vjp_rows(VjpArgs a) {
     ok[k] = EXACT || j < nvec;
     jj[k] = EXACT ? j : min(j, nvec - 1);
   }
+  // bf16 w of LayerNorm rows at 16 elements per thread stays packed (8 registers rather than
+  // 16) and is widened at each use.
+  constexpr bool PACK_W = BF16 && PK == PK_SAME && OP == VJP_LN && NV * V >= 16;
   float wv[NV][V];
+  u32x4 wpk[NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+  for (int k = 0; k < NV; ++k) {
+    if constexpr (PACK_W) wpk[k] = ld16((const uint16_t*)a.w + (int64_t)jj[k] * V);
+    else load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+  }
   double accw[NV][V], accb[NV][V];
 #pragma unroll
   for (int k = 0; k < NV; ++k)
@@ -336,6 +343,12 @@ vjp_rows(VjpArgs a) {
   auto wuse = [&](int k, float (&wl)[V]) {
     if constexpr (PK == PK_F32 && NV * V >= 16) {
       load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wl);
+      return;
+    }
+    if constexpr (PACK_W) {
+      u32x4 wr = wpk[k];
+      __asm__ volatile("" : "+v"(wr));
+      unpack<true>(wr, wl);
       return;
     }
 #pragma unroll
@@ -379,10 +392,11 @@ vjp_rows(VjpArgs a) {
     for (int k = 0; k < NV; ++k) {
       if constexpr (EXACT) {
         if (ok[k]) {
-          float f[V], gf[V];
+          float f[V], gf[V], wl[V];
           unpack<BF16>(xv[k], f);
           unpack<BF16>(gv[k], gf);
-          vjp_accumulate<OP, V, XF>(f, gf, wv[k], ds, px, pd, AllOn{});
+          if constexpr (PACK_W) wuse(k, wl);
+          vjp_accumulate<OP, V, XF>(f, gf, PACK_W ? wl : wv[k], ds, px, pd, AllOn{});
         }
       } else {
         // A chunk past the row's end (a clamped duplicate) enters as zeros, which add
@@ -448,18 +462,23 @@ vjp_rows(VjpArgs a) {
     // Two chunks per thread and the column accumulators leave no registers for the ring
     // below: one buffer pair, the next row copied in after each row, and each row's
     // statistics, barrier and outputs in turn.
+    // LayerNorm at 16 elements per thread loads each row at the top of its own step instead
+    // (NOPF): the next row's buffers beside the current one's and the db column sums spilled
+    // ~60 registers.
+    constexpr bool NOPF = OP == VJP_LN && NV * V >= 16;
     u32x4 xa[NV], ga[NV];
     Piv pa{0.f, 0.f};
-    load_row(0, xa, ga, pa);
+    if constexpr (!NOPF) load_row(0, xa, ga, pa);
     for (int it = 0; it < iters; ++it) {
       u32x4 xb[NV], gb[NV];
       Piv pb{0.f, 0.f};
-      if (it + 1 < iters) load_row(it + 1, xb, gb, pb);
+      if constexpr (NOPF) load_row(it, xa, ga, pa);
+      else if (it + 1 < iters) load_row(it + 1, xb, gb, pb);
       const RowPiv rp = stats(it, xa, ga, pa);
       __syncthreads();
       const VjpRow s = scalars(sums_read(it, rp));
       outputs(it, xa, ga, s);
-      if (it + 1 < iters) {
+      if (!NOPF && it + 1 < iters) {
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
           xa[k] = xb[k];
