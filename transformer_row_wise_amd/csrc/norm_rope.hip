@@ -185,7 +185,7 @@ rope_fast(RopeArgs a) {
   const int64_t outB = (int64_t)a.out2 + (l * a.o2_sl - a.BH1 * a.o2_sbh) * rowb, oB = a.o2_sbh * rowb;
 
   // Each step handles R rows per lane group: all their loads are issued first. The loads
-  // of the first step are issued before the (cos, sin) table of this position is built, so
+  // of the first step are issued before the rotation table of this position is built, so
   // that the table's latency overlaps them.
   const int64_t bh_blk = (int64_t)blockIdx.y * a.iters * RPB * R;
   u32x4 xu[R], xv[R], xq[R][QN];
