@@ -89,12 +89,14 @@ def test_narrow_rows_many(nrm_lib, dt, hidden, wkind):
 @pytest.mark.parametrize("dt,wdt,hidden", [("bf16", "bf16", 8192), ("bf16", "bf16", 4000),
                                            ("bf16", "bf16", 6000), ("bf16", "f32", 2048),
                                            ("bf16", "f32", 1000), ("f32", "f32", 8192),
-                                           ("f32", "f32", 1000)])
+                                           ("f32", "f32", 1000), ("bf16", "f32", 20000),
+                                           ("f32", "f32", 20000)])
 @pytest.mark.parametrize("affine", ["wb", "w", "b"])
 def test_layer_norm_row_pairs(nrm_lib, dt, wdt, hidden, affine):
     """LayerNorm with w and / or b over 4096 rows or more: two rows per block (2, 3 or 4 chunks
     per thread, exact and ragged widths). 4097 rows: the last block's second row is past the
-    end. Compared on the first, middle and last rows."""
+    end. Compared on the first, middle and last rows. Width 20000 stays on one row per block
+    (fp32 parameters beside bf16 data at 4 chunks per thread, fp32 at 6)."""
     say(f"layer_norm row pairs rows=4097 hidden={hidden} {dt} w={wdt} {affine}")
     inp = workloads.row_inputs(4097, hidden, dt, seed=hidden + 17, x=("normal", 0.5, 2.0),
                                w=("normal", 1.0, 0.1), b=("normal", 0.0, 0.1), w_dtype=wdt,

@@ -27,6 +27,8 @@
 // w and b are small and come from L2.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace nrm {
@@ -286,9 +288,13 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
   // LayerNorm with bf16 w and b keeps them packed (8 registers per chunk instead of 16) and
   // widens them where the output uses them.
   constexpr bool LN_PACKED = OP == OP_LN && BF16 && PK == PK_SAME;
-  // Rows of more than 4 chunks per thread (RMS forms only) load w after the row's sum: x, r
-  // and a widened w of 8 chunks would not fit the 128 registers of a 1024-thread block.
-  constexpr bool W_LATE = OP != OP_LN && NV > 4;
+  // Rows of more than 4 chunks per thread load w after the row's sums: x, r and a widened w
+  // of 8 chunks would not fit the 128 registers of a 1024-thread block. LayerNorm loads w and
+  // b chunk by chunk where the output uses them from 4 chunks on: its 768- and 1024-thread
+  // rows then hold two blocks per CU instead of one (fp32 [2730, 12288] affine 61 -> 50 us).
+  // Without w, b (if any) is still loaded early: a test of b inside the output loop costs
+  // more than its registers.
+  constexpr bool W_LATE = OP == OP_LN ? PK != PK_NONE && NV >= 4 : NV > 4;
   float wv[NV][V];
   u32x4 wpk[NV];
   if constexpr (!W_LATE) {
@@ -355,11 +361,19 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     const bool has_b = a.b != nullptr;
     float bv[NV][V];
     u32x4 bpk[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
+    // Rows past 4 chunks, and rows of 4 with w, load b chunk by chunk in the output loop, one
+    // copy of which is compiled for rows with b and one for rows without, so that no test of
+    // b sits between a chunk's loads and its arithmetic.
+    constexpr bool B_LATE = W_LATE || NV > 4;
+    // Chunk k's w (when loaded late) and b (when hb).
+    auto load_wb = [&](int k, bool hb) {
+      if constexpr (W_LATE) {
+        if constexpr (LN_PACKED) wpk[k] = ld16((const uint16_t*)a.w + (int64_t)jj[k] * V);
+        else load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
+      }
       if constexpr (LN_PACKED) {
-        bpk[k] = has_b ? ld16((const uint16_t*)a.b + (int64_t)jj[k] * V) : u32x4{0u, 0u, 0u, 0u};
-      } else if (has_b) {
+        bpk[k] = hb ? ld16((const uint16_t*)a.b + (int64_t)jj[k] * V) : u32x4{0u, 0u, 0u, 0u};
+      } else if (hb) {
         // b has w's dtype; without w its kind is only known at run time.
         if constexpr (PK == PK_NONE) load_param<BF16, V>(a.b, a.w_f32, (int64_t)jj[k] * V, bv[k]);
         else load_pk<BF16, PK, V>(a.b, (int64_t)jj[k] * V, bv[k]);
@@ -367,6 +381,10 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < V; ++e) bv[k][e] = 0.f;
       }
+    };
+    if constexpr (!B_LATE) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) load_wb(k, has_b);
     }
     // A team's first lane holds the row's chunk 0; a block reads the row's first element
     // through the scalar cache.
@@ -406,25 +424,34 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     const double v0 = ds[1] * inv_n - q * q;
     const double var = v0 < 0.0 ? 0.0 : v0;
     const double rstd = rsqrt_row(var + (double)a.eps);
+    auto out_row = [&](auto hb) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      u32x4 xr = xv[k];
-      __asm__ volatile("" : "+v"(xr));  // widen again rather than hold fp64 copies
-      float f[V], wf[V], bf[V];
-      unpack<BF16>(xr, f);
-      if constexpr (LN_PACKED) {
-        u32x4 wr = wpk[k], br = bpk[k];
-        __asm__ volatile("" : "+v"(wr), "+v"(br));  // widen here, not at the load
-        unpack<true>(wr, wf);
-        unpack<true>(br, bf);
-      } else {
+      for (int k = 0; k < NV; ++k) {
+        if constexpr (B_LATE) load_wb(k, decltype(hb)::value);
+        u32x4 xr = xv[k];
+        __asm__ volatile("" : "+v"(xr));  // widen again rather than hold fp64 copies
+        float f[V], wf[V], bf[V];
+        unpack<BF16>(xr, f);
+        if constexpr (LN_PACKED) {
+          u32x4 wr = wpk[k], br = bpk[k];
+          __asm__ volatile("" : "+v"(wr), "+v"(br));  // widen here, not at the load
+          unpack<true>(wr, wf);
+          unpack<true>(br, bf);
+        } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) wf[e] = wv[k][e], bf[e] = bv[k][e];
+          for (int e = 0; e < V; ++e) wf[e] = wv[k][e], bf[e] = bv[k][e];
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
+        if (live && ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
       }
-#pragma unroll
-      for (int e = 0; e < V; ++e)
-        f[e] = f64_to_f32(__builtin_fma(((double)f[e] - mu) * rstd, (double)wf[e], (double)bf[e]));
-      if (live && ok[k]) st16_nt((char*)a.out + base + (int64_t)jj[k] * 16, pack<BF16>(f));
+    };
+    if constexpr (B_LATE) {
+      if (has_b) out_row(std::true_type{});
+      else out_row(std::false_type{});
+    } else {
+      out_row(std::true_type{});
     }
   }
 }

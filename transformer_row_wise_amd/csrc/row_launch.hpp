@@ -146,10 +146,10 @@ hipError_t rowblock_pk(const RowArgs& a, int threads, bool exact, hipStream_t st
   if (a.w == nullptr)
     return exact ? go_rowblock<BF16, OP, NV, PK_NONE, true>(a, threads, stream)
                  : go_rowblock<BF16, OP, NV, PK_NONE, false>(a, threads, stream);
-  // (LayerNorm with fp32 parameters beside bf16 data never takes more than two chunks, and
-  // bf16 rows with fp32 w stop at six: try_rowblock does not come here with them, and those
-  // kernels are not instantiated.)
-  if constexpr (BF16 && ((OP == OP_LN && NV > 2) || NV == 8)) {
+  // (LayerNorm with fp32 parameters beside bf16 data takes two chunks or at least four, and
+  // the RMS forms' bf16 rows with fp32 w stop at six: try_rowblock does not come here with
+  // the others, and those kernels are not instantiated.)
+  if constexpr (BF16 && (OP == OP_LN ? NV == 3 : NV == 8)) {
     if (a.w_f32) return hipErrorInvalidValue;
   } else if constexpr (BF16) {
     if (a.w_f32)
@@ -183,6 +183,8 @@ hipError_t lnpair_pk(const RowArgs& a, int threads, bool exact, hipStream_t stre
     if (a.w_f32)
       return exact ? go_lnpair<BF16, NV, PK_F32, true>(a, threads, stream)
                    : go_lnpair<BF16, NV, PK_F32, false>(a, threads, stream);
+  } else if constexpr (BF16) {
+    if (a.w_f32) return hipErrorInvalidValue;  // not instantiated; try_rowblock never asks
   }
   return exact ? go_lnpair<BF16, NV, PK_SAME, true>(a, threads, stream)
                : go_lnpair<BF16, NV, PK_SAME, false>(a, threads, stream);
@@ -208,13 +210,17 @@ hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* d
   const bool ln_wide = OP == OP_LN && !(BF16 && a.w_f32);
   int64_t nv = ln_wide ? std::min<int64_t>(4, std::max<int64_t>(2, (n + 255) / 256))
                        : std::max<int64_t>(2, (n + 1023) / 1024);
-  // RMS forms past 4096 chunks (16384 fp32 / 32768 bf16 values): 6 or 8 chunks per thread
-  // (the only counts instantiated above 4), up to 8192 chunks.
-  // bf16 rows with fp32 w stop at 6: eight widened fp32 w chunks spill at 8.
-  if (OP != OP_LN && nv > 4) nv = nv <= 6 ? 6 : 8;
-  if (nv == 8 && BF16 && a.w != nullptr && a.w_f32) return hipSuccess;
-  if (nv > (OP == OP_LN ? (ln_wide ? 4 : 2) : 8) || n > nv * 1024 || a.rows > kMaxGrid)
-    return hipSuccess;
+  // LayerNorm past 4096 chunks: as many per thread as 1024 threads need. With fp32
+  // parameters beside bf16 data, rows past 2048 chunks take at least four, the count from
+  // which w and b are loaded chunk by chunk after the row's sums.
+  if (ln_wide && n > 4096) nv = (n + 1023) / 1024;
+  if (OP == OP_LN && !ln_wide && nv > 2) nv = std::max<int64_t>(4, nv);
+  // Past 4096 chunks (16384 fp32 / 32768 bf16 values): 6 or 8 chunks per thread (the only
+  // counts instantiated above 4), up to 8192 chunks, w (and b) loaded after the row's sums.
+  // The RMS forms' bf16 rows with fp32 w stop at 6: eight widened fp32 w chunks spill at 8.
+  if (nv > 4) nv = nv <= 6 ? 6 : 8;
+  if (OP != OP_LN && nv == 8 && BF16 && a.w != nullptr && a.w_f32) return hipSuccess;
+  if (nv > 8 || n > nv * 1024 || a.rows > kMaxGrid) return hipSuccess;
   const int threads = (int)((((n + nv - 1) / nv) + 63) / 64 * 64);
   const bool exact = (int64_t)threads * nv == n;
   *done = true;
@@ -236,7 +242,9 @@ hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* d
     }
   }
   if constexpr (OP == OP_LN) {
-    if (a.rows >= 4096 && (a.w != nullptr || a.b != nullptr)) {
+    // (fp32 parameters beside bf16 data pair only at two chunks: lnpair_pk reads them as fp32
+    // there alone.)
+    if (a.rows >= 4096 && (a.w != nullptr || a.b != nullptr) && (ln_wide || nv == 2)) {
       switch (nv) {
         case 2: return lnpair_pk<BF16, 2>(a, threads, exact, stream);
         case 3: return lnpair_pk<BF16, 3>(a, threads, exact, stream);
@@ -250,12 +258,8 @@ hipError_t try_rowblock(const RowArgs& a, int64_t n, hipStream_t stream, bool* d
     case 2: return rowblock_pk<BF16, OP, 2>(a, threads, exact, stream);
     case 3: return rowblock_pk<BF16, OP, 3>(a, threads, exact, stream);
     case 4: return rowblock_pk<BF16, OP, 4>(a, threads, exact, stream);
-    case 6:
-      if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 6>(a, threads, exact, stream);
-      break;
-    case 8:
-      if constexpr (OP != OP_LN) return rowblock_pk<BF16, OP, 8>(a, threads, exact, stream);
-      break;
+    case 6: return rowblock_pk<BF16, OP, 6>(a, threads, exact, stream);
+    case 8: return rowblock_pk<BF16, OP, 8>(a, threads, exact, stream);
     default: break;
   }
   *done = false;
