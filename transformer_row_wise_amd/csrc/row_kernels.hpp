@@ -7,8 +7,8 @@
 //
 // Shapes of the same arithmetic:
 //   row_block               one block of up to 1024 threads per row, NV 16-byte chunks per
-//                           thread in registers (the default for rows of 129 to 8192 chunks;
-//                           LayerNorm up to 4096, 2048 with fp32 w beside bf16 x);
+//                           thread in registers (the default for rows of 129 to 8192 chunks,
+//                           and for the RMS forms' bf16 rows beside fp32 w up to 6144);
 //   row_team                the same with a team of 4 .. 64 lanes per row and 256 / team
 //                           rows per block (rows of up to 128 chunks);
 //   row_ln_pair,            LayerNorm (with w or b) and RMSNorm (with fp32 w) as row_block
@@ -288,13 +288,14 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
   // LayerNorm with bf16 w and b keeps them packed (8 registers per chunk instead of 16) and
   // widens them where the output uses them.
   constexpr bool LN_PACKED = OP == OP_LN && BF16 && PK == PK_SAME;
-  // Rows of more than 4 chunks per thread load w after the row's sums: x, r and a widened w
-  // of 8 chunks would not fit the 128 registers of a 1024-thread block. LayerNorm loads w and
-  // b chunk by chunk where the output uses them from 4 chunks on: its 768- and 1024-thread
-  // rows then hold two blocks per CU instead of one (fp32 [2730, 12288] affine 61 -> 50 us).
-  // Without w, b (if any) is still loaded early: a test of b inside the output loop costs
-  // more than its registers.
-  constexpr bool W_LATE = OP == OP_LN ? PK != PK_NONE && NV >= 4 : NV > 4;
+  // From 4 chunks per thread on, w is loaded after the row's sums, chunk by chunk where the
+  // output uses it: x, r and a widened w of 8 chunks would not fit the 128 registers of a
+  // 1024-thread block (add-RMSNorm bf16 [512, 65536] 55 -> 49 us), and at 4 the 768- and
+  // 1024-thread rows then hold two blocks per CU instead of one (LayerNorm fp32 [2730, 12288]
+  // affine 61 -> 50 us, RMSNorm bf16 [1024, 32768] 27.7 -> 25.7 us). The RMS forms at 6
+  // chunks load all of w right after the sum instead: chunk by chunk measured 2-7% slower
+  // there (add-RMSNorm fp32 [682, 24576]).
+  constexpr bool W_LATE = PK != PK_NONE && NV >= 4;
   float wv[NV][V];
   u32x4 wpk[NV];
   if constexpr (!W_LATE) {
@@ -334,7 +335,7 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     if constexpr (SUB > 0) ss = group_sum<SUB>(acc);
     else ss = block_row_sum(acc, red_f, nw);
     const float rstd = (float)rstd_f64((double)ss, a.hidden, a.eps);
-    if constexpr (W_LATE) {
+    if constexpr (W_LATE && NV == 6) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
     }
@@ -343,6 +344,7 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     // bf16 172.2-172.8 -> 170.5-171.4 us, [65536, 5120] fp32 921 -> 897 us).
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
+      if constexpr (W_LATE && NV != 6) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
       float f[V];
       unpack<BF16>(xv[k], f);
       if constexpr (OP == OP_ADD_RMS) {
@@ -357,7 +359,8 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     // element p (the row pivots of common.hpp), reduced together with one barrier; var =
     // sum((x-p)^2)/n - (mean - p)^2 loses at most log2(n) bits however large |mean| / sigma
     // is. A constant row gets x - p = 0 everywhere, so mean = p, var = 0 and x - mean = 0
-    // exactly: its output is exactly b. b (like w) is loaded before the row's statistics.
+    // exactly: its output is exactly b. Below 4 chunks per thread b (like w) is loaded
+    // before the row's statistics.
     const bool has_b = a.b != nullptr;
     float bv[NV][V];
     u32x4 bpk[NV];

@@ -4,15 +4,18 @@
 //   n <= 128                         row_team: teams of SUB = 4 .. 64 lanes (two chunks each,
 //                                    the smallest power of two that covers the row), 256 / SUB
 //                                    rows per block;
-//   n <= 8192 (LayerNorm: 4096,      row_block: one block of T threads per row, NV chunks per
-//   2048 with fp32 w beside bf16 x)  thread, NV = max(2, ceil(n / 1024)), 5 and 7 taken as
-//                                    6 and 8 (w loaded after the row's sum past 4) (LayerNorm:
-//                                    clamp(ceil(n / 256), 2, 4)), T = ceil(n / NV) rounded
-//                                    up to a wave (hidden 8192 bf16: 512 threads with 2
-//                                    chunks each, LayerNorm 256 threads with 4); LayerNorm
-//                                    with w or b, and RMSNorm with fp32 w, over 4096 rows
-//                                    or more: row_ln_pair / row_rms_pair, the same per
-//                                    thread for two rows per block;
+//   n <= 8192 (the RMS forms' bf16   row_block: one block of T threads per row, NV chunks per
+//   rows beside fp32 w: 6144)        thread, NV = max(2, ceil(n / 1024)), 5 and 7 taken as
+//                                    6 and 8 (LayerNorm: clamp(ceil(n / 256), 2, 4) up to
+//                                    4096 chunks; with fp32 w beside bf16 x 2 up to 2048,
+//                                    then at least 4), w (and b) loaded after the row's sums
+//                                    from 4 chunks on; T = ceil(n / NV) rounded up to a wave
+//                                    (hidden 8192 bf16: 512 threads with 2 chunks each,
+//                                    LayerNorm 256 threads with 4); LayerNorm with w or b,
+//                                    and RMSNorm with fp32 w, over 4096 rows or more at up
+//                                    to 4 chunks (LayerNorm beside bf16 x: 2):
+//                                    row_ln_pair / row_rms_pair, the same per thread for two
+//                                    rows per block;
 //   hidden or a base address not 16-byte granular, hidden <= 12288: row_elems, one block per
 //   row, K single elements per thread in registers (RMSNorm and LayerNorm);
 //   otherwise the looping kernel (16-byte chunks, or single elements).
