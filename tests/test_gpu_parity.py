@@ -264,15 +264,17 @@ def test_norm_rope_positions(nrm_lib, offset, scale):
             check_rope(nrm_lib, rp, traditional=True)
 
 
-@pytest.mark.parametrize("shape", [(1, 4, 4099, 128), (2, 3, 4100, 64), (1, 16, 4097, 64)],
+@pytest.mark.parametrize("shape", [(1, 4, 4099, 128), (2, 3, 4100, 64), (1, 16, 4097, 64),
+                                   (1, 4, 16411, 128), (1, 2, 8195, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("traditional", [False, True])
 @pytest.mark.parametrize("wkind", ["bf16", "f32", None])
 @pytest.mark.parametrize("cache", [False, True])
 def test_norm_rope_many_positions(nrm_lib, shape, traditional, wkind, cache):
     """Few heads at thousands of positions with every feature rotated: several positions
-    per block (lane groups of 4 or 8), normalised, with bf16, fp32 or no weight, into an
-    output or rows offset .. offset + L of a cache."""
+    per block (lane groups of 4, 8 or 16; 4 to 16 positions per block, the last block
+    partial), normalised, with bf16, fp32 or no weight, into an output or rows
+    offset .. offset + L of a cache."""
     B, H, L, D = shape
     say(f"norm_rope many positions {shape} trad={traditional} w={wkind} cache={cache}")
     rp = workloads.rope_inputs(B, H, L, D, "bf16", seed=L + D, w_dtype=wkind,

@@ -36,6 +36,8 @@
 // rope_multi: rows of few heads at many positions (fewer than 256 rows per position, at least
 // 4096 positions, every feature rotated): a block takes several consecutive positions.
 // rope_generic: any D / dims / alignment, one wave per row, element at a time.
+#include <algorithm>
+
 #include "rope.hpp"
 
 namespace nrm {
@@ -403,7 +405,7 @@ rope_fast(RopeArgs a) {
 // for term: without normalisation the features enter unscaled and the rotation is scaled by
 // mscale; with it (NORM, every feature rotated) the row's sum of squares is a lane exchange
 // inside the group, x w is rotated and the result scaled by rstd mscale.
-template <bool BF16, int MODE, int G, int PB, bool MS, bool NORM>
+template <bool BF16, int MODE, int G, bool MS, bool NORM>
 __global__ void __launch_bounds__(256)
 rope_multi(RopeArgs a) {
   constexpr bool HALF = MODE == M_HALF;
@@ -412,6 +414,7 @@ rope_multi(RopeArgs a) {
   constexpr int SPS = 256 / G;  // row slots per step
   constexpr int NR = 2;         // ring of steps
   extern __shared__ double2 cs_t[];  // [PB][half] (cos, sin)
+  const int PB = a.pb;
   const int half = a.dims / 2;
   const int lane = threadIdx.x & 63;
   const int g = threadIdx.x / G;  // lane group of the block
@@ -623,13 +626,13 @@ hipError_t pick_g(const RopeArgs& a, int g, int qc, hipStream_t stream) {
 
 // rope_multi: normalised rows always scale the rotation (by rstd mscale); rotation-only rows
 // skip a unit mscale's product (exact either way).
-template <bool BF16, int MODE, int G, int PB>
+template <bool BF16, int MODE, int G>
 hipError_t go_multi(const RopeArgs& a, int64_t blocks, hipStream_t stream) {
-  const size_t lds = (size_t)PB * (a.dims / 2) * sizeof(double2);
+  const size_t lds = (size_t)a.pb * (a.dims / 2) * sizeof(double2);
   const unsigned nb = (unsigned)blocks;
-  if (a.normalize) rope_multi<BF16, MODE, G, PB, false, true><<<nb, 256, lds, stream>>>(a);
-  else if (a.mscale != 1.f) rope_multi<BF16, MODE, G, PB, true, false><<<nb, 256, lds, stream>>>(a);
-  else rope_multi<BF16, MODE, G, PB, false, false><<<nb, 256, lds, stream>>>(a);
+  if (a.normalize) rope_multi<BF16, MODE, G, false, true><<<nb, 256, lds, stream>>>(a);
+  else if (a.mscale != 1.f) rope_multi<BF16, MODE, G, true, false><<<nb, 256, lds, stream>>>(a);
+  else rope_multi<BF16, MODE, G, false, false><<<nb, 256, lds, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -651,26 +654,36 @@ hipError_t launch_norm_rope(const RopeArgs& a0, bool aligned16, hipStream_t stre
     const int npc = mode == M_TRAD1 ? a.dims / V : half / V;
     const int nqc = (a.D - a.dims) / V;
     // Every feature rotated, few rows per position and many positions: several positions
-    // per block (rope_multi). With the normalisation only for 64-feature rows: its variant
-    // holds 139 registers (three waves per SIMD), which at 128 features measured no faster
-    // than one position per block (NormRope [1, 32, 4096, 128] bf16: 20.2 us either way;
-    // [4, 8, 8192, 64]: 31.1 -> 20.9 us).
+    // per block (rope_multi). With the normalisation, for 64-feature rows, or for rows of
+    // fewer than 32 heads: its variant holds 139 registers (three waves per SIMD), which at
+    // 128 features and 32 heads measured no faster than one position per block (NormRope
+    // [1, 32, 4096, 128] bf16: 20.2 us either way; [4, 8, 8192, 64]: 31.1 -> 20.9 us), while
+    // with fewer heads one position per block leaves most of its lane groups idle ([1, 8,
+    // 32768, 128] 73.7 -> 43.2 us at four positions per block).
     if (nqc == 0 && mode != M_TRAD1 && a.BH < 256 && a.L >= 4096 &&
-        (npc == 4 || ((npc == 8 || npc == 16) && !a.normalize))) {
-      // Eight positions per block for 4-lane rows (64 features), so that a block still
-      // holds 256 rows at 32 rows per position and its table one entry per thread.
-      const int64_t pb = npc == 4 ? 8 : 4;
+        (npc == 4 || ((npc == 8 || npc == 16) && (!a.normalize || a.BH < 32)))) {
+      // Positions per block: 8 for 64-feature rows (at 32 rows per position a block then
+      // holds 256 rows, and its table is one entry per thread), else 4. NormRope rows of
+      // fewer than 32 heads take enough for 256 rows, at most 32 and at most L / 1024 (a full
+      // round of blocks on the chip): [1, 8, 32768, 128] 43.2 -> 39.5 us at 32, [2, 8, 16384,
+      // 128] 41.9 -> 39.8 us at 16. Rotation-only rows measured slower that way ([1, 16, 32768,
+      // 128] 50.9 -> 69.3 us at 16).
+      const int64_t pb_min = npc == 4 ? 8 : 4;
+      int64_t pb = pb_min;
+      if (a.normalize && a.BH < 32)
+        pb = std::max(pb_min, std::min({(int64_t)32, 256 / a.BH, a.L / 1024}));
       const int64_t blocks = (a.L + pb - 1) / pb;
       if (blocks <= 0x7fffffff) {
+        a.pb = (int)pb;
         const bool half_mode = mode == M_HALF;
         if (npc == 4)
-          return half_mode ? go_multi<BF16, M_HALF, 4, 8>(a, blocks, stream)
-                           : go_multi<BF16, M_TRAD2, 4, 8>(a, blocks, stream);
+          return half_mode ? go_multi<BF16, M_HALF, 4>(a, blocks, stream)
+                           : go_multi<BF16, M_TRAD2, 4>(a, blocks, stream);
         if (npc == 8)
-          return half_mode ? go_multi<BF16, M_HALF, 8, 4>(a, blocks, stream)
-                           : go_multi<BF16, M_TRAD2, 8, 4>(a, blocks, stream);
-        return half_mode ? go_multi<BF16, M_HALF, 16, 4>(a, blocks, stream)
-                         : go_multi<BF16, M_TRAD2, 16, 4>(a, blocks, stream);
+          return half_mode ? go_multi<BF16, M_HALF, 8>(a, blocks, stream)
+                           : go_multi<BF16, M_TRAD2, 8>(a, blocks, stream);
+        return half_mode ? go_multi<BF16, M_HALF, 16>(a, blocks, stream)
+                         : go_multi<BF16, M_TRAD2, 16>(a, blocks, stream);
       }
     }
     for (int g = 4; g <= 64; g *= 2) {

@@ -40,6 +40,7 @@ struct RopeArgs {
   float mscale;           // factor on the rotated features
   int w_f32;
   int iters;              // filled in by the launcher
+  int pb;                 // positions per block of the multi-position kernel, by the launcher
   double log2_base;       // log2(base), filled in by the launcher
 };
 
