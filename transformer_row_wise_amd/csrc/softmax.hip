@@ -30,7 +30,8 @@
 // wave, no barrier) or a multiple of 64 (reductions through LDS, one barrier each); NV is at
 // least 4 where the row allows, so that every thread keeps 64 bytes in flight. Rows of up
 // to 2048 chunks (16384 bf16 or 8192 fp32 values) take it.
-// sm_stream: 256 threads per row looping over the row, U = 4 chunks (16-byte or single
+// sm_stream: 256 threads per row (1024 for rows of 16384 values or more that have a row
+// output or number fewer than 512) looping over the row, U = 4 chunks (16-byte or single
 // elements) per step loaded together, an online (max, sum) per thread (the sum rescaled when
 // the maximum grows), then, for the operations with a row output, a second pass over the
 // row (which the first pass left in the caches where it fits). Any width; the vocabulary-
@@ -698,13 +699,17 @@ hipError_t sm_team(const SmArgs& a, int team, bool exact, hipStream_t stream) {
 // compute unit) about 512 rows are in flight, so the second read of a 256 KB vocabulary row
 // still finds it in the 256 MB Infinity Cache; eight 256-thread blocks per CU keep the same
 // bytes in flight but four times the rows, which evicts each row before its second read.
+// The reductions (LogSumExp, CrossEntropy) take 1024 threads too when there are fewer than
+// 512 rows: with one block per row and most compute units idle, each block's own bytes in
+// flight set the pace (LogSumExp [64, 128256] bf16 18.1 -> 9.6 us, [256, 128256] 20.2 ->
+// 12.8 us).
 template <bool BF16, int OP, int V>
 hipError_t go_sm_stream(const SmArgs& a, hipStream_t stream) {
   constexpr bool OUT = OP == SM_SOFTMAX || OP == SM_CAUSAL || OP == SM_CE_VJP;
   if (a.rows > kSmMaxGrid) return hipErrorInvalidConfiguration;
   const size_t lds1 = OUT && V == Fmt<BF16>::VEC ? 3 * 1024 * 16 : 0;
   const size_t lds2 = OUT && V == Fmt<BF16>::VEC ? 3 * 256 * 16 : 0;
-  if (OUT && a.n >= 16384)
+  if (a.n >= 16384 && (OUT || a.rows < 512))
     sm_stream<BF16, OP, V, 1024><<<(unsigned)a.rows, 1024, lds1, stream>>>(a);
   else
     sm_stream<BF16, OP, V, 256><<<(unsigned)a.rows, 256, lds2, stream>>>(a);
