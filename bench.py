@@ -38,8 +38,10 @@ round and store h, sum of squares, row scalar, normalise, scale by w, round and 
 
 Fields beyond the contract: roofline (algorithmic bytes per launch over the average launch
 time measured with HIP events on the launch stream, against 8 TB/s), copy2_ceiling_GBps (two
-arrays copied into two, the headline's byte pattern without arithmetic), copy_ceiling_GBps (a
-plain 16-byte copy of the same byte count), and cpu_baseline (the fp64 oracle on a bounded
+arrays copied into two, the headline's byte pattern without arithmetic, in that pattern's
+fastest shape), copy2_row_ceiling_GBps (the same copy in the row kernel's work unit: each block
+loads a row's 16 KB of each array and stores nothing until all of it has arrived),
+copy_ceiling_GBps (a plain 16-byte copy of the same byte count), and cpu_baseline (the fp64 oracle on a bounded
 sample of the same workload, in a process pool over the host's cores).
 """
 
@@ -62,6 +64,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_add_rms_norm_bf16_16384x8
 HEADLINE_KERNEL = "row_block<true, 1, 2, 1, true>"  # bf16, add-RMSNorm, 2 chunks/thread, w bf16, exact
 COPY_KERNEL = "copy16_kernel"
 COPY2_KERNEL = "copy16x2_kernel"
+COPY2_ROW_KERNEL = "copy16x2_row_kernel"
 
 
 # Files the headline kernel and the copy kernel that scales the counters are built from.
@@ -178,6 +181,23 @@ def copy2_ceiling(nbytes, steps):
     return 4 * q / (gpu_ms * 1e-3) / 1e9
 
 
+def copy2_row_ceiling(rows, unit_bytes, steps):
+    """GB/s of the two-into-two copy in the row kernel's work unit (nrm_bench_copy2_row): two
+    arrays of rows units of unit_bytes in, two out, every block waiting for its whole unit
+    before it stores (the headline's access pattern in row_block's shape, no arithmetic)."""
+    import torch
+    import transformer_row_wise_amd as nrm
+
+    q = rows * unit_bytes
+    s1 = torch.empty(q, dtype=torch.uint8, device="cuda")
+    s2, d1, d2 = torch.empty_like(s1), torch.empty_like(s1), torch.empty_like(s1)
+    s1.fill_(1)
+    s2.fill_(2)
+    gpu_ms, _ = time_calls(lambda i: nrm.bench_copy2_row(s1, s2, d1, d2, unit_bytes), steps, steps)
+    del s1, s2, d1, d2
+    return 4 * q / (gpu_ms * 1e-3) / 1e9
+
+
 def stored_traffic(nbytes):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel sources; else None."""
@@ -273,6 +293,7 @@ def headline(args):
     print(f"# copy ceilings, {copy_steps} steps each", file=sys.stderr, flush=True)
     ceiling = copy_ceiling(nbytes, copy_steps)
     ceiling2 = copy2_ceiling(nbytes, copy_steps)
+    ceiling_row = copy2_row_ceiling(ROWS, HIDDEN * 2, copy_steps)
     print(f"# timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     gpu_ms, wall_ms = time_calls(step, args.steps, args.warmup)
     achieved = nbytes / (gpu_ms * 1e-3) / 1e9
@@ -280,7 +301,7 @@ def headline(args):
     if args.profile:
         print(json.dumps({"profile_run": True, "avg_launch_us": gpu_ms * 1e3,
                           "achieved_GBps": achieved, "copy_GBps": ceiling,
-                          "copy2_GBps": ceiling2}), flush=True)
+                          "copy2_GBps": ceiling2, "copy2_row_GBps": ceiling_row}), flush=True)
         return
     traffic = stored_traffic(nbytes)
     res = {
@@ -307,6 +328,7 @@ def headline(args):
         "kernel_us_mean": round(gpu_ms * 1e3, 2),
         "copy_ceiling_GBps": round(ceiling, 1),
         "copy2_ceiling_GBps": round(ceiling2, 1),
+        "copy2_row_ceiling_GBps": round(ceiling_row, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -1175,9 +1197,9 @@ def summarize_trace(trace_db):
     alg = add_rms_bytes(ROWS, HIDDEN, 2, 2)
     L = ["# add-RMSNorm bf16 [16384, 8192] on one MI355X: kernel trace and HBM traffic", "",
          "Workload: x, r Student-t(3) with 1% of rows x1e3, w ~ N(1, 0.1) bf16, eps 1e-6. "
-         "`bench.py --profile` first runs the two copy ceilings over the same byte count (the "
-         "16-byte copy, then the two-into-two copy; they also bring the clocks up), then the "
-         "headline kernel (1000 warm-up + 100 timed calls).", "",
+         "`bench.py --profile` first runs the copy ceilings over the same byte count (the "
+         "16-byte copy, the two-into-two copy, and the two-into-two copy in the row kernel's "
+         "work unit; they also bring the clocks up), then the headline kernel (1000 warm-up + 100 timed calls).", "",
          f"Kernel sources hash (`bench.py` `kernel_source_hash`) of the counter runs: "
          f"`{t['kernel_source_hash']}`.", "",
          "## Kernel trace (`rocprofv3 --kernel-trace --stats`)", "",
@@ -1198,6 +1220,12 @@ def summarize_trace(trace_db):
     two = (f" Two arrays into two (the headline's pattern without arithmetic): "
            f"{cb2 / (c2[0] * 1e-6) / 1e9:.0f} GB/s ({100 * cb2 / (c2[0] * 1e-6) / 8e12:.1f}%)."
            if c2 else "")
+    c3 = [r[3] for r in rows if COPY2_ROW_KERNEL in r[0]]
+    cb3 = 4 * ROWS * HIDDEN * 2
+    two += (f" The same copy in the row kernel's work unit (each 512-thread block loads a row's "
+            f"16 KB of each array and stores nothing until all of it has arrived): "
+            f"{cb3 / (c3[0] * 1e-6) / 1e9:.0f} GB/s ({100 * cb3 / (c3[0] * 1e-6) / 8e12:.1f}%)."
+            if c3 else "")
     L += ["", f"Headline kernel: {alg:,} algorithmic bytes / {kavg:.2f} us = "
           f"{alg / (kavg * 1e-6) / 1e9:.0f} GB/s ({100 * alg / (kavg * 1e-6) / 8e12:.1f}% of 8 TB/s). "
           f"Copy of the same byte count: {cb / (cavg * 1e-6) / 1e9:.0f} GB/s "

@@ -414,6 +414,22 @@ nrm_status nrm_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t
 nrm_status nrm_bench_copy2(const void* src1, const void* src2, void* dst1, void* dst2,
                            int64_t bytes, hipStream_t stream);
 
+/*
+ * Measurement helper, not one of the operations above: the copy of nrm_bench_copy2 (dst1 =
+ * src1, dst2 = src2, `bytes` bytes each) in the shape of the row kernels' work unit. Each
+ * 512-thread block copies one unit of `unit_bytes` of each source (unit_bytes / 8192 16-byte
+ * chunks per thread, at chunks t, t + 512, ...), and a barrier after its loads keeps every
+ * store of the block waiting until its whole unit has arrived, as a row's outputs wait for
+ * the row's statistic. With unit_bytes = 16384 this is the residual add-RMSNorm's memory
+ * traffic on [rows, 8192] bf16 rows (x and r read, out and h written) in its kernel's shape,
+ * without the arithmetic: the ceiling of that access pattern, reported beside the pattern's
+ * best copy (nrm_bench_copy2), whose blocks store each chunk as soon as it arrives.
+ * unit_bytes is 8192, 16384 or 32768; bytes a multiple of it. Arrays and errors as
+ * nrm_bench_copy2, and unit_bytes outside that set -> NRM_ERR_SHAPE.
+ */
+nrm_status nrm_bench_copy2_row(const void* src1, const void* src2, void* dst1, void* dst2,
+                               int64_t bytes, int64_t unit_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -85,6 +85,7 @@ def test_null_pointers(L):
     assert rope(L, out=None) == NULL and "out_or_cache" in err(L)
     assert L.nrm_bench_copy(None, P, 16, None) == NULL
     assert L.nrm_bench_copy2(P, P + MB, None, P + 3 * MB, 16, None) == NULL
+    assert L.nrm_bench_copy2_row(P, None, P + 2 * MB, P + 3 * MB, 16384, 16384, None) == NULL
 
 
 def test_shapes(L):
@@ -105,6 +106,10 @@ def test_shapes(L):
     assert "offset + L must be <= cache_len (10), got 7 + 4" in err(L)
     assert L.nrm_bench_copy(P, P + MB, 17, None) == SHAPE
     assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB, P + 3 * MB, 17, None) == SHAPE
+    assert L.nrm_bench_copy2_row(P, P + MB, P + 2 * MB, P + 3 * MB, 16384, 4096, None) == SHAPE
+    assert "unit_bytes must be 8192, 16384 or 32768, got 4096" in err(L)
+    assert L.nrm_bench_copy2_row(P, P + MB, P + 2 * MB, P + 3 * MB, 24576, 16384, None) == SHAPE
+    assert L.nrm_bench_copy2_row(P, P + MB, P + 2 * MB, P + 3 * MB, -16384, 16384, None) == SHAPE
 
 
 def test_dtypes(L):
@@ -134,6 +139,9 @@ def test_aliasing(L):
     assert L.nrm_bench_copy2(P, P + MB, P + 32, P + 3 * MB, 64, None) == ALIAS   # dst1 on src1
     assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB, P + 2 * MB, 64, None) == ALIAS  # dst1 = dst2
     assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB + 8, P + 3 * MB, 64, None) == ALIAS  # unaligned
+    assert L.nrm_bench_copy2_row(P, P + MB, P + 32, P + 3 * MB, 8192, 8192, None) == ALIAS
+    assert L.nrm_bench_copy2_row(P, P + MB, P + 2 * MB, P + 2 * MB, 8192, 8192, None) == ALIAS
+    assert L.nrm_bench_copy2_row(P + 8, P + MB, P + 2 * MB, P + 3 * MB, 8192, 8192, None) == ALIAS
 
 
 def test_zero_rows_is_a_noop(L):
@@ -144,6 +152,7 @@ def test_zero_rows_is_a_noop(L):
     assert rope(L, L_=0, cache=1, cache_len=0) == OK
     assert L.nrm_bench_copy(P, P + MB, 0, None) == OK
     assert L.nrm_bench_copy2(P, P + MB, P + 2 * MB, P + 3 * MB, 0, None) == OK
+    assert L.nrm_bench_copy2_row(P, P + MB, P + 2 * MB, P + 3 * MB, 0, 32768, None) == OK
 
 
 def test_error_message_cleared_by_next_call(L):

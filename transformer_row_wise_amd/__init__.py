@@ -34,7 +34,7 @@ __all__ = [
     "rms_norm_vjp", "layer_norm_vjp", "vjp_workspace_bytes", "rope", "rope_positions",
     "rope_freqs_llama3", "rope_freqs_yarn", "rope_freqs_su", "softmax", "causal_softmax",
     "logsumexp", "cross_entropy", "cross_entropy_vjp", "bench_copy", "bench_copy2",
-    "layer_norm_vjp_noalloc", "NRM_F32",
+    "bench_copy2_row", "layer_norm_vjp_noalloc", "NRM_F32",
     "NRM_BF16", "LIB_PATH",
 ]
 
@@ -71,6 +71,7 @@ _SIGNATURES = {
     "nrm_cross_entropy_vjp": [_vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, _int, _vp],
     "nrm_bench_copy": [_vp, _vp, _i64, _vp],
     "nrm_bench_copy2": [_vp, _vp, _vp, _vp, _i64, _vp],
+    "nrm_bench_copy2_row": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "nrm_last_error": [],
     "nrm_status_name": [_int],
     "nrm_version": [],
@@ -556,6 +557,21 @@ def bench_copy2(src1, src2, dst1, dst2):
     if any(t.numel() * t.element_size() < n for t in (src2, dst1, dst2)):
         raise ValueError("src2, dst1 and dst2 must hold at least as many bytes as src1")
     st = load().nrm_bench_copy2(_ptr(src1), _ptr(src2), _ptr(dst1), _ptr(dst2), n, _stream())
+    if st:
+        _raise(st)
+    return dst1, dst2
+
+
+def bench_copy2_row(src1, src2, dst1, dst2, unit_bytes=16384):
+    """dst1 = src1 and dst2 = src2 in the row kernels' work unit (nrm_bench_copy2_row): each
+    block loads unit_bytes of each source and stores nothing until all of it has arrived."""
+    for t, what in ((src1, "src1"), (src2, "src2"), (dst1, "dst1"), (dst2, "dst2")):
+        _check_act(t, what, src1.device)
+    n = src1.numel() * src1.element_size()
+    if any(t.numel() * t.element_size() < n for t in (src2, dst1, dst2)):
+        raise ValueError("src2, dst1 and dst2 must hold at least as many bytes as src1")
+    st = load().nrm_bench_copy2_row(_ptr(src1), _ptr(src2), _ptr(dst1), _ptr(dst2), n,
+                                    int(unit_bytes), _stream())
     if st:
         _raise(st)
     return dst1, dst2

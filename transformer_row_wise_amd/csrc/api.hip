@@ -699,4 +699,30 @@ nrm_status nrm_bench_copy2(const void* src1, const void* src2, void* dst1, void*
   return launched(fn, nrm::launch_copy16x2(src1, src2, dst1, dst2, bytes / 16, stream));
 }
 
+nrm_status nrm_bench_copy2_row(const void* src1, const void* src2, void* dst1, void* dst2,
+                               int64_t bytes, int64_t unit_bytes, hipStream_t stream) {
+  static const char* fn = "nrm_bench_copy2_row";
+  g_err.clear();
+  if (unit_bytes != 8192 && unit_bytes != 16384 && unit_bytes != 32768)
+    return fail(NRM_ERR_SHAPE, "%s: unit_bytes must be 8192, 16384 or 32768, got %lld", fn,
+                (long long)unit_bytes);
+  if (bytes < 0 || bytes % unit_bytes)
+    return fail(NRM_ERR_SHAPE, "%s: bytes must be a non-negative multiple of unit_bytes (%lld), "
+                "got %lld", fn, (long long)unit_bytes, (long long)bytes);
+  if (bytes == 0) return NRM_OK;
+  if (!src1 || !src2 || !dst1 || !dst2)
+    return fail(NRM_ERR_NULL, "%s: src1, src2, dst1 and dst2 must not be NULL, got %p %p %p %p",
+                fn, src1, src2, dst1, dst2);
+  if (!aligned16(src1) || !aligned16(src2) || !aligned16(dst1) || !aligned16(dst2))
+    return fail(NRM_ERR_ALIAS, "%s: every array must be 16-byte aligned, got %p %p %p %p", fn,
+                src1, src2, dst1, dst2);
+  const auto s1 = span(src1, bytes), s2 = span(src2, bytes), o1 = span(dst1, bytes),
+             o2 = span(dst2, bytes);
+  if (overlap(o1, s1) || overlap(o1, s2) || overlap(o2, s1) || overlap(o2, s2) || overlap(o1, o2))
+    return fail(NRM_ERR_ALIAS, "%s: a destination overlaps a source or the other destination",
+                fn);
+  return launched(fn, nrm::launch_copy16x2_row(src1, src2, dst1, dst2, bytes / 16,
+                                               (int)(unit_bytes / 8192), stream));
+}
+
 }  // extern "C"

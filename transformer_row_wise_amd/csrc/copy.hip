@@ -55,6 +55,50 @@ copy16x2_kernel(const u32x4* s1, const u32x4* s2, u32x4* d1, u32x4* d2, int64_t 
   }
 }
 
+// The same pattern with a row kernel's work unit: each 512-thread block copies one unit of NV
+// 16-byte chunks per thread of each source (chunks t, t + 512, ...: a unit of 8 KB * NV per
+// array, as row_block holds a row), and a barrier after the loads keeps every store of the
+// block waiting until its whole unit has arrived, as a row's outputs wait for its statistic.
+// That is add-RMSNorm's memory traffic in row_block's shape without its arithmetic.
+template <int NV>
+__global__ void __launch_bounds__(512)
+copy16x2_row_kernel(const u32x4* s1, const u32x4* s2, u32x4* d1, u32x4* d2) {
+  const int64_t base = (int64_t)blockIdx.x * 512 * NV + threadIdx.x;
+  u32x4 a[NV], b[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    a[k] = ld16_nt(s1 + base + k * 512);
+    b[k] = ld16_nt(s2 + base + k * 512);
+  }
+  // The loaded values are inputs of this empty statement, so the loads have completed before
+  // the barrier.
+#pragma unroll
+  for (int k = 0; k < NV; ++k) __asm__ volatile("" ::"v"(a[k]), "v"(b[k]) : "memory");
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    st16_nt(d1 + base + k * 512, a[k]);
+    st16_nt(d2 + base + k * 512, b[k]);
+  }
+}
+
+hipError_t launch_copy16x2_row(const void* s1, const void* s2, void* d1, void* d2, int64_t n16,
+                               int nv, hipStream_t stream) {
+  const int64_t unit = 512 * (int64_t)nv;
+  if (nv < 1 || n16 % unit) return hipErrorInvalidValue;
+  const int64_t blocks = n16 / unit;
+  if (blocks > kMaxCopyGrid) return hipErrorInvalidValue;
+  const u32x4 *a = (const u32x4*)s1, *b = (const u32x4*)s2;
+  u32x4 *c = (u32x4*)d1, *d = (u32x4*)d2;
+  switch (nv) {
+    case 1: copy16x2_row_kernel<1><<<(unsigned)blocks, 512, 0, stream>>>(a, b, c, d); break;
+    case 2: copy16x2_row_kernel<2><<<(unsigned)blocks, 512, 0, stream>>>(a, b, c, d); break;
+    case 4: copy16x2_row_kernel<4><<<(unsigned)blocks, 512, 0, stream>>>(a, b, c, d); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_copy16x2(const void* s1, const void* s2, void* d1, void* d2, int64_t n16,
                            hipStream_t stream) {
   const int64_t blocks = (n16 + 511) / 512;

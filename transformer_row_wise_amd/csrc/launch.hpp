@@ -21,5 +21,7 @@ hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream);
 hipError_t launch_copy16(const void* src, void* dst, int64_t n16, hipStream_t stream);
 hipError_t launch_copy16x2(const void* s1, const void* s2, void* d1, void* d2, int64_t n16,
                            hipStream_t stream);
+hipError_t launch_copy16x2_row(const void* s1, const void* s2, void* d1, void* d2, int64_t n16,
+                               int nv, hipStream_t stream);
 
 }  // namespace nrm
