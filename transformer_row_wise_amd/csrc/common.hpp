@@ -359,22 +359,6 @@ __device__ __forceinline__ double rstd_f64(double sum, int64_t n, float eps) {
   return 1.0 / __builtin_sqrt(sum / (double)n + (double)eps);
 }
 
-// rstd = 1 / sqrt(ss / n + eps) in fp32 from an fp32 sum of squares, for the RMS forms (whose
-// outputs multiply by an fp32 rstd anyway): the hardware reciprocal square root (relative error
-// about 2^-23) and one Newton step y (3 - t y^2) / 2, within about one fp32 ulp of the exact
-// value. It replaces an fp64 division and square root, a long dependent chain that sat between a
-// row's barrier and its first store (add-RMSNorm bf16 [16384, 8192] 172.0 -> 170.4 us). Scaling
-// ss by 4^k scales t by 4^k exactly and the Newton step by 2^-k exactly; the GPU tests check that
-// a row scaled by 2^k gives bit-identical outputs. t outside the fp32 normal range (0, inf, NaN,
-// denormals) takes the exact fp64 form, so an all-zero row with eps = 0 still gives NaN and an
-// overflowed sum gives 0.
-__device__ __forceinline__ float rstd_rms(float ss, int64_t n, double inv_n, float eps) {
-  const float t = __builtin_fmaf(ss, (float)inv_n, eps);
-  if (!(t >= 0x1p-126f && t <= 0x1p+126f)) return (float)rstd_f64((double)ss, n, eps);
-  const float y = __builtin_amdgcn_rsqf(t);
-  return y * __builtin_fmaf(-0.5f * t * y, y, 1.5f);
-}
-
 // The same statistic from inv_n = 1/n, for short rows where its instruction count shows: the
 // fp32 hardware reciprocal square root (relative error ~1e-7) refined by two Newton steps
 // y <- y + y (1 - t y^2) / 2, each of which squares the relative error, so the result is

@@ -149,7 +149,7 @@ row_regs(RowArgs a) {
       }
     }
     const float ss = row_sum<WPR>(acc, red_f);
-    const float rstd = rstd_rms(ss, a.hidden, a.inv_n, a.eps);
+    const float rstd = (float)rstd_f64((double)ss, a.hidden, a.eps);
 
     char* orow = (char*)a.out + base;
     const bool has_w = a.w != nullptr;
@@ -334,7 +334,7 @@ __device__ __forceinline__ void row_block_body(RowArgs a) {
     float ss;
     if constexpr (SUB > 0) ss = group_sum<SUB>(acc);
     else ss = block_row_sum(acc, red_f, nw);
-    const float rstd = rstd_rms(ss, a.hidden, a.inv_n, a.eps);
+    const float rstd = (float)rstd_f64((double)ss, a.hidden, a.eps);
     if constexpr (W_LATE && NV == 6) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) load_pk<BF16, PK, V>(a.w, (int64_t)jj[k] * V, wv[k]);
@@ -650,7 +650,7 @@ row_rms_pair(RowArgs a) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     if (r == 1 && !live1) break;
-    const float rstd = rstd_rms(ss[r], a.hidden, a.inv_n, a.eps);
+    const float rstd = (float)rstd_f64((double)ss[r], a.hidden, a.eps);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       float f[V];
@@ -691,7 +691,7 @@ row_chunked(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < V; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
       }
-      const float rstd = rstd_rms(row_sum<WPR>(acc, red_f), a.hidden, a.inv_n, a.eps);
+      const float rstd = (float)rstd_f64((double)row_sum<WPR>(acc, red_f), a.hidden, a.eps);
       // Each thread re-reads exactly the chunks it wrote or read in the first pass.
       const void* src = OP == OP_ADD_RMS ? (const void*)a.h : a.x;
       for (int64_t j = threadIdx.x; j < nch; j += 256) {
@@ -804,7 +804,7 @@ row_elems(RowArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < K; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
-    const float rstd = rstd_rms(block_row_sum(acc, red_f, nw), a.hidden, a.inv_n, a.eps);
+    const float rstd = (float)rstd_f64((double)block_row_sum(acc, red_f, nw), a.hidden, a.eps);
 #pragma unroll
     for (int e = 0; e < K; ++e) y[e] = (f[e] * rstd) * wv[e];
   } else {
