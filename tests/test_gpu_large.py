@@ -1,5 +1,7 @@
-"""Arrays past 2^31 elements (4 GiB of bf16): every element offset overflows 32 bits somewhere in
-the array. Each input is K distinct rows drawn by the workload recipe and repeated on the device
+"""Arrays past 2^31 elements (4 GiB of bf16), and rows of 2^23 to 2^25 elements.
+
+Past 2^31 elements every element offset overflows 32 bits somewhere in the array. Each input is
+K distinct rows drawn by the workload recipe and repeated on the device
 until the array is that large, so every output row must equal the output of its base row bit for
 bit (the kernels are deterministic, and a repeated row meets the same arithmetic: with K even the
 two-row LayerNorm blocks keep each base row in the same slot). The test checks that for every
@@ -7,7 +9,8 @@ row on the device, and checks the base rows against the fp64 oracle. Column sums
 rows repeated 2^12 times are 2^12 times the base rows' sums, which rounding keeps exact, so the
 oracle of the base rows gives them too. NormRope rows differ by position: every (b, h) holds the
 same [L, D] block, so each must equal (0, 0) bit for bit, and (0, 0) is compared with the
-oracle at all L positions (also into a cache)."""
+oracle at all L positions (also into a cache). The very wide rows are compared with the oracle
+on every element."""
 
 import pytest
 import torch
@@ -199,3 +202,63 @@ def test_large_norm_rope_bf16(nrm_lib, traditional):
         # the written rows are the plain output bit for bit; the rows before offset stay zero
         assert torch.equal(_bits(cache[:, :, off:]), _bits(out)), "cache rows differ from out"
         assert not bool(_bits(cache[:, :, :off]).any()), "cache rows before offset changed"
+
+
+@pytest.mark.parametrize("op,dt,n", [("rms", "bf16", 2 ** 25 + 8), ("rms", "bf16", 2 ** 25 + 3),
+                                     ("add", "f32", 2 ** 24 + 4), ("ln", "bf16", 2 ** 25 + 8)],
+                         ids=lambda v: str(v))
+def test_very_wide_rows(nrm_lib, op, dt, n):
+    """A few rows of 2^24 to 2^25 elements (the looping kernels; 2^25 + 3 one element at a
+    time), every element against the oracle."""
+    say(f"very wide rows {op} {dt} [3, {n}]")
+    inp = workloads.row_inputs(3, n, dt, seed=80, r=("normal", 0.0, 1.0) if op == "add" else None,
+                               x=("normal", 0.5, 2.0) if op == "ln" else ("normal", 0.0, 1.0),
+                               b=("normal", 0.0, 0.1) if op == "ln" else None)
+    x, w = inp.x.to(DEV), inp.w.to(DEV)
+    if op == "rms":
+        got = nrm_lib.rms_norm(x, w, inp.eps)
+        want = oracle.rms_norm(f64(inp.x), f64(inp.w), inp.eps, dt)
+    elif op == "add":
+        got, h = nrm_lib.add_rms_norm(x, inp.r.to(DEV), w, inp.eps)
+        want, want_h = oracle.add_rms_norm(f64(inp.x), f64(inp.r), f64(inp.w), inp.eps, dt)
+        assert_h_exact(h, want_h)
+    else:
+        got = nrm_lib.layer_norm(x, w, inp.b.to(DEV), inp.eps)
+        want = oracle.layer_norm(f64(inp.x), f64(inp.w), f64(inp.b), inp.eps, dt)
+    compare.check_output(got, want, dt, what=f"{op} out")
+
+
+@pytest.mark.parametrize("dt,n", [("bf16", 2 ** 25 + 3), ("f32", 2 ** 24)], ids=str)
+def test_very_wide_softmax_family(nrm_lib, dt, n):
+    """Softmax, LogSumExp, CrossEntropy and its gradient over rows of 2^24 to 2^25 columns."""
+    say(f"very wide softmax family {dt} [2, {n}]")
+    inp = workloads.ce_inputs(2, n, dt, seed=81, g="normal")
+    x, tgt, g = inp.logits.to(DEV), inp.targets.to(DEV), inp.g.to(DEV)
+    xs = f64(inp.logits)
+    compare.check_output(nrm_lib.softmax(x), oracle.softmax.softmax(xs, dt), dt, what="softmax")
+    compare.check_output(nrm_lib.logsumexp(x), oracle.softmax.logsumexp(xs, dt), dt,
+                         what="logsumexp")
+    t = inp.targets.numpy()
+    compare.check_f32(f64(nrm_lib.cross_entropy(x, tgt)), oracle.softmax.cross_entropy(xs, t),
+                      what="loss")
+    compare.check_output(nrm_lib.cross_entropy_vjp(x, tgt, g),
+                         oracle.softmax.cross_entropy_vjp(xs, t, f64(inp.g), dt), dt,
+                         what="dlogits")
+
+
+@pytest.mark.parametrize("ln,dt,n", [(False, "bf16", 2 ** 24 + 8), (True, "f32", 2 ** 23 + 4)],
+                         ids=str)
+def test_very_wide_vjp(nrm_lib, ln, dt, n):
+    """The backward over a few rows of 2^23 to 2^24 elements (the looping kernel): dx, dw and db
+    on every element."""
+    say(f"very wide {'LayerNorm' if ln else 'RMSNorm'} backward {dt} [3, {n}]")
+    inp = workloads.row_inputs(3, n, dt, seed=82, g=("normal", 0.0, 1.0))
+    x, w, g = inp.x.to(DEV), inp.w.to(DEV), inp.g.to(DEV)
+    if ln:
+        got = nrm_lib.layer_norm_vjp(x, w, g, inp.eps)
+        want = oracle.layer_norm_vjp(f64(inp.x), f64(inp.w), None, f64(inp.g), inp.eps, dt)
+    else:
+        got = nrm_lib.rms_norm_vjp(x, w, g, inp.eps)
+        want = oracle.rms_norm_vjp(f64(inp.x), f64(inp.w), f64(inp.g), inp.eps, dt)
+    for gt, wt, what in zip(got, want, ("dx", "dw", "db")):
+        compare.check_output(gt, wt, dt, what=what)
