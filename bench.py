@@ -285,7 +285,7 @@ def headline(args):
     def step(_):
         nrm.add_rms_norm(x, r, w, inp.eps, out=out, h=h)
 
-    # The copy ceilings run first: about 1.3 s of streaming at the same byte count, which
+    # The three copy ceilings run first: about 1 s of streaming at the same byte count, which
     # brings the GPU to the clocks it holds under sustained load (it needs about a second), so
     # that the headline's few timed steps are not taken on the way up. Under a profiler they
     # stay short.
