@@ -155,6 +155,35 @@ def test_zero_rows_is_a_noop(L):
     assert L.nrm_bench_copy2_row(P, P + MB, P + 2 * MB, P + 3 * MB, 0, 32768, None) == OK
 
 
+def test_error_message_is_per_thread(L):
+    """nrm_last_error belongs to the calling host thread: while one thread fails a call and
+    another makes a valid (empty) one, each reads back only its own result, over many rounds
+    in which both calls finish before either thread reads its message."""
+    import threading
+
+    rounds = 200
+    gate = threading.Barrier(2)
+    seen = {"bad": [], "ok": []}
+
+    def worker(kind):
+        for i in range(rounds):
+            st = rms(L, rows=-1 - i) if kind == "bad" else ln(L, rows=0)
+            gate.wait()
+            seen[kind].append((st, err(L), i))
+            gate.wait()
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in ("bad", "ok")]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(60)
+    assert len(seen["bad"]) == rounds and len(seen["ok"]) == rounds
+    for st, msg, i in seen["bad"]:
+        assert st == SHAPE and f"rows must be >= 0, got {-1 - i}" in msg
+    for st, msg, _ in seen["ok"]:
+        assert st == OK and msg == ""
+
+
 def test_error_message_cleared_by_next_call(L):
     assert rms(L, rows=-1) == SHAPE and err(L)
     assert rms(L, rows=0) == OK and err(L) == ""
