@@ -320,10 +320,8 @@ hipError_t try_block(const RowArgs& a, int per_thread, hipStream_t stream, bool*
   return hipSuccess;
 }
 
-}  // namespace
-
 template <bool BF16, int OP>
-hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream) {
+hipError_t launch_row_once(const RowArgs& a, bool aligned16, hipStream_t stream) {
   constexpr int V = Fmt<BF16>::VEC;
   const int path = forced_path();
   const bool vec = aligned16 && a.hidden % V == 0 && path != PATH_SCALAR;
@@ -359,6 +357,42 @@ hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream) {
     if (done) return err;
   }
   return go_chunked<BF16, OP, V>(a, stream);
+}
+
+// Bytes one launch streams at most (every array's rows: x and out, and r and h for
+// add-RMSNorm). On MI355X one launch over much more than 1 GiB streams slower than the same
+// rows launched in consecutive pieces of about 1 GiB, though each piece ends with a drain:
+// add-RMSNorm bf16 [65536, 5120] 445.6 -> 434.7 us, fp32 [65536, 5120] 890.3 -> 862.4 us, bf16
+// [65536, 8192] 745.6 -> 701.2 us; at 1 GiB itself (bf16 [16384, 8192]) one launch is fastest.
+constexpr int64_t kLaunchBytes = int64_t(1) << 30;
+
+}  // namespace
+
+// Rows of whole 16-byte chunks on the automatic path are launched in pieces of at most
+// kLaunchBytes (an even number of rows, so that the two-row kernels see whole pairs); each
+// piece is the same call on the rows it covers, at offset pointers (a row's outputs depend on
+// that row and the parameters only).
+template <bool BF16, int OP>
+hipError_t launch_row(const RowArgs& a, bool aligned16, hipStream_t stream) {
+  constexpr int V = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  const int64_t row_bytes = a.hidden * ESZ * (OP == OP_ADD_RMS ? 4 : 2);
+  const bool whole = aligned16 && a.hidden % V == 0 && forced_path() == PATH_AUTO;
+  if (!whole || row_bytes <= 0 || a.rows <= kLaunchBytes / row_bytes)
+    return launch_row_once<BF16, OP>(a, aligned16, stream);
+  const int64_t per = std::max<int64_t>(2, (kLaunchBytes / row_bytes) & ~int64_t(1));
+  for (int64_t r0 = 0; r0 < a.rows; r0 += per) {
+    RowArgs p = a;
+    const int64_t off = r0 * a.hidden * ESZ;
+    p.x = (const char*)a.x + off;
+    if (a.r) p.r = (const char*)a.r + off;
+    p.out = (char*)a.out + off;
+    if (a.h) p.h = (char*)a.h + off;
+    p.rows = std::min(per, a.rows - r0);
+    const hipError_t e = launch_row_once<BF16, OP>(p, aligned16, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nrm
