@@ -473,6 +473,31 @@ CONFIG_IDS = ["1", "2", "3a", "3b", "4a", "4b", "4c", "4d", "5a", "5b", "5c", "5
 NEXT_IDS = ["6a", "7a", "8a", "8b", "9a", "9b", "9c", "9d", "9e"]
 # Kernel dispatches of one call, where more than one (the backward adds its column sums).
 DISPATCHES_PER_CALL = {"6a": 2, "7a": 2}
+# The library launches a row call (RMSNorm, add-RMSNorm, LayerNorm on rows of whole 16-byte
+# chunks) that streams more than this many bytes over all its arrays as consecutive pieces of
+# at most that many (an even number of rows each); the forward configurations' row calls:
+# (rows, hidden), element bytes, arrays streamed (x, r, out, h for add-RMSNorm; x, out).
+LAUNCH_BYTES = 1 << 30
+FWD_ROW_CALLS = {"1": ((64, 512), 4, 4), "2": ((4096, 4096), 2, 4), "3a": ((16384, 8192), 2, 2),
+                 "3b": ((16384, 8192), 2, 2), "5a": ((16384, 8192), 2, 4),
+                 "5b": ((16384, 8192), 4, 4), "5c": ((65536, 5120), 2, 4),
+                 "5d": ((65536, 5120), 4, 4)}
+
+
+def row_call_launches(rows, hidden, elem_bytes, arrays):
+    """Kernel launches of one row call of that shape under the library's split rule."""
+    row_bytes = hidden * elem_bytes * arrays
+    if rows <= LAUNCH_BYTES // row_bytes:
+        return 1
+    per = max(2, (LAUNCH_BYTES // row_bytes) & ~1)
+    return -(-rows // per)
+
+
+def dispatches_per_call(cid):
+    if cid in FWD_ROW_CALLS:
+        (rows, hidden), es, arrays = FWD_ROW_CALLS[cid]
+        return row_call_launches(rows, hidden, es, arrays)
+    return DISPATCHES_PER_CALL.get(cid, 1)
 SUITE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_suite_configs.json")
 SUITE_MD = os.path.join(ROOT, "profiles", "suite_configs.md")
 CAL_BYTES = 512 * 2**20  # the calibration copy, bytes each way
@@ -912,7 +937,7 @@ def summarize_configs(trace_db, fetch_db, write_db):
     fe = _dispatches(fetch_db, "FETCH_SIZE")
     wr = _dispatches(write_db, "WRITE_SIZE")
 
-    per_call = 1 + sum(DISPATCHES_PER_CALL.get(c, 1) for c in CONFIG_IDS + NEXT_IDS)
+    per_call = 1 + sum(dispatches_per_call(c) for c in CONFIG_IDS + NEXT_IDS)
 
     def split(rows):
         """Dispatches in run order -> {case: [per-call lists of dispatches]}."""
@@ -922,7 +947,7 @@ def summarize_configs(trace_db, fetch_db, write_db):
                              "and CONFIG_IDS + NEXT_IDS differ")
         out, i = {"cal": rows[:calls]}, calls
         for cid in CONFIG_IDS + NEXT_IDS:
-            nd = DISPATCHES_PER_CALL.get(cid, 1)
+            nd = dispatches_per_call(cid)
             out[cid] = [rows[i + c * nd:i + (c + 1) * nd] for c in range(calls)]
             i += nd * calls
         return out
