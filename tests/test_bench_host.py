@@ -62,11 +62,13 @@ def test_summarize_configs_attributes_dispatches(tmp_path, monkeypatch):
     def seq(calls, value):
         out = [("void nrm::copy16_kernel(...)", value("cal"))] * calls
         for cid in ids:
+            nd = bench.dispatches_per_call(cid)
             for _ in range(calls):
-                nd = bench.DISPATCHES_PER_CALL.get(cid, 1)
-                out.append((f"void nrm::kernel_{cid}(nrm::Args)", value(cid)))
-                if nd == 2:
+                if cid in bench.DISPATCHES_PER_CALL:  # the backward: its kernel, then column sums
+                    out.append((f"void nrm::kernel_{cid}(nrm::Args)", value(cid)))
                     out.append(("void nrm::vjp_colsum<true>(double const*)", 1.0))
+                else:  # a row call split into nd launches, each a share of the call's bytes
+                    out += [(f"void nrm::kernel_{cid}(nrm::Args)", value(cid) / nd)] * nd
         return out
 
     # the calibration copy reads half its bytes on FETCH_SIZE (scale 2) and all on WRITE_SIZE
@@ -82,7 +84,7 @@ def test_summarize_configs_attributes_dispatches(tmp_path, monkeypatch):
     for cid in ids:
         c = t["cases"][cid]
         assert c["kernel"].startswith(f"kernel_{cid}")
-        assert c["dispatches_per_call"] == bench.DISPATCHES_PER_CALL.get(cid, 1)
+        assert c["dispatches_per_call"] == bench.dispatches_per_call(cid)
         colsum = 2 * 1.0 * 1024 / 1e6 if cid in bench.DISPATCHES_PER_CALL else 0.0
         assert c["fetch_MB"] == pytest.approx(meta[cid]["bytes"] / 2 / 1e6 + colsum, abs=0.011)
         assert c["write_MB"] == pytest.approx(meta[cid]["bytes"] / 2 / 1e6 + colsum / 2, abs=0.011)
@@ -90,3 +92,17 @@ def test_summarize_configs_attributes_dispatches(tmp_path, monkeypatch):
     _fake_db(tmp_path / "bad.db", seq(3, fetch)[:-1], "FETCH_SIZE")
     with pytest.raises(SystemExit, match="not a multiple"):
         bench.summarize_configs(str(tmp_path / "tr.db"), str(tmp_path / "bad.db"), str(tmp_path / "w.db"))
+
+
+def test_row_call_launches():
+    """The library's split of row calls over 1 GiB, as the counter attribution counts it: the
+    1 GiB headline call is one launch; the larger at-scale calls are several."""
+    assert bench.row_call_launches(16384, 8192, 2, 4) == 1         # exactly 1 GiB
+    assert bench.row_call_launches(16385, 8192, 2, 4) == 2         # one row more
+    assert bench.row_call_launches(16384, 8192, 4, 4) == 2         # 8192 rows a piece
+    assert bench.row_call_launches(65536, 5120, 2, 4) == 3         # 26214 rows a piece
+    assert bench.row_call_launches(65536, 5120, 4, 4) == 6         # 13106 rows a piece
+    assert bench.row_call_launches(65539, 8192, 2, 2) == 3         # 32768, 32768, 3
+    assert bench.row_call_launches(3, 2 ** 28, 2, 4) == 2          # rows over 1 GiB: two a piece
+    assert [bench.dispatches_per_call(c) for c in ("5a", "5b", "5c", "5d", "6a", "9a")] == \
+        [1, 2, 3, 6, 2, 1]

@@ -262,3 +262,27 @@ def test_very_wide_vjp(nrm_lib, ln, dt, n):
         want = oracle.rms_norm_vjp(f64(inp.x), f64(inp.w), f64(inp.g), inp.eps, dt)
     for gt, wt, what in zip(got, want, ("dx", "dw", "db")):
         compare.check_output(gt, wt, dt, what=what)
+
+
+def test_launch_pieces_layer_norm(nrm_lib):
+    """A LayerNorm call over more than 1 GiB runs as pieces of whole rows: [65539, 8192] bf16
+    is two pieces of 32768 rows (two-row kernel) and a tail of 3 (one row per block). Every
+    row before the tail equals its base row bit for bit; the base rows and the tail match the
+    oracle."""
+    reps = 993
+    n = K * reps + 1
+    say(f"LayerNorm bf16 [{n}, 8192] in launch pieces")
+    inp = workloads.row_inputs(K, 8192, "bf16", seed=83, x=("normal", 0.5, 2.0),
+                               b=("normal", 0.0, 0.1))
+    x = tile(inp.x, reps + 1)[:n].contiguous()
+    assert x.shape[0] == n and x.shape[0] * 8192 * 2 * 2 > 2 ** 30
+    out = nrm_lib.layer_norm(x, inp.w.to(DEV), inp.b.to(DEV), inp.eps)
+    torch.cuda.synchronize()
+    del x
+    head = 2 * 32768
+    assert_rows_repeat(out[:head - head % K], "out")
+    want = oracle.layer_norm(f64(inp.x), f64(inp.w), f64(inp.b), inp.eps, "bf16")
+    compare.check_output(out[:K], want, "bf16", what="base rows")
+    tail = list(range(head - head % K, n))
+    compare.check_output(out[tail], want[[i % K for i in tail]], "bf16",
+                         what="rows after the last whole repeat, the tail included")
