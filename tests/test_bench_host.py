@@ -106,3 +106,14 @@ def test_row_call_launches():
     assert bench.row_call_launches(3, 2 ** 28, 2, 4) == 2          # rows over 1 GiB: two a piece
     assert [bench.dispatches_per_call(c) for c in ("5a", "5b", "5c", "5d", "6a", "9a")] == \
         [1, 2, 3, 6, 2, 1]
+
+
+def test_committed_counters_match_the_sources():
+    """The committed counter summaries were taken on the current sources, so the bench's
+    `traffic` and the per-configuration traffic table are not silently dropped as stale:
+    any source or flag change has to come with retaken counters."""
+    with open(bench.TRAFFIC_FILE) as f:
+        assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash()
+    with open(bench.SUITE_TRAFFIC_FILE) as f:
+        assert json.load(f)["library_source_hash"] == bench.library_source_hash()
+    assert bench.stored_traffic(0) is not None

@@ -19,8 +19,6 @@
 //   hidden or a base address not 16-byte granular, hidden <= 12288: row_elems, one block per
 //   row, K single elements per thread in registers (RMSNorm and LayerNorm);
 //   otherwise the looping kernel (16-byte chunks, or single elements).
-// A call of whole 16-byte rows on the automatic path that streams more than 1 GiB over all
-// its arrays runs as consecutive launches over pieces of at most 1 GiB (launch_row below).
 // Measured on MI355X for add-RMSNorm bf16 [16384, 8192]: row_block streams at ~6.25 TB/s,
 // one wave per row (the whole row in one wave's registers) at ~5.2 TB/s, the 512-thread
 // register kernel without streaming hints at ~5.9 TB/s. Those two stay available through
