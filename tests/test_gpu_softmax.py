@@ -143,6 +143,32 @@ def test_softmax_special_values(nrm_lib):
             compare.check_output(lse, oracle.softmax.logsumexp(f64(xs), dt), dt, what="lse")
 
 
+def test_causal_softmax_special_values(nrm_lib):
+    """Causal rows of 512 columns (rows_per_block 640, so rows 0-127 keep no column) with
+    special kept scores, in waves beside ordinary rows: kept scores all at the dtype's lowest
+    value (the maximum is that value, masked scores count as much as kept ones), all -inf
+    (only the masked columns remain), a NaN, a +inf, huge values; every slot of a row past
+    its cut is then either skipped as a whole or computed, and both must agree."""
+    R, L, rows = 640, 512, 640
+    for dt in ("bf16", "f32"):
+        say(f"causal softmax special values {dt}")
+        x = workloads.scores((1, R, L), "f32", seed=17)
+        lowest = -3.3895313892515355e38 if dt == "bf16" else float(np.finfo(np.float32).min)
+        x[0, 200, :73] = lowest             # cut 72: every kept score the lowest value
+        x[0, 300, :173] = -float("inf")     # cut 172: every kept score -inf
+        x[0, 401, 5] = float("nan")         # cut 273
+        x[0, 502, 10] = float("inf")        # cut 374
+        x[0, 150, :23] = 1e30               # cut 22
+        x[0, 131, 3] = -float("inf")        # cut 3: one of four kept scores -inf
+        xs = x.to(torch.bfloat16) if dt == "bf16" else x
+        for path in (None, "scalar"):
+            with forced_path(path):
+                got = nrm_lib.causal_softmax(dev(xs), rows)
+                torch.cuda.synchronize()
+            compare.check_output(got, oracle.softmax.causal_softmax(f64(xs), rows, dt), dt,
+                                 what=f"causal softmax, path {path}")
+
+
 def test_softmax_misaligned_bases(nrm_lib):
     """Rows starting 2 bytes past a 16-byte boundary (a view one element into a buffer):
     head, chunk body and tail per row, with an output of the same phase; an output of another

@@ -248,10 +248,29 @@ sm_rows(SmArgs a) {
     return f;
   };
 
+  // CausalSoftmax with up to four chunks per thread: a chunk slot that lies wholly past the
+  // causal cut in every lane of the wave (all its scores are the lowest value, or absent past
+  // the row's end) is handled as a whole, behind a wave-uniform branch. It adds that value to
+  // the maximum; once every lane's maximum exceeds it, its exponentials are exactly +0 (the
+  // difference is at least 2^104), so the sum pass adds nothing for it. Rows of a causal
+  // block keep half their columns on average, so a wave skips ~3/8 of the per-element work:
+  // bf16 [32, 2048, 2048] 72.5 -> 70.7 us, [64, 1024, 1024] 37.1 -> 36.2 us, fp32
+  // [256, 512, 512] 73.6 -> 72.9 us. Teams of 16 lanes (four rows per wave) measured slower
+  // with the branches (bf16 [256, 512, 512] 44.5 -> 47.4 us) and keep the straight passes.
+  constexpr bool SKIP = OP == SM_CAUSAL && !MASK_LOAD && SUB != 16;
+  auto wave_none = [&](bool c) { return __builtin_amdgcn_ballot_w64(c) == 0; };
+  auto past_cut = [&](int k) { return chunk(k) * V > cut; };
+
   float m = -__builtin_inff();
   float xt = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
+    if constexpr (SKIP) {
+      if (wave_none(!past_cut(k))) {
+        m = fmaxf(m, ok(k) ? lowest : -__builtin_inff());
+        continue;
+      }
+    }
     float f[V];
     unpack<BF16>(xv[k], f);
 #pragma unroll
@@ -290,6 +309,15 @@ sm_rows(SmArgs a) {
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
+    if constexpr (SKIP) {
+      if (wave_none(!past_cut(k) || !(m > lowest))) {
+        if constexpr (KEEP) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) ek[k][e] = 0.f;
+        }
+        continue;
+      }
+    }
     float f[V];
     unpack<BF16>(xv[k], f);
 #pragma unroll
