@@ -119,10 +119,14 @@ def test_rms_norm_row_pairs(nrm_lib, dt, wdt, hidden):
     check_rms(nrm_lib, inp, rows_sel=np.r_[0:3, 2047:2050, 4093:4097])
 
 
-# Widths that are not whole 16-byte chunks: one block per row with 1 (33), 2 (100), 4 (up to
-# 4096), 8 (up to 8192) or 12 (up to 12288) elements per thread; 12289 takes the looping kernel.
-ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 1001), ("bf16", 4100), ("bf16", 8191),
-         ("bf16", 10001), ("bf16", 12287), ("bf16", 12289), ("f32", 1001), ("f32", 4097),
+# Widths that are not whole 16-byte chunks: one block per row of at most 256 threads with 1
+# (33, 100), 2 (300), 4 (1001), 8 (2047) or 16 (3000, 4095) elements per thread; RMSNorm and
+# LayerNorm rows over 4096 with 8 (up to 8192) or 12 (up to 12288) per thread, add-RMSNorm
+# there with 16 (4100: 320 threads, the last three of a thread's elements past the row's end
+# in most threads); 12289 takes the looping kernel.
+ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 300), ("bf16", 1001), ("bf16", 2047),
+         ("bf16", 3000), ("bf16", 4095), ("bf16", 4100), ("bf16", 8191), ("bf16", 10001),
+         ("bf16", 12287), ("bf16", 12289), ("f32", 1001), ("f32", 2047), ("f32", 4097),
          ("f32", 12285)]
 
 

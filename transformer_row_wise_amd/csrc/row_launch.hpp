@@ -17,7 +17,7 @@
 //                                    row_ln_pair / row_rms_pair, the same per thread for two
 //                                    rows per block;
 //   hidden or a base address not 16-byte granular, hidden <= 12288: row_elems, one block per
-//   row, K single elements per thread in registers (RMSNorm and LayerNorm);
+//   row, K single elements per thread in registers;
 //   otherwise the looping kernel (16-byte chunks, or single elements).
 // Measured on MI355X for add-RMSNorm bf16 [16384, 8192]: row_block streams at ~6.25 TB/s,
 // one wave per row (the whole row in one wave's registers) at ~5.2 TB/s, the 512-thread
@@ -75,19 +75,36 @@ hipError_t go_rowelems(const RowArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Rows of single elements (a width or base that is not 16-byte granular), up to 12288:
-// row_elems with K = 4 where the thread count allows it (only a thread's last element past
-// the row's end), else 2 or 1, and 8 or 12 for rows over 4096 and 8192. *done = false for
-// wider rows.
+// Rows of single elements (a width or base that is not 16-byte granular). First choice: the
+// fewest elements per thread K (1, 2, 4, 8 or 16) whose block has at most 256 threads and
+// leaves only a thread's last element past the row's end, so that several rows are in
+// flight per compute unit (add-RMSNorm: bf16 rows at K <= 8 only). Otherwise RMSNorm and
+// LayerNorm rows up to 12288 take K = 4, 2 or 1 up to 4096 (blocks of up to 1024 threads), 8
+// up to 8192 and 12 above, and add-RMSNorm rows the looping kernel (*done = false). On
+// MI355X (us, against K = 4 in blocks of up to 1024 threads, and add-RMSNorm on the looping
+// kernel): RMSNorm bf16 [16384, 2047] 40.2 -> 31.4, [8192, 4095] 43.0 -> 32.8, LayerNorm bf16
+// 64.5 -> 44.0 and 72.5 -> 38.3, fp32 [8192, 2047] 37.5 -> 29.0, [4096, 4095] 40.0 -> 29.0;
+// add-RMSNorm bf16 [33520, 1001] 82.5 -> 65.9, [16384, 2047] 75.8 -> 63.7. add-RMSNorm here
+// measured no faster at 16 per thread (bf16 [8192, 4095] 72.1 against 72.8) nor in fp32
+// ([8192, 2047] 51.1 against 56.0), nor at [8184, 4100] bf16 with 576 threads per row (44%
+// of peak on the looping kernel, 40% here).
 template <bool BF16, int OP>
 hipError_t try_rowelems(const RowArgs& a, hipStream_t stream, bool* done) {
   const int64_t n = a.hidden;
-  *done = n <= 12288;
-  if (!*done) return hipSuccess;
-  auto fits = [n](int64_t k) {
-    const int64_t t = ((n + k - 1) / k + 63) / 64 * 64;
-    return t * (k - 1) <= n && t <= 1024;
+  *done = true;
+  auto threads = [n](int64_t k) { return ((n + k - 1) / k + 63) / 64 * 64; };
+  auto small = [&](int64_t k) {
+    if (OP == OP_ADD_RMS && (!BF16 || k > 8)) return false;
+    return threads(k) <= 256 && threads(k) * (k - 1) <= n;
   };
+  if (small(1)) return go_rowelems<BF16, OP, 1>(a, stream);
+  if (small(2)) return go_rowelems<BF16, OP, 2>(a, stream);
+  if (small(4)) return go_rowelems<BF16, OP, 4>(a, stream);
+  if (small(8)) return go_rowelems<BF16, OP, 8>(a, stream);
+  if (small(16)) return go_rowelems<BF16, OP, 16>(a, stream);
+  *done = OP != OP_ADD_RMS && n <= 12288;
+  if (!*done) return hipSuccess;
+  auto fits = [&](int64_t k) { return threads(k) * (k - 1) <= n && threads(k) <= 1024; };
   if (n > 8192) return go_rowelems<BF16, OP, 12>(a, stream);
   if (n > 4096) return go_rowelems<BF16, OP, 8>(a, stream);
   if (fits(4)) return go_rowelems<BF16, OP, 4>(a, stream);
@@ -326,14 +343,10 @@ hipError_t launch_row_once(const RowArgs& a, bool aligned16, hipStream_t stream)
   const int path = forced_path();
   const bool vec = aligned16 && a.hidden % V == 0 && path != PATH_SCALAR;
   if (!vec) {
-    // add-RMSNorm (two loads and two stores of single elements) keeps the looping kernel:
-    // at [8184, 4100] bf16 it streams at 44% of peak there against 40% in row_elems.
-    if constexpr (OP != OP_ADD_RMS) {
-      if (path == PATH_AUTO) {
-        bool done = false;
-        const hipError_t e = try_rowelems<BF16, OP>(a, stream, &done);
-        if (done) return e;
-      }
+    if (path == PATH_AUTO) {
+      bool done = false;
+      const hipError_t e = try_rowelems<BF16, OP>(a, stream, &done);
+      if (done) return e;
     }
     return go_chunked<BF16, OP, 1>(a, stream);
   }
