@@ -120,14 +120,16 @@ def test_rms_norm_row_pairs(nrm_lib, dt, wdt, hidden):
 
 
 # Widths that are not whole 16-byte chunks: one block per row of at most 256 threads with 1
-# (33, 100), 2 (300), 4 (1001), 8 (2047) or 16 (3000, 4095) elements per thread; RMSNorm and
-# LayerNorm rows over 4096 with 8 (up to 8192) or 12 (up to 12288) per thread, add-RMSNorm
-# there with 16 (4100: 320 threads, the last three of a thread's elements past the row's end
-# in most threads); 12289 takes the looping kernel.
-ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 300), ("bf16", 1001), ("bf16", 2047),
-         ("bf16", 3000), ("bf16", 4095), ("bf16", 4100), ("bf16", 8191), ("bf16", 10001),
-         ("bf16", 12287), ("bf16", 12289), ("f32", 1001), ("f32", 2047), ("f32", 4097),
-         ("f32", 12285)]
+# (33, 100), 2 (300, 521: 320 threads for RMSNorm and LayerNorm) or 4 (1001) elements per
+# thread, and ceil(hidden / 256) from 1025 to 4096 (1100: 5, 1300: 6, 1537: 7, 2047: 8,
+# 2500: 10, 3000: 12, 3500: 14, 4095: 16; add-RMSNorm up to 2048 in bf16); RMSNorm and
+# LayerNorm rows over 4096 with 8 (up to 8192) or 12 (up to 12288) per thread; add-RMSNorm
+# rows otherwise, and 12289, take the looping kernel.
+ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 300), ("bf16", 521), ("bf16", 1001),
+         ("bf16", 1100), ("bf16", 1300), ("bf16", 1537), ("bf16", 2047), ("bf16", 2500),
+         ("bf16", 3000), ("bf16", 3500), ("bf16", 4095), ("bf16", 4100), ("bf16", 8191),
+         ("bf16", 10001), ("bf16", 12287), ("bf16", 12289), ("f32", 1001), ("f32", 2047),
+         ("f32", 3333), ("f32", 4097), ("f32", 12285)]
 
 
 @pytest.mark.parametrize("dt,hidden", ELEMS)

@@ -75,34 +75,46 @@ hipError_t go_rowelems(const RowArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Rows of single elements (a width or base that is not 16-byte granular). First choice: the
-// fewest elements per thread K (1, 2, 4, 8 or 16) whose block has at most 256 threads and
-// leaves only a thread's last element past the row's end, so that several rows are in
-// flight per compute unit (add-RMSNorm: bf16 rows at K <= 8 only). Otherwise RMSNorm and
-// LayerNorm rows up to 12288 take K = 4, 2 or 1 up to 4096 (blocks of up to 1024 threads), 8
-// up to 8192 and 12 above, and add-RMSNorm rows the looping kernel (*done = false). On
-// MI355X (us, against K = 4 in blocks of up to 1024 threads, and add-RMSNorm on the looping
-// kernel): RMSNorm bf16 [16384, 2047] 40.2 -> 31.4, [8192, 4095] 43.0 -> 32.8, LayerNorm bf16
-// 64.5 -> 44.0 and 72.5 -> 38.3, fp32 [8192, 2047] 37.5 -> 29.0, [4096, 4095] 40.0 -> 29.0;
-// add-RMSNorm bf16 [33520, 1001] 82.5 -> 65.9, [16384, 2047] 75.8 -> 63.7. add-RMSNorm here
-// measured no faster at 16 per thread (bf16 [8192, 4095] 72.1 against 72.8) nor in fp32
-// ([8192, 2047] 51.1 against 56.0), nor at [8184, 4100] bf16 with 576 threads per row (44%
-// of peak on the looping kernel, 40% here).
+// row_elems with k elements per thread, k in [K, KMAX], picked at run time.
+template <bool BF16, int OP, int K, int KMAX>
+hipError_t go_rowelems_k(const RowArgs& a, int k, hipStream_t stream) {
+  if (k == K) return go_rowelems<BF16, OP, K>(a, stream);
+  if constexpr (K < KMAX) return go_rowelems_k<BF16, OP, K + 1, KMAX>(a, k, stream);
+  return hipErrorInvalidConfiguration;
+}
+
+// Rows of single elements (a width or base that is not 16-byte granular), in blocks of at
+// most 256 threads where possible, so that several rows are in flight per compute unit:
+// rows of 1025 to 4096 take K = ceil(n / 256) elements per thread (5 to 16) in blocks of 256
+// (then only a thread's last element can be past the row's end); narrower rows the fewest K
+// of 1, 2 or 4 whose block has at most 256 threads with the same property. add-RMSNorm takes
+// these shapes for bf16 rows up to 2048 only. Otherwise RMSNorm and LayerNorm rows up to
+// 12288 take K = 4, 2 or 1 (blocks of up to 1024 threads) up to 4096, 8 up to 8192 and 12
+// above, and add-RMSNorm rows the looping kernel (*done = false). On MI355X (us, against K =
+// 4 or 8 in blocks of up to 1024 threads, and add-RMSNorm on the looping kernel): RMSNorm bf16
+// [16384, 1300] 35.7 -> 24.9, [12288, 2500] 46.4 -> 29.1, [8192, 4095] 43.0 -> 33.0,
+// LayerNorm bf16 53.5 -> 38.9, 69.2 -> 37.5 and 72.5 -> 36.2, fp32 [4096, 4095] 38.3 -> 28.9;
+// add-RMSNorm bf16 [16384, 1300] 56.3 -> 44.2, [33520, 1001] 82.5 -> 64.6, [16384, 2047]
+// 75.8 -> 63.7. add-RMSNorm here measured no faster
+// at 16 per thread (bf16 [8192, 4095] 72.1 against 72.8) nor in fp32 ([8192, 2047] 51.1
+// against 56.0), nor at [8184, 4100] bf16 with 576 threads per row (44% of peak on the looping
+// kernel, 40% here).
 template <bool BF16, int OP>
 hipError_t try_rowelems(const RowArgs& a, hipStream_t stream, bool* done) {
   const int64_t n = a.hidden;
   *done = true;
+  constexpr bool ADD = OP == OP_ADD_RMS;
+  if (n > 1024 && n <= (ADD ? 2048 : 4096) && (!ADD || BF16))
+    return go_rowelems_k<BF16, OP, 5, ADD ? 8 : 16>(a, (int)((n + 255) / 256), stream);
   auto threads = [n](int64_t k) { return ((n + k - 1) / k + 63) / 64 * 64; };
   auto small = [&](int64_t k) {
-    if (OP == OP_ADD_RMS && (!BF16 || k > 8)) return false;
+    if (ADD && !BF16) return false;
     return threads(k) <= 256 && threads(k) * (k - 1) <= n;
   };
   if (small(1)) return go_rowelems<BF16, OP, 1>(a, stream);
   if (small(2)) return go_rowelems<BF16, OP, 2>(a, stream);
   if (small(4)) return go_rowelems<BF16, OP, 4>(a, stream);
-  if (small(8)) return go_rowelems<BF16, OP, 8>(a, stream);
-  if (small(16)) return go_rowelems<BF16, OP, 16>(a, stream);
-  *done = OP != OP_ADD_RMS && n <= 12288;
+  *done = !ADD && n <= 12288;
   if (!*done) return hipSuccess;
   auto fits = [&](int64_t k) { return threads(k) * (k - 1) <= n && threads(k) <= 1024; };
   if (n > 8192) return go_rowelems<BF16, OP, 12>(a, stream);
