@@ -123,11 +123,12 @@ def test_rms_norm_row_pairs(nrm_lib, dt, wdt, hidden):
 # (33, 100), 2 (300, 521: 320 threads for RMSNorm and LayerNorm) or 4 (1001) elements per
 # thread, and ceil(hidden / 256) from 1025 to 4096 (1100: 5, 1300: 6, 1537: 7, 2047: 8,
 # 2500: 10, 3000: 12, 3500: 14, 4095: 16; add-RMSNorm up to 2048 in bf16); RMSNorm and
-# LayerNorm rows over 4096 with 8 (up to 8192) or 12 (up to 12288) per thread; add-RMSNorm
-# rows otherwise, and 12289, take the looping kernel.
+# LayerNorm rows of 4097 to 8192 with ceil(hidden / 512) per thread in blocks of 512 (4100
+# and 4097: 9, 6500: 13, 8191: 16), wider rows with 12; add-RMSNorm rows otherwise, and
+# 12289, take the looping kernel.
 ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 300), ("bf16", 521), ("bf16", 1001),
          ("bf16", 1100), ("bf16", 1300), ("bf16", 1537), ("bf16", 2047), ("bf16", 2500),
-         ("bf16", 3000), ("bf16", 3500), ("bf16", 4095), ("bf16", 4100), ("bf16", 8191),
+         ("bf16", 3000), ("bf16", 3500), ("bf16", 4095), ("bf16", 4100), ("bf16", 6500), ("bf16", 8191),
          ("bf16", 10001), ("bf16", 12287), ("bf16", 12289), ("f32", 1001), ("f32", 2047),
          ("f32", 3333), ("f32", 4097), ("f32", 12285)]
 
