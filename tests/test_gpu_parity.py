@@ -124,8 +124,9 @@ def test_rms_norm_row_pairs(nrm_lib, dt, wdt, hidden):
 # thread, and ceil(hidden / 256) from 1025 to 4096 (1100: 5, 1300: 6, 1537: 7, 2047: 8,
 # 2500: 10, 3000: 12, 3500: 14, 4095: 16; add-RMSNorm up to 2048 in bf16); RMSNorm and
 # LayerNorm rows of 4097 to 8192 with ceil(hidden / 512) per thread in blocks of 512 (4100
-# and 4097: 9, 6500: 13, 8191: 16), wider rows with 12; add-RMSNorm rows otherwise, and
-# 12289, take the looping kernel.
+# and 4097: 9, 6500: 13, 8191: 16), rows up to 12288 with ceil(hidden / 768) in blocks of up
+# to 768 (10001: 14, 12285 and 12287: 16); add-RMSNorm rows otherwise, and 12289, take the
+# looping kernel.
 ELEMS = [("bf16", 33), ("bf16", 100), ("bf16", 300), ("bf16", 521), ("bf16", 1001),
          ("bf16", 1100), ("bf16", 1300), ("bf16", 1537), ("bf16", 2047), ("bf16", 2500),
          ("bf16", 3000), ("bf16", 3500), ("bf16", 4095), ("bf16", 4100), ("bf16", 6500), ("bf16", 8191),

@@ -83,24 +83,24 @@ hipError_t go_rowelems_k(const RowArgs& a, int k, hipStream_t stream) {
   return hipErrorInvalidConfiguration;
 }
 
-// Rows of single elements (a width or base that is not 16-byte granular), in blocks of at
-// most 256 threads where possible, so that several rows are in flight per compute unit:
-// rows of 1025 to 4096 take K = ceil(n / 256) elements per thread (5 to 16) in blocks of 256
-// (then only a thread's last element can be past the row's end); narrower rows the fewest K
-// of 1, 2 or 4 whose block has at most 256 threads with the same property. add-RMSNorm takes
-// these shapes for bf16 rows up to 2048 only. Otherwise RMSNorm and LayerNorm rows up to
-// 4096 take K = 4, 2 or 1 (blocks of up to 1024 threads), rows of 4097 to 8192 K = ceil(n /
-// 512) (9 to 16) in blocks of 512 (bf16 [5000, 6500] RMSNorm 36.6 -> 31.7 us, LayerNorm
-// 61.0 -> 43.2 us against K = 8 in blocks of up to 1024), wider rows K = 12; add-RMSNorm rows
-// the looping kernel (*done = false). On MI355X (us, against K = 4 or 8 in blocks of up to
-// 1024 threads, and add-RMSNorm on the looping kernel): RMSNorm bf16
-// [16384, 1300] 35.7 -> 24.9, [12288, 2500] 46.4 -> 29.1, [8192, 4095] 43.0 -> 33.0,
-// LayerNorm bf16 53.5 -> 38.9, 69.2 -> 37.5 and 72.5 -> 36.2, fp32 [4096, 4095] 38.3 -> 28.9;
-// add-RMSNorm bf16 [16384, 1300] 56.3 -> 44.2, [33520, 1001] 82.5 -> 64.6, [16384, 2047]
-// 75.8 -> 63.7. add-RMSNorm here measured no faster
-// at 16 per thread (bf16 [8192, 4095] 72.1 against 72.8) nor in fp32 ([8192, 2047] 51.1
-// against 56.0), nor at [8184, 4100] bf16 with 576 threads per row (44% of peak on the looping
-// kernel, 40% here).
+// Rows of single elements (a width or base that is not 16-byte granular), in blocks of at most
+// 256 threads where possible, so that several rows are in flight per compute unit: rows of 1025
+// to 4096 take K = ceil(n / 256) elements per thread (5 to 16) in blocks of 256 (then only a
+// thread's last element can be past the row's end); narrower rows the fewest K of 1, 2 or 4 whose
+// block has at most 256 threads with the same property. add-RMSNorm takes these shapes for bf16
+// rows up to 2048 only. Otherwise RMSNorm and LayerNorm rows up to 4096 take K = 4, 2 or 1
+// (blocks of up to 1024 threads), rows of 4097 to 8192 K = ceil(n / 512) (9 to 16) in blocks of
+// 512 (bf16 [5000, 6500] RMSNorm 36.6 -> 31.7 us, LayerNorm 61.0 -> 43.2 us against K = 8 in
+// blocks of up to 1024), rows of 8193 to 12288 K = ceil(n / 768) (11 to 16) in blocks of up to
+// 768 (bf16 [3000, 10001] LayerNorm 61.2 -> 40.7 us against K = 12 in blocks of up to 1024);
+// add-RMSNorm rows the looping kernel (*done = false). On MI355X (us, against K = 4 or 8 in
+// blocks of up to 1024 threads, and add-RMSNorm on the looping kernel): RMSNorm bf16 [16384,
+// 1300] 35.7 -> 24.9, [12288, 2500] 46.4 -> 29.1, [8192, 4095] 43.0 -> 33.0, LayerNorm bf16 53.5
+// -> 38.9, 69.2 -> 37.5 and 72.5 -> 36.2, fp32 [4096, 4095] 38.3 -> 28.9; add-RMSNorm bf16
+// [16384, 1300] 56.3 -> 44.2, [33520, 1001] 82.5 -> 64.6, [16384, 2047] 75.8 -> 63.7. add-RMSNorm
+// here measured no faster at 16 per thread (bf16 [8192, 4095] 72.1 against 72.8) nor in fp32
+// ([8192, 2047] 51.1 against 56.0), nor at [8184, 4100] bf16 with 576 threads per row (44% of
+// peak on the looping kernel, 40% here).
 template <bool BF16, int OP>
 hipError_t try_rowelems(const RowArgs& a, hipStream_t stream, bool* done) {
   const int64_t n = a.hidden;
@@ -119,7 +119,7 @@ hipError_t try_rowelems(const RowArgs& a, hipStream_t stream, bool* done) {
   *done = !ADD && n <= 12288;
   if (!*done) return hipSuccess;
   auto fits = [&](int64_t k) { return threads(k) * (k - 1) <= n && threads(k) <= 1024; };
-  if (n > 8192) return go_rowelems<BF16, OP, 12>(a, stream);
+  if (n > 8192) return go_rowelems_k<BF16, OP, 11, 16>(a, (int)((n + 767) / 768), stream);
   if (n > 4096) return go_rowelems_k<BF16, OP, 9, 16>(a, (int)((n + 511) / 512), stream);
   if (fits(4)) return go_rowelems<BF16, OP, 4>(a, stream);
   if (fits(2)) return go_rowelems<BF16, OP, 2>(a, stream);
